@@ -1,0 +1,191 @@
+"""One token-skipping denoising iteration, step by step (test infrastructure).
+
+Order of operations (ES-dLLM technical summary 2.1; SureLock 2.1):
+  1. embed the current tokens;
+  2. run layers below the boundary b on every position (on a full step, every
+     layer runs on every position);
+  3. at layer b, score every position from the previous iteration's
+     confidence (or KL) and the change of the hidden state entering layer b
+     since the previous iteration (Eq. 1), keep that hidden state for the next
+     iteration, and select the active rows;
+  4. run layers b..L-1 on the active rows only: their fresh K/V overwrite the
+     cache rows, and they attend over the whole cache, so skipped positions
+     contribute the K/V cached when they were last computed;
+  5. write the active rows' final hidden state, run the LM head on them and
+     compute confidence, argmax and local KL; skipped positions keep all of
+     their previous statistics;
+  6. SureLock lock update and/or confidence unmasking of the current block.
+
+Readings where the pages leave a step open: one boundary per iteration; the
+mask id is the last vocabulary entry and is excluded from softmax and argmax;
+a locked row (force == 2) skips every layer and the LM head, its cached K/V
+stay attendable; step 0 has no previous posterior, so its KL is +inf.
+"""
+from __future__ import annotations
+
+from dataclasses import dataclass, field
+
+import numpy as np
+
+from .importance import VAR_L1N, importance_score
+from .numerics import store_fn
+from .post import surelock_update, unmask_topn
+from .selection import FORCE_EXCLUDED, select_thresh_cap, select_topk
+from .transformer import layer_rows, lm_logits
+from .vocab import conf_kl
+
+SEL_TOPK, SEL_THRESH_CAP, SEL_UNLOCKED = 0, 1, 2
+
+
+@dataclass
+class OracleModel:
+    weights: dict
+    n_heads: int
+    n_kv_heads: int
+    mask_id: int
+    mode: str = "bf16"
+    rope_base: float = 10000.0
+    eps: float = 1e-5
+
+    @property
+    def n_layers(self) -> int:
+        return len(self.weights["layers"])
+
+
+@dataclass
+class ScoreCfg:
+    alpha: float = 0.5
+    conf_inverted: bool = False
+    var: int = VAR_L1N
+    sel: int = SEL_TOPK
+    k: int = 1
+    tau: float = 0.0
+
+
+@dataclass
+class StepCfg:
+    boundary_layer: int
+    full_step: bool
+    score: ScoreCfg = field(default_factory=ScoreCfg)
+    lock_kl_eps: float = -1.0      # < 0 disables locking
+    lock_conf_min: float = 0.9
+    unmask_n: int = 0
+    block_lo: int = 0
+    block_hi: int = 0
+
+
+@dataclass
+class OracleState:
+    tokens: np.ndarray
+    k_cache: list
+    v_cache: list
+    h_bnd_prev: np.ndarray | None
+    h_fin: np.ndarray
+    conf: np.ndarray
+    kl: np.ndarray
+    argmax: np.ndarray
+    logits_prev: np.ndarray | None
+    force: np.ndarray
+    have_prev: bool = False
+
+    def copy(self) -> "OracleState":
+        return OracleState(
+            self.tokens.copy(), [k.copy() for k in self.k_cache], [v.copy() for v in self.v_cache],
+            None if self.h_bnd_prev is None else self.h_bnd_prev.copy(), self.h_fin.copy(),
+            self.conf.copy(), self.kl.copy(), self.argmax.copy(),
+            None if self.logits_prev is None else self.logits_prev.copy(), self.force.copy(), self.have_prev)
+
+
+def new_state(model: OracleModel, tokens: np.ndarray, track_kl: bool) -> OracleState:
+    B, S = tokens.shape
+    w = model.weights
+    d = w["embed"].shape[1]
+    V = w["embed"].shape[0]
+    D = w["layers"][0]["wq"].shape[0] // model.n_heads
+    Hkv = model.n_kv_heads
+    L = model.n_layers
+    return OracleState(
+        tokens=np.array(tokens, dtype=np.int64),
+        k_cache=[np.zeros((B, S, Hkv, D)) for _ in range(L)],
+        v_cache=[np.zeros((B, S, Hkv, D)) for _ in range(L)],
+        h_bnd_prev=None,
+        h_fin=np.zeros((B, S, d)),
+        conf=np.zeros((B, S)),
+        kl=np.full((B, S), np.inf),
+        argmax=np.zeros((B, S), dtype=np.int64),
+        logits_prev=np.zeros((B * S, V)) if track_kl else None,
+        force=np.zeros((B, S), dtype=np.uint8),
+    )
+
+
+def _select(scfg: ScoreCfg, scores: np.ndarray, force: np.ndarray) -> np.ndarray:
+    if scfg.sel == SEL_TOPK:
+        return select_topk(scores, force, scfg.k)
+    if scfg.sel == SEL_THRESH_CAP:
+        return select_thresh_cap(scores, force, scfg.tau, scfg.k)
+    if scfg.sel == SEL_UNLOCKED:
+        return select_topk(scores, force, len(scores))
+    raise ValueError(f"unknown selection mode {scfg.sel}")
+
+
+def skip_step(model: OracleModel, st: OracleState, cfg: StepCfg) -> tuple[OracleState, dict]:
+    """Run one iteration; returns the new state and {"rows", "scores"}."""
+    st = st.copy()
+    store = store_fn(model.mode)
+    w = model.weights
+    B, S = st.tokens.shape
+    d = w["embed"].shape[1]
+    L = model.n_layers
+    b_lay = int(cfg.boundary_layer)
+    if not (0 <= b_lay <= L):
+        raise ValueError("boundary layer out of range")
+    full = bool(cfg.full_step)
+    if not full and st.h_bnd_prev is None:
+        raise ValueError("a sparse step needs the previous boundary hidden state")
+
+    x = w["embed"][st.tokens.reshape(-1)].reshape(B * S, d).copy()
+    rows = np.arange(B * S)                   # flat b*S + i of the rows being computed
+    scores = None
+    h_bnd_new = None
+
+    def boundary():
+        nonlocal rows, x, scores, h_bnd_new
+        h_bnd_new = x.reshape(B, S, d).copy()
+        if full:
+            return
+        s = importance_score(x, st.h_bnd_prev.reshape(B * S, d), st.conf.reshape(-1), st.kl.reshape(-1),
+                             alpha=cfg.score.alpha, var=cfg.score.var, conf_inverted=cfg.score.conf_inverted)
+        scores = s.reshape(B, S)
+        sel = [b * S + _select(cfg.score, scores[b], st.force[b]) for b in range(B)]
+        rows = np.concatenate(sel).astype(np.int64)
+        x = x[rows].copy()
+
+    for l in range(L):
+        if l == b_lay:
+            boundary()
+        lw = w["layers"][l]
+        x = layer_rows(lw, x, rows % S, rows // S, st.k_cache[l], st.v_cache[l],
+                       n_heads=model.n_heads, n_kv_heads=model.n_kv_heads,
+                       rope_base=model.rope_base, eps=model.eps, store=store)
+    if b_lay == L:
+        boundary()
+
+    st.h_bnd_prev = h_bnd_new
+    hf = st.h_fin.reshape(B * S, d)
+    hf[rows] = x
+    z = lm_logits(x, w["final_norm"], w["lm_head"], model.eps, store)
+    zp = None if (st.logits_prev is None or not st.have_prev) else st.logits_prev[rows]
+    conf, arg, kl = conf_kl(z, zp, model.mask_id)
+    st.conf.reshape(-1)[rows] = conf
+    st.argmax.reshape(-1)[rows] = arg
+    st.kl.reshape(-1)[rows] = kl
+    if st.logits_prev is not None:
+        st.logits_prev[rows] = z
+    if cfg.lock_kl_eps >= 0:
+        st.force = surelock_update(st.force.reshape(-1), rows, st.conf.reshape(-1), st.kl.reshape(-1),
+                                   st.have_prev, cfg.lock_kl_eps, cfg.lock_conf_min).reshape(B, S)
+    if cfg.unmask_n > 0:
+        st.tokens = unmask_topn(st.tokens, st.conf, st.argmax, model.mask_id,
+                                cfg.block_lo, cfg.block_hi, cfg.unmask_n)
+    st.have_prev = True
+    return st, {"rows": rows, "scores": scores, "logits": z}

@@ -1,0 +1,212 @@
+"""Whole-iteration pins of the oracle (CPU only, exact float64 mode).
+
+P1  with every row active, the partial update equals dense recompute;
+P2  skipped rows keep their cached K/V, final hidden state and statistics bit for bit;
+P5  if nothing changed since the cache was filled, active rows equal dense recompute;
+P6  the LM head on every row of the final hidden state reproduces the cached statistics;
+plus SureLock locking (locked rows are never recomputed yet stay attended).
+"""
+import numpy as np
+import pytest
+
+from oracle import dense_forward, lm_logits, conf_kl, layer_rows
+from oracle.importance import VAR_COS, VAR_L1N
+from oracle.step import (SEL_THRESH_CAP, SEL_TOPK, SEL_UNLOCKED, OracleModel, ScoreCfg,
+                         StepCfg, new_state, skip_step)
+
+L, d, Hq, Hkv, D, F, V, B, S = 3, 32, 4, 2, 8, 48, 41, 2, 12
+MASK = V - 1
+
+
+def tiny_model(seed=0, mode="exact"):
+    rng = np.random.default_rng(seed)
+    def w(*shape, std=0.3):
+        return rng.standard_normal(shape) * std
+    layers = []
+    for _ in range(L):
+        layers.append({"attn_norm": 1.0 + 0.1 * w(d), "wq": w(Hq * D, d), "wk": w(Hkv * D, d),
+                       "wv": w(Hkv * D, d), "wo": w(d, Hq * D), "ffn_norm": 1.0 + 0.1 * w(d),
+                       "wg": w(F, d), "wu": w(F, d), "wd": w(d, F)})
+    weights = {"embed": w(V, d, std=1.0), "layers": layers, "final_norm": 1.0 + 0.1 * w(d), "lm_head": w(V, d)}
+    return OracleModel(weights, Hq, Hkv, MASK, mode=mode)
+
+
+def tokens(seed=1, n_prompt=6):
+    rng = np.random.default_rng(seed)
+    t = rng.integers(0, V - 1, (B, S))
+    t[:, n_prompt:] = MASK
+    return t
+
+
+def dense(model, tok, b=None):
+    return dense_forward(model.weights, tok, n_heads=Hq, n_kv_heads=Hkv, rope_base=model.rope_base,
+                         eps=model.eps, store=lambda v: v, boundary_layer=b)
+
+
+def full_step(model, tok, b, track_kl=True):
+    st = new_state(model, tok, track_kl)
+    return skip_step(model, st, StepCfg(boundary_layer=b, full_step=True))
+
+
+def test_full_step_equals_dense():
+    m = tiny_model()
+    tok = tokens()
+    st, _ = full_step(m, tok, 1)
+    ref = dense(m, tok, 1)
+    for l in range(L):
+        np.testing.assert_allclose(st.k_cache[l], ref["k"][l], rtol=1e-12, atol=1e-12)
+        np.testing.assert_allclose(st.v_cache[l], ref["v"][l], rtol=1e-12, atol=1e-12)
+    np.testing.assert_allclose(st.h_fin, ref["h_fin"], rtol=1e-12, atol=1e-12)
+    np.testing.assert_allclose(st.h_bnd_prev, ref["h_bnd"], rtol=1e-12, atol=1e-12)
+    conf, arg, _ = conf_kl(ref["logits"].reshape(B * S, V), None, MASK)
+    np.testing.assert_allclose(st.conf.reshape(-1), conf, rtol=1e-12)
+    np.testing.assert_array_equal(st.argmax.reshape(-1), arg)
+
+
+@pytest.mark.parametrize("b", [0, 1, 3])
+def test_p1_all_rows_active_equals_dense(b):
+    m = tiny_model(3)
+    tok0 = tokens(4)
+    st, _ = full_step(m, tok0, b)
+    tok1 = tok0.copy()
+    tok1[:, 7] = 5                     # the input changed since the cache was filled
+    st.tokens = tok1
+    cfg = StepCfg(boundary_layer=b, full_step=False, score=ScoreCfg(alpha=0.5, var=VAR_L1N, k=S))
+    st2, info = skip_step(m, st, cfg)
+    assert len(info["rows"]) == B * S
+    ref = dense(m, tok1, b)
+    np.testing.assert_allclose(st2.h_fin, ref["h_fin"], rtol=1e-11, atol=1e-11)
+    for l in range(L):
+        np.testing.assert_allclose(st2.k_cache[l], ref["k"][l], rtol=1e-11, atol=1e-11)
+    np.testing.assert_allclose(info["logits"], ref["logits"].reshape(B * S, V), rtol=1e-10, atol=1e-10)
+
+
+@pytest.mark.parametrize("b", [0, 2])
+def test_p2_skipped_rows_bytes_unchanged(b):
+    m = tiny_model(5)
+    tok0 = tokens(6)
+    st, _ = full_step(m, tok0, b)
+    st.tokens[:, 8] = 3
+    k = 4
+    cfg = StepCfg(boundary_layer=b, full_step=False, score=ScoreCfg(alpha=0.5, var=VAR_COS, conf_inverted=True, k=k))
+    st2, info = skip_step(m, st, cfg)
+    rows = info["rows"]
+    assert len(rows) == B * k
+    skipped = np.setdiff1d(np.arange(B * S), rows)
+    for l in range(b, L):
+        for before, after in ((st.k_cache[l], st2.k_cache[l]), (st.v_cache[l], st2.v_cache[l])):
+            fb = before.reshape(B * S, -1)
+            fa = after.reshape(B * S, -1)
+            assert np.array_equal(fb[skipped], fa[skipped])
+            assert not np.array_equal(fb[rows], fa[rows])
+    for name in ("h_fin", "conf", "kl", "argmax"):
+        fb = getattr(st, name).reshape(B * S, -1)
+        fa = getattr(st2, name).reshape(B * S, -1)
+        assert np.array_equal(fb[skipped], fa[skipped]), name
+    assert np.array_equal(st.logits_prev[skipped], st2.logits_prev[skipped])
+    # layers below the boundary were recomputed on every row
+    if b > 0:
+        assert not np.array_equal(st.k_cache[0], st2.k_cache[0])
+
+
+def test_p5_unchanged_input_sparse_equals_dense_on_active_rows():
+    m = tiny_model(7)
+    tok = tokens(8)
+    st, _ = full_step(m, tok, 1)
+    cfg = StepCfg(boundary_layer=1, full_step=False, score=ScoreCfg(alpha=0.3, var=VAR_L1N, k=5))
+    st2, info = skip_step(m, st, cfg)
+    ref = dense(m, tok, 1)
+    rows = info["rows"]
+    np.testing.assert_allclose(st2.h_fin.reshape(B * S, d)[rows], ref["h_fin"].reshape(B * S, d)[rows], rtol=1e-11, atol=1e-12)
+    np.testing.assert_allclose(info["logits"], ref["logits"].reshape(B * S, V)[rows], rtol=1e-10, atol=1e-11)
+    # the importance change term is zero on every row: the ranking follows confidence
+    np.testing.assert_allclose(info["scores"], 0.3 * st.conf.astype(np.float32), rtol=1e-6)
+
+
+def test_p6_lm_head_on_all_rows_reproduces_statistics():
+    m = tiny_model(9)
+    tok = tokens(10)
+    st, _ = full_step(m, tok, 2)
+    st.tokens[:, 9] = 1
+    st2, info = skip_step(m, st, StepCfg(boundary_layer=2, full_step=False, score=ScoreCfg(k=3)))
+    z = lm_logits(st2.h_fin.reshape(B * S, d), m.weights["final_norm"], m.weights["lm_head"], m.eps, lambda v: v)
+    conf, arg, _ = conf_kl(z, None, MASK)
+    np.testing.assert_allclose(conf, st2.conf.reshape(-1), rtol=1e-13)
+    np.testing.assert_array_equal(arg, st2.argmax.reshape(-1))
+    np.testing.assert_allclose(z, st2.logits_prev, rtol=1e-13)
+
+
+def test_kl_zero_when_input_unchanged_and_lock():
+    m = tiny_model(11)
+    tok = tokens(12)
+    st, _ = full_step(m, tok, 0)
+    assert np.all(np.isinf(st.kl))
+    cfg = StepCfg(boundary_layer=0, full_step=False, score=ScoreCfg(sel=SEL_UNLOCKED, alpha=0.0, var=VAR_L1N),
+                  lock_kl_eps=1e-12, lock_conf_min=-1.0)
+    st2, info = skip_step(m, st, cfg)
+    # same tokens, every row recomputed: every posterior is identical, KL = 0, all rows lock
+    np.testing.assert_allclose(st2.kl, 0.0, atol=1e-12)
+    assert np.all(st2.force == 2)
+
+
+def test_locked_rows_skip_compute_but_stay_attended():
+    m = tiny_model(13)
+    tok = tokens(14)
+    st, _ = full_step(m, tok, 0)
+    st.force[:, :4] = 2                     # lock the first four positions of each sequence
+    st.tokens[:, 10] = 2                     # change the input of an unlocked position
+    cfg = StepCfg(boundary_layer=0, full_step=False, score=ScoreCfg(sel=SEL_UNLOCKED))
+    st2, info = skip_step(m, st, cfg)
+    rows = info["rows"]
+    assert len(rows) == B * (S - 4) and np.all(rows % S >= 4)
+    for l in range(L):
+        assert np.array_equal(st.k_cache[l][:, :4], st2.k_cache[l][:, :4])
+    # reference: attention of the active rows over cache rows whose first four positions
+    # hold the K/V computed when the rows were last run
+    x = m.weights["embed"][st.tokens.reshape(-1)][rows]
+    kc = [k.copy() for k in st.k_cache]
+    vc = [v.copy() for v in st.v_cache]
+    for l in range(L):
+        x = layer_rows(m.weights["layers"][l], x, rows % S, rows // S, kc[l], vc[l], n_heads=Hq,
+                       n_kv_heads=Hkv, rope_base=m.rope_base, eps=m.eps, store=lambda v: v)
+    np.testing.assert_allclose(st2.h_fin.reshape(B * S, d)[rows], x, rtol=1e-13)
+    # and this differs from a dense recompute (the locked rows' stale K/V matter)
+    ref = dense(m, st.tokens)
+    assert not np.allclose(st2.h_fin.reshape(B * S, d)[rows], ref["h_fin"].reshape(B * S, d)[rows], rtol=1e-9)
+
+
+def test_thresh_cap_step_and_unmask():
+    m = tiny_model(15)
+    tok = tokens(16)
+    st, _ = full_step(m, tok, 1)
+    st.force[:, :6] = 2                       # prompt rows excluded
+    st.force[:, 8] = 1                        # forced row
+    st.tokens[:, 7] = 4
+    cfg = StepCfg(boundary_layer=1, full_step=False,
+                  score=ScoreCfg(alpha=0.0, var=VAR_COS, sel=SEL_THRESH_CAP, tau=1e-3, k=3),
+                  unmask_n=2, block_lo=6, block_hi=12)
+    st2, info = skip_step(m, st, cfg)
+    rows = info["rows"]
+    for bb in range(B):
+        r = rows[rows // S == bb] % S
+        assert 8 in r and len(r) <= 3 and np.all(r >= 6)
+    # unmask picked the two most confident masked positions of the block
+    for bb in range(B):
+        changed = np.nonzero(st2.tokens[bb] != st.tokens[bb])[0]
+        assert len(changed) == 2 and np.all((changed >= 6) & (changed < 12))
+        masked = [i for i in range(6, 12) if st.tokens[bb, i] == MASK]
+        order = sorted(masked, key=lambda i: (-st2.conf[bb, i], i))
+        assert sorted(order[:2]) == changed.tolist()
+
+
+def test_bf16_mode_close_to_exact():
+    me = tiny_model(17, "exact")
+    mb = tiny_model(17, "bf16")
+    from oracle.numerics import round_bf16
+    for mm in (me, mb):   # bf16-valued weights for both
+        mm.weights["embed"] = round_bf16(mm.weights["embed"])
+    tok = tokens(18)
+    se, _ = full_step(me, tok, 1)
+    sb, _ = full_step(mb, tok, 1)
+    err = np.abs(sb.h_fin - se.h_fin).max() / np.abs(se.h_fin).max()
+    assert 0 < err < 2e-2
