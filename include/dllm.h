@@ -1,0 +1,226 @@
+/*
+ * dllm.h -- C ABI of libdllm: one token-skipping denoising iteration of a
+ * bidirectional masked-diffusion transformer on an MI355X (gfx950).
+ *
+ * Method sources (cited by page title and section):
+ *  [ES]  "ES-dLLM: Efficient Inference for Diffusion Large Language Models by
+ *        Early-Skipping", gist.science summary, technical summary section 2.1
+ *        (item 1: importance score, Eq. 1; item 2: partial cache update and
+ *        early skip) and section 2.2 (periodic refresh).
+ *  [SL]  "Stopping Computation for Converged Tokens in Masked Diffusion-LM
+ *        Decoding" (SureLock), gist.science summary, technical summary
+ *        section 2.1 (items 1-4: local-KL lock rule, skipped Q-projection and
+ *        FFN, cached K/V stay attendable, O(M_t N d) cost).
+ *  [DC]  dLLM-Cache explainer (aibr.jp), section 3 (similarity-gated partial
+ *        response update, long-interval prompt cache) and section 4 (update
+ *        ratio rho).
+ *  [DUS] "Plan for Speed: Dilated Scheduling for Masked Diffusion Language
+ *        Models", gist.science summary, technical summary section 2.
+ *
+ * Conventions shared by every entry point
+ *  - All pointers named in a struct or argument list as "device" are device
+ *    pointers on the current HIP device; "host" pointers are read during the
+ *    call only.  The library never allocates, frees or retains memory: the
+ *    caller owns every buffer.  Device buffers must be 16-byte aligned.
+ *  - Matrices are row-major.  Weights use the nn.Linear layout [out, in].
+ *  - Element type (dllm_dtype) applies to weights, activations and K/V caches;
+ *    logits, scores, confidence and KL are always fp32.
+ *  - `stream` is a hipStream_t (NULL = the legacy default stream).  Work is
+ *    enqueued on it and the call returns without synchronising.
+ *  - Every function returns a dllm_status.  Arguments are validated on the
+ *    host before any launch; on error nothing is launched.  DLLM_ELAUNCH
+ *    reports a failed kernel launch.  Faults inside kernels surface at the
+ *    caller's next synchronisation.  Device-resident indices and token ids
+ *    are preconditions (token ids outside [0, V) are clamped).
+ *  - Row layout of "active" buffers: padded per sequence.  Row r = b*k_max + j
+ *    holds the j-th active position of sequence b when j < n_active[b]; rows
+ *    with j >= n_active[b] are dead and their contents are unspecified.
+ *  - Calls on one stream are ordered; calls that share a workspace or state
+ *    must not overlap on different streams.
+ */
+#ifndef DLLM_H
+#define DLLM_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum {
+  DLLM_OK = 0,
+  DLLM_EINVAL = 1,     /* bad argument (NULL pointer, out-of-range value) */
+  DLLM_ESHAPE = 2,     /* unsupported or inconsistent shape */
+  DLLM_EDTYPE = 3,     /* unknown dtype */
+  DLLM_EWORKSPACE = 4, /* workspace missing or smaller than required */
+  DLLM_ELAUNCH = 5     /* a kernel launch failed */
+} dllm_status;
+
+typedef enum { DLLM_F32 = 0, DLLM_BF16 = 1 } dllm_dtype;
+
+/* Change term of the importance score ([ES] Eq. 1 and variants). */
+typedef enum {
+  DLLM_VAR_L1N = 0,   /* ||Hc-Hp||_1 / (sqrt(w) ||Hp||_2)      [ES] Eq. 1 */
+  DLLM_VAR_COS = 1,   /* 1 - cos(Hc, Hp) = 0.5 || Hc/|Hc| - Hp/|Hp| ||^2  [DC] sec. 3 */
+  DLLM_VAR_L2REL = 2, /* ||Hc-Hp||_2 / ||Hp||_2 */
+  DLLM_VAR_KL = 3,    /* previous step's local KL              [SL] 2.1 item 1 */
+  DLLM_VAR_NONE = 4   /* 0 */
+} dllm_var;
+
+/* Active-row selection ([ES] 2.1 item 2; [DC] sec. 3-4; [SL] 2.1 item 2). */
+typedef enum {
+  DLLM_SEL_TOPK = 0,       /* the k best candidates */
+  DLLM_SEL_THRESH_CAP = 1, /* forced rows and rows scoring > tau, capped at k */
+  DLLM_SEL_UNLOCKED = 2    /* every candidate (SureLock compaction) */
+} dllm_sel;
+
+/* force[] values: per position. */
+enum { DLLM_FORCE_NONE = 0, DLLM_FORCE_ON = 1, DLLM_FORCE_EXCLUDED = 2 };
+
+typedef struct {
+  int32_t B, S;                 /* sequences, positions per sequence */
+  int32_t d;                    /* hidden size */
+  int32_t n_heads, n_kv_heads;  /* query heads, K/V heads (GQA group = n_heads/n_kv_heads) */
+  int32_t head_dim;             /* D (128, or 64 for the fp32 path) */
+  int32_t d_ff;                 /* SwiGLU width F */
+  int32_t vocab;                /* V */
+  int32_t n_layers;             /* L */
+} dllm_dims;
+
+typedef struct {
+  const void *attn_norm;  /* device [d] */
+  const void *w_qkv;      /* device [(Hq + 2 Hkv) D, d]: Q rows, then K rows, then V rows */
+  const void *w_o;        /* device [d, Hq D] */
+  const void *ffn_norm;   /* device [d] */
+  const void *w_gate_up;  /* device [2F, d]: gate rows, then up rows */
+  const void *w_down;     /* device [d, F] */
+} dllm_layer_w;
+
+typedef struct {
+  dllm_dims dims;
+  int32_t dtype;                 /* dllm_dtype */
+  float rope_base;               /* rotate-half RoPE base (1e4) */
+  float rms_eps;                 /* RMSNorm epsilon (1e-5) */
+  int32_t mask_id;               /* mask token; excluded from softmax/argmax */
+  const void *embed;             /* device [V, d] */
+  const dllm_layer_w *layers;    /* host array [L] */
+  const void *final_norm;        /* device [d] */
+  const void *lm_head;           /* device [V, d] */
+} dllm_model;
+
+typedef struct {
+  float alpha;            /* weight of the confidence term ([ES] Eq. 1) */
+  int32_t conf_inverted;  /* 0: phi(c) = c as in Eq. 1;  1: phi(c) = 1 - c */
+  int32_t var;            /* dllm_var */
+  int32_t sel;            /* dllm_sel */
+  int32_t k;              /* rows kept per sequence (cap for THRESH_CAP) */
+  float tau;              /* THRESH_CAP threshold (score > tau qualifies) */
+} dllm_score_cfg;
+
+/* Persistent per-run state.  The library reads and writes the device arrays
+ * and flips bnd_cur / sets have_prev in this host struct. */
+typedef struct {
+  int32_t *tokens;        /* device [B, S] token ids (in/out: unmasking writes them) */
+  void **k_cache;         /* host array [L] of device [B, S, Hkv, D] */
+  void **v_cache;         /* host array [L] of device [B, S, Hkv, D] */
+  void *h_bnd[2];         /* device [B, S, d] x2: hidden state entering the boundary layer */
+  int32_t bnd_cur;        /* index of h_bnd holding the previous step's state */
+  void *h_fin;            /* device [B, S, d] final hidden state */
+  float *conf;            /* device [B, S] max softmax probability */
+  float *kl;              /* device [B, S] local KL (+inf before a previous posterior exists) */
+  int32_t *argmax;        /* device [B, S] most likely non-mask token */
+  float *logits_prev;     /* device [B*S, V] previous logits, or NULL (then KL is not tracked) */
+  uint8_t *force;         /* device [B, S] dllm_force values, or NULL (all 0) */
+  int32_t *idx;           /* device [B, k_max] out: active positions (ascending, -1 padded) */
+  int32_t *n_active;      /* device [B] out */
+  int32_t k_max;          /* row stride of idx; >= S on full steps */
+  int32_t have_prev;      /* 0 until the first step has run */
+} dllm_state;
+
+typedef struct {
+  int32_t boundary_layer;   /* b: layers < b run on all rows; 0 <= b <= L */
+  int32_t full_step;        /* 1: every layer on every row (first step, refresh) */
+  dllm_score_cfg score;
+  float lock_kl_eps;        /* SureLock epsilon; < 0 disables locking */
+  float lock_conf_min;      /* lock also requires conf > this */
+  int32_t unmask_n;         /* unmask this many masked positions per sequence (0: none) */
+  int32_t block_lo, block_hi; /* unmasking window [lo, hi) */
+  void *ws;                 /* device workspace */
+  size_t ws_bytes;
+} dllm_step_cfg;
+
+/* Bytes of device workspace needed by dllm_skip_step / dllm_layer_sparse for
+ * these dims and an active-row stride k_max.  Returns 0 on invalid input. */
+size_t dllm_workspace_size(const dllm_dims *dims, int32_t dtype, int32_t k_max);
+
+/* Importance scores and active-row selection ([ES] 2.1 items 1-2 and Eq. 1;
+ * [DC] sec. 3-4; [SL] 2.1 items 1-2).
+ *  h_cur, h_prev: device [B, S, width] (dtype)   -- current / previous tensor
+ *  conf_prev, kl_prev: device [B, S] fp32 (kl_prev may be NULL unless var = KL)
+ *  force: device [B, S] or NULL; FORCE_ON rows always come first, FORCE_EXCLUDED
+ *         rows are never selected.
+ *  score = alpha * phi(conf) + (1 - alpha) * psi, computed in fp32.
+ *  Selection order: forced, then score descending (NaN last, -0 == +0), then
+ *  lower index.  Outputs: score_out device [B, S] (may be NULL),
+ *  idx_out device [B, k_max] ascending and -1 padded, n_active_out device [B].
+ *  h_next: device [B, S, width] or NULL: receives a copy of h_cur.
+ *  Requires cfg->k <= k_max, width % 8 == 0 (bf16) or % 4 == 0 (fp32). */
+int dllm_score_select(const void *h_cur, const void *h_prev, void *h_next, int32_t dtype,
+                      const float *conf_prev, const float *kl_prev, const uint8_t *force,
+                      int32_t B, int32_t S, int32_t width, const dllm_score_cfg *cfg,
+                      float *score_out, int32_t *idx_out, int32_t *n_active_out, int32_t k_max,
+                      void *stream);
+
+/* Gather active rows ([ES] 2.1 item 2: selected positions continue).
+ *  src device [B, S, width] -> dst device [B*k_max, width] (padded rows). */
+int dllm_gather_rows(const void *src, const int32_t *idx, const int32_t *n_active, int32_t B,
+                     int32_t S, int32_t k_max, int32_t width, int32_t dtype, void *dst, void *stream);
+
+/* Scatter active rows back ([ES] 2.1 item 2: in-place cache update).
+ *  src device [B*k_max, width] -> dst device [B, S, width]; other rows untouched. */
+int dllm_scatter_rows(const void *src, const int32_t *idx, const int32_t *n_active, int32_t B,
+                      int32_t S, int32_t k_max, int32_t width, int32_t dtype, void *dst, void *stream);
+
+/* One transformer layer on the active rows only ([ES] 2.1 item 2; [SL] 2.1
+ * items 2-4): RMSNorm -> QKV GEMM -> RoPE at the rows' absolute positions ->
+ * K/V written into the caches at (b, idx) -> bidirectional GQA attention of
+ * the active queries over all S cached keys -> O GEMM + residual -> RMSNorm
+ * -> SwiGLU FFN + residual.
+ *  x_act: device [B*k_max, d] residual stream of the active rows (in/out).
+ *  idx/n_active: as produced by dllm_score_select.
+ *  k_cache/v_cache: device [B, S, Hkv, D] of this layer; only rows (b, idx)
+ *  are written.  ws: dllm_workspace_size(dims, dtype, k_max) bytes. */
+int dllm_layer_sparse(const dllm_model *model, int32_t layer, void *x_act, const int32_t *idx,
+                      const int32_t *n_active, int32_t k_max, void *k_cache, void *v_cache,
+                      void *ws, size_t ws_bytes, void *stream);
+
+/* Fused confidence / argmax / local-KL pass over the vocabulary ([SL] 2.1
+ * item 1: D = KL(p_t || p_{t-1}); [ES] Eq. 1 confidence c).
+ *  logits: device [R, V] fp32; row_pos: device [R], row r belongs to flat
+ *  position row_pos[r] = b*S + i, or -1 (dead row, skipped).
+ *  logits_prev: device [B*S, V] or NULL.  When non-NULL the row's previous
+ *  logits are read (if have_prev) and then overwritten with logits[r].
+ *  conf, argmax: device [B*S]; kl: device [B*S] or NULL (+inf without have_prev).
+ *  exclude_id: vocabulary id treated as -inf (the mask token), or -1. */
+int dllm_confidence_kl(const float *logits, float *logits_prev, const int32_t *row_pos, int32_t R,
+                       int32_t V, int32_t exclude_id, int32_t have_prev, float *conf,
+                       int32_t *argmax, float *kl, void *stream);
+
+/* One full denoising iteration ([ES] 2.1; [SL] 2.1): embed, dense layers
+ * below the boundary, score + select at the boundary, sparse layers,
+ * final-hidden scatter, LM head on the active rows, confidence/KL, then the
+ * SureLock lock update and/or confidence unmasking of [block_lo, block_hi).
+ * On a full step every row is active (state->k_max must be >= S). */
+int dllm_skip_step(const dllm_model *model, dllm_state *state, const dllm_step_cfg *cfg, void *stream);
+
+/* Human-readable text of a dllm_status. */
+const char *dllm_status_string(int status);
+
+/* Library ABI version (major * 100 + minor). */
+int dllm_version(void);
+
+#ifdef __cplusplus
+}
+#endif
+#endif /* DLLM_H */

@@ -63,14 +63,15 @@ def torch_dtype(dims: Dims):
     return torch.float32 if dims.dtype == "f32" else torch.bfloat16
 
 
-def layer_weights(dims: Dims, layer: int, device="cpu", seed_base: int | None = None) -> dict:
+def layer_weights(dims: Dims, layer: int, device="cpu", seed_base: int | None = None,
+                  std: float = WEIGHT_STD) -> dict:
     """Separate per-layer tensors, each in the storage dtype of the workload."""
     cid = dims.cfg_id if seed_base is None else seed_base
     dt = torch_dtype(dims)
     Hq, Hkv, D, d, F = dims.n_heads, dims.n_kv_heads, dims.head_dim, dims.d, dims.d_ff
 
     def w(tid, shape):
-        return normal(seed_of(cid, layer, tid), shape, WEIGHT_STD, dt, device)
+        return normal(seed_of(cid, layer, tid), shape, std, dt, device)
 
     return {
         "attn_norm": torch.ones(d, dtype=dt, device=device),
@@ -85,14 +86,14 @@ def layer_weights(dims: Dims, layer: int, device="cpu", seed_base: int | None = 
     }
 
 
-def model_weights(dims: Dims, device="cpu", seed_base: int | None = None) -> dict:
+def model_weights(dims: Dims, device="cpu", seed_base: int | None = None, std: float = WEIGHT_STD) -> dict:
     cid = dims.cfg_id if seed_base is None else seed_base
     dt = torch_dtype(dims)
     return {
-        "embed": normal(seed_of(cid, 10_000, T_EMBED), (dims.vocab, dims.d), WEIGHT_STD, dt, device),
-        "layers": [layer_weights(dims, l, device, seed_base) for l in range(dims.n_layers)],
+        "embed": normal(seed_of(cid, 10_000, T_EMBED), (dims.vocab, dims.d), std, dt, device),
+        "layers": [layer_weights(dims, l, device, seed_base, std) for l in range(dims.n_layers)],
         "final_norm": torch.ones(dims.d, dtype=dt, device=device),
-        "lm_head": normal(seed_of(cid, 10_000, T_LM), (dims.vocab, dims.d), WEIGHT_STD, dt, device),
+        "lm_head": normal(seed_of(cid, 10_000, T_LM), (dims.vocab, dims.d), std, dt, device),
     }
 
 

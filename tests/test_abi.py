@@ -1,0 +1,79 @@
+"""The C-ABI library loads and exports every entry point of include/dllm.h (CPU only).
+
+Only host-side entry points run here: workspace planning and argument
+validation, which return before any kernel launch.
+"""
+import ctypes
+import os
+import re
+
+import pytest
+
+from token_skipping_denoise_amd import _ffi
+
+HEADER = os.path.join(os.path.dirname(os.path.dirname(os.path.abspath(__file__))), "include", "dllm.h")
+
+
+def declared_functions():
+    src = open(HEADER).read()
+    src = re.sub(r"/\*.*?\*/", "", src, flags=re.S)
+    return sorted(set(re.findall(r"\b(dllm_[a-z_]+)\s*\(", src)))
+
+
+@pytest.fixture(scope="module")
+def lib():
+    if not os.path.exists(_ffi.LIB_PATH):
+        pytest.fail("libdllm.so is not built (run __graft_entry__.build())")
+    return _ffi.load()
+
+
+def test_every_declared_symbol_is_exported(lib):
+    names = declared_functions()
+    assert set(names) == set(_ffi.EXPORTED)
+    for n in names:
+        assert hasattr(lib, n), n
+
+
+def test_version_and_status_strings(lib):
+    assert lib.dllm_version() == 100
+    assert lib.dllm_status_string(0) == b"ok"
+    assert lib.dllm_status_string(4) == b"workspace missing or too small"
+
+
+def test_workspace_size_planning(lib):
+    d = _ffi.Dims(1, 512, 4096, 32, 32, 128, 12288, 126464, 32)
+    n128 = lib.dllm_workspace_size(ctypes.byref(d), _ffi.DLLM_BF16, 128)
+    n512 = lib.dllm_workspace_size(ctypes.byref(d), _ffi.DLLM_BF16, 512)
+    assert 0 < n128 <= n512
+    # logits of every row dominate: at least B*S*V*4 bytes
+    assert n512 >= 512 * 126464 * 4
+    # invalid: head_dim 64 unsupported by the bf16 attention, k_max > S, bad dtype
+    bad = _ffi.Dims(1, 512, 4096, 64, 64, 64, 12288, 126464, 32)
+    assert lib.dllm_workspace_size(ctypes.byref(bad), _ffi.DLLM_BF16, 128) == 0
+    assert lib.dllm_workspace_size(ctypes.byref(d), _ffi.DLLM_BF16, 513) == 0
+    assert lib.dllm_workspace_size(ctypes.byref(d), 7, 128) == 0
+    tiny = _ffi.Dims(1, 128, 256, 4, 4, 64, 768, 1024, 2)
+    assert lib.dllm_workspace_size(ctypes.byref(tiny), _ffi.DLLM_F32, 32) > 0
+
+
+def test_argument_validation_returns_before_launch(lib):
+    cfg = _ffi.ScoreCfg(0.5, 0, 0, 0, 4, 0.0)
+    fake = ctypes.c_void_p(16)   # never dereferenced: validation fails first
+    # NULL inputs
+    assert lib.dllm_score_select(None, None, None, 1, None, None, None, 1, 8, 8, ctypes.byref(cfg),
+                                 None, None, None, 4, None) == 1
+    # k > k_max
+    cfg_big = _ffi.ScoreCfg(0.5, 0, 0, 0, 9, 0.0)
+    assert lib.dllm_score_select(fake, fake, None, 1, fake, None, None, 1, 8, 8, ctypes.byref(cfg_big),
+                                 fake, fake, fake, 4, None) == 1
+    # width not a multiple of 8 for bf16
+    assert lib.dllm_score_select(fake, fake, None, 1, fake, None, None, 1, 8, 12, ctypes.byref(cfg),
+                                 fake, fake, fake, 4, None) == 2
+    # bad dtype
+    assert lib.dllm_gather_rows(fake, fake, fake, 1, 8, 4, 8, 5, fake, None) == 3
+    # k_max > S
+    assert lib.dllm_gather_rows(fake, fake, fake, 1, 8, 9, 8, 1, fake, None) == 2
+    # confidence pass with a bad exclude id
+    assert lib.dllm_confidence_kl(fake, None, fake, 4, 10, 10, 0, fake, fake, None, None) == 2
+    # skip step without a model
+    assert lib.dllm_skip_step(None, None, None, None) == 1

@@ -1,0 +1,255 @@
+"""End-to-end parity of dllm_skip_step with the oracle's iteration (GPU)."""
+import numpy as np
+import pytest
+import torch
+
+import synth
+from oracle.importance import VAR_COS, VAR_L1N
+from oracle.selection import FORCE_EXCLUDED
+from oracle.step import (SEL_THRESH_CAP, SEL_TOPK, SEL_UNLOCKED, OracleModel, ScoreCfg, StepCfg, new_state,
+                         skip_step)
+from synth import workloads
+from tests.gpu_util import DEV, assert_close, np64, selection_gap
+from tests.helpers import oracle_weights
+from token_skipping_denoise_amd import api
+
+pytestmark = pytest.mark.gpu
+
+
+def _models(dims, std=workloads.WEIGHT_STD):
+    w = workloads.model_weights(dims, std=std)
+    wd = {"embed": w["embed"].to(DEV), "final_norm": w["final_norm"].to(DEV), "lm_head": w["lm_head"].to(DEV),
+          "layers": [{k: t.to(DEV) for k, t in lw.items()} for lw in w["layers"]]}
+    gm = api.Model(wd, dims.n_heads, dims.n_kv_heads, dims.mask_id)
+    om = OracleModel(oracle_weights(w), dims.n_heads, dims.n_kv_heads, dims.mask_id,
+                     mode="exact" if dims.dtype == "f32" else "bf16")
+    return gm, om
+
+
+def _score_cfg_pair(alpha, var, sel, k, tau=0.0, conf_inverted=False):
+    return (api.score_cfg(alpha=alpha, conf_inverted=conf_inverted, var=var, sel=sel, k=k, tau=tau),
+            ScoreCfg(alpha=alpha, conf_inverted=conf_inverted, var=var, sel=sel, k=k, tau=tau))
+
+
+def _compare_state(gs, os_, rows, tol, what, check_argmax_gap=True):
+    B, S = os_.tokens.shape
+    flat = np.asarray(rows)
+    assert_close(np64(gs.h_fin).reshape(B * S, -1)[flat], os_.h_fin.reshape(B * S, -1)[flat], tol, f"{what} h_fin")
+    assert_close(np64(gs.conf).reshape(-1)[flat], os_.conf.reshape(-1)[flat], max(tol, 1e-4), f"{what} conf")
+    if gs.logits_prev is not None:
+        assert_close(np64(gs.logits_prev)[flat], os_.logits_prev[flat], tol, f"{what} logits")
+
+
+def _argmax_ok(gs, os_, rows, margin):
+    """argmax must match wherever the oracle's top-2 logit gap exceeds `margin`."""
+    if os_.logits_prev is None:
+        return
+    B, S = os_.tokens.shape
+    ga = gs.argmax.cpu().numpy().reshape(-1)
+    for r in rows:
+        z = os_.logits_prev[r].copy()
+        z[-1] = -np.inf
+        top2 = np.sort(z)[-2:]
+        if top2[1] - top2[0] > margin:
+            assert ga[r] == os_.argmax.reshape(-1)[r], f"argmax row {r}"
+
+
+def test_tiny_fp32_two_iterations():
+    """The tiny fp32 workload: full iteration, unmask 4, then an early-skip iteration (top 25% after layer 0)."""
+    dims = workloads.TINY
+    gm, om = _models(dims)
+    tok = workloads.initial_tokens(dims)
+    gs = api.State(gm, tok.to(DEV), k_max=32, track_kl=True)
+    ws = api.alloc_workspace(gm, dims.B, dims.S, 32)
+    os_ = new_state(om, tok.numpy(), track_kl=True)
+    lo, hi = dims.prompt, dims.S
+    # iteration t-1: full
+    api.skip_step(gm, gs, api.step_cfg(1, True, unmask_n=4, block_lo=lo, block_hi=hi, ws=ws))
+    os_, _ = skip_step(om, os_, StepCfg(boundary_layer=1, full_step=True, unmask_n=4, block_lo=lo, block_hi=hi))
+    torch.cuda.synchronize()
+    allrows = np.arange(dims.B * dims.S)
+    _compare_state(gs, os_, allrows, 1e-4, "full")
+    np.testing.assert_array_equal(gs.argmax.cpu().numpy(), os_.argmax)
+    np.testing.assert_array_equal(gs.tokens.cpu().numpy(), os_.tokens)
+    for l in range(dims.n_layers):
+        assert_close(np64(gs.k_cache[l]), os_.k_cache[l], 1e-4, f"K cache {l}")
+        assert_close(np64(gs.v_cache[l]), os_.v_cache[l], 1e-4, f"V cache {l}")
+    # iteration t: layer 0 full, layer 1 on the top 25% by 0.5 (1 - conf) + 0.5 (1 - cos)
+    gsc, osc = _score_cfg_pair(0.5, VAR_COS, SEL_TOPK, 32, conf_inverted=True)
+    api.skip_step(gm, gs, api.step_cfg(1, False, gsc, unmask_n=4, block_lo=lo, block_hi=hi, ws=ws))
+    os_, info = skip_step(om, os_, StepCfg(boundary_layer=1, full_step=False, score=osc, unmask_n=4,
+                                           block_lo=lo, block_hi=hi))
+    torch.cuda.synchronize()
+    gap = selection_gap(info["scores"][0], None, 32)
+    assert gap > 1e-6, f"near tie at the selection boundary ({gap})"
+    idx = gs.idx.cpu().numpy()
+    assert int(gs.n_active[0]) == 32
+    np.testing.assert_array_equal(idx[0], info["rows"])
+    _compare_state(gs, os_, info["rows"], 1e-4, "sparse")
+    np.testing.assert_array_equal(gs.tokens.cpu().numpy(), os_.tokens)
+    np.testing.assert_array_equal(gs.argmax.cpu().numpy(), os_.argmax)
+    for l in range(dims.n_layers):
+        assert_close(np64(gs.k_cache[l]), os_.k_cache[l], 1e-4, f"K cache {l} after sparse")
+    np.testing.assert_allclose(np64(gs.kl).reshape(-1)[info["rows"]], os_.kl.reshape(-1)[info["rows"]],
+                               rtol=1e-3, atol=1e-6)
+
+
+def _designed_conf(B, S, k, seed):
+    """Confidences whose top-k per sequence are separated from the rest by a wide gap."""
+    u = synth.uniform01(synth.seed_of(seed), (B, S)).numpy().astype(np.float64)
+    conf = 0.3 * u
+    for b in range(B):
+        top = synth.permutation(synth.seed_of(seed, b), S)[:k].numpy()
+        conf[b, top] = 0.6 + 0.4 * u[b, top]
+    return conf.astype(np.float32)
+
+
+@pytest.mark.parametrize("b_lay", [0, 1, 3])
+def test_bf16_early_skip_iteration(b_lay):
+    dims = workloads.shrink(workloads.LLADA, n_layers=3, d=256, n_heads=2, n_kv_heads=2, d_ff=512, vocab=1000,
+                            B=2, S=96, prompt=48)
+    k = 24
+    print(f"bf16 early-skip b={b_lay}", flush=True)
+    gm, om = _models(dims, std=0.05)
+    tok = workloads.initial_tokens(dims)
+    gs = api.State(gm, tok.to(DEV), k_max=k, track_kl=True)
+    ws = api.alloc_workspace(gm, dims.B, dims.S, k)
+    os_ = new_state(om, tok.numpy(), track_kl=True)
+    api.skip_step(gm, gs, api.step_cfg(b_lay, True, ws=ws))
+    os_, _ = skip_step(om, os_, StepCfg(boundary_layer=b_lay, full_step=True))
+    torch.cuda.synchronize()
+    _compare_state(gs, os_, np.arange(dims.B * dims.S), 2e-2, "full")
+    # same designed confidences and the same newly unmasked tokens on both sides
+    conf = _designed_conf(dims.B, dims.S, k, 77)
+    gs.conf.copy_(torch.from_numpy(conf))
+    os_.conf = conf.astype(np.float64)
+    new_tok = tok.clone()
+    new_tok[:, 50:53] = torch.tensor([5, 6, 7], dtype=torch.int32)
+    gs.tokens.copy_(new_tok)
+    os_.tokens = new_tok.numpy().astype(np.int64)
+    k_before = [t.cpu().clone() for t in gs.k_cache]
+    gsc, osc = _score_cfg_pair(0.5, VAR_L1N, SEL_TOPK, k)
+    api.skip_step(gm, gs, api.step_cfg(b_lay, False, gsc, ws=ws))
+    os_, info = skip_step(om, os_, StepCfg(boundary_layer=b_lay, full_step=False, score=osc))
+    torch.cuda.synchronize()
+    rows = info["rows"]
+    got_rows = [b * dims.S + int(i) for b in range(dims.B) for i in gs.idx[b, :int(gs.n_active[b])].cpu()]
+    assert got_rows == rows.tolist()
+    _compare_state(gs, os_, rows, 2e-2, "sparse")
+    _argmax_ok(gs, os_, rows, margin=0.05)
+    skipped = np.setdiff1d(np.arange(dims.B * dims.S), rows)
+    for l in range(dims.n_layers):
+        kc = gs.k_cache[l].cpu().reshape(dims.B * dims.S, -1)
+        assert_close(np64(kc)[rows], os_.k_cache[l].reshape(dims.B * dims.S, -1)[rows], 2e-2, f"K {l}")
+        if l >= b_lay:   # skipped rows keep their cached K/V bit for bit
+            assert torch.equal(kc[skipped], k_before[l].reshape(dims.B * dims.S, -1)[skipped])
+    # the boundary state for the next iteration is the hidden state entering layer b
+    assert_close(np64(gs.h_bnd_prev).reshape(dims.B * dims.S, -1), os_.h_bnd_prev.reshape(dims.B * dims.S, -1),
+                 2e-2, "h_bnd")
+
+
+def test_bf16_gqa_surelock_iteration():
+    dims = workloads.shrink(workloads.DREAM, n_layers=2, d=256, n_heads=4, n_kv_heads=1, d_ff=384, vocab=1000,
+                            B=3, S=80, prompt=40)
+    gm, om = _models(dims, std=0.05)
+    tok = workloads.initial_tokens(dims)
+    gs = api.State(gm, tok.to(DEV), k_max=dims.S, track_kl=True)
+    ws = api.alloc_workspace(gm, dims.B, dims.S, dims.S)
+    os_ = new_state(om, tok.numpy(), track_kl=True)
+    api.skip_step(gm, gs, api.step_cfg(0, True, ws=ws))
+    os_, _ = skip_step(om, os_, StepCfg(boundary_layer=0, full_step=True))
+    # lock a seeded 40% of positions per sequence on both sides; change three tokens
+    force = np.zeros((dims.B, dims.S), dtype=np.uint8)
+    for b in range(dims.B):
+        force[b, synth.permutation(synth.seed_of(88, b), dims.S)[:32].numpy()] = FORCE_EXCLUDED
+    gs.force.copy_(torch.from_numpy(force))
+    os_.force = force.copy()
+    new_tok = tok.clone()
+    new_tok[:, 45:48] = torch.tensor([1, 2, 3], dtype=torch.int32)
+    gs.tokens.copy_(new_tok)
+    os_.tokens = new_tok.numpy().astype(np.int64)
+    kc_before = [t.cpu().clone() for t in gs.k_cache]
+    gsc, osc = _score_cfg_pair(0.0, VAR_L1N, SEL_UNLOCKED, dims.S)
+    eps = 5e-3
+    api.skip_step(gm, gs, api.step_cfg(0, False, gsc, lock_kl_eps=eps, lock_conf_min=-1.0, ws=ws))
+    os_, info = skip_step(om, os_, StepCfg(boundary_layer=0, full_step=False, score=osc, lock_kl_eps=eps,
+                                           lock_conf_min=-1.0))
+    torch.cuda.synchronize()
+    rows = info["rows"]
+    assert len(rows) == dims.B * (dims.S - 32)
+    got_rows = [b * dims.S + int(i) for b in range(dims.B) for i in gs.idx[b, :int(gs.n_active[b])].cpu()]
+    assert got_rows == rows.tolist()
+    _compare_state(gs, os_, rows, 2e-2, "surelock")
+    # locked rows: cached K/V untouched at every layer
+    locked = np.nonzero(force.reshape(-1) == FORCE_EXCLUDED)[0]
+    for l in range(dims.n_layers):
+        kc = gs.k_cache[l].cpu().reshape(dims.B * dims.S, -1)
+        assert torch.equal(kc[locked], kc_before[l].reshape(dims.B * dims.S, -1)[locked])
+    # KL and the lock rule, away from the threshold
+    gkl = np64(gs.kl).reshape(-1)[rows]
+    okl = os_.kl.reshape(-1)[rows]
+    np.testing.assert_allclose(gkl, okl, rtol=5e-2, atol=2e-4)
+    gf = gs.force.cpu().numpy().reshape(-1)
+    of = os_.force.reshape(-1)
+    assert np.all(gf[locked] == FORCE_EXCLUDED)
+    clear = np.abs(okl - eps) > 5e-4
+    assert np.array_equal(gf[rows][clear], of[rows][clear])
+
+
+def test_bf16_thresh_cap_forced_rows():
+    """Cosine-gated partial update with forced (dilated-schedule) rows and excluded prompt rows."""
+    dims = workloads.shrink(workloads.LLADA_LONG, n_layers=2, d=256, n_heads=2, n_kv_heads=2, d_ff=512,
+                            vocab=1000, B=2, S=128, prompt=96)
+    k = 12
+    gm, om = _models(dims, std=0.05)
+    tok = workloads.initial_tokens(dims)
+    gs = api.State(gm, tok.to(DEV), k_max=k, track_kl=False)
+    ws = api.alloc_workspace(gm, dims.B, dims.S, k)
+    os_ = new_state(om, tok.numpy(), track_kl=False)
+    api.skip_step(gm, gs, api.step_cfg(0, True, ws=ws))
+    os_, _ = skip_step(om, os_, StepCfg(boundary_layer=0, full_step=True))
+    force = np.zeros((dims.B, dims.S), dtype=np.uint8)
+    force[:, :dims.prompt] = FORCE_EXCLUDED
+    force[:, [96, 104]] = 1
+    gs.force.copy_(torch.from_numpy(force))
+    os_.force = force.copy()
+    new_tok = tok.clone()
+    new_tok[:, [100, 112, 120]] = 9
+    gs.tokens.copy_(new_tok)
+    os_.tokens = new_tok.numpy().astype(np.int64)
+    gsc, osc = _score_cfg_pair(0.0, VAR_COS, SEL_THRESH_CAP, k, tau=1e-4)
+    api.skip_step(gm, gs, api.step_cfg(0, False, gsc, ws=ws))
+    os_, info = skip_step(om, os_, StepCfg(boundary_layer=0, full_step=False, score=osc))
+    torch.cuda.synchronize()
+    rows = info["rows"]
+    got_rows = [b * dims.S + int(i) for b in range(dims.B) for i in gs.idx[b, :int(gs.n_active[b])].cpu()]
+    # the changed tokens and forced rows must be in; ties near tau are not expected at these sizes
+    assert got_rows == rows.tolist()
+    for b in range(dims.B):
+        assert {b * dims.S + 96, b * dims.S + 104} <= set(got_rows)
+        assert all(r % dims.S >= dims.prompt for r in got_rows)
+    _compare_state(gs, os_, rows, 2e-2, "thresh")
+
+
+def test_all_rows_active_equals_full_step_on_gpu():
+    """Property at any size: a sparse step with every row active reproduces a full step."""
+    dims = workloads.shrink(workloads.LLADA, n_layers=2, d=256, n_heads=2, n_kv_heads=2, d_ff=512, vocab=1000,
+                            B=1, S=64, prompt=32)
+    gm, _ = _models(dims, std=0.05)
+    tok = workloads.initial_tokens(dims)
+    outs = []
+    for sparse in (False, True):
+        gs = api.State(gm, tok.to(DEV), k_max=dims.S, track_kl=False)
+        ws = api.alloc_workspace(gm, dims.B, dims.S, dims.S)
+        api.skip_step(gm, gs, api.step_cfg(1, True, ws=ws))
+        gs.tokens[:, 40] = 3
+        if sparse:
+            api.skip_step(gm, gs, api.step_cfg(1, False, api.score_cfg(k=dims.S), ws=ws))
+        else:
+            api.skip_step(gm, gs, api.step_cfg(1, True, ws=ws))
+        torch.cuda.synchronize()
+        outs.append((gs.h_fin.cpu(), gs.conf.cpu(), [t.cpu() for t in gs.k_cache]))
+    assert torch.equal(outs[0][0], outs[1][0])
+    assert torch.equal(outs[0][1], outs[1][1])
+    for a, b in zip(outs[0][2], outs[1][2]):
+        assert torch.equal(a, b)

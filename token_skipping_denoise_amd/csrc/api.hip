@@ -1,0 +1,396 @@
+// C ABI of libdllm: argument validation, workspace planning and the launch
+// order of one token-skipping denoising iteration.  Everything is enqueued on
+// the caller's stream; nothing is allocated and no host synchronisation
+// happens inside a call (the active-row count stays on the device; grids are
+// sized for the row capacity and dead tiles exit early).
+#include <hip/hip_runtime.h>
+#include <stddef.h>
+#include <stdint.h>
+
+#include <algorithm>
+
+#include "../../include/dllm.h"
+#include "kernels.h"
+
+using namespace dllm;
+
+namespace {
+
+constexpr size_t kAlign = 256;
+size_t align_up(size_t v) { return (v + kAlign - 1) / kAlign * kAlign; }
+int esize(int dtype) { return dtype == DLLM_F32 ? 4 : 2; }
+
+#define DLLM_TRY(expr)                       \
+  do {                                       \
+    if ((expr) != hipSuccess) return DLLM_ELAUNCH; \
+  } while (0)
+
+// Workspace layout for (dims, dtype, k_max).
+struct WsLayout {
+  size_t xfull, xact, xn, q, o, h, part, logits, scores, idx_id, nact_full, rowpos_d, rowpos_s, total;
+};
+
+long max_part_floats(const dllm_dims& d, int dtype, long M) {
+  const int NQKV = (d.n_heads + 2 * d.n_kv_heads) * d.head_dim;
+  const int HQD = d.n_heads * d.head_dim;
+  const int Ns[4] = {NQKV, d.d, 2 * d.d_ff, d.d};
+  const int Ks[4] = {d.d, HQD, d.d, d.d_ff};
+  long best = 0;
+  for (int i = 0; i < 4; ++i) {
+    const GemmPlan p = gemm_plan(dtype, (int)M, Ns[i], Ks[i]);
+    best = std::max(best, (long)p.splits * M * Ns[i]);
+  }
+  return best;
+}
+
+bool plan_ws(const dllm_dims& d, int dtype, int k_max, WsLayout& L) {
+  const long Rd = (long)d.B * d.S, Rs = (long)d.B * k_max, R = std::max(Rd, Rs);
+  const int es = esize(dtype);
+  const long HQD = (long)d.n_heads * d.head_dim;
+  size_t off = 0;
+  auto take = [&](size_t bytes) {
+    const size_t o = off;
+    off += align_up(bytes);
+    return o;
+  };
+  L.xfull = take(Rd * d.d * es);
+  L.xact = take(Rs * d.d * es);
+  L.xn = take(R * d.d * es);
+  L.q = take(R * HQD * es);
+  L.o = take(R * HQD * es);
+  L.h = take(R * (long)d.d_ff * es);
+  L.part = take(std::max(max_part_floats(d, dtype, Rd), max_part_floats(d, dtype, Rs)) * sizeof(float));
+  L.logits = take(R * (long)d.vocab * sizeof(float));
+  L.scores = take(Rd * sizeof(float));
+  L.idx_id = take(Rd * sizeof(int32_t));
+  L.nact_full = take(d.B * sizeof(int32_t));
+  L.rowpos_d = take(Rd * sizeof(int32_t));
+  L.rowpos_s = take(Rs * sizeof(int32_t));
+  L.total = off;
+  return true;
+}
+
+int check_dims(const dllm_dims* d, int dtype) {
+  if (!d) return DLLM_EINVAL;
+  if (dtype != DLLM_F32 && dtype != DLLM_BF16) return DLLM_EDTYPE;
+  if (d->B < 1 || d->S < 1 || d->d < 1 || d->n_heads < 1 || d->n_kv_heads < 1 || d->head_dim < 1 || d->d_ff < 1 ||
+      d->vocab < 2 || d->n_layers < 1)
+    return DLLM_ESHAPE;
+  if (d->n_heads % d->n_kv_heads) return DLLM_ESHAPE;
+  if (d->head_dim % 2) return DLLM_ESHAPE;
+  if (dtype == DLLM_BF16) {
+    // MFMA GEMM: every reduction dim a multiple of 64; attention head dim 128
+    if (d->head_dim != 128 || d->d % 64 || (d->n_heads * d->head_dim) % 64 || d->d_ff % 64) return DLLM_ESHAPE;
+  } else {
+    if ((d->head_dim != 64 && d->head_dim != 128) || d->d % 4 || d->d_ff % 4) return DLLM_ESHAPE;
+  }
+  if ((long)d->B * d->S > (1L << 30)) return DLLM_ESHAPE;
+  return DLLM_OK;
+}
+
+int check_width(int width, int dtype) {
+  if (width < 1) return DLLM_ESHAPE;
+  return (width % (dtype == DLLM_F32 ? 4 : 8)) ? DLLM_ESHAPE : DLLM_OK;
+}
+
+bool aligned16(const void* p) { return ((uintptr_t)p & 15u) == 0; }
+
+struct Ctx {
+  const dllm_model* m;
+  const dllm_dims* d;
+  int dtype;
+  char* ws;
+  WsLayout L;
+  hipStream_t s;
+  template <typename T>
+  T* at(size_t off) const {
+    return reinterpret_cast<T*>(ws + off);
+  }
+};
+
+// One layer on rows r = b*kx + j (live iff j < nact[b]); xn holds rmsnorm(x) * attn_norm on entry.
+int run_layer(const Ctx& c, int l, void* x, const int32_t* nact, const int32_t* row_pos, int kx, void* kc, void* vc,
+              const void* next_g) {
+  const dllm_dims& d = *c.d;
+  const dllm_layer_w& w = c.m->layers[l];
+  const int R = d.B * kx;
+  const int HQD = d.n_heads * d.head_dim;
+  const int NQKV = (d.n_heads + 2 * d.n_kv_heads) * d.head_dim;
+  float* part = c.at<float>(c.L.part);
+  void* xn = c.ws + c.L.xn;
+  void* q = c.ws + c.L.q;
+  void* o = c.ws + c.L.o;
+  void* h = c.ws + c.L.h;
+  const float eps = c.m->rms_eps;
+
+  GemmPlan p = gemm_plan(c.dtype, R, NQKV, d.d);
+  DLLM_TRY(launch_gemm(c.dtype, p, xn, w.w_qkv, part, R, NQKV, d.d, nact, kx, c.s));
+  DLLM_TRY(launch_qkv_epilogue(c.dtype, part, p.splits, (long)R * NQKV, row_pos, R, d.S, d.n_heads, d.n_kv_heads,
+                               d.head_dim, c.m->rope_base, q, kc, vc, c.s));
+  DLLM_TRY(launch_attention(c.dtype, q, kc, vc, o, nact, d.B, d.S, kx, d.n_heads, d.n_kv_heads, d.head_dim, c.s));
+  p = gemm_plan(c.dtype, R, d.d, HQD);
+  DLLM_TRY(launch_gemm(c.dtype, p, o, w.w_o, part, R, d.d, HQD, nact, kx, c.s));
+  DLLM_TRY(launch_resid_norm(c.dtype, part, p.splits, (long)R * d.d, row_pos, R, d.d, x, w.ffn_norm, eps, xn, c.s));
+  p = gemm_plan(c.dtype, R, 2 * d.d_ff, d.d);
+  DLLM_TRY(launch_gemm(c.dtype, p, xn, w.w_gate_up, part, R, 2 * d.d_ff, d.d, nact, kx, c.s));
+  DLLM_TRY(launch_swiglu(c.dtype, part, p.splits, (long)R * 2 * d.d_ff, row_pos, R, d.d_ff, h, c.s));
+  p = gemm_plan(c.dtype, R, d.d, d.d_ff);
+  DLLM_TRY(launch_gemm(c.dtype, p, h, w.w_down, part, R, d.d, d.d_ff, nact, kx, c.s));
+  DLLM_TRY(launch_resid_norm(c.dtype, part, p.splits, (long)R * d.d, row_pos, R, d.d, x, next_g, eps, xn, c.s));
+  return DLLM_OK;
+}
+
+int check_model(const dllm_model* m) {
+  if (!m) return DLLM_EINVAL;
+  int st = check_dims(&m->dims, m->dtype);
+  if (st) return st;
+  if (!m->embed || !m->layers || !m->final_norm || !m->lm_head) return DLLM_EINVAL;
+  if (m->mask_id < -1 || m->mask_id >= m->dims.vocab) return DLLM_EINVAL;
+  if (!(m->rope_base > 0.f) || !(m->rms_eps >= 0.f)) return DLLM_EINVAL;
+  for (int l = 0; l < m->dims.n_layers; ++l) {
+    const dllm_layer_w& w = m->layers[l];
+    if (!w.attn_norm || !w.w_qkv || !w.w_o || !w.ffn_norm || !w.w_gate_up || !w.w_down) return DLLM_EINVAL;
+  }
+  return DLLM_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
+int dllm_version(void) { return 100; }
+
+const char* dllm_status_string(int status) {
+  switch (status) {
+    case DLLM_OK: return "ok";
+    case DLLM_EINVAL: return "invalid argument";
+    case DLLM_ESHAPE: return "unsupported or inconsistent shape";
+    case DLLM_EDTYPE: return "unknown dtype";
+    case DLLM_EWORKSPACE: return "workspace missing or too small";
+    case DLLM_ELAUNCH: return "kernel launch failed";
+    default: return "unknown status";
+  }
+}
+
+size_t dllm_workspace_size(const dllm_dims* dims, int32_t dtype, int32_t k_max) {
+  if (check_dims(dims, dtype) != DLLM_OK || k_max < 1 || k_max > dims->S) return 0;
+  WsLayout L;
+  plan_ws(*dims, dtype, k_max, L);
+  return L.total;
+}
+
+int dllm_score_select(const void* h_cur, const void* h_prev, void* h_next, int32_t dtype, const float* conf_prev,
+                      const float* kl_prev, const uint8_t* force, int32_t B, int32_t S, int32_t width,
+                      const dllm_score_cfg* cfg, float* score_out, int32_t* idx_out, int32_t* n_active_out,
+                      int32_t k_max, void* stream) {
+  if (dtype != DLLM_F32 && dtype != DLLM_BF16) return DLLM_EDTYPE;
+  if (!cfg || !h_cur || !h_prev || !conf_prev || !score_out || !idx_out || !n_active_out) return DLLM_EINVAL;
+  if (B < 1 || S < 1 || k_max < 1 || k_max > S) return DLLM_ESHAPE;
+  if (check_width(width, dtype)) return DLLM_ESHAPE;
+  if (!aligned16(h_cur) || !aligned16(h_prev) || (h_next && !aligned16(h_next))) return DLLM_EINVAL;
+  if (cfg->var < DLLM_VAR_L1N || cfg->var > DLLM_VAR_NONE) return DLLM_EINVAL;
+  if (cfg->var == DLLM_VAR_KL && !kl_prev) return DLLM_EINVAL;
+  if (cfg->sel < DLLM_SEL_TOPK || cfg->sel > DLLM_SEL_UNLOCKED) return DLLM_EINVAL;
+  if (cfg->sel != DLLM_SEL_UNLOCKED && (cfg->k < 0 || cfg->k > k_max)) return DLLM_EINVAL;
+  if (cfg->sel == DLLM_SEL_UNLOCKED && k_max != S) return DLLM_EINVAL;
+  hipStream_t s = (hipStream_t)stream;
+  DLLM_TRY(launch_score(dtype, h_cur, h_prev, h_next, conf_prev, kl_prev, force, B * S, width, cfg->alpha,
+                        cfg->conf_inverted, cfg->var, score_out, s));
+  DLLM_TRY(launch_select(score_out, force, B, S, cfg->sel, cfg->k, cfg->tau, k_max, idx_out, n_active_out, s));
+  return DLLM_OK;
+}
+
+static int gather_scatter(bool gather, const void* src, const int32_t* idx, const int32_t* n_active, int32_t B,
+                          int32_t S, int32_t k_max, int32_t width, int32_t dtype, void* dst, void* stream,
+                          int32_t* row_pos_ws) {
+  (void)row_pos_ws;
+  if (dtype != DLLM_F32 && dtype != DLLM_BF16) return DLLM_EDTYPE;
+  if (!src || !idx || !n_active || !dst) return DLLM_EINVAL;
+  if (B < 1 || S < 1 || k_max < 1 || k_max > S || check_width(width, dtype)) return DLLM_ESHAPE;
+  if (!aligned16(src) || !aligned16(dst)) return DLLM_EINVAL;
+  return DLLM_OK;
+}
+
+// Gather/scatter compute the row positions on the fly from idx/n_active (no workspace).
+namespace {
+__global__ void k_gs_rows(bool gather, const uint4* __restrict__ src, const int32_t* __restrict__ idx,
+                          const int32_t* __restrict__ n_active, int S, int k_max, int nchunk, uint4* __restrict__ dst) {
+  const int r = blockIdx.x;
+  const int b = r / k_max, j = r - b * k_max;
+  if (j >= n_active[b]) return;
+  const int i = idx[r];
+  if (i < 0 || i >= S) return;
+  const long pos = (long)b * S + i;
+  const uint4* s4 = src + (gather ? pos : (long)r) * nchunk;
+  uint4* d4 = dst + (gather ? (long)r : pos) * nchunk;
+  for (int c = threadIdx.x; c < nchunk; c += blockDim.x) d4[c] = s4[c];
+}
+}  // namespace
+
+int dllm_gather_rows(const void* src, const int32_t* idx, const int32_t* n_active, int32_t B, int32_t S,
+                     int32_t k_max, int32_t width, int32_t dtype, void* dst, void* stream) {
+  int st = gather_scatter(true, src, idx, n_active, B, S, k_max, width, dtype, dst, stream, nullptr);
+  if (st) return st;
+  const int nchunk = width * esize(dtype) / 16;
+  hipLaunchKernelGGL(k_gs_rows, dim3(B * k_max), dim3(256), 0, (hipStream_t)stream, true, (const uint4*)src, idx,
+                     n_active, S, k_max, nchunk, (uint4*)dst);
+  return hipGetLastError() == hipSuccess ? DLLM_OK : DLLM_ELAUNCH;
+}
+
+int dllm_scatter_rows(const void* src, const int32_t* idx, const int32_t* n_active, int32_t B, int32_t S,
+                      int32_t k_max, int32_t width, int32_t dtype, void* dst, void* stream) {
+  int st = gather_scatter(false, src, idx, n_active, B, S, k_max, width, dtype, dst, stream, nullptr);
+  if (st) return st;
+  const int nchunk = width * esize(dtype) / 16;
+  hipLaunchKernelGGL(k_gs_rows, dim3(B * k_max), dim3(256), 0, (hipStream_t)stream, false, (const uint4*)src, idx,
+                     n_active, S, k_max, nchunk, (uint4*)dst);
+  return hipGetLastError() == hipSuccess ? DLLM_OK : DLLM_ELAUNCH;
+}
+
+int dllm_layer_sparse(const dllm_model* model, int32_t layer, void* x_act, const int32_t* idx,
+                      const int32_t* n_active, int32_t k_max, void* k_cache, void* v_cache, void* ws, size_t ws_bytes,
+                      void* stream) {
+  int st = check_model(model);
+  if (st) return st;
+  const dllm_dims& d = model->dims;
+  if (layer < 0 || layer >= d.n_layers) return DLLM_EINVAL;
+  if (!x_act || !idx || !n_active || !k_cache || !v_cache) return DLLM_EINVAL;
+  if (k_max < 1 || k_max > d.S) return DLLM_ESHAPE;
+  if (!aligned16(x_act)) return DLLM_EINVAL;
+  Ctx c{model, &d, model->dtype, (char*)ws, {}, (hipStream_t)stream};
+  plan_ws(d, c.dtype, k_max, c.L);
+  if (!ws || ws_bytes < c.L.total) return DLLM_EWORKSPACE;
+  int32_t* row_pos = c.at<int32_t>(c.L.rowpos_s);
+  const int R = d.B * k_max;
+  DLLM_TRY(launch_row_pos(idx, n_active, d.B, d.S, k_max, row_pos, c.s));
+  // xn = rmsnorm(x_act) * attn_norm (scatter mode with no copy target = norm only)
+  DLLM_TRY(launch_scatter_norm(c.dtype, x_act, row_pos, R, d.d, nullptr, model->layers[layer].attn_norm,
+                               model->rms_eps, c.ws + c.L.xn, c.s));
+  return run_layer(c, layer, x_act, n_active, row_pos, k_max, k_cache, v_cache, nullptr);
+}
+
+int dllm_confidence_kl(const float* logits, float* logits_prev, const int32_t* row_pos, int32_t R, int32_t V,
+                       int32_t exclude_id, int32_t have_prev, float* conf, int32_t* argmax, float* kl, void* stream) {
+  if (!logits || !row_pos || !conf || !argmax) return DLLM_EINVAL;
+  if (R < 0 || V < 2 || exclude_id >= V) return DLLM_ESHAPE;
+  DLLM_TRY(launch_conf_kl(logits, logits_prev, row_pos, R, V, exclude_id, have_prev, conf, argmax, kl,
+                          (hipStream_t)stream));
+  return DLLM_OK;
+}
+
+int dllm_skip_step(const dllm_model* model, dllm_state* state, const dllm_step_cfg* cfg, void* stream) {
+  int st = check_model(model);
+  if (st) return st;
+  if (!state || !cfg) return DLLM_EINVAL;
+  const dllm_dims& d = model->dims;
+  const int L = d.n_layers, B = d.B, S = d.S;
+  const int full = cfg->full_step ? 1 : 0;
+  const int b_lay = cfg->boundary_layer;
+  if (b_lay < 0 || b_lay > L) return DLLM_EINVAL;
+  if (!state->tokens || !state->k_cache || !state->v_cache || !state->h_bnd[0] || !state->h_bnd[1] ||
+      !state->h_fin || !state->conf || !state->kl || !state->argmax || !state->idx || !state->n_active)
+    return DLLM_EINVAL;
+  for (int l = 0; l < L; ++l)
+    if (!state->k_cache[l] || !state->v_cache[l]) return DLLM_EINVAL;
+  const int kx = state->k_max;
+  if (kx < 1 || kx > S) return DLLM_ESHAPE;
+  if (state->bnd_cur != 0 && state->bnd_cur != 1) return DLLM_EINVAL;
+  const dllm_score_cfg& sc = cfg->score;
+  if (!full) {
+    if (!state->have_prev) return DLLM_EINVAL;  // a sparse step needs the previous boundary state
+    if (sc.var < DLLM_VAR_L1N || sc.var > DLLM_VAR_NONE) return DLLM_EINVAL;
+    if (sc.sel < DLLM_SEL_TOPK || sc.sel > DLLM_SEL_UNLOCKED) return DLLM_EINVAL;
+    if (sc.sel != DLLM_SEL_UNLOCKED && (sc.k < 0 || sc.k > kx)) return DLLM_EINVAL;
+    if (sc.sel == DLLM_SEL_UNLOCKED && kx != S) return DLLM_EINVAL;
+  }
+  if (cfg->unmask_n < 0 || cfg->unmask_n > 256) return DLLM_EINVAL;
+  if (cfg->unmask_n > 0 && (cfg->block_lo < 0 || cfg->block_hi > S || cfg->block_lo > cfg->block_hi))
+    return DLLM_EINVAL;
+  if (cfg->lock_kl_eps >= 0.f && !state->force) return DLLM_EINVAL;
+
+  Ctx c{model, &d, model->dtype, (char*)cfg->ws, {}, (hipStream_t)stream};
+  plan_ws(d, c.dtype, kx, c.L);
+  if (!cfg->ws || cfg->ws_bytes < c.L.total) return DLLM_EWORKSPACE;
+  const int es = esize(c.dtype);
+  const size_t row_bytes = (size_t)d.d * es;
+  const int Rd = B * S, Rs = B * kx;
+  void* xfull = c.ws + c.L.xfull;
+  void* xact = c.ws + c.L.xact;
+  void* xn = c.ws + c.L.xn;
+  int32_t* idx_id = c.at<int32_t>(c.L.idx_id);
+  int32_t* nact_full = c.at<int32_t>(c.L.nact_full);
+  int32_t* rp_d = c.at<int32_t>(c.L.rowpos_d);
+  int32_t* rp_s = c.at<int32_t>(c.L.rowpos_s);
+  void* h_prev = state->h_bnd[state->bnd_cur];
+  void* h_next = state->h_bnd[1 - state->bnd_cur];
+  const float eps = model->rms_eps;
+
+  DLLM_TRY(launch_identity_rows(B, S, idx_id, nact_full, c.s));
+  DLLM_TRY(launch_row_pos(idx_id, nact_full, B, S, S, rp_d, c.s));
+  // embedding (+ first layer's norm when layer 0 runs dense)
+  const bool l0_dense = full || b_lay > 0;
+  DLLM_TRY(launch_embed_norm(c.dtype, model->embed, state->tokens, d.vocab, Rd, d.d,
+                             l0_dense ? model->layers[0].attn_norm : nullptr, eps, xfull, xn, c.s));
+
+  auto boundary = [&]() -> int {
+    if (full) {
+      DLLM_TRY(launch_copy(xfull, h_next, (size_t)Rd * row_bytes, c.s));
+      return DLLM_OK;
+    }
+    float* scores = c.at<float>(c.L.scores);
+    DLLM_TRY(launch_score(c.dtype, xfull, h_prev, h_next, state->conf, state->kl, state->force, Rd, d.d, sc.alpha,
+                          sc.conf_inverted, sc.var, scores, c.s));
+    DLLM_TRY(launch_select(scores, state->force, B, S, sc.sel, sc.k, sc.tau, kx, state->idx, state->n_active, c.s));
+    DLLM_TRY(launch_row_pos(state->idx, state->n_active, B, S, kx, rp_s, c.s));
+    const void* g = (b_lay < L) ? model->layers[b_lay].attn_norm : model->final_norm;
+    DLLM_TRY(launch_gather_norm(c.dtype, xfull, rp_s, Rs, d.d, xact, g, eps, xn, c.s));
+    return DLLM_OK;
+  };
+
+  for (int l = 0; l < L; ++l) {
+    if (l == b_lay) {
+      st = boundary();
+      if (st) return st;
+    }
+    const bool dense = full || l < b_lay;
+    const void* next_g;
+    if (l + 1 == L) next_g = model->final_norm;
+    else if (!full && l + 1 == b_lay) next_g = nullptr;  // the boundary gather normalises the active rows
+    else next_g = model->layers[l + 1].attn_norm;
+    if (dense)
+      st = run_layer(c, l, xfull, nact_full, rp_d, S, state->k_cache[l], state->v_cache[l], next_g);
+    else
+      st = run_layer(c, l, xact, state->n_active, rp_s, kx, state->k_cache[l], state->v_cache[l], next_g);
+    if (st) return st;
+  }
+  if (b_lay == L) {
+    st = boundary();
+    if (st) return st;
+  }
+
+  // final hidden state of the computed rows; xn already holds rmsnorm(x) * final_norm
+  const int R = full ? Rd : Rs;
+  const int32_t* rp = full ? rp_d : rp_s;
+  const int32_t* nact = full ? nact_full : state->n_active;
+  const int kk = full ? S : kx;
+  if (full) DLLM_TRY(launch_copy(xfull, state->h_fin, (size_t)Rd * row_bytes, c.s));
+  else DLLM_TRY(launch_scatter_norm(c.dtype, xact, rp_s, Rs, d.d, state->h_fin, nullptr, eps, nullptr, c.s));
+
+  float* logits = c.at<float>(c.L.logits);
+  GemmPlan p = gemm_plan(c.dtype, R, d.vocab, d.d);
+  p.splits = 1;
+  DLLM_TRY(launch_gemm(c.dtype, p, xn, model->lm_head, logits, R, d.vocab, d.d, nact, kk, c.s));
+  DLLM_TRY(launch_conf_kl(logits, state->logits_prev, rp, R, d.vocab, model->mask_id, state->have_prev, state->conf,
+                          state->argmax, state->kl, c.s));
+  if (cfg->lock_kl_eps >= 0.f && state->have_prev)
+    DLLM_TRY(launch_lock_update(rp, R, state->conf, state->kl, cfg->lock_kl_eps, cfg->lock_conf_min, state->force,
+                                c.s));
+  if (cfg->unmask_n > 0)
+    DLLM_TRY(launch_unmask(state->tokens, state->conf, state->argmax, B, S, model->mask_id, cfg->block_lo,
+                           cfg->block_hi, cfg->unmask_n, c.s));
+  state->bnd_cur = 1 - state->bnd_cur;
+  state->have_prev = 1;
+  return DLLM_OK;
+}
+
+}  // extern "C"

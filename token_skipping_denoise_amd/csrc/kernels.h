@@ -1,0 +1,70 @@
+// Launch wrappers of the libdllm kernels (internal; not part of the C ABI).
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace dllm {
+
+// ---------------- row kernels (rowops.hip) ----------------
+// x[r] = embed[tok[r]] for r < rows; if g: xn[r] = rmsnorm(x[r]) * g.
+hipError_t launch_embed_norm(int dtype, const void* embed, const int32_t* tokens, int V, int rows, int d,
+                             const void* g, float eps, void* x, void* xn, hipStream_t s);
+// dst[r] = src[row_pos[r]] for live rows; if g: dst_norm[r] = rmsnorm(dst[r]) * g.
+hipError_t launch_gather_norm(int dtype, const void* src, const int32_t* row_pos, int R, int w, void* dst,
+                              const void* g, float eps, void* dst_norm, hipStream_t s);
+// dst[row_pos[r]] = src[r] for live rows; if g: dst_norm[r] = rmsnorm(src[r]) * g.
+hipError_t launch_scatter_norm(int dtype, const void* src, const int32_t* row_pos, int R, int w, void* dst,
+                               const void* g, float eps, void* dst_norm, hipStream_t s);
+// row_pos[b*k_max + j] = b*S + idx[b*k_max + j] if j < n_active[b], else -1.
+hipError_t launch_row_pos(const int32_t* idx, const int32_t* n_active, int B, int S, int k_max,
+                          int32_t* row_pos, hipStream_t s);
+// idx[b*S + i] = i, n_active[b] = S.
+hipError_t launch_identity_rows(int B, int S, int32_t* idx, int32_t* n_active, hipStream_t s);
+// Sum split-K partials of the QKV GEMM, apply RoPE at position row_pos % S, write Q [R, Hq*D]
+// and K/V rows into the caches [B, S, Hkv, D].
+hipError_t launch_qkv_epilogue(int dtype, const float* part, int splits, long split_stride,
+                               const int32_t* row_pos, int R, int S, int Hq, int Hkv, int D, float rope_base,
+                               void* q, void* kc, void* vc, hipStream_t s);
+// x[r] += sum of partials; if g: xn[r] = rmsnorm(x[r]) * g.
+hipError_t launch_resid_norm(int dtype, const float* part, int splits, long split_stride, const int32_t* row_pos,
+                             int R, int d, void* x, const void* g, float eps, void* xn, hipStream_t s);
+// h[r, c] = silu(P[r, c]) * P[r, F + c] with P the summed partials [R, 2F].
+hipError_t launch_swiglu(int dtype, const float* part, int splits, long split_stride, const int32_t* row_pos,
+                         int R, int F, void* h, hipStream_t s);
+hipError_t launch_copy(const void* src, void* dst, size_t bytes, hipStream_t s);
+
+// ---------------- GEMM (gemm.hip) ----------------
+// C[s][m][n] = sum_{k in split s} A[m][k] * W[n][k] (fp32 partials, split stride M*N).
+// Row tiles whose rows are all dead (j >= n_active[b], r = b*k_max + j) are skipped;
+// n_active == nullptr means every row is live.
+struct GemmPlan {
+  int bm, bn, splits;
+};
+GemmPlan gemm_plan(int dtype, int M, int N, int K);
+hipError_t launch_gemm(int dtype, const GemmPlan& p, const void* A, const void* W, float* C, int M, int N, int K,
+                       const int32_t* n_active, int k_max, hipStream_t s);
+
+// ---------------- attention (attention.hip) ----------------
+// o[r, h, :] = softmax(q[r, h] . Kc[b, :, h/g] / sqrt(D)) Vc[b, :, h/g] over all S keys.
+hipError_t launch_attention(int dtype, const void* q, const void* kc, const void* vc, void* o,
+                            const int32_t* n_active, int B, int S, int k_max, int Hq, int Hkv, int D, hipStream_t s);
+
+// ---------------- score / select (score_select.hip) ----------------
+hipError_t launch_score(int dtype, const void* h_cur, const void* h_prev, void* h_next, const float* conf_prev,
+                        const float* kl_prev, const uint8_t* force, int rows, int width, float alpha,
+                        int conf_inverted, int var, float* score, hipStream_t s);
+hipError_t launch_select(const float* score, const uint8_t* force, int B, int S, int sel, int k, float tau,
+                         int k_max, int32_t* idx, int32_t* n_active, hipStream_t s);
+
+// ---------------- vocabulary pass (vocab.hip) ----------------
+hipError_t launch_conf_kl(const float* logits, float* logits_prev, const int32_t* row_pos, int R, int V,
+                          int exclude_id, int have_prev, float* conf, int32_t* argmax, float* kl, hipStream_t s);
+
+// ---------------- post-step (post.hip) ----------------
+hipError_t launch_lock_update(const int32_t* row_pos, int R, const float* conf, const float* kl, float eps,
+                              float conf_min, uint8_t* force, hipStream_t s);
+hipError_t launch_unmask(int32_t* tokens, const float* conf, const int32_t* argmax, int B, int S, int mask_id,
+                         int lo, int hi, int n, hipStream_t s);
+
+}  // namespace dllm

@@ -1,0 +1,90 @@
+// Post-step updates that stay on the device (no host synchronisation).
+//
+// * SureLock lock rule (technical summary 2.1 item 1): a recomputed position
+//   locks once its local KL is at or below epsilon and its confidence exceeds
+//   the optional minimum; locking is permanent.
+// * Confidence unmasking (ES-dLLM summary section 1; SureLock section 1): the
+//   n most confident masked positions of the current block receive their
+//   argmax token; ties go to the lower position.
+#include "common.h"
+#include "kernels.h"
+
+namespace dllm {
+
+__global__ void k_lock_update(const int32_t* __restrict__ row_pos, int R, const float* __restrict__ conf,
+                              const float* __restrict__ kl, float eps, float conf_min, uint8_t* __restrict__ force) {
+  const int r = blockIdx.x * blockDim.x + threadIdx.x;
+  if (r >= R) return;
+  const int pos = row_pos[r];
+  if (pos < 0) return;
+  if (kl[pos] <= eps && conf[pos] > conf_min) force[pos] = 2;
+}
+
+hipError_t launch_lock_update(const int32_t* row_pos, int R, const float* conf, const float* kl, float eps,
+                              float conf_min, uint8_t* force, hipStream_t s) {
+  if (R <= 0) return hipSuccess;
+  hipLaunchKernelGGL(k_lock_update, dim3((R + 255) / 256), dim3(256), 0, s, row_pos, R, conf, kl, eps, conf_min, force);
+  return hipGetLastError();
+}
+
+constexpr int kUT = 256;
+constexpr int kMaxUnmask = 256;
+
+// One workgroup per sequence; n rounds of a block-wide arg-max over (conf desc, position asc).
+__global__ __launch_bounds__(kUT) void k_unmask(int32_t* __restrict__ tokens, const float* __restrict__ conf,
+                                                const int32_t* __restrict__ argmax, int S, int mask_id, int lo, int hi,
+                                                int n) {
+  __shared__ int chosen[kMaxUnmask];
+  __shared__ float bc[kUT];
+  __shared__ int bi[kUT];
+  const int b = blockIdx.x, tid = threadIdx.x;
+  int32_t* tok = tokens + (long)b * S;
+  const float* cf = conf + (long)b * S;
+  int n_chosen = 0;
+  for (int it = 0; it < n; ++it) {
+    float best = -INFINITY;
+    int bidx = 0x7fffffff;
+    for (int i = lo + tid; i < hi; i += kUT) {
+      if (tok[i] != mask_id) continue;
+      bool taken = false;
+      for (int c = 0; c < n_chosen; ++c) taken |= (chosen[c] == i);
+      if (taken) continue;
+      const float c = cf[i];
+      if (c > best || (c == best && i < bidx)) {
+        best = c;
+        bidx = i;
+      }
+    }
+    bc[tid] = best;
+    bi[tid] = bidx;
+    __syncthreads();
+    for (int w = kUT / 2; w > 0; w >>= 1) {
+      if (tid < w) {
+        const float c2 = bc[tid + w];
+        const int i2 = bi[tid + w];
+        if (c2 > bc[tid] || (c2 == bc[tid] && i2 < bi[tid])) {
+          bc[tid] = c2;
+          bi[tid] = i2;
+        }
+      }
+      __syncthreads();
+    }
+    const int pick = bi[0];
+    __syncthreads();
+    if (pick == 0x7fffffff) break;
+    if (tid == 0) chosen[n_chosen] = pick;
+    ++n_chosen;
+    __syncthreads();
+  }
+  for (int c = tid; c < n_chosen; c += kUT) tok[chosen[c]] = argmax[(long)b * S + chosen[c]];
+}
+
+hipError_t launch_unmask(int32_t* tokens, const float* conf, const int32_t* argmax, int B, int S, int mask_id, int lo,
+                         int hi, int n, hipStream_t s) {
+  if (B <= 0 || n <= 0 || hi <= lo) return hipSuccess;
+  if (n > kMaxUnmask) return hipErrorInvalidValue;
+  hipLaunchKernelGGL(k_unmask, dim3(B), dim3(kUT), 0, s, tokens, conf, argmax, S, mask_id, lo, hi, n);
+  return hipGetLastError();
+}
+
+}  // namespace dllm

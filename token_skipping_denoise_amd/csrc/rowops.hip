@@ -1,0 +1,284 @@
+// Row-wise kernels: embedding, gather/scatter of active rows, RMSNorm, and the
+// reduction epilogues of the split-K GEMMs (RoPE + K/V cache scatter, residual
+// add + RMSNorm, SwiGLU).  These are HBM/latency bound: one wavefront per row
+// for the row-norm kernels, 16-byte vector accesses throughout.
+//
+// Sources: partial update of active rows and in-place cache update
+// (ES-dLLM summary, technical summary 2.1 item 2); fresh K/V of active rows
+// overwrite the cache while other rows keep theirs (SureLock summary 2.1
+// items 2-3).  Layer internals (RMSNorm, rotate-half RoPE, SwiGLU) are the
+// plain reading of the LLaDA/Dream model family named on the pages.
+#include "common.h"
+#include "kernels.h"
+
+namespace dllm {
+
+enum RowMode { kEmbed = 0, kGather = 1, kScatter = 2 };
+
+// One wavefront per row: copy a row (by token id, gather or scatter) and
+// optionally write its RMSNorm * g.
+template <typename T, int MODE>
+__global__ __launch_bounds__(256) void k_rows_norm(const T* __restrict__ src, const int32_t* __restrict__ map,
+                                                   int V, int rows, int w, T* __restrict__ dst,
+                                                   const T* __restrict__ g, float eps, T* __restrict__ dst_norm) {
+  using E = Elem<T>;
+  const int lane = threadIdx.x & 63;
+  const int r = blockIdx.x * 4 + (threadIdx.x >> 6);
+  if (r >= rows) return;
+  long src_row, dst_row;
+  if (MODE == kEmbed) {
+    int t = map[r];
+    t = t < 0 ? 0 : (t >= V ? V - 1 : t);
+    src_row = t;
+    dst_row = r;
+  } else {
+    const int pos = map[r];
+    if (pos < 0) return;
+    src_row = (MODE == kGather) ? pos : r;
+    dst_row = (MODE == kGather) ? r : pos;
+  }
+  const int nchunk = w / E::kVec;
+  const uint4* s4 = reinterpret_cast<const uint4*>(src + src_row * (long)w);
+  uint4* d4 = dst ? reinterpret_cast<uint4*>(dst + dst_row * (long)w) : nullptr;
+  float ss = 0.f;
+  for (int c = lane; c < nchunk; c += kWave) {
+    const uint4 v = s4[c];
+    if (d4) d4[c] = v;
+    float f[E::kVec];
+    E::unpack(v, f);
+#pragma unroll
+    for (int e = 0; e < E::kVec; ++e) ss += f[e] * f[e];
+  }
+  if (!g) return;
+  ss = wave_sum(ss);
+  const float inv = 1.0f / sqrtf(ss / (float)w + eps);
+  const uint4* g4 = reinterpret_cast<const uint4*>(g);
+  uint4* n4 = reinterpret_cast<uint4*>(dst_norm + (long)r * w);
+  for (int c = lane; c < nchunk; c += kWave) {
+    float f[E::kVec], gf[E::kVec];
+    E::unpack(s4[c], f);
+    E::unpack(g4[c], gf);
+#pragma unroll
+    for (int e = 0; e < E::kVec; ++e) f[e] = f[e] * inv * gf[e];
+    n4[c] = E::pack(f);
+  }
+}
+
+template <int MODE>
+static hipError_t rows_norm(int dtype, const void* src, const int32_t* map, int V, int rows, int w, void* dst,
+                            const void* g, float eps, void* dst_norm, hipStream_t s) {
+  if (rows <= 0) return hipSuccess;
+  dim3 grid((rows + 3) / 4), block(256);
+  if (dtype == 0)
+    hipLaunchKernelGGL((k_rows_norm<float, MODE>), grid, block, 0, s, (const float*)src, map, V, rows, w,
+                       (float*)dst, (const float*)g, eps, (float*)dst_norm);
+  else
+    hipLaunchKernelGGL((k_rows_norm<bf16, MODE>), grid, block, 0, s, (const bf16*)src, map, V, rows, w,
+                       (bf16*)dst, (const bf16*)g, eps, (bf16*)dst_norm);
+  return hipGetLastError();
+}
+
+hipError_t launch_embed_norm(int dtype, const void* embed, const int32_t* tokens, int V, int rows, int d,
+                             const void* g, float eps, void* x, void* xn, hipStream_t s) {
+  return rows_norm<kEmbed>(dtype, embed, tokens, V, rows, d, x, g, eps, xn, s);
+}
+hipError_t launch_gather_norm(int dtype, const void* src, const int32_t* row_pos, int R, int w, void* dst,
+                              const void* g, float eps, void* dst_norm, hipStream_t s) {
+  return rows_norm<kGather>(dtype, src, row_pos, 0, R, w, dst, g, eps, dst_norm, s);
+}
+hipError_t launch_scatter_norm(int dtype, const void* src, const int32_t* row_pos, int R, int w, void* dst,
+                               const void* g, float eps, void* dst_norm, hipStream_t s) {
+  return rows_norm<kScatter>(dtype, src, row_pos, 0, R, w, dst, g, eps, dst_norm, s);
+}
+
+__global__ void k_row_pos(const int32_t* __restrict__ idx, const int32_t* __restrict__ n_active, int B, int S,
+                          int k_max, int32_t* __restrict__ row_pos) {
+  const int r = blockIdx.x * blockDim.x + threadIdx.x;
+  if (r >= B * k_max) return;
+  const int b = r / k_max, j = r - b * k_max;
+  int p = -1;
+  if (j < n_active[b]) {
+    const int i = idx[r];
+    p = (i >= 0 && i < S) ? b * S + i : -1;
+  }
+  row_pos[r] = p;
+}
+
+hipError_t launch_row_pos(const int32_t* idx, const int32_t* n_active, int B, int S, int k_max, int32_t* row_pos,
+                          hipStream_t s) {
+  const int n = B * k_max;
+  if (n <= 0) return hipSuccess;
+  hipLaunchKernelGGL(k_row_pos, dim3((n + 255) / 256), dim3(256), 0, s, idx, n_active, B, S, k_max, row_pos);
+  return hipGetLastError();
+}
+
+__global__ void k_identity_rows(int B, int S, int32_t* __restrict__ idx, int32_t* __restrict__ n_active) {
+  const int r = blockIdx.x * blockDim.x + threadIdx.x;
+  if (r < B * S) idx[r] = r % S;
+  if (r < B) n_active[r] = S;
+}
+
+hipError_t launch_identity_rows(int B, int S, int32_t* idx, int32_t* n_active, hipStream_t s) {
+  const int n = B * S;
+  hipLaunchKernelGGL(k_identity_rows, dim3((n + 255) / 256), dim3(256), 0, s, B, S, idx, n_active);
+  return hipGetLastError();
+}
+
+// ---- GEMM epilogues ----
+__device__ __forceinline__ float sum_splits(const float* __restrict__ p, int splits, long stride, long off) {
+  float v = p[off];
+  for (int k = 1; k < splits; ++k) v += p[off + k * stride];
+  return v;
+}
+
+// One workgroup per row.  Columns of the QKV product: [Q: Hq*D | K: Hkv*D | V: Hkv*D].
+template <typename T>
+__global__ __launch_bounds__(256) void k_qkv_epilogue(const float* __restrict__ part, int splits, long sstride,
+                                                      const int32_t* __restrict__ row_pos, int S, int Hq, int Hkv,
+                                                      int D, float rope_base, T* __restrict__ q, T* __restrict__ kc,
+                                                      T* __restrict__ vc) {
+  using E = Elem<T>;
+  __shared__ float cs[128], sn[128];
+  const int r = blockIdx.x;
+  const int pos = row_pos[r];
+  if (pos < 0) return;
+  const int b = pos / S, i = pos - b * S;
+  const int half = D / 2;
+  const int NQ = Hq * D, NK = Hkv * D, N = NQ + 2 * NK;
+  // rotation angles in double: theta_j = base^(-2j/D), angle = i * theta_j
+  for (int j = threadIdx.x; j < half; j += blockDim.x) {
+    const double theta = exp2(-(2.0 * j / (double)D) * log2((double)rope_base));
+    double sv, cv;
+    sincos((double)i * theta, &sv, &cv);
+    cs[j] = (float)cv;
+    sn[j] = (float)sv;
+  }
+  __syncthreads();
+  const long base = (long)r * N;
+  const int npairs = (Hq + Hkv) * half;
+  for (int p = threadIdx.x; p < npairs; p += blockDim.x) {
+    const int hh = p / half, j = p - hh * half;
+    const int c1 = hh * D + j, c2 = c1 + half;
+    const float x1 = sum_splits(part, splits, sstride, base + c1);
+    const float x2 = sum_splits(part, splits, sstride, base + c2);
+    const float y1 = x1 * cs[j] - x2 * sn[j];
+    const float y2 = x2 * cs[j] + x1 * sn[j];
+    if (hh < Hq) {
+      E::st(q, (long)r * NQ + c1, y1);
+      E::st(q, (long)r * NQ + c2, y2);
+    } else {
+      const long o = ((long)pos * Hkv + (hh - Hq)) * D;
+      E::st(kc, o + j, y1);
+      E::st(kc, o + j + half, y2);
+    }
+  }
+  for (int c = threadIdx.x; c < NK; c += blockDim.x)
+    E::st(vc, (long)pos * NK + c, sum_splits(part, splits, sstride, base + NQ + NK + c));
+}
+
+hipError_t launch_qkv_epilogue(int dtype, const float* part, int splits, long split_stride, const int32_t* row_pos,
+                               int R, int S, int Hq, int Hkv, int D, float rope_base, void* q, void* kc, void* vc,
+                               hipStream_t s) {
+  if (R <= 0) return hipSuccess;
+  if (dtype == 0)
+    hipLaunchKernelGGL(k_qkv_epilogue<float>, dim3(R), dim3(256), 0, s, part, splits, split_stride, row_pos, S, Hq,
+                       Hkv, D, rope_base, (float*)q, (float*)kc, (float*)vc);
+  else
+    hipLaunchKernelGGL(k_qkv_epilogue<bf16>, dim3(R), dim3(256), 0, s, part, splits, split_stride, row_pos, S, Hq,
+                       Hkv, D, rope_base, (bf16*)q, (bf16*)kc, (bf16*)vc);
+  return hipGetLastError();
+}
+
+// One wavefront per row: x += sum(partials) (rounded to storage), then xn = rmsnorm(x) * g.
+template <typename T>
+__global__ __launch_bounds__(256) void k_resid_norm(const float* __restrict__ part, int splits, long sstride,
+                                                    const int32_t* __restrict__ row_pos, int R, int d,
+                                                    T* __restrict__ x, const T* __restrict__ g, float eps,
+                                                    T* __restrict__ xn) {
+  using E = Elem<T>;
+  const int lane = threadIdx.x & 63;
+  const int r = blockIdx.x * 4 + (threadIdx.x >> 6);
+  if (r >= R || row_pos[r] < 0) return;
+  const int nchunk = d / E::kVec;
+  uint4* x4 = reinterpret_cast<uint4*>(x + (long)r * d);
+  const float* pr = part + (long)r * d;
+  float ss = 0.f;
+  for (int c = lane; c < nchunk; c += kWave) {
+    float f[E::kVec];
+    E::unpack(x4[c], f);
+#pragma unroll
+    for (int e = 0; e < E::kVec; ++e) f[e] += sum_splits(pr, splits, sstride, c * E::kVec + e);
+    const uint4 packed = E::pack(f);
+    x4[c] = packed;
+    E::unpack(packed, f);  // the stored (rounded) values feed the norm
+#pragma unroll
+    for (int e = 0; e < E::kVec; ++e) ss += f[e] * f[e];
+  }
+  if (!g) return;
+  ss = wave_sum(ss);
+  const float inv = 1.0f / sqrtf(ss / (float)d + eps);
+  const uint4* g4 = reinterpret_cast<const uint4*>(g);
+  uint4* n4 = reinterpret_cast<uint4*>(xn + (long)r * d);
+  for (int c = lane; c < nchunk; c += kWave) {
+    float f[E::kVec], gf[E::kVec];
+    E::unpack(x4[c], f);
+    E::unpack(g4[c], gf);
+#pragma unroll
+    for (int e = 0; e < E::kVec; ++e) f[e] = f[e] * inv * gf[e];
+    n4[c] = E::pack(f);
+  }
+}
+
+hipError_t launch_resid_norm(int dtype, const float* part, int splits, long split_stride, const int32_t* row_pos,
+                             int R, int d, void* x, const void* g, float eps, void* xn, hipStream_t s) {
+  if (R <= 0) return hipSuccess;
+  dim3 grid((R + 3) / 4), block(256);
+  if (dtype == 0)
+    hipLaunchKernelGGL(k_resid_norm<float>, grid, block, 0, s, part, splits, split_stride, row_pos, R, d, (float*)x,
+                       (const float*)g, eps, (float*)xn);
+  else
+    hipLaunchKernelGGL(k_resid_norm<bf16>, grid, block, 0, s, part, splits, split_stride, row_pos, R, d, (bf16*)x,
+                       (const bf16*)g, eps, (bf16*)xn);
+  return hipGetLastError();
+}
+
+template <typename T>
+__global__ __launch_bounds__(256) void k_swiglu(const float* __restrict__ part, int splits, long sstride,
+                                                const int32_t* __restrict__ row_pos, int R, int F, T* __restrict__ h) {
+  const long n4 = (long)R * F / 4;
+  for (long e4 = blockIdx.x * (long)blockDim.x + threadIdx.x; e4 < n4; e4 += (long)gridDim.x * blockDim.x) {
+    const long e = e4 * 4;
+    const int r = (int)(e / F);
+    if (row_pos[r] < 0) continue;
+    const int c = (int)(e - (long)r * F);
+    const long base = (long)r * 2 * F + c;
+#pragma unroll
+    for (int t = 0; t < 4; ++t) {
+      const float gt = sum_splits(part, splits, sstride, base + t);
+      const float up = sum_splits(part, splits, sstride, base + F + t);
+      const float sg = gt / (1.0f + expf(-gt));
+      Elem<T>::st(h, e + t, sg * up);
+    }
+  }
+}
+
+hipError_t launch_swiglu(int dtype, const float* part, int splits, long split_stride, const int32_t* row_pos, int R,
+                         int F, void* h, hipStream_t s) {
+  if (R <= 0) return hipSuccess;
+  const long n4 = (long)R * F / 4;
+  const int grid = (int)((n4 + 255) / 256 < 8192 ? (n4 + 255) / 256 : 8192);
+  if (dtype == 0)
+    hipLaunchKernelGGL(k_swiglu<float>, dim3(grid), dim3(256), 0, s, part, splits, split_stride, row_pos, R, F,
+                       (float*)h);
+  else
+    hipLaunchKernelGGL(k_swiglu<bf16>, dim3(grid), dim3(256), 0, s, part, splits, split_stride, row_pos, R, F,
+                       (bf16*)h);
+  return hipGetLastError();
+}
+
+hipError_t launch_copy(const void* src, void* dst, size_t bytes, hipStream_t s) {
+  if (bytes == 0) return hipSuccess;
+  return hipMemcpyAsync(dst, src, bytes, hipMemcpyDeviceToDevice, s);
+}
+
+}  // namespace dllm

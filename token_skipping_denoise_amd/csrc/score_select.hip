@@ -1,0 +1,277 @@
+// Importance scoring and active-row selection.
+//
+// Score (ES-dLLM summary, technical summary 2.1 item 1, Eq. 1): a weighted sum
+// of the previous iteration's confidence and the relative change of the
+// hidden state since the previous iteration; the change may instead be the
+// cosine change (dLLM-Cache explainer, section 3), the relative L2 change, or
+// the previous local KL (SureLock summary 2.1 item 1).
+//
+// Selection (ES-dLLM 2.1 item 2: keep the top-k positions; dLLM-Cache
+// section 3-4: recompute rows whose similarity is low, at a bounded ratio;
+// SureLock 2.1 item 2: locked rows never run again): one workgroup per
+// sequence runs an exact radix select over order-preserving 32-bit keys
+// (4 passes of 8 bits, LDS histograms), then a stable block-wide compaction
+// writes the chosen positions in ascending order.  Ties go to the lower
+// index, so the result is unique and bit-reproducible.
+#include <float.h>
+
+#include "common.h"
+#include "kernels.h"
+
+namespace dllm {
+
+enum { kVarL1N = 0, kVarCos = 1, kVarL2Rel = 2, kVarKL = 3, kVarNone = 4 };
+enum { kSelTopK = 0, kSelThreshCap = 1, kSelUnlocked = 2 };
+
+// One wavefront per row.  Sums are accumulated per lane in index order and
+// combined by a fixed butterfly, so the result is deterministic.
+template <typename T>
+__global__ __launch_bounds__(256) void k_score(const T* __restrict__ h_cur, const T* __restrict__ h_prev,
+                                               T* __restrict__ h_next, const float* __restrict__ conf_prev,
+                                               const float* __restrict__ kl_prev, const uint8_t* __restrict__ force,
+                                               int rows, int w, float alpha, int conf_inverted, int var,
+                                               float* __restrict__ score) {
+  using E = Elem<T>;
+  const int lane = threadIdx.x & 63;
+  const int r = blockIdx.x * 4 + (threadIdx.x >> 6);
+  if (r >= rows) return;
+  const int nchunk = w / E::kVec;
+  const uint4* a4 = reinterpret_cast<const uint4*>(h_cur + (long)r * w);
+  const uint4* b4 = reinterpret_cast<const uint4*>(h_prev + (long)r * w);
+  uint4* n4 = h_next ? reinterpret_cast<uint4*>(h_next + (long)r * w) : nullptr;
+  float l1 = 0.f, l2 = 0.f, na = 0.f, nb = 0.f;
+  int diff = 0;
+  const bool need_rows = (var == kVarL1N || var == kVarCos || var == kVarL2Rel);
+  if (need_rows || n4) {
+    for (int c = lane; c < nchunk; c += kWave) {
+      const uint4 va = a4[c];
+      if (n4) n4[c] = va;
+      if (!need_rows) continue;
+      const uint4 vb = b4[c];
+      float fa[E::kVec], fb[E::kVec];
+      E::unpack(va, fa);
+      E::unpack(vb, fb);
+#pragma unroll
+      for (int e = 0; e < E::kVec; ++e) {
+        const float dlt = fa[e] - fb[e];
+        diff |= (fa[e] != fb[e]);
+        l1 += fabsf(dlt);
+        l2 += dlt * dlt;
+        na += fa[e] * fa[e];
+        nb += fb[e] * fb[e];
+      }
+    }
+  }
+  float psi = 0.f;
+  if (var == kVarKL) {
+    psi = kl_prev[r];
+  } else if (need_rows) {
+    l1 = wave_sum(l1);
+    l2 = wave_sum(l2);
+    na = wave_sum(na);
+    nb = wave_sum(nb);
+    diff = wave_or(diff);
+    if (var == kVarL1N) {
+      psi = (nb == 0.f) ? (diff ? FLT_MAX : 0.f) : l1 / (sqrtf((float)w) * sqrtf(nb));
+    } else if (var == kVarL2Rel) {
+      psi = (nb == 0.f) ? (diff ? FLT_MAX : 0.f) : sqrtf(l2) / sqrtf(nb);
+    } else {  // cosine change, stable form 0.5 * || a/|a| - b/|b| ||^2
+      if (na == 0.f || nb == 0.f) {
+        psi = diff ? FLT_MAX : 0.f;
+      } else {
+        const float ia = 1.0f / sqrtf(na), ib = 1.0f / sqrtf(nb);
+        float c2 = 0.f;
+        for (int c = lane; c < nchunk; c += kWave) {
+          float fa[E::kVec], fb[E::kVec];
+          E::unpack(a4[c], fa);
+          E::unpack(b4[c], fb);
+#pragma unroll
+          for (int e = 0; e < E::kVec; ++e) {
+            const float t = fa[e] * ia - fb[e] * ib;
+            c2 += t * t;
+          }
+        }
+        psi = 0.5f * wave_sum(c2);
+      }
+    }
+  }
+  if (lane == 0) {
+    const float c = conf_prev[r];
+    const float phi = conf_inverted ? 1.0f - c : c;
+    score[r] = alpha * phi + (1.0f - alpha) * psi;
+  }
+  (void)force;
+}
+
+hipError_t launch_score(int dtype, const void* h_cur, const void* h_prev, void* h_next, const float* conf_prev,
+                        const float* kl_prev, const uint8_t* force, int rows, int width, float alpha,
+                        int conf_inverted, int var, float* score, hipStream_t s) {
+  if (rows <= 0) return hipSuccess;
+  dim3 grid((rows + 3) / 4), block(256);
+  if (dtype == 0)
+    hipLaunchKernelGGL(k_score<float>, grid, block, 0, s, (const float*)h_cur, (const float*)h_prev, (float*)h_next,
+                       conf_prev, kl_prev, force, rows, width, alpha, conf_inverted, var, score);
+  else
+    hipLaunchKernelGGL(k_score<bf16>, grid, block, 0, s, (const bf16*)h_cur, (const bf16*)h_prev, (bf16*)h_next,
+                       conf_prev, kl_prev, force, rows, width, alpha, conf_inverted, var, score);
+  return hipGetLastError();
+}
+
+// ---------------------------------------------------------------------------
+// Selection
+// ---------------------------------------------------------------------------
+constexpr int kSelThreads = 1024;
+constexpr int kSelWaves = kSelThreads / kWave;
+
+// Order-preserving key: larger key = selected earlier.  NaN -> 0 (below -inf),
+// -0 -> +0, forced rows -> 0xFFFFFFFF (above +inf).
+__device__ __forceinline__ uint32_t score_key(float f) {
+  uint32_t u = __float_as_uint(f);
+  if ((u & 0x7fffffffu) > 0x7f800000u) return 0u;
+  if (u == 0x80000000u) u = 0u;
+  return (u & 0x80000000u) ? ~u : (u | 0x80000000u);
+}
+
+struct BlockScan {
+  int wave_tot[kSelWaves];
+};
+
+// Exclusive prefix count of `flag` over the block (thread order) and the block total.
+__device__ __forceinline__ int block_excl_count(bool flag, BlockScan& sh, int& total) {
+  const int lane = threadIdx.x & 63, wv = threadIdx.x >> 6;
+  const unsigned long long m = __ballot(flag);
+  const int in_wave = __popcll(m & ((1ull << lane) - 1ull));
+  if (lane == 0) sh.wave_tot[wv] = __popcll(m);
+  __syncthreads();
+  int before = 0;
+  total = 0;
+  for (int i = 0; i < kSelWaves; ++i) {
+    const int t = sh.wave_tot[i];
+    if (i < wv) before += t;
+    total += t;
+  }
+  __syncthreads();
+  return before + in_wave;
+}
+
+__device__ __forceinline__ int block_count(bool flag, BlockScan& sh) {
+  int total;
+  (void)block_excl_count(flag, sh, total);
+  return total;
+}
+
+__global__ __launch_bounds__(kSelThreads) void k_select(const float* __restrict__ score,
+                                                        const uint8_t* __restrict__ force, int S, int sel, int k,
+                                                        float tau, int k_max, int32_t* __restrict__ idx,
+                                                        int32_t* __restrict__ n_active) {
+  __shared__ BlockScan sh;
+  __shared__ int hist[256];
+  __shared__ int bcast[2];
+  const int b = blockIdx.x;
+  const float* sc = score + (long)b * S;
+  const uint8_t* fo = force ? force + (long)b * S : nullptr;
+  const int tid = threadIdx.x;
+
+  // candidates and threshold qualifiers
+  int n_cand = 0, n_q = 0;
+  for (int i0 = 0; i0 < S; i0 += kSelThreads) {
+    const int i = i0 + tid;
+    bool cand = false, q = false;
+    if (i < S) {
+      const int f = fo ? fo[i] : 0;
+      cand = (f != 2);
+      q = cand && (f == 1 || sc[i] > tau);
+    }
+    n_cand += block_count(cand, sh);
+    n_q += block_count(q, sh);
+  }
+  int k_eff = (sel == kSelUnlocked) ? n_cand : (sel == kSelThreshCap ? min(k, n_q) : min(k, n_cand));
+  if (k_eff < 0) k_eff = 0;
+
+  // radix select of the k_eff-th largest key
+  uint32_t kth = 0u;
+  int take_eq = 0;  // how many keys equal to kth are taken (lowest indices first)
+  const bool take_all = (k_eff >= n_cand);
+  if (!take_all && k_eff > 0) {
+    uint32_t prefix = 0u, hmask = 0u;
+    int remaining = k_eff;
+    for (int shift = 24; shift >= 0; shift -= 8) {
+      for (int t = tid; t < 256; t += kSelThreads) hist[t] = 0;
+      __syncthreads();
+      for (int i = tid; i < S; i += kSelThreads) {
+        const int f = fo ? fo[i] : 0;
+        if (f == 2) continue;
+        const uint32_t key = (f == 1) ? 0xffffffffu : score_key(sc[i]);
+        if ((key & hmask) == prefix) atomicAdd(&hist[(key >> shift) & 255u], 1);
+      }
+      __syncthreads();
+      if (tid < kWave) {
+        // lane l owns bins 4l..4l+3; find the bin where the count from the top reaches `remaining`
+        int own = hist[4 * tid] + hist[4 * tid + 1] + hist[4 * tid + 2] + hist[4 * tid + 3];
+        int above = own;  // inclusive suffix sum over lanes >= tid
+#pragma unroll
+        for (int o = 1; o < kWave; o <<= 1) {
+          const int v = __shfl_down(above, o, kWave);
+          if (tid + o < kWave) above += v;
+        }
+        int acc = above - own;  // keys in bins above this lane's bins
+        for (int dgt = 4 * tid + 3; dgt >= 4 * tid; --dgt) {
+          const int hcount = hist[dgt];
+          if (acc < remaining && acc + hcount >= remaining) {
+            bcast[0] = dgt;
+            bcast[1] = acc;
+          }
+          acc += hcount;
+        }
+      }
+      __syncthreads();
+      const int dgt = bcast[0];
+      remaining -= bcast[1];
+      prefix |= (uint32_t)dgt << shift;
+      hmask |= 0xffu << shift;
+      __syncthreads();
+    }
+    kth = prefix;
+    take_eq = remaining;
+  }
+
+  // stable compaction in ascending index order
+  int carry_eq = 0, carry_sel = 0;
+  int32_t* out = idx + (long)b * k_max;
+  for (int i0 = 0; i0 < S; i0 += kSelThreads) {
+    const int i = i0 + tid;
+    bool gt = false, eq = false;
+    if (i < S) {
+      const int f = fo ? fo[i] : 0;
+      if (f != 2) {
+        if (take_all) {
+          gt = true;
+        } else if (k_eff > 0) {
+          const uint32_t key = (f == 1) ? 0xffffffffu : score_key(sc[i]);
+          gt = key > kth;
+          eq = key == kth;
+        }
+      }
+    }
+    int tot_eq;
+    const int eq_rank = carry_eq + block_excl_count(eq, sh, tot_eq);
+    const bool flag = gt || (eq && eq_rank < take_eq);
+    int tot_sel;
+    const int opos = carry_sel + block_excl_count(flag, sh, tot_sel);
+    if (flag && opos < k_max) out[opos] = i;
+    carry_eq += tot_eq;
+    carry_sel += tot_sel;
+  }
+  const int n = min(carry_sel, k_max);
+  for (int j = n + tid; j < k_max; j += kSelThreads) out[j] = -1;
+  if (tid == 0) n_active[b] = n;
+}
+
+hipError_t launch_select(const float* score, const uint8_t* force, int B, int S, int sel, int k, float tau,
+                         int k_max, int32_t* idx, int32_t* n_active, hipStream_t s) {
+  if (B <= 0) return hipSuccess;
+  hipLaunchKernelGGL(k_select, dim3(B), dim3(kSelThreads), 0, s, score, force, S, sel, k, tau, k_max, idx, n_active);
+  return hipGetLastError();
+}
+
+}  // namespace dllm
