@@ -1,0 +1,248 @@
+"""Benchmark: denoised tokens/s of the token-skipping denoising path on one MI355X.
+
+Default workload: the LLaDA-8B-shaped stack (32 layers, d 4096, 32 heads x 128,
+SwiGLU 12288, vocab 126464, bf16, random init N(0, 0.02)), batch 1, prompt 256,
+generation 256 in semi-autoregressive blocks of 32 over 64 denoising
+iterations, 4 tokens unmasked per iteration.  Iteration 0 runs every layer on
+every position; iterations 1..63 run layers 0-3 on all positions and layers
+4-31 on the top 25% (k = 128) by importance = 0.5 * conf + 0.5 * L1 change of
+the hidden state entering layer 4 (Eq. 1), skipped rows reusing cached K/V.
+One bench step = one whole generation (64 iterations); value = generated
+tokens / second.
+
+Prints ONE JSON line (rank 0, N = 1).  `roofline` describes the dominant
+kernel -- the gate/up + SwiGLU product of the skipped layers (128 active rows),
+timed live with HIP events bracketing each of its launches inside the timed
+region; `cpu_baseline` times the CPU oracle on a bounded sample (one dense
+layer, one sparse layer and the LM head) and extrapolates to a generation.
+"""
+from __future__ import annotations
+
+import argparse
+import ctypes
+import json
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+if ROOT not in sys.path:
+    sys.path.insert(0, ROOT)
+
+import torch  # noqa: E402
+
+from synth import workloads  # noqa: E402
+from token_skipping_denoise_amd import _ffi, api  # noqa: E402
+
+HBM_PEAK_GBS = 8000.0      # MI355X HBM3E, GB/s
+BF16_PEAK_TFLOPS = 2500.0  # MI355X dense bf16 MFMA
+
+
+class HipEvents:
+    """Raw hipEvent_t pairs (created through the HIP runtime) for the library's timing hook."""
+
+    def __init__(self, n: int):
+        self.hip = ctypes.CDLL("libamdhip64.so")
+        self.hip.hipEventCreate.argtypes = [ctypes.POINTER(ctypes.c_void_p)]
+        self.hip.hipEventElapsedTime.argtypes = [ctypes.POINTER(ctypes.c_float), ctypes.c_void_p, ctypes.c_void_p]
+        self.hip.hipEventDestroy.argtypes = [ctypes.c_void_p]
+        self.n = n
+        self.start = (ctypes.c_void_p * n)()
+        self.stop = (ctypes.c_void_p * n)()
+        for arr in (self.start, self.stop):
+            for i in range(n):
+                ev = ctypes.c_void_p()
+                if self.hip.hipEventCreate(ctypes.byref(ev)) != 0:
+                    raise RuntimeError("hipEventCreate failed")
+                arr[i] = ev
+
+    def elapsed_ms(self, count: int) -> list[float]:
+        out = []
+        for i in range(count):
+            ms = ctypes.c_float()
+            if self.hip.hipEventElapsedTime(ctypes.byref(ms), self.start[i], self.stop[i]) != 0:
+                raise RuntimeError("hipEventElapsedTime failed")
+            out.append(ms.value)
+        return out
+
+    def close(self):
+        for arr in (self.start, self.stop):
+            for i in range(self.n):
+                self.hip.hipEventDestroy(arr[i])
+
+
+def llada_generation(dims, k_sparse=128, boundary=4, steps=64, block=32):
+    """Per-iteration (cfg kwargs) of the semi-autoregressive early-skip generation."""
+    per_block = steps // ((dims.S - dims.prompt) // block)
+    out = []
+    for t in range(steps):
+        lo = dims.prompt + (t // per_block) * block
+        if t == 0:
+            out.append(dict(boundary_layer=boundary, full_step=True, score=None, unmask_n=4, block_lo=lo, block_hi=lo + block))
+        else:
+            sc = api.score_cfg(alpha=0.5, conf_inverted=False, var=api.VAR_L1N, sel=api.SEL_TOPK, k=k_sparse)
+            out.append(dict(boundary_layer=boundary, full_step=False, score=sc, unmask_n=4, block_lo=lo, block_hi=lo + block))
+    return out
+
+
+def run_generation(model, state, tok0, plan, ws):
+    state.tokens.copy_(tok0)
+    state.c.have_prev = 0
+    state.c.bnd_cur = 0
+    for kw in plan:
+        api.skip_step(model, state, api.step_cfg(ws=ws, **kw))
+
+
+def ffn_up_bytes(dims, rows: int) -> float:
+    """Algorithmic HBM bytes of one gate/up + SwiGLU launch: weights + input rows + output rows."""
+    e = 2
+    return (2 * dims.d_ff * dims.d + rows * dims.d + rows * dims.d_ff) * e
+
+
+def cpu_baseline(model_w_gpu, dims, k_sparse, boundary, steps):
+    """Time the oracle (float64 NumPy, bf16 storage rounding) on one dense layer, one sparse layer and the
+    LM head, then extrapolate to one generation."""
+    import numpy as np
+    from threadpoolctl import threadpool_info
+
+    from oracle.numerics import store_fn
+    from oracle.transformer import layer_rows, lm_logits
+    import synth
+
+    store = store_fn("bf16")
+    lw = {k: v.detach().to("cpu", torch.float64).numpy() for k, v in model_w_gpu["layers"][0].items()}
+    B, S, d = dims.B, dims.S, dims.d
+    x = synth.normal(synth.seed_of(900), (B * S, d), 1.0, torch.bfloat16).double().numpy()
+    kc = synth.normal(synth.seed_of(901), (B, S, dims.n_kv_heads, dims.head_dim), 1.0, torch.bfloat16).double().numpy()
+    vc = synth.normal(synth.seed_of(902), (B, S, dims.n_kv_heads, dims.head_dim), 1.0, torch.bfloat16).double().numpy()
+    rows_all = np.arange(B * S)
+
+    def t_layer(rows):
+        t0 = time.perf_counter()
+        layer_rows(lw, x[rows], rows % S, rows // S, kc, vc, n_heads=dims.n_heads, n_kv_heads=dims.n_kv_heads,
+                   rope_base=1e4, eps=1e-5, store=store)
+        return time.perf_counter() - t0
+
+    t_dense = t_layer(rows_all)
+    t_sparse = t_layer(rows_all[:k_sparse])
+    del lw
+    head = model_w_gpu["lm_head"].detach().to("cpu", torch.float64).numpy()
+    g = model_w_gpu["final_norm"].detach().to("cpu", torch.float64).numpy()
+    t0 = time.perf_counter()
+    lm_logits(x[:k_sparse], g, head, 1e-5, store)
+    t_head_sparse = time.perf_counter() - t0
+    t_head_dense = t_head_sparse * (B * S) / k_sparse
+    L = dims.n_layers
+    t_gen = (L * t_dense + t_head_dense) + (steps - 1) * (boundary * t_dense + (L - boundary) * t_sparse + t_head_sparse)
+    n_threads = max((p.get("num_threads", 1) for p in threadpool_info() if p.get("user_api") == "blas"), default=1)
+    gen_tokens = B * (S - dims.prompt)
+    return {
+        "value": gen_tokens / t_gen,
+        "unit": "tokens/s",
+        "cores": int(n_threads),
+        "kind": "oracle",
+        "sample": (f"oracle (float64 NumPy, bf16 storage) timed on one dense layer ({B * S} rows, {t_dense:.2f} s), "
+                   f"one sparse layer ({k_sparse} rows, {t_sparse:.2f} s) and the LM head on {k_sparse} rows "
+                   f"({t_head_sparse:.2f} s); extrapolated to one {steps}-iteration generation "
+                   f"({t_gen:.1f} s); host os.cpu_count()={os.cpu_count()}"),
+    }
+
+
+def main():
+    ap = argparse.ArgumentParser(description=__doc__.split("\n")[0])
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=3, help="timed generations")
+    ap.add_argument("--warmup", type=int, default=1, help="untimed generations")
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--no-kernel-timing", action="store_true")
+    args = ap.parse_args()
+    if args.gpus != 1:
+        print(f"bench.py runs on one GPU only: --gpus {args.gpus} is not supported "
+              "(sequences shard with no exchange; see the design notes)", file=sys.stderr)
+        sys.exit(2)
+    if not torch.cuda.is_available():
+        print("bench.py needs a GPU", file=sys.stderr)
+        sys.exit(2)
+
+    dims = workloads.LLADA
+    dev = "cuda:0"
+    k_sparse, boundary, n_iter = 128, 4, 64
+    t0 = time.perf_counter()
+    w = workloads.model_weights(dims, device=dev)
+    model = api.Model(w, dims.n_heads, dims.n_kv_heads, dims.mask_id)
+    torch.cuda.synchronize()
+    t_setup = time.perf_counter() - t0
+    tok0 = workloads.initial_tokens(dims, device=dev)
+    state = api.State(model, tok0.clone(), k_max=k_sparse, track_kl=False)
+    ws = api.alloc_workspace(model, dims.B, dims.S, k_sparse)
+    plan = llada_generation(dims, k_sparse, boundary, n_iter)
+
+    for _ in range(args.warmup):
+        run_generation(model, state, tok0, plan, ws)
+    torch.cuda.synchronize()
+
+    lib = _ffi.load()
+    n_launch = args.steps * (n_iter - 1) * (dims.n_layers - boundary)
+    timing = None
+    events = None
+    if not args.no_kernel_timing:
+        events = HipEvents(n_launch)
+        timing = _ffi.Timing(_ffi.TK_FFN_UP, k_sparse * dims.B, n_launch, 0,
+                             ctypes.cast(events.start, ctypes.POINTER(ctypes.c_void_p)),
+                             ctypes.cast(events.stop, ctypes.POINTER(ctypes.c_void_p)))
+        lib.dllm_set_timing(ctypes.byref(timing))
+
+    torch.cuda.synchronize()
+    t_start = time.perf_counter()
+    for _ in range(args.steps):
+        run_generation(model, state, tok0, plan, ws)
+    torch.cuda.synchronize()
+    elapsed = time.perf_counter() - t_start
+    if timing is not None:
+        lib.dllm_set_timing(None)
+
+    gen_tokens = dims.B * (dims.S - dims.prompt)
+    value = gen_tokens * args.steps / elapsed
+    roofline = None
+    if timing is not None and timing.count > 0:
+        durs = events.elapsed_ms(timing.count)
+        avg_ms = sum(durs) / len(durs)
+        bytes_per = ffn_up_bytes(dims, k_sparse * dims.B)
+        achieved = bytes_per / (avg_ms * 1e-3) / 1e9
+        roofline = {"bound": "hbm", "achieved": round(achieved, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                    "frac": round(achieved / HBM_PEAK_GBS, 4), "traffic": None,
+                    "kernel": "k_gemm_bf16<64,128,1> (gate/up + SwiGLU, 128 active rows)",
+                    "launches": timing.count, "avg_us": round(avg_ms * 1e3, 2),
+                    "bytes_per_launch": int(bytes_per)}
+        events.close()
+
+    cpu = None
+    if not args.no_cpu_baseline:
+        cpu = cpu_baseline(w, dims, k_sparse, boundary, n_iter)
+
+    line = {
+        "metric": "denoised tokens/s at 8B shapes on 1 MI355X",
+        "value": round(value, 2),
+        "unit": "tokens/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(elapsed / args.steps * 1e3, 3),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "bf16",
+        "data": "synthetic (seeded random-init weights N(0,0.02); prompt tokens uniform)",
+        "config": {"workload": "LLaDA-8B-shaped 32-layer early-skip generation (prompt 256 + gen 256, blocks of 32, "
+                               "64 iterations, layers 4-31 on top-128 rows)",
+                   "batch": dims.B, "seq_len": dims.S, "layers": dims.n_layers, "hidden": dims.d,
+                   "vocab": dims.vocab, "active_rows": k_sparse, "boundary_layer": boundary,
+                   "iterations_per_step": n_iter, "setup_s": round(t_setup, 1)},
+        "roofline": roofline,
+        "cpu_baseline": cpu,
+    }
+    print(json.dumps(line), flush=True)
+
+
+if __name__ == "__main__":
+    main()

@@ -214,6 +214,38 @@ int dllm_confidence_kl(const float *logits, float *logits_prev, const int32_t *r
  * On a full step every row is active (state->k_max must be >= S). */
 int dllm_skip_step(const dllm_model *model, dllm_state *state, const dllm_step_cfg *cfg, void *stream);
 
+/* Kernel classes the measurement hook can bracket. */
+typedef enum {
+  DLLM_TK_NONE = 0,
+  DLLM_TK_QKV = 1,      /* QKV product of a layer */
+  DLLM_TK_ATTN = 2,     /* bidirectional attention of a layer */
+  DLLM_TK_O = 3,        /* output projection of a layer */
+  DLLM_TK_FFN_UP = 4,   /* gate/up product with the SwiGLU epilogue */
+  DLLM_TK_FFN_DOWN = 5, /* down projection of a layer */
+  DLLM_TK_LM_HEAD = 6,  /* LM-head product */
+  DLLM_TK_VOCAB = 7,    /* confidence / argmax / KL vocabulary pass */
+  DLLM_TK_SCORE = 8,    /* importance scores */
+  DLLM_TK_SELECT = 9    /* active-row selection */
+} dllm_timed_kernel;
+
+typedef struct {
+  int32_t kernel;     /* dllm_timed_kernel to bracket */
+  int32_t max_rows;   /* only launches whose row capacity is <= max_rows (0: all) */
+  int32_t capacity;   /* number of event pairs in start/stop */
+  int32_t count;      /* out: event pairs recorded so far (the caller resets it) */
+  void **start;       /* host array [capacity] of caller-created hipEvent_t */
+  void **stop;        /* host array [capacity] of caller-created hipEvent_t */
+} dllm_timing;
+
+/* Measurement hook for benchmarks: while installed, each launch of the chosen
+ * kernel class made by dllm_skip_step / dllm_layer_sparse is bracketed by
+ * hipEventRecord(start[i]) / hipEventRecord(stop[i]) on that call's stream,
+ * for i = count, count+1, ... until capacity is reached.  The struct must
+ * outlive its installation; NULL removes the hook.  Process-wide, not
+ * thread-safe, not for use under stream capture.  Returns DLLM_EINVAL for a
+ * malformed struct. */
+int dllm_set_timing(dllm_timing *timing);
+
 /* Human-readable text of a dllm_status. */
 const char *dllm_status_string(int status);
 

@@ -91,7 +91,7 @@ def test_tiny_fp32_two_iterations():
     for l in range(dims.n_layers):
         assert_close(np64(gs.k_cache[l]), os_.k_cache[l], 1e-4, f"K cache {l} after sparse")
     np.testing.assert_allclose(np64(gs.kl).reshape(-1)[info["rows"]], os_.kl.reshape(-1)[info["rows"]],
-                               rtol=1e-3, atol=1e-6)
+                               rtol=2e-3, atol=2e-6)
 
 
 def _designed_conf(B, S, k, seed):

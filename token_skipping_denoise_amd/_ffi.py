@@ -15,7 +15,9 @@ FORCE_NONE, FORCE_ON, FORCE_EXCLUDED = 0, 1, 2
 EXPORTED = (
     "dllm_workspace_size", "dllm_score_select", "dllm_gather_rows", "dllm_scatter_rows",
     "dllm_layer_sparse", "dllm_confidence_kl", "dllm_skip_step", "dllm_status_string", "dllm_version",
+    "dllm_set_timing",
 )
+TK_NONE, TK_QKV, TK_ATTN, TK_O, TK_FFN_UP, TK_FFN_DOWN, TK_LM_HEAD, TK_VOCAB, TK_SCORE, TK_SELECT = range(10)
 
 
 class Dims(Structure):
@@ -50,6 +52,11 @@ class StepCfg(Structure):
                 ("block_lo", c_int32), ("block_hi", c_int32), ("ws", c_void_p), ("ws_bytes", c_size_t)]
 
 
+class Timing(Structure):
+    _fields_ = [("kernel", c_int32), ("max_rows", c_int32), ("capacity", c_int32), ("count", c_int32),
+                ("start", POINTER(c_void_p)), ("stop", POINTER(c_void_p))]
+
+
 _LIB = None
 
 
@@ -82,6 +89,8 @@ def load(path: str = LIB_PATH) -> ctypes.CDLL:
     lib.dllm_skip_step.argtypes = [POINTER(ModelC), POINTER(StateC), POINTER(StepCfg), c_void_p]
     lib.dllm_status_string.restype = ctypes.c_char_p
     lib.dllm_status_string.argtypes = [c_int32]
+    lib.dllm_set_timing.restype = c_int32
+    lib.dllm_set_timing.argtypes = [POINTER(Timing)]
     lib.dllm_version.restype = c_int32
     lib.dllm_version.argtypes = []
     _LIB = lib

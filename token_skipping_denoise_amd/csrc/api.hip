@@ -25,6 +25,27 @@ int esize(int dtype) { return dtype == DLLM_F32 ? 4 : 2; }
     if ((expr) != hipSuccess) return DLLM_ELAUNCH; \
   } while (0)
 
+// Measurement hook: brackets launches of one kernel class with caller-created events.
+dllm_timing* g_timing = nullptr;
+
+struct TimedRegion {
+  dllm_timing* t = nullptr;
+  hipStream_t s;
+  int slot = -1;
+  TimedRegion(int kernel, int rows, hipStream_t st) : s(st) {
+    dllm_timing* g = g_timing;
+    if (!g || g->kernel != kernel || (g->max_rows > 0 && rows > g->max_rows) || g->count >= g->capacity) return;
+    t = g;
+    slot = g->count;
+    hipEventRecord((hipEvent_t)g->start[slot], s);
+  }
+  ~TimedRegion() {
+    if (!t) return;
+    hipEventRecord((hipEvent_t)t->stop[slot], s);
+    t->count = slot + 1;
+  }
+};
+
 // Workspace layout for (dims, dtype, k_max).
 struct WsLayout {
   size_t xfull, xact, xn, q, o, h, part, logits, scores, idx_id, nact_full, rowpos_d, rowpos_s, total;
@@ -124,18 +145,37 @@ int run_layer(const Ctx& c, int l, void* x, const int32_t* nact, const int32_t* 
   const float eps = c.m->rms_eps;
 
   GemmPlan p = gemm_plan(c.dtype, R, NQKV, d.d);
-  DLLM_TRY(launch_gemm(c.dtype, p, xn, w.w_qkv, part, R, NQKV, d.d, nact, kx, c.s));
+  {
+    TimedRegion t(DLLM_TK_QKV, R, c.s);
+    DLLM_TRY(launch_gemm(c.dtype, p, xn, w.w_qkv, part, R, NQKV, d.d, nact, kx, c.s));
+  }
   DLLM_TRY(launch_qkv_epilogue(c.dtype, part, p.splits, (long)R * NQKV, row_pos, R, d.S, d.n_heads, d.n_kv_heads,
                                d.head_dim, c.m->rope_base, q, kc, vc, c.s));
-  DLLM_TRY(launch_attention(c.dtype, q, kc, vc, o, nact, d.B, d.S, kx, d.n_heads, d.n_kv_heads, d.head_dim, c.s));
+  {
+    TimedRegion t(DLLM_TK_ATTN, R, c.s);
+    DLLM_TRY(launch_attention(c.dtype, q, kc, vc, o, nact, d.B, d.S, kx, d.n_heads, d.n_kv_heads, d.head_dim, c.s));
+  }
   p = gemm_plan(c.dtype, R, d.d, HQD);
-  DLLM_TRY(launch_gemm(c.dtype, p, o, w.w_o, part, R, d.d, HQD, nact, kx, c.s));
+  {
+    TimedRegion t(DLLM_TK_O, R, c.s);
+    DLLM_TRY(launch_gemm(c.dtype, p, o, w.w_o, part, R, d.d, HQD, nact, kx, c.s));
+  }
   DLLM_TRY(launch_resid_norm(c.dtype, part, p.splits, (long)R * d.d, row_pos, R, d.d, x, w.ffn_norm, eps, xn, c.s));
-  p = gemm_plan(c.dtype, R, 2 * d.d_ff, d.d);
-  DLLM_TRY(launch_gemm(c.dtype, p, xn, w.w_gate_up, part, R, 2 * d.d_ff, d.d, nact, kx, c.s));
-  DLLM_TRY(launch_swiglu(c.dtype, part, p.splits, (long)R * 2 * d.d_ff, row_pos, R, d.d_ff, h, c.s));
+  if (c.dtype == DLLM_BF16) {
+    p = gemm_plan(c.dtype, R, d.d_ff, d.d, true);
+    TimedRegion t(DLLM_TK_FFN_UP, R, c.s);
+    DLLM_TRY(launch_gemm_swiglu(p, xn, w.w_gate_up, h, R, d.d_ff, d.d, nact, kx, c.s));
+  } else {
+    p = gemm_plan(c.dtype, R, 2 * d.d_ff, d.d);
+    TimedRegion t(DLLM_TK_FFN_UP, R, c.s);
+    DLLM_TRY(launch_gemm(c.dtype, p, xn, w.w_gate_up, part, R, 2 * d.d_ff, d.d, nact, kx, c.s));
+    DLLM_TRY(launch_swiglu(c.dtype, part, p.splits, (long)R * 2 * d.d_ff, row_pos, R, d.d_ff, h, c.s));
+  }
   p = gemm_plan(c.dtype, R, d.d, d.d_ff);
-  DLLM_TRY(launch_gemm(c.dtype, p, h, w.w_down, part, R, d.d, d.d_ff, nact, kx, c.s));
+  {
+    TimedRegion t(DLLM_TK_FFN_DOWN, R, c.s);
+    DLLM_TRY(launch_gemm(c.dtype, p, h, w.w_down, part, R, d.d, d.d_ff, nact, kx, c.s));
+  }
   DLLM_TRY(launch_resid_norm(c.dtype, part, p.splits, (long)R * d.d, row_pos, R, d.d, x, next_g, eps, xn, c.s));
   return DLLM_OK;
 }
@@ -159,6 +199,12 @@ int check_model(const dllm_model* m) {
 extern "C" {
 
 int dllm_version(void) { return 100; }
+
+int dllm_set_timing(dllm_timing* t) {
+  if (t && (t->capacity < 0 || (t->capacity > 0 && (!t->start || !t->stop)))) return DLLM_EINVAL;
+  g_timing = t;
+  return DLLM_OK;
+}
 
 const char* dllm_status_string(int status) {
   switch (status) {
@@ -338,9 +384,15 @@ int dllm_skip_step(const dllm_model* model, dllm_state* state, const dllm_step_c
       return DLLM_OK;
     }
     float* scores = c.at<float>(c.L.scores);
-    DLLM_TRY(launch_score(c.dtype, xfull, h_prev, h_next, state->conf, state->kl, state->force, Rd, d.d, sc.alpha,
-                          sc.conf_inverted, sc.var, scores, c.s));
-    DLLM_TRY(launch_select(scores, state->force, B, S, sc.sel, sc.k, sc.tau, kx, state->idx, state->n_active, c.s));
+    {
+      TimedRegion t(DLLM_TK_SCORE, Rd, c.s);
+      DLLM_TRY(launch_score(c.dtype, xfull, h_prev, h_next, state->conf, state->kl, state->force, Rd, d.d, sc.alpha,
+                            sc.conf_inverted, sc.var, scores, c.s));
+    }
+    {
+      TimedRegion t(DLLM_TK_SELECT, Rd, c.s);
+      DLLM_TRY(launch_select(scores, state->force, B, S, sc.sel, sc.k, sc.tau, kx, state->idx, state->n_active, c.s));
+    }
     DLLM_TRY(launch_row_pos(state->idx, state->n_active, B, S, kx, rp_s, c.s));
     const void* g = (b_lay < L) ? model->layers[b_lay].attn_norm : model->final_norm;
     DLLM_TRY(launch_gather_norm(c.dtype, xfull, rp_s, Rs, d.d, xact, g, eps, xn, c.s));
@@ -379,9 +431,15 @@ int dllm_skip_step(const dllm_model* model, dllm_state* state, const dllm_step_c
   float* logits = c.at<float>(c.L.logits);
   GemmPlan p = gemm_plan(c.dtype, R, d.vocab, d.d);
   p.splits = 1;
-  DLLM_TRY(launch_gemm(c.dtype, p, xn, model->lm_head, logits, R, d.vocab, d.d, nact, kk, c.s));
-  DLLM_TRY(launch_conf_kl(logits, state->logits_prev, rp, R, d.vocab, model->mask_id, state->have_prev, state->conf,
-                          state->argmax, state->kl, c.s));
+  {
+    TimedRegion t(DLLM_TK_LM_HEAD, R, c.s);
+    DLLM_TRY(launch_gemm(c.dtype, p, xn, model->lm_head, logits, R, d.vocab, d.d, nact, kk, c.s));
+  }
+  {
+    TimedRegion t(DLLM_TK_VOCAB, R, c.s);
+    DLLM_TRY(launch_conf_kl(logits, state->logits_prev, rp, R, d.vocab, model->mask_id, state->have_prev,
+                            state->conf, state->argmax, state->kl, c.s));
+  }
   if (cfg->lock_kl_eps >= 0.f && state->have_prev)
     DLLM_TRY(launch_lock_update(rp, R, state->conf, state->kl, cfg->lock_kl_eps, cfg->lock_conf_min, state->force,
                                 c.s));

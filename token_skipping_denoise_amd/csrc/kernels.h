@@ -41,9 +41,12 @@ hipError_t launch_copy(const void* src, void* dst, size_t bytes, hipStream_t s);
 struct GemmPlan {
   int bm, bn, splits;
 };
-GemmPlan gemm_plan(int dtype, int M, int N, int K);
+GemmPlan gemm_plan(int dtype, int M, int N, int K, bool swiglu = false);
 hipError_t launch_gemm(int dtype, const GemmPlan& p, const void* A, const void* W, float* C, int M, int N, int K,
                        const int32_t* n_active, int k_max, hipStream_t s);
+// H[m][f] = silu(sum_k A[m][k] Wg[f][k]) * sum_k A[m][k] Wu[f][k], W_gate_up = [Wg; Wu] (bf16 only).
+hipError_t launch_gemm_swiglu(const GemmPlan& p, const void* A, const void* W_gate_up, void* H, int M, int F, int K,
+                              const int32_t* n_active, int k_max, hipStream_t s);
 
 // ---------------- attention (attention.hip) ----------------
 // o[r, h, :] = softmax(q[r, h] . Kc[b, :, h/g] / sqrt(D)) Vc[b, :, h/g] over all S keys.

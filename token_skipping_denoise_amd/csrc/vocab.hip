@@ -101,8 +101,8 @@ __global__ __launch_bounds__(kVT) void k_conf_kl(const float* __restrict__ logit
     argmax[pos] = f.am;
     if (kl) {
       if (do_kl) {
-        const float lse = f.m + logf(f.s), lsep = f.mp + logf(f.sp);
-        kl[pos] = fmaxf(0.f, f.t / f.s - (lse - lsep));
+        // lse - lse' = (m - m') + log(s / s'): avoids cancelling two O(log V) quantities
+        kl[pos] = fmaxf(0.f, f.t / f.s - (f.m - f.mp) - logf(f.s / f.sp));
       } else {
         kl[pos] = INFINITY;
       }
