@@ -22,6 +22,9 @@ CASES = {
     "bf16_full_rows": (workloads.shrink(workloads.LLADA, n_layers=1, d=512, n_heads=4, n_kv_heads=4, d_ff=1024,
                                         vocab=1000, B=1, S=192, prompt=96), 0.05, [192], 192),
     "f32_tiny": (workloads.shrink(workloads.TINY, n_layers=1, B=2, S=70), 0.1, [17, 30], 30),
+    # few query blocks over 9 key tiles (ragged): the key range is split across workgroups
+    "bf16_split_kv": (workloads.shrink(workloads.DREAM, n_layers=1, d=256, n_heads=2, n_kv_heads=1, d_ff=384,
+                                       vocab=1000, B=1, S=520, prompt=256), 0.1, [40], 40),
 }
 
 

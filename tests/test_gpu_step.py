@@ -104,9 +104,10 @@ def _designed_conf(B, S, k, seed):
     return conf.astype(np.float32)
 
 
-@pytest.mark.parametrize("b_lay", [0, 1, 3])
-def test_bf16_early_skip_iteration(b_lay):
-    dims = workloads.shrink(workloads.LLADA, n_layers=3, d=256, n_heads=2, n_kv_heads=2, d_ff=512, vocab=1000,
+@pytest.mark.parametrize("b_lay,vocab", [(0, 1000), (1, 1000), (3, 1000), (1, 32768)])
+def test_bf16_early_skip_iteration(b_lay, vocab):
+    # vocab 32768 with 48 active rows exercises the sliced vocabulary pass
+    dims = workloads.shrink(workloads.LLADA, n_layers=3, d=256, n_heads=2, n_kv_heads=2, d_ff=512, vocab=vocab,
                             B=2, S=96, prompt=48)
     k = 24
     print(f"bf16 early-skip b={b_lay}", flush=True)

@@ -48,7 +48,7 @@ struct TimedRegion {
 
 // Workspace layout for (dims, dtype, k_max).
 struct WsLayout {
-  size_t xfull, xact, xn, q, o, h, part, logits, scores, idx_id, nact_full, rowpos_d, rowpos_s, total;
+  size_t xfull, xact, xn, q, o, h, part, attn, vpart, logits, scores, idx_id, nact_full, rowpos_d, rowpos_s, total;
 };
 
 long max_part_floats(const dllm_dims& d, int dtype, long M) {
@@ -81,6 +81,9 @@ bool plan_ws(const dllm_dims& d, int dtype, int k_max, WsLayout& L) {
   L.o = take(R * HQD * es);
   L.h = take(R * (long)d.d_ff * es);
   L.part = take(std::max(max_part_floats(d, dtype, Rd), max_part_floats(d, dtype, Rs)) * sizeof(float));
+  L.attn = take(std::max(attention_part_bytes(dtype, d.B, d.S, d.S, d.n_heads, d.n_kv_heads),
+                         attention_part_bytes(dtype, d.B, d.S, k_max, d.n_heads, d.n_kv_heads)));
+  L.vpart = take(std::max(conf_kl_part_bytes((int)Rd, d.vocab), conf_kl_part_bytes((int)Rs, d.vocab)));
   L.logits = take(R * (long)d.vocab * sizeof(float));
   L.scores = take(Rd * sizeof(float));
   L.idx_id = take(Rd * sizeof(int32_t));
@@ -153,7 +156,8 @@ int run_layer(const Ctx& c, int l, void* x, const int32_t* nact, const int32_t* 
                                d.head_dim, c.m->rope_base, q, kc, vc, c.s));
   {
     TimedRegion t(DLLM_TK_ATTN, R, c.s);
-    DLLM_TRY(launch_attention(c.dtype, q, kc, vc, o, nact, d.B, d.S, kx, d.n_heads, d.n_kv_heads, d.head_dim, c.s));
+    DLLM_TRY(launch_attention(c.dtype, q, kc, vc, o, nact, d.B, d.S, kx, d.n_heads, d.n_kv_heads, d.head_dim,
+                              c.at<float>(c.L.attn), c.s));
   }
   p = gemm_plan(c.dtype, R, d.d, HQD);
   {
@@ -319,7 +323,7 @@ int dllm_confidence_kl(const float* logits, float* logits_prev, const int32_t* r
                        int32_t exclude_id, int32_t have_prev, float* conf, int32_t* argmax, float* kl, void* stream) {
   if (!logits || !row_pos || !conf || !argmax) return DLLM_EINVAL;
   if (R < 0 || V < 2 || exclude_id >= V) return DLLM_ESHAPE;
-  DLLM_TRY(launch_conf_kl(logits, logits_prev, row_pos, R, V, exclude_id, have_prev, conf, argmax, kl,
+  DLLM_TRY(launch_conf_kl(logits, logits_prev, row_pos, R, V, exclude_id, have_prev, conf, argmax, kl, nullptr,
                           (hipStream_t)stream));
   return DLLM_OK;
 }
@@ -438,7 +442,7 @@ int dllm_skip_step(const dllm_model* model, dllm_state* state, const dllm_step_c
   {
     TimedRegion t(DLLM_TK_VOCAB, R, c.s);
     DLLM_TRY(launch_conf_kl(logits, state->logits_prev, rp, R, d.vocab, model->mask_id, state->have_prev,
-                            state->conf, state->argmax, state->kl, c.s));
+                            state->conf, state->argmax, state->kl, c.ws + c.L.vpart, c.s));
   }
   if (cfg->lock_kl_eps >= 0.f && state->have_prev)
     DLLM_TRY(launch_lock_update(rp, R, state->conf, state->kl, cfg->lock_kl_eps, cfg->lock_conf_min, state->force,

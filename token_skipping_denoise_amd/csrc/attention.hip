@@ -62,13 +62,16 @@ constexpr int kHD = 128;          // head dim
 constexpr int kLDK = kHD + 8;     // K tile row stride (elements)
 constexpr int kLDV = kKT + 4;     // V^T tile row stride (elements)
 
+// With nsplit > 1 the key tiles are divided among nsplit workgroups (split-KV): each writes
+// its unnormalised output and softmax statistics (max, sum, in the exp2 domain) to `part`,
+// and k_attn_merge combines them.
 __global__ __launch_bounds__(256, 2) void k_attn_bf16(const uint16_t* __restrict__ q, const uint16_t* __restrict__ kc,
                                                       const uint16_t* __restrict__ vc, uint16_t* __restrict__ o,
                                                       const int32_t* __restrict__ n_active, int S, int k_max, int Hq,
-                                                      int Hkv, float scale_log2e) {
+                                                      int Hkv, float scale_log2e, int nsplit, float* __restrict__ part) {
   __shared__ __attribute__((aligned(16))) uint16_t Ks[2][kKT * kLDK];
   __shared__ __attribute__((aligned(16))) uint16_t Vt[2][kHD * kLDV];
-  const int b = blockIdx.z, hk = blockIdx.y;
+  const int b = blockIdx.z / nsplit, split = blockIdx.z - b * nsplit, hk = blockIdx.y;
   const int g = Hq / Hkv;
   const int nq = n_active[b] * g;
   const int qb0 = blockIdx.x * 128;
@@ -131,13 +134,14 @@ __global__ __launch_bounds__(256, 2) void k_attn_bf16(const uint16_t* __restrict
     for (int e = 0; e < 16; ++e) oacc[db][e] = 0.f;
   float m_run = -INFINITY, l_run = 0.f;
 
-  const int ntiles = (S + kKT - 1) / kKT;
-  load_global(0);
+  const int ntiles_all = (S + kKT - 1) / kKT;
+  const int t_begin = (int)((long)split * ntiles_all / nsplit), t_end = (int)((long)(split + 1) * ntiles_all / nsplit);
+  load_global(t_begin * kKT);
   store_lds(0);
   __syncthreads();
-  for (int t = 0; t < ntiles; ++t) {
-    const int buf = t & 1;
-    const bool more = t + 1 < ntiles;
+  for (int t = t_begin; t < t_end; ++t) {
+    const int buf = (t - t_begin) & 1;
+    const bool more = t + 1 < t_end;
     if (more) load_global((t + 1) * kKT);
 
     // S^T for two 32-key blocks
@@ -209,6 +213,24 @@ __global__ __launch_bounds__(256, 2) void k_attn_bf16(const uint16_t* __restrict
   }
 
   if (!qvalid) return;
+  if (nsplit > 1) {
+    // partial layout: [split][row][head][D + 2] = unnormalised O, then (m, l)
+    const long n_rows = (long)(gridDim.z / nsplit) * k_max;  // B * k_max
+    float* pp = part + (((long)split * n_rows + qrow) * Hq + h) * (kHD + 2);
+#pragma unroll
+    for (int db = 0; db < kHD / 32; ++db)
+#pragma unroll
+      for (int e4 = 0; e4 < 4; ++e4) {
+        const int d = db * 32 + 8 * e4 + 4 * hi;
+        *reinterpret_cast<float2*>(pp + d) = make_float2(oacc[db][4 * e4], oacc[db][4 * e4 + 1]);
+        *reinterpret_cast<float2*>(pp + d + 2) = make_float2(oacc[db][4 * e4 + 2], oacc[db][4 * e4 + 3]);
+      }
+    if (hi == 0) {
+      pp[kHD] = m_run;
+      pp[kHD + 1] = l_run;
+    }
+    return;
+  }
   const float inv_l = 1.0f / l_run;
   uint16_t* op = o + (qrow * Hq + h) * kHD;
 #pragma unroll
@@ -222,8 +244,44 @@ __global__ __launch_bounds__(256, 2) void k_attn_bf16(const uint16_t* __restrict
     }
 }
 
+// Combine split-KV partials: O = sum_s O_s 2^(m_s - M) / sum_s l_s 2^(m_s - M).
+__global__ __launch_bounds__(128) void k_attn_merge(const float* __restrict__ part, int nsplit, long split_stride,
+                                                    const int32_t* __restrict__ n_active, int k_max, int Hq,
+                                                    uint16_t* __restrict__ o) {
+  const int r = blockIdx.x, h = blockIdx.y, d = threadIdx.x;
+  const int b = r / k_max, j = r - b * k_max;
+  if (j >= n_active[b]) return;
+  const float* p0 = part + ((long)r * Hq + h) * (kHD + 2);
+  float M = -INFINITY;
+  for (int sp = 0; sp < nsplit; ++sp) M = fmaxf(M, p0[sp * split_stride + kHD]);
+  float L = 0.f, acc = 0.f;
+  for (int sp = 0; sp < nsplit; ++sp) {
+    const float* ps = p0 + sp * split_stride;
+    const float w = exp2f(ps[kHD] - M);
+    L += ps[kHD + 1] * w;
+    acc += ps[d] * w;
+  }
+  o[((long)r * Hq + h) * kHD + d] = f2bf(acc / L);
+}
+
+int attention_splits(int dtype, int B, int S, int k_max, int Hq, int Hkv) {
+  if (dtype == 0) return 1;
+  const int g = Hq / Hkv;
+  const long wgs = (long)((k_max * g + 127) / 128) * Hkv * B;
+  const int ntiles = (S + kKT - 1) / kKT;
+  int ns = 1;
+  while (ns < 4 && wgs * ns < 256 && ntiles / (ns * 2) >= 2) ns *= 2;
+  return ns;
+}
+
+size_t attention_part_bytes(int dtype, int B, int S, int k_max, int Hq, int Hkv) {
+  const int ns = attention_splits(dtype, B, S, k_max, Hq, Hkv);
+  return ns > 1 ? (size_t)ns * B * k_max * Hq * (kHD + 2) * sizeof(float) : 0;
+}
+
 hipError_t launch_attention(int dtype, const void* q, const void* kc, const void* vc, void* o,
-                            const int32_t* n_active, int B, int S, int k_max, int Hq, int Hkv, int D, hipStream_t s) {
+                            const int32_t* n_active, int B, int S, int k_max, int Hq, int Hkv, int D, float* part,
+                            hipStream_t s) {
   if (B <= 0 || k_max <= 0) return hipSuccess;
   if (dtype == 0) {
     if (D % kWave != 0 || D > 2 * kWave) return hipErrorInvalidValue;
@@ -235,8 +293,13 @@ hipError_t launch_attention(int dtype, const void* q, const void* kc, const void
   const int g = Hq / Hkv;
   const int qblocks = (k_max * g + 127) / 128;
   const float scale_log2e = (float)(1.0 / sqrt((double)D) * 1.4426950408889634);
-  hipLaunchKernelGGL(k_attn_bf16, dim3(qblocks, Hkv, B), dim3(256), 0, s, (const uint16_t*)q, (const uint16_t*)kc,
-                     (const uint16_t*)vc, (uint16_t*)o, n_active, S, k_max, Hq, Hkv, scale_log2e);
+  const int ns = attention_splits(dtype, B, S, k_max, Hq, Hkv);
+  if (ns > 1 && !part) return hipErrorInvalidValue;
+  hipLaunchKernelGGL(k_attn_bf16, dim3(qblocks, Hkv, B * ns), dim3(256), 0, s, (const uint16_t*)q, (const uint16_t*)kc,
+                     (const uint16_t*)vc, (uint16_t*)o, n_active, S, k_max, Hq, Hkv, scale_log2e, ns, part);
+  if (ns > 1)
+    hipLaunchKernelGGL(k_attn_merge, dim3(B * k_max, Hq), dim3(kHD), 0, s, part, ns, (long)B * k_max * Hq * (kHD + 2),
+                       n_active, k_max, Hq, (uint16_t*)o);
   return hipGetLastError();
 }
 

@@ -7,10 +7,11 @@
 // CDNA matrix cores.
 //
 // bf16 path: v_mfma_f32_32x32x16_bf16 (gfx950), fp32 accumulation,
-// 256 threads = 2x2 wavefronts, BK = 64, double-buffered LDS tiles padded to
-// 72 elements per row (conflict-free 16-byte fragment reads), global loads for
-// tile k+1 issued before the MFMAs of tile k.  Split-K writes fp32 partials
-// that the row epilogues reduce; row tiles with no live row exit at once.
+// 256 threads = 2x2 wavefronts, BK = 64, tiles streamed from memory straight
+// into a multi-stage LDS ring with global_load_lds_dwordx4 (no register
+// staging), XOR-swizzled so MFMA fragment reads are conflict-free.  Split-K
+// writes fp32 partials that the row epilogues reduce; row tiles with no live
+// row exit at once.
 // Workgroup ids are remapped so that each XCD works on a contiguous range of
 // tiles, m-tile fastest, so tiles sharing a weight panel share that XCD's L2.
 //
@@ -23,8 +24,6 @@ namespace dllm {
 typedef __bf16 bf16x8_t __attribute__((ext_vector_type(8)));
 typedef float f32x16_t __attribute__((ext_vector_type(16)));
 
-constexpr int kBK = 64;
-constexpr int kLDK = kBK + 8;  // padded LDS row (elements)
 
 __device__ __forceinline__ bool tile_live(int m0, int bm, int M, const int32_t* __restrict__ n_active, int k_max) {
   if (!n_active) return true;
@@ -53,29 +52,58 @@ __device__ __forceinline__ void decode_tile(int nt, int tiles_m, int tiles_n, in
 //          in each wavefront's half of the tile the first TN/2 column blocks
 //          hold gate rows and the last TN/2 the matching up rows, so a lane
 //          holds both factors of its outputs.  splits must be 1.
-template <int BM, int BN, int EPI>
-__global__ __launch_bounds__(256, 2) void k_gemm_bf16(const uint16_t* __restrict__ A, const uint16_t* __restrict__ W,
-                                                      float* __restrict__ C, uint16_t* __restrict__ H, int M, int N,
-                                                      int K, int splits, int tiles_m, int tiles_n,
-                                                      const int32_t* __restrict__ n_active, int k_max) {
-  constexpr int TM = BM / 64, TN = BN / 64;        // 32x32 MFMA tiles per wavefront
-  constexpr int CA = BM / 32, CB = BN / 32;        // 16-byte chunks per thread per tile
+//
+// Direct-to-LDS variant (gfx950 global_load_lds_dwordx4): tiles stream from
+// memory straight into an NS-stage LDS ring with no register staging, so
+// NS-1 tiles stay in flight while one is multiplied.  BK = 64: a tile row is
+// 128 bytes = 8 chunks of 16 bytes; one wave load instruction fills 8 rows
+// (1 KB), and chunk c of row r is stored at slot c ^ (r & 7), so the 32-row
+// MFMA fragment reads hit 32 distinct banks.
+// s_waitcnt with only vmcnt constrained (expcnt/lgkmcnt left at their maxima).
+template <int N>
+__device__ __forceinline__ void wait_vm() {
+  static_assert(N >= 0 && N < 64, "vmcnt is a 6-bit field");
+  __builtin_amdgcn_s_waitcnt((N & 15) | ((N >> 4) << 14) | (7 << 4) | (15 << 8));
+}
+// Wait until at most `ahead` stages of PER loads each are still in flight (ahead <= MAXA).
+// An if-chain on a uniform value: a switch would become a jump table (a scalar load and an
+// indirect branch on every K step).
+template <int MAXA, int PER>
+__device__ __forceinline__ void wait_stages(int ahead) {
+  if constexpr (MAXA <= 0) {
+    wait_vm<0>();
+  } else {
+    if (ahead >= MAXA) wait_vm<MAXA * PER>();
+    else wait_stages<MAXA - 1, PER>(ahead);
+  }
+}
+
+typedef __attribute__((address_space(3))) void lds_void;
+
+template <int BM, int BN, int NS, int EPI, int OCC>
+__global__ __launch_bounds__(256, OCC) void k_gemm_lds(const uint16_t* __restrict__ A, const uint16_t* __restrict__ W,
+                                                     float* __restrict__ C, uint16_t* __restrict__ H, int M, int N,
+                                                     int K, int splits, int tiles_m, int tiles_n,
+                                                     const int32_t* __restrict__ n_active, int k_max) {
+  constexpr int BK = 64;
+  constexpr int TM = BM / 64, TN = BN / 64;
+  constexpr int LA = BM / 32, LB = BN / 32;  // load instructions per wave per stage (8 rows each)
+  constexpr int STAGE = (BM + BN) * BK;      // elements per stage
   static_assert(EPI == 0 || TN % 2 == 0, "fused SwiGLU needs an even number of column blocks per wave");
-  __shared__ __attribute__((aligned(16))) uint16_t As[2][BM * kLDK];
-  __shared__ __attribute__((aligned(16))) uint16_t Bs[2][BN * kLDK];
+  __shared__ __attribute__((aligned(1024))) uint16_t smem[NS * STAGE];
 
   int tmi, tni, sp;
   decode_tile(tiles_m * tiles_n * splits, tiles_m, tiles_n, tmi, tni, sp);
   const int m0 = tmi * BM;
   if (!tile_live(m0, BM, M, n_active, k_max)) return;
-
-  const int nkb = K / kBK;
+  const int nkb = K / BK;
   const int kb0 = (int)((long)sp * nkb / splits), kb1 = (int)((long)(sp + 1) * nkb / splits);
-  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int nk = kb1 - kb0;
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int wm = wave >> 1, wn = wave & 1;
 
-  // weight row feeding B-tile row c
-  const int F = N;  // EPI == 1: N is the SwiGLU width F (W has 2F rows)
+  const int F = N;
   const int h0 = tni * (BN / 2);
   auto w_row = [&](int c) -> int {
     if (EPI == 0) return tni * BN + c;
@@ -84,37 +112,29 @@ __global__ __launch_bounds__(256, 2) void k_gemm_bf16(const uint16_t* __restrict
     return (jb < TN / 2) ? h0 + half * (BN / 4) + jb * 32 + t : F + h0 + half * (BN / 4) + (jb - TN / 2) * 32 + t;
   };
   const int w_rows = (EPI == 0) ? N : 2 * F;
-  int wr[CB];
+  const int lrow = lane >> 3, lchunk = (lane & 7) ^ lrow;
+  const uint16_t* ga[LA];
+  const uint16_t* gb[LB];
 #pragma unroll
-  for (int i = 0; i < CB; ++i) wr[i] = w_row((tid + 256 * i) >> 3);
-
-  uint4 ra[2][CA], rb[2][CB];
-  auto load_global = [&](int set, int kb) {
-    const long k0 = (long)kb * kBK;
+  for (int i = 0; i < LA; ++i) {
+    const int row = (wave + 4 * i) * 8 + lrow;
+    ga[i] = A + (long)min(m0 + row, M - 1) * K + lchunk * 8;
+  }
 #pragma unroll
-    for (int i = 0; i < CA; ++i) {
-      const int c = tid + 256 * i, row = c >> 3, kc = c & 7;
-      const int g = m0 + row;
-      ra[set][i] = (g < M) ? *reinterpret_cast<const uint4*>(A + (long)g * K + k0 + kc * 8) : make_uint4(0, 0, 0, 0);
-    }
+  for (int i = 0; i < LB; ++i) {
+    const int row = (wave + 4 * i) * 8 + lrow;
+    gb[i] = W + (long)min(w_row(row), w_rows - 1) * K + lchunk * 8;
+  }
+  auto issue = [&](int stage, int kb) {
+    const long k0 = (long)kb * BK;
+    uint16_t* base = smem + stage * STAGE;
 #pragma unroll
-    for (int i = 0; i < CB; ++i) {
-      const int kc = (tid + 256 * i) & 7;
-      const int g = wr[i];
-      rb[set][i] = (g < w_rows) ? *reinterpret_cast<const uint4*>(W + (long)g * K + k0 + kc * 8) : make_uint4(0, 0, 0, 0);
-    }
-  };
-  auto store_lds = [&](int set, int buf) {
+    for (int i = 0; i < LA; ++i)
+      __builtin_amdgcn_global_load_lds((const void*)(ga[i] + k0), (lds_void*)(base + (wave + 4 * i) * 8 * BK), 16, 0, 0);
 #pragma unroll
-    for (int i = 0; i < CA; ++i) {
-      const int c = tid + 256 * i, row = c >> 3, kc = c & 7;
-      *reinterpret_cast<uint4*>(&As[buf][row * kLDK + kc * 8]) = ra[set][i];
-    }
-#pragma unroll
-    for (int i = 0; i < CB; ++i) {
-      const int c = tid + 256 * i, row = c >> 3, kc = c & 7;
-      *reinterpret_cast<uint4*>(&Bs[buf][row * kLDK + kc * 8]) = rb[set][i];
-    }
+    for (int i = 0; i < LB; ++i)
+      __builtin_amdgcn_global_load_lds((const void*)(gb[i] + k0), (lds_void*)(base + BM * BK + (wave + 4 * i) * 8 * BK),
+                                       16, 0, 0);
   };
 
   f32x16_t acc[TM][TN];
@@ -125,44 +145,44 @@ __global__ __launch_bounds__(256, 2) void k_gemm_bf16(const uint16_t* __restrict
 #pragma unroll
       for (int e = 0; e < 16; ++e) acc[i][j][e] = 0.f;
 
-  const int frow = lane & 31, fk = (lane >> 5) * 8;
-  auto compute = [&](int buf) {
+  const int swz = lane & 7, hi = lane >> 5, r32 = lane & 31;
+  // fragments of step ks+1 are read from LDS while the MFMAs of step ks run
+  auto load_frags = [&](const uint16_t* base, int ks, bf16x8_t* af, bf16x8_t* bfr) {
+    const int slot = ((ks * 2 + hi) ^ swz) * 8;
 #pragma unroll
-    for (int ks = 0; ks < kBK / 16; ++ks) {
-      bf16x8_t af[TM], bfr[TN];
+    for (int i = 0; i < TM; ++i)
+      af[i] = *reinterpret_cast<const bf16x8_t*>(base + (wm * (BM / 2) + i * 32 + r32) * BK + slot);
+#pragma unroll
+    for (int j = 0; j < TN; ++j)
+      bfr[j] = *reinterpret_cast<const bf16x8_t*>(base + BM * BK + (wn * (BN / 2) + j * 32 + r32) * BK + slot);
+  };
+  auto compute = [&](int stage) {
+    const uint16_t* base = smem + stage * STAGE;
+    bf16x8_t af[2][TM], bfr[2][TN];
+    load_frags(base, 0, af[0], bfr[0]);
+#pragma unroll
+    for (int ks = 0; ks < BK / 16; ++ks) {
+      if (ks + 1 < BK / 16) load_frags(base, ks + 1, af[(ks + 1) & 1], bfr[(ks + 1) & 1]);
 #pragma unroll
       for (int i = 0; i < TM; ++i)
-        af[i] = *reinterpret_cast<const bf16x8_t*>(&As[buf][(wm * (BM / 2) + i * 32 + frow) * kLDK + ks * 16 + fk]);
 #pragma unroll
-      for (int j = 0; j < TN; ++j)
-        bfr[j] = *reinterpret_cast<const bf16x8_t*>(&Bs[buf][(wn * (BN / 2) + j * 32 + frow) * kLDK + ks * 16 + fk]);
-#pragma unroll
-      for (int i = 0; i < TM; ++i)
-#pragma unroll
-        for (int j = 0; j < TN; ++j) acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(af[i], bfr[j], acc[i][j], 0, 0, 0);
+        for (int j = 0; j < TN; ++j)
+          acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(af[ks & 1][i], bfr[ks & 1][j], acc[i][j], 0, 0, 0);
+      // keep the order: the next step's LDS reads are issued before this step's MFMAs
+      if (ks + 1 < BK / 16) __builtin_amdgcn_sched_group_barrier(0x100, TM + TN, 0);
+      __builtin_amdgcn_sched_group_barrier(0x008, TM * TN, 0);
     }
   };
 
-  // Pipeline: tiles kb+1 and kb+2 are in flight (two register sets) while tile kb is multiplied from LDS.
-  const int nk = kb1 - kb0;
-  if (nk > 0) {
-    load_global(0, kb0);
-    if (nk > 1) load_global(1, kb0 + 1);
-    store_lds(0, 0);
-    __syncthreads();
-  }
-  for (int it = 0; it < nk; it += 2) {
-    // even step: compute tile it from buffer 0; set 0 is free, set 1 holds tile it+1
-    if (it + 2 < nk) load_global(0, kb0 + it + 2);
-    compute(0);
-    if (it + 1 < nk) store_lds(1, 1);
-    __syncthreads();
-    if (it + 1 >= nk) break;
-    // odd step: compute tile it+1 from buffer 1; set 1 is free, set 0 holds tile it+2
-    if (it + 3 < nk) load_global(1, kb0 + it + 3);
-    compute(1);
-    if (it + 2 < nk) store_lds(0, 0);
-    __syncthreads();
+#pragma unroll
+  for (int s = 0; s < NS - 1; ++s)
+    if (s < nk) issue(s, kb0 + s);
+  for (int t = 0; t < nk; ++t) {
+    wait_stages<NS - 2, LA + LB>(nk - 1 - t);  // tiles after t may stay in flight
+    // barrier without a memory fence: a fence would wait for every load in flight
+    __builtin_amdgcn_s_barrier();
+    if (t + NS - 1 < nk) issue((t + NS - 1) % NS, kb0 + t + NS - 1);
+    compute(t % NS);
   }
 
   if (EPI == 0) {
@@ -244,38 +264,49 @@ __global__ __launch_bounds__(256) void k_gemm_f32(const float* __restrict__ A, c
     }
 }
 
+#ifndef DLLM_LDS_CASES
+#define DLLM_LDS_CASES                                                                              \
+  DLLM_LDS_CASE(64, 64, 4) DLLM_LDS_CASE(64, 64, 6) DLLM_LDS_CASE(128, 64, 3) DLLM_LDS_CASE(128, 64, 4)    \
+  DLLM_LDS_CASE(64, 128, 4) DLLM_LDS_CASE(128, 128, 2) DLLM_LDS_CASE(128, 128, 3) DLLM_LDS_CASE(128, 128, 4) \
+  DLLM_LDS_CASE(256, 128, 2) DLLM_LDS_CASE(256, 128, 3)
+#endif
+#ifndef DLLM_LDS_SWIGLU_CASES
+#define DLLM_LDS_SWIGLU_CASES                                                                       \
+  DLLM_LDS_CASE(64, 128, 4) DLLM_LDS_CASE(128, 128, 2) DLLM_LDS_CASE(128, 128, 3) DLLM_LDS_CASE(128, 128, 4) \
+  DLLM_LDS_CASE(256, 128, 2) DLLM_LDS_CASE(256, 128, 3)
+#endif
+
 GemmPlan gemm_plan(int dtype, int M, int N, int K, bool swiglu) {
-  GemmPlan p{64, 64, 1};
+  GemmPlan p{64, 64, 1, 64, 2};
   if (dtype == 0) {
     const int tiles = ((M + 63) / 64) * ((N + 63) / 64);
     while (!swiglu && tiles * p.splits < 256 && (K / 16) / (p.splits * 2) >= 8) p.splits *= 2;
     return p;
   }
-  // Few active rows: the product streams its weights once (HBM bound); 64-row tiles
-  // give two workgroups per weight panel, the second reading the panel from L2.
-  p.bm = (M <= 128) ? 64 : 128;
-  p.bn = (swiglu || M > 128 || N >= 16384) ? 128 : 64;
+  // Direct-to-LDS kernel (pd = 10 + stages).  Rules from a tile sweep on the LLaDA-8B layer
+  // shapes: few rows (HBM bound on the weights) -> 128-row tiles, 64 columns for narrow
+  // outputs, 3-4 stages in flight and split-K until ~512 workgroups; many rows (MFMA bound)
+  // -> 128x128 tiles, 2 stages so two workgroups share a CU.
+  const bool few = M <= 192;
+  p.bm = 128;
+  p.bn = (swiglu || !few || N > 8192) ? 128 : 64;
+  p.pd = 10 + (few ? (p.bn == 64 ? 4 : 3) : (swiglu ? 2 : 4));
   if (swiglu) return p;  // the fused epilogue needs the whole reduction in one workgroup
   const long tiles = (long)((M + p.bm - 1) / p.bm) * ((N + p.bn - 1) / p.bn);
-  const int nkb = K / kBK;
-  // split K until every CU has a workgroup, while the fp32 partial round trip
-  // (8 M N bytes per split) stays under a quarter of the weight bytes when few rows are active
-  for (;;) {
-    const int s2 = p.splits * 2;
-    if (tiles * p.splits >= 256 || nkb / s2 < 8) break;
-    if (M <= 256 && 8.0 * s2 * M * (double)N > 0.25 * 2.0 * (double)N * K) break;
-    if (s2 > 4) break;
-    p.splits = s2;
-  }
+  const long target = few ? 512 : 256;
+  const int max_splits = few ? 4 : 2;
+  while (tiles * p.splits < target && p.splits < max_splits && K / (p.splits * 2) >= 1024) p.splits *= 2;
   return p;
 }
 
-template <int BM, int BN, int EPI>
-static void launch_bf16(const GemmPlan& p, const void* A, const void* W, float* C, void* H, int M, int N, int K,
-                        const int32_t* n_active, int k_max, hipStream_t s) {
+template <int BM, int BN, int NS, int EPI>
+static void launch_lds(const GemmPlan& p, const void* A, const void* W, float* C, void* H, int M, int N, int K,
+                       const int32_t* n_active, int k_max, hipStream_t s) {
   const int ncols = EPI == 0 ? BN : BN / 2;
   const int tm = (M + BM - 1) / BM, tn = (N + ncols - 1) / ncols;
-  hipLaunchKernelGGL((k_gemm_bf16<BM, BN, EPI>), dim3(tm * tn * p.splits), dim3(256), 0, s, (const uint16_t*)A,
+  constexpr int lds_bytes = NS * (BM + BN) * 64 * 2;
+  constexpr int occ = lds_bytes <= 80 * 1024 ? 2 : 1;
+  hipLaunchKernelGGL((k_gemm_lds<BM, BN, NS, EPI, occ>), dim3(tm * tn * p.splits), dim3(256), 0, s, (const uint16_t*)A,
                      (const uint16_t*)W, C, (uint16_t*)H, M, N, K, p.splits, tm, tn, n_active, k_max);
 }
 
@@ -288,23 +319,31 @@ hipError_t launch_gemm(int dtype, const GemmPlan& p, const void* A, const void* 
                        N, K, p.splits, tm, tn, n_active, k_max);
     return hipGetLastError();
   }
-  if (K % kBK != 0) return hipErrorInvalidValue;
-  if (p.bm == 64 && p.bn == 64) launch_bf16<64, 64, 0>(p, A, W, C, nullptr, M, N, K, n_active, k_max, s);
-  else if (p.bm == 128 && p.bn == 64) launch_bf16<128, 64, 0>(p, A, W, C, nullptr, M, N, K, n_active, k_max, s);
-  else if (p.bm == 64 && p.bn == 128) launch_bf16<64, 128, 0>(p, A, W, C, nullptr, M, N, K, n_active, k_max, s);
-  else if (p.bm == 128 && p.bn == 128) launch_bf16<128, 128, 0>(p, A, W, C, nullptr, M, N, K, n_active, k_max, s);
-  else return hipErrorInvalidValue;
-  return hipGetLastError();
+  if (K % 64 != 0) return hipErrorInvalidValue;
+#define DLLM_LDS_CASE(BM_, BN_, NS_)                                                                \
+  if (p.bm == BM_ && p.bn == BN_ && p.bk == 64 && p.pd == 10 + NS_) {                               \
+    launch_lds<BM_, BN_, NS_, 0>(p, A, W, C, nullptr, M, N, K, n_active, k_max, s);                 \
+    return hipGetLastError();                                                                       \
+  }
+  DLLM_LDS_CASES
+#undef DLLM_LDS_CASE
+#undef DLLM_GEMM_CASE
+  return hipErrorInvalidValue;
 }
 
 hipError_t launch_gemm_swiglu(const GemmPlan& p, const void* A, const void* W_gate_up, void* H, int M, int F, int K,
                               const int32_t* n_active, int k_max, hipStream_t s) {
   if (M <= 0 || F <= 0) return hipSuccess;
-  if (K % kBK != 0 || F % (p.bn / 2) != 0 || p.splits != 1) return hipErrorInvalidValue;
-  if (p.bm == 64 && p.bn == 128) launch_bf16<64, 128, 1>(p, A, W_gate_up, nullptr, H, M, F, K, n_active, k_max, s);
-  else if (p.bm == 128 && p.bn == 128) launch_bf16<128, 128, 1>(p, A, W_gate_up, nullptr, H, M, F, K, n_active, k_max, s);
-  else return hipErrorInvalidValue;
-  return hipGetLastError();
+  if (K % 64 != 0 || F % (p.bn / 2) != 0 || p.splits != 1) return hipErrorInvalidValue;
+#define DLLM_LDS_CASE(BM_, BN_, NS_)                                                                \
+  if (p.bm == BM_ && p.bn == BN_ && p.bk == 64 && p.pd == 10 + NS_) {                               \
+    launch_lds<BM_, BN_, NS_, 1>(p, A, W_gate_up, nullptr, H, M, F, K, n_active, k_max, s);         \
+    return hipGetLastError();                                                                       \
+  }
+  DLLM_LDS_SWIGLU_CASES
+#undef DLLM_LDS_CASE
+#undef DLLM_SWIGLU_CASE
+  return hipErrorInvalidValue;
 }
 
 }  // namespace dllm

@@ -39,7 +39,7 @@ hipError_t launch_copy(const void* src, void* dst, size_t bytes, hipStream_t s);
 // Row tiles whose rows are all dead (j >= n_active[b], r = b*k_max + j) are skipped;
 // n_active == nullptr means every row is live.
 struct GemmPlan {
-  int bm, bn, splits;
+  int bm, bn, splits, bk, pd;  // tile rows, tile columns, K splits, K tile, 10 + LDS stages (bf16)
 };
 GemmPlan gemm_plan(int dtype, int M, int N, int K, bool swiglu = false);
 hipError_t launch_gemm(int dtype, const GemmPlan& p, const void* A, const void* W, float* C, int M, int N, int K,
@@ -50,8 +50,12 @@ hipError_t launch_gemm_swiglu(const GemmPlan& p, const void* A, const void* W_ga
 
 // ---------------- attention (attention.hip) ----------------
 // o[r, h, :] = softmax(q[r, h] . Kc[b, :, h/g] / sqrt(D)) Vc[b, :, h/g] over all S keys.
+// Split-KV (bf16, few query blocks): `part` needs attention_part_bytes(...) bytes.
+int attention_splits(int dtype, int B, int S, int k_max, int Hq, int Hkv);
+size_t attention_part_bytes(int dtype, int B, int S, int k_max, int Hq, int Hkv);
 hipError_t launch_attention(int dtype, const void* q, const void* kc, const void* vc, void* o,
-                            const int32_t* n_active, int B, int S, int k_max, int Hq, int Hkv, int D, hipStream_t s);
+                            const int32_t* n_active, int B, int S, int k_max, int Hq, int Hkv, int D, float* part,
+                            hipStream_t s);
 
 // ---------------- score / select (score_select.hip) ----------------
 hipError_t launch_score(int dtype, const void* h_cur, const void* h_prev, void* h_next, const float* conf_prev,
@@ -61,8 +65,12 @@ hipError_t launch_select(const float* score, const uint8_t* force, int B, int S,
                          int k_max, int32_t* idx, int32_t* n_active, hipStream_t s);
 
 // ---------------- vocabulary pass (vocab.hip) ----------------
+// Rows are split into vocabulary slices when few rows are active; `partial` needs
+// conf_kl_part_bytes(R, V) bytes (may be null when that is 0).
+size_t conf_kl_part_bytes(int R, int V);
 hipError_t launch_conf_kl(const float* logits, float* logits_prev, const int32_t* row_pos, int R, int V,
-                          int exclude_id, int have_prev, float* conf, int32_t* argmax, float* kl, hipStream_t s);
+                          int exclude_id, int have_prev, float* conf, int32_t* argmax, float* kl, void* partial,
+                          hipStream_t s);
 
 // ---------------- post-step (post.hip) ----------------
 hipError_t launch_lock_update(const int32_t* row_pos, int R, const float* conf, const float* kl, float eps,

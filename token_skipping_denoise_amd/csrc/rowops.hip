@@ -125,6 +125,11 @@ hipError_t launch_identity_rows(int B, int S, int32_t* idx, int32_t* n_active, h
 }
 
 // ---- GEMM epilogues ----
+constexpr int kMaxHalf = 64;  // head dims up to 128
+struct RopeTable {
+  double theta[kMaxHalf];
+};
+
 __device__ __forceinline__ float sum_splits(const float* __restrict__ p, int splits, long stride, long off) {
   float v = p[off];
   for (int k = 1; k < splits; ++k) v += p[off + k * stride];
@@ -132,30 +137,34 @@ __device__ __forceinline__ float sum_splits(const float* __restrict__ p, int spl
 }
 
 // One workgroup per row.  Columns of the QKV product: [Q: Hq*D | K: Hkv*D | V: Hkv*D].
+// Rotation angles i * theta_j are formed in double and reduced modulo 2 pi before the
+// single-precision sine and cosine (theta_j = base^(-2j/D) comes from the host in double).
 template <typename T>
 __global__ __launch_bounds__(256) void k_qkv_epilogue(const float* __restrict__ part, int splits, long sstride,
                                                       const int32_t* __restrict__ row_pos, int S, int Hq, int Hkv,
-                                                      int D, float rope_base, T* __restrict__ q, T* __restrict__ kc,
+                                                      int D, RopeTable rt, T* __restrict__ q, T* __restrict__ kc,
                                                       T* __restrict__ vc) {
   using E = Elem<T>;
-  __shared__ float cs[128], sn[128];
+  __shared__ float cs[kMaxHalf], sn[kMaxHalf];
   const int r = blockIdx.x;
   const int pos = row_pos[r];
   if (pos < 0) return;
   const int b = pos / S, i = pos - b * S;
+  (void)b;
   const int half = D / 2;
   const int NQ = Hq * D, NK = Hkv * D, N = NQ + 2 * NK;
-  // rotation angles in double: theta_j = base^(-2j/D), angle = i * theta_j
   for (int j = threadIdx.x; j < half; j += blockDim.x) {
-    const double theta = exp2(-(2.0 * j / (double)D) * log2((double)rope_base));
-    double sv, cv;
-    sincos((double)i * theta, &sv, &cv);
-    cs[j] = (float)cv;
-    sn[j] = (float)sv;
+    const double a = (double)i * rt.theta[j];
+    const double red = a - 6.283185307179586 * rint(a * 0.15915494309189535);
+    float sv, cv;
+    sincosf((float)red, &sv, &cv);
+    cs[j] = cv;
+    sn[j] = sv;
   }
   __syncthreads();
   const long base = (long)r * N;
   const int npairs = (Hq + Hkv) * half;
+#pragma unroll 4
   for (int p = threadIdx.x; p < npairs; p += blockDim.x) {
     const int hh = p / half, j = p - hh * half;
     const int c1 = hh * D + j, c2 = c1 + half;
@@ -172,6 +181,7 @@ __global__ __launch_bounds__(256) void k_qkv_epilogue(const float* __restrict__ 
       E::st(kc, o + j + half, y2);
     }
   }
+#pragma unroll 4
   for (int c = threadIdx.x; c < NK; c += blockDim.x)
     E::st(vc, (long)pos * NK + c, sum_splits(part, splits, sstride, base + NQ + NK + c));
 }
@@ -180,65 +190,95 @@ hipError_t launch_qkv_epilogue(int dtype, const float* part, int splits, long sp
                                int R, int S, int Hq, int Hkv, int D, float rope_base, void* q, void* kc, void* vc,
                                hipStream_t s) {
   if (R <= 0) return hipSuccess;
+  if (D / 2 > kMaxHalf) return hipErrorInvalidValue;
+  RopeTable rt;
+  for (int j = 0; j < D / 2; ++j) rt.theta[j] = pow((double)rope_base, -2.0 * j / (double)D);
   if (dtype == 0)
     hipLaunchKernelGGL(k_qkv_epilogue<float>, dim3(R), dim3(256), 0, s, part, splits, split_stride, row_pos, S, Hq,
-                       Hkv, D, rope_base, (float*)q, (float*)kc, (float*)vc);
+                       Hkv, D, rt, (float*)q, (float*)kc, (float*)vc);
   else
     hipLaunchKernelGGL(k_qkv_epilogue<bf16>, dim3(R), dim3(256), 0, s, part, splits, split_stride, row_pos, S, Hq,
-                       Hkv, D, rope_base, (bf16*)q, (bf16*)kc, (bf16*)vc);
+                       Hkv, D, rt, (bf16*)q, (bf16*)kc, (bf16*)vc);
   return hipGetLastError();
 }
 
-// One wavefront per row: x += sum(partials) (rounded to storage), then xn = rmsnorm(x) * g.
+// One workgroup per row: x += sum(partials) (rounded to storage), then xn = rmsnorm(x) * g.
+// Every load of the row is issued up front (values stay in registers), so the row costs
+// about one memory round trip.
+constexpr int kRowChunks = 4;  // 16-byte chunks per thread: rows up to 1024 chunks
+
+__device__ __forceinline__ float block_sum256(float v, float* red) {
+  v = wave_sum(v);
+  if ((threadIdx.x & 63) == 0) red[threadIdx.x >> 6] = v;
+  __syncthreads();
+  return red[0] + red[1] + red[2] + red[3];
+}
+
 template <typename T>
 __global__ __launch_bounds__(256) void k_resid_norm(const float* __restrict__ part, int splits, long sstride,
                                                     const int32_t* __restrict__ row_pos, int R, int d,
                                                     T* __restrict__ x, const T* __restrict__ g, float eps,
                                                     T* __restrict__ xn) {
   using E = Elem<T>;
-  const int lane = threadIdx.x & 63;
-  const int r = blockIdx.x * 4 + (threadIdx.x >> 6);
-  if (r >= R || row_pos[r] < 0) return;
-  const int nchunk = d / E::kVec;
+  constexpr int V = E::kVec;
+  __shared__ float red[4];
+  const int r = blockIdx.x;
+  if (row_pos[r] < 0) return;
+  const int nchunk = d / V;
   uint4* x4 = reinterpret_cast<uint4*>(x + (long)r * d);
   const float* pr = part + (long)r * d;
+  float f[kRowChunks][V];
   float ss = 0.f;
-  for (int c = lane; c < nchunk; c += kWave) {
-    float f[E::kVec];
-    E::unpack(x4[c], f);
 #pragma unroll
-    for (int e = 0; e < E::kVec; ++e) f[e] += sum_splits(pr, splits, sstride, c * E::kVec + e);
-    const uint4 packed = E::pack(f);
+  for (int k = 0; k < kRowChunks; ++k) {
+    const int c = threadIdx.x + 256 * k;
+    if (c >= nchunk) break;
+    E::unpack(x4[c], f[k]);
+    for (int sp = 0; sp < splits; ++sp) {
+      const float4* p4 = reinterpret_cast<const float4*>(pr + sp * sstride + (long)c * V);
+#pragma unroll
+      for (int e4 = 0; e4 < V / 4; ++e4) {
+        const float4 a = p4[e4];
+        f[k][4 * e4] += a.x;
+        f[k][4 * e4 + 1] += a.y;
+        f[k][4 * e4 + 2] += a.z;
+        f[k][4 * e4 + 3] += a.w;
+      }
+    }
+    const uint4 packed = E::pack(f[k]);
     x4[c] = packed;
-    E::unpack(packed, f);  // the stored (rounded) values feed the norm
+    E::unpack(packed, f[k]);  // the stored (rounded) values feed the norm
 #pragma unroll
-    for (int e = 0; e < E::kVec; ++e) ss += f[e] * f[e];
+    for (int e = 0; e < V; ++e) ss += f[k][e] * f[k][e];
   }
   if (!g) return;
-  ss = wave_sum(ss);
+  ss = block_sum256(ss, red);
   const float inv = 1.0f / sqrtf(ss / (float)d + eps);
   const uint4* g4 = reinterpret_cast<const uint4*>(g);
   uint4* n4 = reinterpret_cast<uint4*>(xn + (long)r * d);
-  for (int c = lane; c < nchunk; c += kWave) {
-    float f[E::kVec], gf[E::kVec];
-    E::unpack(x4[c], f);
+#pragma unroll
+  for (int k = 0; k < kRowChunks; ++k) {
+    const int c = threadIdx.x + 256 * k;
+    if (c >= nchunk) break;
+    float gf[V];
     E::unpack(g4[c], gf);
 #pragma unroll
-    for (int e = 0; e < E::kVec; ++e) f[e] = f[e] * inv * gf[e];
-    n4[c] = E::pack(f);
+    for (int e = 0; e < V; ++e) f[k][e] = f[k][e] * inv * gf[e];
+    n4[c] = E::pack(f[k]);
   }
 }
 
 hipError_t launch_resid_norm(int dtype, const float* part, int splits, long split_stride, const int32_t* row_pos,
                              int R, int d, void* x, const void* g, float eps, void* xn, hipStream_t s) {
   if (R <= 0) return hipSuccess;
-  dim3 grid((R + 3) / 4), block(256);
+  const int vec = dtype == 0 ? 4 : 8;
+  if (d % vec != 0 || d / vec > 256 * kRowChunks) return hipErrorInvalidValue;
   if (dtype == 0)
-    hipLaunchKernelGGL(k_resid_norm<float>, grid, block, 0, s, part, splits, split_stride, row_pos, R, d, (float*)x,
-                       (const float*)g, eps, (float*)xn);
+    hipLaunchKernelGGL(k_resid_norm<float>, dim3(R), dim3(256), 0, s, part, splits, split_stride, row_pos, R, d,
+                       (float*)x, (const float*)g, eps, (float*)xn);
   else
-    hipLaunchKernelGGL(k_resid_norm<bf16>, grid, block, 0, s, part, splits, split_stride, row_pos, R, d, (bf16*)x,
-                       (const bf16*)g, eps, (bf16*)xn);
+    hipLaunchKernelGGL(k_resid_norm<bf16>, dim3(R), dim3(256), 0, s, part, splits, split_stride, row_pos, R, d,
+                       (bf16*)x, (const bf16*)g, eps, (bf16*)xn);
   return hipGetLastError();
 }
 

@@ -29,15 +29,39 @@ __device__ __forceinline__ float rescale(float s, float m_old, float m_new) {
   return (m_old == -INFINITY) ? 0.f : s * expf(m_old - m_new);
 }
 
+__device__ __forceinline__ Part combine(const Part& a, const Part& b) {
+  Part c;
+  c.m = fmaxf(a.m, b.m);
+  c.s = rescale(a.s, a.m, c.m) + rescale(b.s, b.m, c.m);
+  c.t = rescale(a.t, a.m, c.m) + rescale(b.t, b.m, c.m);
+  c.am = (a.m > b.m) ? a.am : (b.m > a.m ? b.am : min(a.am, b.am));
+  c.mp = fmaxf(a.mp, b.mp);
+  c.sp = rescale(a.sp, a.mp, c.mp) + rescale(b.sp, b.mp, c.mp);
+  return c;
+}
+
+__device__ __forceinline__ void finish(const Part& f, int pos, bool do_kl, float* conf, int32_t* argmax, float* kl) {
+  conf[pos] = 1.0f / f.s;
+  argmax[pos] = f.am;
+  if (kl) {
+    // lse - lse' = (m - m') + log(s / s'): avoids cancelling two O(log V) quantities
+    kl[pos] = do_kl ? fmaxf(0.f, f.t / f.s - (f.m - f.mp) - logf(f.s / f.sp)) : INFINITY;
+  }
+}
+
+// One workgroup per (row, vocabulary slice).  With nparts == 1 it writes the row's
+// statistics; otherwise it writes its slice's partial state to `partial` for k_conf_kl_merge.
 __global__ __launch_bounds__(kVT) void k_conf_kl(const float* __restrict__ logits, float* __restrict__ logits_prev,
                                                  const int32_t* __restrict__ row_pos, int V, int exclude_id,
                                                  int have_prev, float* __restrict__ conf, int32_t* __restrict__ argmax,
-                                                 float* __restrict__ kl) {
+                                                 float* __restrict__ kl, int nparts, int slice,
+                                                 Part* __restrict__ partial) {
   __shared__ Part sh[kVT];
   const int r = blockIdx.x;
   const int pos = row_pos[r];
   if (pos < 0) return;
   const int tid = threadIdx.x;
+  const int v0 = blockIdx.y * slice, v1 = min(V, v0 + slice);
   const float* z = logits + (long)r * V;
   float* zp = logits_prev ? logits_prev + (long)pos * V : nullptr;
   const bool do_kl = zp && have_prev;
@@ -62,18 +86,21 @@ __global__ __launch_bounds__(kVT) void k_conf_kl(const float* __restrict__ logit
       p.sp += expf(xp - p.mp);
     }
   };
-  const int V4 = ((long)z & 15) == 0 && (zp == nullptr || ((long)zp & 15) == 0) ? V / 4 : 0;
-  for (int c = tid; c < V4; c += kVT) {
-    const float4 a = reinterpret_cast<const float4*>(z)[c];
+  // 16-byte path when the slice and both rows are 16-byte aligned
+  const bool vec = ((((long)(z + v0)) | (zp ? (long)(zp + v0) : 0)) & 15) == 0;
+  const int n4 = vec ? (v1 - v0) / 4 : 0;
+  for (int c = tid; c < n4; c += kVT) {
+    const int v = v0 + 4 * c;
+    const float4 a = *reinterpret_cast<const float4*>(z + v);
     float4 bp = make_float4(0.f, 0.f, 0.f, 0.f);
-    if (do_kl) bp = reinterpret_cast<const float4*>(zp)[c];
-    if (zp) reinterpret_cast<float4*>(zp)[c] = a;
-    take(4 * c + 0, a.x, bp.x);
-    take(4 * c + 1, a.y, bp.y);
-    take(4 * c + 2, a.z, bp.z);
-    take(4 * c + 3, a.w, bp.w);
+    if (do_kl) bp = *reinterpret_cast<const float4*>(zp + v);
+    if (zp) *reinterpret_cast<float4*>(zp + v) = a;
+    take(v + 0, a.x, bp.x);
+    take(v + 1, a.y, bp.y);
+    take(v + 2, a.z, bp.z);
+    take(v + 3, a.w, bp.w);
   }
-  for (int v = 4 * V4 + tid; v < V; v += kVT) {
+  for (int v = v0 + 4 * n4 + tid; v < v1; v += kVT) {
     const float a = z[v];
     const float bp = do_kl ? zp[v] : 0.f;
     if (zp) zp[v] = a;
@@ -82,39 +109,50 @@ __global__ __launch_bounds__(kVT) void k_conf_kl(const float* __restrict__ logit
   sh[tid] = p;
   __syncthreads();
   for (int w = kVT / 2; w > 0; w >>= 1) {
-    if (tid < w) {
-      const Part a = sh[tid], b = sh[tid + w];
-      Part c;
-      c.m = fmaxf(a.m, b.m);
-      c.s = rescale(a.s, a.m, c.m) + rescale(b.s, b.m, c.m);
-      c.t = rescale(a.t, a.m, c.m) + rescale(b.t, b.m, c.m);
-      c.am = (a.m > b.m) ? a.am : (b.m > a.m ? b.am : min(a.am, b.am));
-      c.mp = fmaxf(a.mp, b.mp);
-      c.sp = rescale(a.sp, a.mp, c.mp) + rescale(b.sp, b.mp, c.mp);
-      sh[tid] = c;
-    }
+    if (tid < w) sh[tid] = combine(sh[tid], sh[tid + w]);
     __syncthreads();
   }
   if (tid == 0) {
-    const Part f = sh[0];
-    conf[pos] = 1.0f / f.s;
-    argmax[pos] = f.am;
-    if (kl) {
-      if (do_kl) {
-        // lse - lse' = (m - m') + log(s / s'): avoids cancelling two O(log V) quantities
-        kl[pos] = fmaxf(0.f, f.t / f.s - (f.m - f.mp) - logf(f.s / f.sp));
-      } else {
-        kl[pos] = INFINITY;
-      }
-    }
+    if (nparts == 1) finish(sh[0], pos, do_kl, conf, argmax, kl);
+    else partial[(long)r * nparts + blockIdx.y] = sh[0];
   }
 }
 
+// Combine the slices of each row in slice order (deterministic).
+__global__ void k_conf_kl_merge(const Part* __restrict__ partial, int nparts, const int32_t* __restrict__ row_pos,
+                                int R, int have_prev, int has_prev_buf, float* __restrict__ conf,
+                                int32_t* __restrict__ argmax, float* __restrict__ kl) {
+  const int r = blockIdx.x * blockDim.x + threadIdx.x;
+  if (r >= R) return;
+  const int pos = row_pos[r];
+  if (pos < 0) return;
+  Part f = partial[(long)r * nparts];
+  for (int k = 1; k < nparts; ++k) f = combine(f, partial[(long)r * nparts + k]);
+  finish(f, pos, has_prev_buf && have_prev, conf, argmax, kl);
+}
+
+int conf_kl_parts(int R, int V) {
+  int parts = 1;
+  while (parts < 32 && (long)R * parts < 2048 && V / (parts * 2) >= 4096) parts *= 2;
+  return parts;
+}
+
+size_t conf_kl_part_bytes(int R, int V) {
+  const int parts = conf_kl_parts(R, V);
+  return parts > 1 ? (size_t)R * parts * sizeof(Part) : 0;
+}
+
 hipError_t launch_conf_kl(const float* logits, float* logits_prev, const int32_t* row_pos, int R, int V,
-                          int exclude_id, int have_prev, float* conf, int32_t* argmax, float* kl, hipStream_t s) {
+                          int exclude_id, int have_prev, float* conf, int32_t* argmax, float* kl, void* partial,
+                          hipStream_t s) {
   if (R <= 0) return hipSuccess;
-  hipLaunchKernelGGL(k_conf_kl, dim3(R), dim3(kVT), 0, s, logits, logits_prev, row_pos, V, exclude_id, have_prev,
-                     conf, argmax, kl);
+  const int parts = partial ? conf_kl_parts(R, V) : 1;  // no scratch: one workgroup per row
+  const int slice = ((V + parts - 1) / parts + 3) / 4 * 4;
+  hipLaunchKernelGGL(k_conf_kl, dim3(R, parts), dim3(kVT), 0, s, logits, logits_prev, row_pos, V, exclude_id,
+                     have_prev, conf, argmax, kl, parts, slice, (Part*)partial);
+  if (parts > 1)
+    hipLaunchKernelGGL(k_conf_kl_merge, dim3((R + 63) / 64), dim3(64), 0, s, (const Part*)partial, parts, row_pos, R,
+                       have_prev, logits_prev != nullptr, conf, argmax, kl);
   return hipGetLastError();
 }
 
