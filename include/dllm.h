@@ -134,7 +134,8 @@ typedef struct {
   uint8_t *force;         /* device [B, S] dllm_force values, or NULL (all 0) */
   int32_t *idx;           /* device [B, k_max] out: active positions (ascending, -1 padded) */
   int32_t *n_active;      /* device [B] out */
-  int32_t k_max;          /* row stride of idx; >= S on full steps */
+  int32_t k_max;          /* row stride of idx and of the active-row buffers (1..S); a full
+                             step leaves idx / n_active unchanged */
   int32_t have_prev;      /* 0 until the first step has run */
 } dllm_state;
 
