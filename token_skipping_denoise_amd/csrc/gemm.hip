@@ -163,14 +163,15 @@ __global__ __launch_bounds__(256, OCC) void k_gemm_lds(const uint16_t* __restric
 #pragma unroll
     for (int ks = 0; ks < BK / 16; ++ks) {
       if (ks + 1 < BK / 16) load_frags(base, ks + 1, af[(ks + 1) & 1], bfr[(ks + 1) & 1]);
+      // scheduling fence: the next step's LDS reads stay ahead of this step's MFMAs (the
+      // scheduler would otherwise sink them behind the MFMAs and stall on their latency)
+      __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
       for (int i = 0; i < TM; ++i)
 #pragma unroll
         for (int j = 0; j < TN; ++j)
           acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(af[ks & 1][i], bfr[ks & 1][j], acc[i][j], 0, 0, 0);
-      // keep the order: the next step's LDS reads are issued before this step's MFMAs
-      if (ks + 1 < BK / 16) __builtin_amdgcn_sched_group_barrier(0x100, TM + TN, 0);
-      __builtin_amdgcn_sched_group_barrier(0x008, TM * TN, 0);
+      __builtin_amdgcn_sched_barrier(0);
     }
   };
 
@@ -290,11 +291,11 @@ GemmPlan gemm_plan(int dtype, int M, int N, int K, bool swiglu) {
   const bool few = M <= 192;
   p.bm = 128;
   p.bn = (swiglu || !few || N > 8192) ? 128 : 64;
-  p.pd = 10 + (few ? (p.bn == 64 ? 4 : 3) : (swiglu ? 2 : 4));
+  p.pd = 10 + (few ? (p.bn == 64 ? 4 : 3) : 2);
   if (swiglu) return p;  // the fused epilogue needs the whole reduction in one workgroup
   const long tiles = (long)((M + p.bm - 1) / p.bm) * ((N + p.bn - 1) / p.bn);
   const long target = few ? 512 : 256;
-  const int max_splits = few ? 4 : 2;
+  const int max_splits = 4;
   while (tiles * p.splits < target && p.splits < max_splits && K / (p.splits * 2) >= 1024) p.splits *= 2;
   return p;
 }

@@ -126,9 +126,6 @@ hipError_t launch_identity_rows(int B, int S, int32_t* idx, int32_t* n_active, h
 
 // ---- GEMM epilogues ----
 constexpr int kMaxHalf = 64;  // head dims up to 128
-struct RopeTable {
-  double theta[kMaxHalf];
-};
 
 __device__ __forceinline__ float sum_splits(const float* __restrict__ p, int splits, long stride, long off) {
   float v = p[off];
@@ -137,68 +134,109 @@ __device__ __forceinline__ float sum_splits(const float* __restrict__ p, int spl
 }
 
 // One workgroup per row.  Columns of the QKV product: [Q: Hq*D | K: Hkv*D | V: Hkv*D].
-// Rotation angles i * theta_j are formed in double and reduced modulo 2 pi before the
-// single-precision sine and cosine (theta_j = base^(-2j/D) comes from the host in double).
+// Rotation angles i * theta_j, theta_j = base^(-2j/D), are formed in double and reduced
+// modulo 2 pi before the single-precision sine and cosine.  Each thread owns groups of four
+// rotation pairs (and four V columns); all of its 16-byte partial loads are issued before
+// any arithmetic, so a row costs about one memory round trip per split.
+constexpr int kQkvGroups = 8;  // 4-pair groups per thread: up to 8192 pairs per row
+
+template <typename T>
+__device__ __forceinline__ void store4(T* p, long off, const float* v) {
+  if constexpr (sizeof(T) == 4) {
+    *reinterpret_cast<float4*>(p + off) = make_float4(v[0], v[1], v[2], v[3]);
+  } else {
+    const uint32_t w0 = (uint32_t)f2bf(v[0]) | ((uint32_t)f2bf(v[1]) << 16);
+    const uint32_t w1 = (uint32_t)f2bf(v[2]) | ((uint32_t)f2bf(v[3]) << 16);
+    *reinterpret_cast<uint2*>(p + off) = make_uint2(w0, w1);
+  }
+}
+
 template <typename T>
 __global__ __launch_bounds__(256) void k_qkv_epilogue(const float* __restrict__ part, int splits, long sstride,
                                                       const int32_t* __restrict__ row_pos, int S, int Hq, int Hkv,
-                                                      int D, RopeTable rt, T* __restrict__ q, T* __restrict__ kc,
+                                                      int D, double log2_base, T* __restrict__ q, T* __restrict__ kc,
                                                       T* __restrict__ vc) {
-  using E = Elem<T>;
   __shared__ float cs[kMaxHalf], sn[kMaxHalf];
   const int r = blockIdx.x;
   const int pos = row_pos[r];
   if (pos < 0) return;
-  const int b = pos / S, i = pos - b * S;
-  (void)b;
-  const int half = D / 2;
+  const int i = pos % S;
+  const int half = D / 2, g4 = half / 4;  // 4-pair groups per head
   const int NQ = Hq * D, NK = Hkv * D, N = NQ + 2 * NK;
   for (int j = threadIdx.x; j < half; j += blockDim.x) {
-    const double a = (double)i * rt.theta[j];
+    const double a = (double)i * exp2(-2.0 * j / (double)D * log2_base);
     const double red = a - 6.283185307179586 * rint(a * 0.15915494309189535);
     float sv, cv;
     sincosf((float)red, &sv, &cv);
     cs[j] = cv;
     sn[j] = sv;
   }
-  __syncthreads();
-  const long base = (long)r * N;
-  const int npairs = (Hq + Hkv) * half;
-#pragma unroll 4
-  for (int p = threadIdx.x; p < npairs; p += blockDim.x) {
-    const int hh = p / half, j = p - hh * half;
-    const int c1 = hh * D + j, c2 = c1 + half;
-    const float x1 = sum_splits(part, splits, sstride, base + c1);
-    const float x2 = sum_splits(part, splits, sstride, base + c2);
-    const float y1 = x1 * cs[j] - x2 * sn[j];
-    const float y2 = x2 * cs[j] + x1 * sn[j];
-    if (hh < Hq) {
-      E::st(q, (long)r * NQ + c1, y1);
-      E::st(q, (long)r * NQ + c2, y2);
-    } else {
-      const long o = ((long)pos * Hkv + (hh - Hq)) * D;
-      E::st(kc, o + j, y1);
-      E::st(kc, o + j + half, y2);
+  const float* pr = part + (long)r * N;
+  const int ngroups = (Hq + Hkv) * g4;   // rotation groups
+  const int vgroups = NK / 4;            // V column groups
+  float x1[kQkvGroups][4], x2[kQkvGroups][4], xv[kQkvGroups][4];
+#pragma unroll
+  for (int k = 0; k < kQkvGroups; ++k)
+#pragma unroll
+    for (int e = 0; e < 4; ++e) x1[k][e] = x2[k][e] = xv[k][e] = 0.f;
+  for (int sp = 0; sp < splits; ++sp) {
+    const float* ps = pr + sp * sstride;
+#pragma unroll
+    for (int k = 0; k < kQkvGroups; ++k) {
+      const int gi = threadIdx.x + 256 * k;
+      if (gi < ngroups) {
+        const int hh = gi / g4, j0 = (gi - hh * g4) * 4;
+        const float4 a = *reinterpret_cast<const float4*>(ps + hh * D + j0);
+        const float4 b = *reinterpret_cast<const float4*>(ps + hh * D + j0 + half);
+        x1[k][0] += a.x; x1[k][1] += a.y; x1[k][2] += a.z; x1[k][3] += a.w;
+        x2[k][0] += b.x; x2[k][1] += b.y; x2[k][2] += b.z; x2[k][3] += b.w;
+      }
+      if (gi < vgroups) {
+        const float4 v = *reinterpret_cast<const float4*>(ps + NQ + NK + gi * 4);
+        xv[k][0] += v.x; xv[k][1] += v.y; xv[k][2] += v.z; xv[k][3] += v.w;
+      }
     }
   }
-#pragma unroll 4
-  for (int c = threadIdx.x; c < NK; c += blockDim.x)
-    E::st(vc, (long)pos * NK + c, sum_splits(part, splits, sstride, base + NQ + NK + c));
+  __syncthreads();
+#pragma unroll
+  for (int k = 0; k < kQkvGroups; ++k) {
+    const int gi = threadIdx.x + 256 * k;
+    if (gi < ngroups) {
+      const int hh = gi / g4, j0 = (gi - hh * g4) * 4;
+      float y1[4], y2[4];
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        const float c = cs[j0 + e], sgn = sn[j0 + e];
+        y1[e] = x1[k][e] * c - x2[k][e] * sgn;
+        y2[e] = x2[k][e] * c + x1[k][e] * sgn;
+      }
+      if (hh < Hq) {
+        store4(q, (long)r * NQ + hh * D + j0, y1);
+        store4(q, (long)r * NQ + hh * D + j0 + half, y2);
+      } else {
+        const long o = ((long)pos * Hkv + (hh - Hq)) * D;
+        store4(kc, o + j0, y1);
+        store4(kc, o + j0 + half, y2);
+      }
+    }
+    if (gi < vgroups) store4(vc, (long)pos * NK + gi * 4, xv[k]);
+  }
 }
 
 hipError_t launch_qkv_epilogue(int dtype, const float* part, int splits, long split_stride, const int32_t* row_pos,
                                int R, int S, int Hq, int Hkv, int D, float rope_base, void* q, void* kc, void* vc,
                                hipStream_t s) {
   if (R <= 0) return hipSuccess;
-  if (D / 2 > kMaxHalf) return hipErrorInvalidValue;
-  RopeTable rt;
-  for (int j = 0; j < D / 2; ++j) rt.theta[j] = pow((double)rope_base, -2.0 * j / (double)D);
+  if (D / 2 > kMaxHalf || (D / 2) % 4 != 0 || (Hq + Hkv) * (D / 8) > 256 * kQkvGroups ||
+      Hkv * D / 4 > 256 * kQkvGroups)
+    return hipErrorInvalidValue;
+  const double log2_base = log2((double)rope_base);
   if (dtype == 0)
     hipLaunchKernelGGL(k_qkv_epilogue<float>, dim3(R), dim3(256), 0, s, part, splits, split_stride, row_pos, S, Hq,
-                       Hkv, D, rt, (float*)q, (float*)kc, (float*)vc);
+                       Hkv, D, log2_base, (float*)q, (float*)kc, (float*)vc);
   else
     hipLaunchKernelGGL(k_qkv_epilogue<bf16>, dim3(R), dim3(256), 0, s, part, splits, split_stride, row_pos, S, Hq,
-                       Hkv, D, rt, (bf16*)q, (bf16*)kc, (bf16*)vc);
+                       Hkv, D, log2_base, (bf16*)q, (bf16*)kc, (bf16*)vc);
   return hipGetLastError();
 }
 
@@ -214,8 +252,8 @@ __device__ __forceinline__ float block_sum256(float v, float* red) {
   return red[0] + red[1] + red[2] + red[3];
 }
 
-template <typename T>
-__global__ __launch_bounds__(256) void k_resid_norm(const float* __restrict__ part, int splits, long sstride,
+template <typename T, int SPLITS>
+__global__ __launch_bounds__(256) void k_resid_norm(const float* __restrict__ part, int splits_unused, long sstride,
                                                     const int32_t* __restrict__ row_pos, int R, int d,
                                                     T* __restrict__ x, const T* __restrict__ g, float eps,
                                                     T* __restrict__ xn) {
@@ -234,7 +272,8 @@ __global__ __launch_bounds__(256) void k_resid_norm(const float* __restrict__ pa
     const int c = threadIdx.x + 256 * k;
     if (c >= nchunk) break;
     E::unpack(x4[c], f[k]);
-    for (int sp = 0; sp < splits; ++sp) {
+#pragma unroll
+    for (int sp = 0; sp < SPLITS; ++sp) {
       const float4* p4 = reinterpret_cast<const float4*>(pr + sp * sstride + (long)c * V);
 #pragma unroll
       for (int e4 = 0; e4 < V / 4; ++e4) {
@@ -273,12 +312,24 @@ hipError_t launch_resid_norm(int dtype, const float* part, int splits, long spli
   if (R <= 0) return hipSuccess;
   const int vec = dtype == 0 ? 4 : 8;
   if (d % vec != 0 || d / vec > 256 * kRowChunks) return hipErrorInvalidValue;
-  if (dtype == 0)
-    hipLaunchKernelGGL(k_resid_norm<float>, dim3(R), dim3(256), 0, s, part, splits, split_stride, row_pos, R, d,
-                       (float*)x, (const float*)g, eps, (float*)xn);
-  else
-    hipLaunchKernelGGL(k_resid_norm<bf16>, dim3(R), dim3(256), 0, s, part, splits, split_stride, row_pos, R, d,
-                       (bf16*)x, (const bf16*)g, eps, (bf16*)xn);
+#define DLLM_RN(T_, SP_)                                                                              \
+  hipLaunchKernelGGL((k_resid_norm<T_, SP_>), dim3(R), dim3(256), 0, s, part, splits, split_stride, row_pos, R, d, \
+                     (T_*)x, (const T_*)g, eps, (T_*)xn)
+#define DLLM_RN_SPLITS(T_)                          \
+  switch (splits) {                                 \
+    case 1: DLLM_RN(T_, 1); break;                  \
+    case 2: DLLM_RN(T_, 2); break;                  \
+    case 4: DLLM_RN(T_, 4); break;                  \
+    case 8: DLLM_RN(T_, 8); break;                  \
+    default: return hipErrorInvalidValue;           \
+  }
+  if (dtype == 0) {
+    DLLM_RN_SPLITS(float)
+  } else {
+    DLLM_RN_SPLITS(bf16)
+  }
+#undef DLLM_RN_SPLITS
+#undef DLLM_RN
   return hipGetLastError();
 }
 
