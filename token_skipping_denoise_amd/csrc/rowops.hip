@@ -15,16 +15,28 @@ namespace dllm {
 
 enum RowMode { kEmbed = 0, kGather = 1, kScatter = 2 };
 
-// One wavefront per row: copy a row (by token id, gather or scatter) and
-// optionally write its RMSNorm * g.
+constexpr int kRowChunks = 4;  // 16-byte chunks per thread: rows up to 1024 chunks
+
+__device__ __forceinline__ float block_sum256(float v, float* red) {
+  v = wave_sum(v);
+  if ((threadIdx.x & 63) == 0) red[threadIdx.x >> 6] = v;
+  __syncthreads();
+  return red[0] + red[1] + red[2] + red[3];
+}
+
+
+
+// One workgroup per row: copy a row (by token id, gather or scatter) and optionally write
+// its RMSNorm * g.  The sum of squares uses the same chunk assignment and reduction order
+// as k_resid_norm, so a row normalised here and one normalised there are bit-identical.
 template <typename T, int MODE>
 __global__ __launch_bounds__(256) void k_rows_norm(const T* __restrict__ src, const int32_t* __restrict__ map,
                                                    int V, int rows, int w, T* __restrict__ dst,
                                                    const T* __restrict__ g, float eps, T* __restrict__ dst_norm) {
   using E = Elem<T>;
-  const int lane = threadIdx.x & 63;
-  const int r = blockIdx.x * 4 + (threadIdx.x >> 6);
-  if (r >= rows) return;
+  constexpr int VE = E::kVec;
+  __shared__ float red[4];
+  const int r = blockIdx.x;
   long src_row, dst_row;
   if (MODE == kEmbed) {
     int t = map[r];
@@ -37,30 +49,35 @@ __global__ __launch_bounds__(256) void k_rows_norm(const T* __restrict__ src, co
     src_row = (MODE == kGather) ? pos : r;
     dst_row = (MODE == kGather) ? r : pos;
   }
-  const int nchunk = w / E::kVec;
+  const int nchunk = w / VE;
   const uint4* s4 = reinterpret_cast<const uint4*>(src + src_row * (long)w);
   uint4* d4 = dst ? reinterpret_cast<uint4*>(dst + dst_row * (long)w) : nullptr;
+  float f[kRowChunks][VE];
   float ss = 0.f;
-  for (int c = lane; c < nchunk; c += kWave) {
+#pragma unroll
+  for (int k = 0; k < kRowChunks; ++k) {
+    const int c = threadIdx.x + 256 * k;
+    if (c >= nchunk) break;
     const uint4 v = s4[c];
     if (d4) d4[c] = v;
-    float f[E::kVec];
-    E::unpack(v, f);
+    E::unpack(v, f[k]);
 #pragma unroll
-    for (int e = 0; e < E::kVec; ++e) ss += f[e] * f[e];
+    for (int e = 0; e < VE; ++e) ss += f[k][e] * f[k][e];
   }
   if (!g) return;
-  ss = wave_sum(ss);
+  ss = block_sum256(ss, red);
   const float inv = 1.0f / sqrtf(ss / (float)w + eps);
   const uint4* g4 = reinterpret_cast<const uint4*>(g);
   uint4* n4 = reinterpret_cast<uint4*>(dst_norm + (long)r * w);
-  for (int c = lane; c < nchunk; c += kWave) {
-    float f[E::kVec], gf[E::kVec];
-    E::unpack(s4[c], f);
+#pragma unroll
+  for (int k = 0; k < kRowChunks; ++k) {
+    const int c = threadIdx.x + 256 * k;
+    if (c >= nchunk) break;
+    float gf[VE];
     E::unpack(g4[c], gf);
 #pragma unroll
-    for (int e = 0; e < E::kVec; ++e) f[e] = f[e] * inv * gf[e];
-    n4[c] = E::pack(f);
+    for (int e = 0; e < VE; ++e) f[k][e] = f[k][e] * inv * gf[e];
+    n4[c] = E::pack(f[k]);
   }
 }
 
@@ -68,7 +85,8 @@ template <int MODE>
 static hipError_t rows_norm(int dtype, const void* src, const int32_t* map, int V, int rows, int w, void* dst,
                             const void* g, float eps, void* dst_norm, hipStream_t s) {
   if (rows <= 0) return hipSuccess;
-  dim3 grid((rows + 3) / 4), block(256);
+  if (w / (dtype == 0 ? 4 : 8) > 256 * kRowChunks) return hipErrorInvalidValue;
+  dim3 grid(rows), block(256);
   if (dtype == 0)
     hipLaunchKernelGGL((k_rows_norm<float, MODE>), grid, block, 0, s, (const float*)src, map, V, rows, w,
                        (float*)dst, (const float*)g, eps, (float*)dst_norm);
@@ -243,15 +261,6 @@ hipError_t launch_qkv_epilogue(int dtype, const float* part, int splits, long sp
 // One workgroup per row: x += sum(partials) (rounded to storage), then xn = rmsnorm(x) * g.
 // Every load of the row is issued up front (values stay in registers), so the row costs
 // about one memory round trip.
-constexpr int kRowChunks = 4;  // 16-byte chunks per thread: rows up to 1024 chunks
-
-__device__ __forceinline__ float block_sum256(float v, float* red) {
-  v = wave_sum(v);
-  if ((threadIdx.x & 63) == 0) red[threadIdx.x >> 6] = v;
-  __syncthreads();
-  return red[0] + red[1] + red[2] + red[3];
-}
-
 template <typename T, int SPLITS>
 __global__ __launch_bounds__(256) void k_resid_norm(const float* __restrict__ part, int splits_unused, long sstride,
                                                     const int32_t* __restrict__ row_pos, int R, int d,
