@@ -156,7 +156,18 @@ def main():
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-kernel-timing", action="store_true")
     ap.add_argument("--no-graph", action="store_true", help="launch eagerly instead of replaying a HIP graph")
+    ap.add_argument("--calibrate-copy", action="store_true",
+                    help="only copy a 1 GiB buffer once (reference for the HBM byte counters) and exit")
     args = ap.parse_args()
+    if args.calibrate_copy:
+        n = 1 << 30
+        src = torch.ones(n // 4, dtype=torch.float32, device="cuda:0")
+        dst = torch.empty_like(src)
+        torch.cuda.synchronize()
+        dst.copy_(src)
+        torch.cuda.synchronize()
+        print(json.dumps({"copy_bytes_read": n, "copy_bytes_written": n}))
+        return
     if args.gpus != 1:
         print(f"bench.py runs on one GPU only: --gpus {args.gpus} is not supported "
               "(sequences shard with no exchange; see the design notes)", file=sys.stderr)

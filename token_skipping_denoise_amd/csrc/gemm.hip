@@ -57,8 +57,8 @@ __device__ __forceinline__ void decode_tile(int nt, int tiles_m, int tiles_n, in
 // memory straight into an NS-stage LDS ring with no register staging, so
 // NS-1 tiles stay in flight while one is multiplied.  BK = 64: a tile row is
 // 128 bytes = 8 chunks of 16 bytes; one wave load instruction fills 8 rows
-// (1 KB), and chunk c of row r is stored at slot c ^ (r & 7), so the 32-row
-// MFMA fragment reads hit 32 distinct banks.
+// (1 KB), and chunk c of row r is stored at slot c ^ ((r >> 1) & 7), so the
+// MFMA fragment reads (32 rows at one chunk index) are free of bank conflicts.
 // s_waitcnt with only vmcnt constrained (expcnt/lgkmcnt left at their maxima).
 template <int N>
 __device__ __forceinline__ void wait_vm() {
@@ -112,18 +112,23 @@ __global__ __launch_bounds__(256, OCC) void k_gemm_lds(const uint16_t* __restric
     return (jb < TN / 2) ? h0 + half * (BN / 4) + jb * 32 + t : F + h0 + half * (BN / 4) + (jb - TN / 2) * 32 + t;
   };
   const int w_rows = (EPI == 0) ? N : 2 * F;
-  const int lrow = lane >> 3, lchunk = (lane & 7) ^ lrow;
+  // A tile row is 128 bytes, half of the 64 banks: rows r and r+1 fall in opposite bank
+  // halves, so the chunk slot is swizzled by (r >> 1) & 7 and any 16 consecutive rows read at
+  // one chunk index touch all 64 banks once.
+  const int lrow = lane >> 3;
   const uint16_t* ga[LA];
   const uint16_t* gb[LB];
 #pragma unroll
   for (int i = 0; i < LA; ++i) {
     const int row = (wave + 4 * i) * 8 + lrow;
-    ga[i] = A + (long)min(m0 + row, M - 1) * K + lchunk * 8;
+    const int chunk = (lane & 7) ^ ((row >> 1) & 7);
+    ga[i] = A + (long)min(m0 + row, M - 1) * K + chunk * 8;
   }
 #pragma unroll
   for (int i = 0; i < LB; ++i) {
     const int row = (wave + 4 * i) * 8 + lrow;
-    gb[i] = W + (long)min(w_row(row), w_rows - 1) * K + lchunk * 8;
+    const int chunk = (lane & 7) ^ ((row >> 1) & 7);
+    gb[i] = W + (long)min(w_row(row), w_rows - 1) * K + chunk * 8;
   }
   auto issue = [&](int stage, int kb) {
     const long k0 = (long)kb * BK;
@@ -145,7 +150,7 @@ __global__ __launch_bounds__(256, OCC) void k_gemm_lds(const uint16_t* __restric
 #pragma unroll
       for (int e = 0; e < 16; ++e) acc[i][j][e] = 0.f;
 
-  const int swz = lane & 7, hi = lane >> 5, r32 = lane & 31;
+  const int swz = (lane >> 1) & 7, hi = lane >> 5, r32 = lane & 31;  // fragment rows start at multiples of 32
   // fragments of step ks+1 are read from LDS while the MFMAs of step ks run
   auto load_frags = [&](const uint16_t* base, int ks, bf16x8_t* af, bf16x8_t* bfr) {
     const int slot = ((ks * 2 + hi) ^ swz) * 8;
