@@ -75,6 +75,13 @@ typedef enum {
   DLLM_SEL_UNLOCKED = 2    /* every candidate (SureLock compaction) */
 } dllm_sel;
 
+/* How a step unmasks positions of [block_lo, block_hi) (with unmask_n > 0). */
+typedef enum {
+  DLLM_UNMASK_CONF = 0,   /* the unmask_n most confident masked positions (ES-dLLM sec. 1) */
+  DLLM_UNMASK_FORCED = 1  /* every masked position with force == DLLM_FORCE_ON: the positions a
+                             dilated schedule plans for this round ([DUS] sec. 2) */
+} dllm_unmask_mode;
+
 /* force[] values: per position. */
 enum { DLLM_FORCE_NONE = 0, DLLM_FORCE_ON = 1, DLLM_FORCE_EXCLUDED = 2 };
 
@@ -147,6 +154,7 @@ typedef struct {
   float lock_conf_min;      /* lock also requires conf > this */
   int32_t unmask_n;         /* unmask this many masked positions per sequence (0: none) */
   int32_t block_lo, block_hi; /* unmasking window [lo, hi) */
+  int32_t unmask_mode;      /* dllm_unmask_mode */
   void *ws;                 /* device workspace */
   size_t ws_bytes;
 } dllm_step_cfg;

@@ -37,6 +37,6 @@ from .transformer import (  # noqa: F401
 from .importance import psi, importance_score  # noqa: F401
 from .selection import order_before, select_topk, select_thresh_cap  # noqa: F401
 from .vocab import conf_kl_row, conf_kl  # noqa: F401
-from .post import surelock_update, unmask_topn  # noqa: F401
+from .post import surelock_update, unmask_forced, unmask_topn  # noqa: F401
 from .dus import dus_rounds  # noqa: F401
 from .step import OracleModel, OracleState, StepCfg, ScoreCfg, skip_step, new_state  # noqa: F401

@@ -8,6 +8,9 @@
 * Confidence unmasking (ES-dLLM summary section 1; SureLock section 1): in
   each iteration the most confident masked positions of the current block are
   replaced by their argmax token; ties go to the lower index.
+* Planned unmasking (DUS summary, technical summary section 2): the positions
+  a dilated schedule assigns to the current round are unmasked together,
+  whatever their confidence; the schedule marks them with force == 1.
 """
 from __future__ import annotations
 
@@ -38,4 +41,16 @@ def unmask_topn(tokens: np.ndarray, conf: np.ndarray, argmax: np.ndarray, mask_i
         cand.sort(key=lambda i: (-float(conf[b, i]), i))
         for i in cand[:n]:
             out[b, i] = argmax[b, i]
+    return out
+
+
+def unmask_forced(tokens: np.ndarray, force: np.ndarray, argmax: np.ndarray, mask_id: int,
+                  lo: int, hi: int) -> np.ndarray:
+    """tokens/force/argmax: [B, S].  Unmask every masked position of [lo, hi) with force == 1."""
+    out = np.array(tokens, copy=True)
+    B = tokens.shape[0]
+    for b in range(B):
+        for i in range(lo, hi):
+            if tokens[b, i] == mask_id and force[b, i] == 1:
+                out[b, i] = argmax[b, i]
     return out

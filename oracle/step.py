@@ -14,7 +14,8 @@ Order of operations (ES-dLLM technical summary 2.1; SureLock 2.1):
   5. write the active rows' final hidden state, run the LM head on them and
      compute confidence, argmax and local KL; skipped positions keep all of
      their previous statistics;
-  6. SureLock lock update and/or confidence unmasking of the current block.
+  6. SureLock lock update and/or unmasking of the current block (by
+     confidence, or the positions a dilated schedule plans for this round).
 
 Readings where the pages leave a step open: one boundary per iteration; the
 mask id is the last vocabulary entry and is excluded from softmax and argmax;
@@ -29,12 +30,13 @@ import numpy as np
 
 from .importance import VAR_L1N, importance_score
 from .numerics import store_fn
-from .post import surelock_update, unmask_topn
+from .post import surelock_update, unmask_forced, unmask_topn
 from .selection import FORCE_EXCLUDED, select_thresh_cap, select_topk
 from .transformer import layer_rows, lm_logits
 from .vocab import conf_kl
 
 SEL_TOPK, SEL_THRESH_CAP, SEL_UNLOCKED = 0, 1, 2
+UNMASK_CONF, UNMASK_FORCED = 0, 1
 
 
 @dataclass
@@ -72,6 +74,7 @@ class StepCfg:
     unmask_n: int = 0
     block_lo: int = 0
     block_hi: int = 0
+    unmask_mode: int = UNMASK_CONF
 
 
 @dataclass
@@ -185,7 +188,10 @@ def skip_step(model: OracleModel, st: OracleState, cfg: StepCfg) -> tuple[Oracle
         st.force = surelock_update(st.force.reshape(-1), rows, st.conf.reshape(-1), st.kl.reshape(-1),
                                    st.have_prev, cfg.lock_kl_eps, cfg.lock_conf_min).reshape(B, S)
     if cfg.unmask_n > 0:
-        st.tokens = unmask_topn(st.tokens, st.conf, st.argmax, model.mask_id,
-                                cfg.block_lo, cfg.block_hi, cfg.unmask_n)
+        if cfg.unmask_mode == UNMASK_FORCED:
+            st.tokens = unmask_forced(st.tokens, st.force, st.argmax, model.mask_id, cfg.block_lo, cfg.block_hi)
+        else:
+            st.tokens = unmask_topn(st.tokens, st.conf, st.argmax, model.mask_id,
+                                    cfg.block_lo, cfg.block_hi, cfg.unmask_n)
     st.have_prev = True
     return st, {"rows": rows, "scores": scores, "logits": z}

@@ -6,8 +6,9 @@ import torch
 import synth
 from oracle.importance import VAR_COS, VAR_L1N
 from oracle.selection import FORCE_EXCLUDED
-from oracle.step import (SEL_THRESH_CAP, SEL_TOPK, SEL_UNLOCKED, OracleModel, ScoreCfg, StepCfg, new_state,
-                         skip_step)
+from oracle.dus import dus_rounds
+from oracle.step import (SEL_THRESH_CAP, SEL_TOPK, SEL_UNLOCKED, UNMASK_FORCED, OracleModel, ScoreCfg, StepCfg,
+                         new_state, skip_step)
 from synth import workloads
 from tests.gpu_util import DEV, assert_close, np64, selection_gap
 from tests.helpers import oracle_weights
@@ -230,6 +231,57 @@ def test_bf16_thresh_cap_forced_rows():
         assert {b * dims.S + 96, b * dims.S + 104} <= set(got_rows)
         assert all(r % dims.S >= dims.prompt for r in got_rows)
     _compare_state(gs, os_, rows, 2e-2, "thresh")
+
+
+def test_bf16_dilated_block_decode():
+    """A block decoded by dilated rounds: each round recomputes a capped, cosine-gated set that always holds
+    the round's planned positions, and unmasks exactly those positions."""
+    dims = workloads.shrink(workloads.LLADA_LONG, n_layers=2, d=256, n_heads=2, n_kv_heads=2, d_ff=512,
+                            vocab=1000, B=2, S=96, prompt=64)
+    k, blk, a = 16, 16, 2
+    lo, hi = dims.prompt, dims.prompt + blk
+    gm, om = _models(dims, std=0.05)
+    tok = workloads.initial_tokens(dims)
+    gs = api.State(gm, tok.to(DEV), k_max=k, track_kl=True)
+    ws = api.alloc_workspace(gm, dims.B, dims.S, k)
+    os_ = new_state(om, tok.numpy(), track_kl=True)
+    api.skip_step(gm, gs, api.step_cfg(0, True, ws=ws))
+    os_, _ = skip_step(om, os_, StepCfg(boundary_layer=0, full_step=True))
+    gsc, osc = _score_cfg_pair(0.0, VAR_COS, SEL_THRESH_CAP, k, tau=1e-4)
+    for rnd, plan in enumerate(dus_rounds(blk, a)):
+        print(f"dilated round {rnd}: {plan}", flush=True)
+        force = np.zeros((dims.B, dims.S), dtype=np.uint8)
+        force[:, :dims.prompt] = FORCE_EXCLUDED
+        force[:, [lo + p for p in plan]] = 1
+        gs.force.copy_(torch.from_numpy(force))
+        os_.force = force.copy()
+        api.skip_step(gm, gs, api.step_cfg(0, False, gsc, unmask_n=1, block_lo=lo, block_hi=hi,
+                                           unmask_mode=api.UNMASK_FORCED, ws=ws))
+        os_, info = skip_step(om, os_, StepCfg(boundary_layer=0, full_step=False, score=osc, unmask_n=1,
+                                               block_lo=lo, block_hi=hi, unmask_mode=UNMASK_FORCED))
+        torch.cuda.synchronize()
+        rows = info["rows"]
+        got_rows = [b * dims.S + int(i) for b in range(dims.B) for i in gs.idx[b, :int(gs.n_active[b])].cpu()]
+        assert got_rows == rows.tolist()
+        for b in range(dims.B):
+            assert {b * dims.S + lo + p for p in plan} <= set(got_rows)
+        _compare_state(gs, os_, rows, 2e-2, f"round {rnd}")
+        # the planned positions take the argmax: the oracle's token wherever its top-2 logit gap is clear of
+        # rounding; in a near tie the GPU's pick is kept on both sides so later rounds see the same tokens
+        gt = gs.tokens.cpu().numpy()
+        planned = np.zeros((dims.B, dims.S), dtype=bool)
+        planned[:, [lo + p for p in plan]] = True
+        assert np.array_equal(gt[~planned], os_.tokens[~planned])
+        assert np.array_equal(gt[planned], gs.argmax.cpu().numpy()[planned])
+        for b, i in zip(*np.nonzero(planned)):
+            z = os_.logits_prev[b * dims.S + i].copy()
+            z[dims.mask_id] = -np.inf
+            top2 = np.sort(z)[-2:]
+            if top2[1] - top2[0] > 1e-2:
+                assert gt[b, i] == os_.tokens[b, i], f"round {rnd} position {b},{i}"
+            else:
+                os_.tokens[b, i] = gt[b, i]
+    assert not np.any(gs.tokens.cpu().numpy()[:, lo:hi] == dims.mask_id)
 
 
 def test_all_rows_active_equals_full_step_on_gpu():

@@ -6,7 +6,7 @@ import numpy as np
 import pytest
 
 from oracle.dus import dus_rounds, n_rounds
-from oracle.post import surelock_update, unmask_topn
+from oracle.post import surelock_update, unmask_forced, unmask_topn
 
 GOLDEN = os.path.join(os.path.dirname(__file__), "golden", "dus_worked_example.txt")
 
@@ -72,3 +72,49 @@ def test_dus_round_count_and_partition(a):
 
 def test_dus_block16_rounds():
     assert dus_rounds(16, 2) == [[0, 8], [4, 12], [2, 6, 10, 14], [1, 3, 5, 7, 9, 11, 13, 15]]
+
+
+def test_unmask_forced_marks_only():
+    mask = 99
+    tok = np.array([[5, mask, mask, mask, 8, mask, mask]])
+    force = np.array([[2, 1, 0, 1, 1, 2, 1]], dtype=np.uint8)
+    arg = np.array([[1, 11, 12, 13, 14, 15, 16]])
+    out = unmask_forced(tok, force, arg, mask, 0, 6)
+    # position 4 is not masked, 5 is excluded (2), 6 lies outside [0, 6)
+    assert out.tolist() == [[5, 11, mask, 13, 8, mask, mask]]
+
+
+def test_dus_rounds_unmask_every_position_once():
+    """Driving unmask_forced with the dilated rounds fills a block exactly once per position."""
+    mask, lo, B = 50, 3, 16
+    tok = np.full((1, lo + B + 2), mask)
+    tok[0, :lo] = 1
+    arg = np.arange(tok.size).reshape(tok.shape) + 100
+    seen = np.zeros(tok.shape[1], dtype=int)
+    for r in dus_rounds(B, 2):
+        force = np.zeros(tok.shape, dtype=np.uint8)
+        force[0, [lo + p for p in r]] = 1
+        new = unmask_forced(tok, force, arg, mask, lo, lo + B)
+        changed = np.nonzero(new[0] != tok[0])[0]
+        assert sorted(changed.tolist()) == sorted(lo + p for p in r)
+        seen[changed] += 1
+        tok = new
+    assert seen[lo:lo + B].tolist() == [1] * B and seen.sum() == B
+    assert tok[0, lo + B:].tolist() == [mask, mask]
+
+
+def test_unmask_forced_agrees_with_top_n_on_its_picks():
+    """Marking exactly the top-n confident masked positions makes both rules agree."""
+    rng = np.random.default_rng(11)
+    mask = 7
+    tok = rng.integers(0, 7, size=(3, 40))
+    tok[rng.uniform(size=tok.shape) < 0.6] = mask
+    conf = rng.uniform(size=tok.shape)
+    arg = rng.integers(0, 7, size=tok.shape)
+    n = 5
+    force = np.zeros(tok.shape, dtype=np.uint8)
+    for b in range(3):
+        cand = [i for i in range(4, 36) if tok[b, i] == mask]
+        for i in sorted(cand, key=lambda i: -conf[b, i])[:n]:
+            force[b, i] = 1
+    assert np.array_equal(unmask_forced(tok, force, arg, mask, 4, 36), unmask_topn(tok, conf, arg, mask, 4, 36, n))

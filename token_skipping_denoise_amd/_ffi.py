@@ -11,6 +11,7 @@ DLLM_F32, DLLM_BF16 = 0, 1
 VAR_L1N, VAR_COS, VAR_L2REL, VAR_KL, VAR_NONE = 0, 1, 2, 3, 4
 SEL_TOPK, SEL_THRESH_CAP, SEL_UNLOCKED = 0, 1, 2
 FORCE_NONE, FORCE_ON, FORCE_EXCLUDED = 0, 1, 2
+UNMASK_CONF, UNMASK_FORCED = 0, 1
 
 EXPORTED = (
     "dllm_workspace_size", "dllm_score_select", "dllm_gather_rows", "dllm_scatter_rows",
@@ -49,7 +50,8 @@ class StateC(Structure):
 class StepCfg(Structure):
     _fields_ = [("boundary_layer", c_int32), ("full_step", c_int32), ("score", ScoreCfg),
                 ("lock_kl_eps", c_float), ("lock_conf_min", c_float), ("unmask_n", c_int32),
-                ("block_lo", c_int32), ("block_hi", c_int32), ("ws", c_void_p), ("ws_bytes", c_size_t)]
+                ("block_lo", c_int32), ("block_hi", c_int32), ("unmask_mode", c_int32), ("ws", c_void_p),
+                ("ws_bytes", c_size_t)]
 
 
 class Timing(Structure):

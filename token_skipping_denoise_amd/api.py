@@ -12,7 +12,7 @@ import torch
 
 from . import _ffi
 from ._ffi import (DLLM_BF16, DLLM_F32, FORCE_EXCLUDED, FORCE_NONE, FORCE_ON, SEL_THRESH_CAP, SEL_TOPK,  # noqa: F401
-                   SEL_UNLOCKED, VAR_COS, VAR_KL, VAR_L1N, VAR_L2REL, VAR_NONE)
+                   SEL_UNLOCKED, UNMASK_CONF, UNMASK_FORCED, VAR_COS, VAR_KL, VAR_L1N, VAR_L2REL, VAR_NONE)
 
 
 class DllmError(RuntimeError):
@@ -221,7 +221,8 @@ class State:
 
 
 def step_cfg(boundary_layer: int, full_step: bool, score: _ffi.ScoreCfg | None = None, *, lock_kl_eps=-1.0,
-             lock_conf_min=0.9, unmask_n=0, block_lo=0, block_hi=0, ws=None) -> _ffi.StepCfg:
+             lock_conf_min=0.9, unmask_n=0, block_lo=0, block_hi=0, unmask_mode=UNMASK_CONF,
+             ws=None) -> _ffi.StepCfg:
     c = _ffi.StepCfg()
     c.boundary_layer = int(boundary_layer)
     c.full_step = int(bool(full_step))
@@ -231,6 +232,7 @@ def step_cfg(boundary_layer: int, full_step: bool, score: _ffi.ScoreCfg | None =
     c.unmask_n = int(unmask_n)
     c.block_lo = int(block_lo)
     c.block_hi = int(block_hi)
+    c.unmask_mode = int(unmask_mode)
     if ws is not None:
         c.ws = _ptr(ws)
         c.ws_bytes = ws.numel() * ws.element_size()

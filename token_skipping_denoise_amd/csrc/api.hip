@@ -354,6 +354,8 @@ int dllm_skip_step(const dllm_model* model, dllm_state* state, const dllm_step_c
     if (sc.sel == DLLM_SEL_UNLOCKED && kx != S) return DLLM_EINVAL;
   }
   if (cfg->unmask_n < 0 || cfg->unmask_n > 256) return DLLM_EINVAL;
+  if (cfg->unmask_mode != DLLM_UNMASK_CONF && cfg->unmask_mode != DLLM_UNMASK_FORCED) return DLLM_EINVAL;
+  if (cfg->unmask_n > 0 && cfg->unmask_mode == DLLM_UNMASK_FORCED && !state->force) return DLLM_EINVAL;
   if (cfg->unmask_n > 0 && (cfg->block_lo < 0 || cfg->block_hi > S || cfg->block_lo > cfg->block_hi))
     return DLLM_EINVAL;
   if (cfg->lock_kl_eps >= 0.f && !state->force) return DLLM_EINVAL;
@@ -447,9 +449,14 @@ int dllm_skip_step(const dllm_model* model, dllm_state* state, const dllm_step_c
   if (cfg->lock_kl_eps >= 0.f && state->have_prev)
     DLLM_TRY(launch_lock_update(rp, R, state->conf, state->kl, cfg->lock_kl_eps, cfg->lock_conf_min, state->force,
                                 c.s));
-  if (cfg->unmask_n > 0)
-    DLLM_TRY(launch_unmask(state->tokens, state->conf, state->argmax, B, S, model->mask_id, cfg->block_lo,
-                           cfg->block_hi, cfg->unmask_n, c.s));
+  if (cfg->unmask_n > 0) {
+    if (cfg->unmask_mode == DLLM_UNMASK_FORCED)
+      DLLM_TRY(launch_unmask_forced(state->tokens, state->force, state->argmax, B, S, model->mask_id, cfg->block_lo,
+                                    cfg->block_hi, c.s));
+    else
+      DLLM_TRY(launch_unmask(state->tokens, state->conf, state->argmax, B, S, model->mask_id, cfg->block_lo,
+                             cfg->block_hi, cfg->unmask_n, c.s));
+  }
   state->bnd_cur = 1 - state->bnd_cur;
   state->have_prev = 1;
   return DLLM_OK;

@@ -77,5 +77,8 @@ hipError_t launch_lock_update(const int32_t* row_pos, int R, const float* conf, 
                               float conf_min, uint8_t* force, hipStream_t s);
 hipError_t launch_unmask(int32_t* tokens, const float* conf, const int32_t* argmax, int B, int S, int mask_id,
                          int lo, int hi, int n, hipStream_t s);
+// tokens[b, i] = argmax[b, i] for masked i in [lo, hi) with force[b, i] == 1.
+hipError_t launch_unmask_forced(int32_t* tokens, const uint8_t* force, const int32_t* argmax, int B, int S,
+                                int mask_id, int lo, int hi, hipStream_t s);
 
 }  // namespace dllm

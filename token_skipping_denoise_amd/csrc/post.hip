@@ -6,6 +6,9 @@
 // * Confidence unmasking (ES-dLLM summary section 1; SureLock section 1): the
 //   n most confident masked positions of the current block receive their
 //   argmax token; ties go to the lower position.
+// * Planned unmasking (DUS summary, technical summary section 2): the masked
+//   positions that a dilated schedule assigns to this round (marked FORCE_ON)
+//   receive their argmax token.
 #include "common.h"
 #include "kernels.h"
 
@@ -84,6 +87,25 @@ hipError_t launch_unmask(int32_t* tokens, const float* conf, const int32_t* argm
   if (B <= 0 || n <= 0 || hi <= lo) return hipSuccess;
   if (n > kMaxUnmask) return hipErrorInvalidValue;
   hipLaunchKernelGGL(k_unmask, dim3(B), dim3(kUT), 0, s, tokens, conf, argmax, S, mask_id, lo, hi, n);
+  return hipGetLastError();
+}
+
+__global__ void k_unmask_forced(int32_t* __restrict__ tokens, const uint8_t* __restrict__ force,
+                                const int32_t* __restrict__ argmax, int B, int S, int mask_id, int lo, int hi) {
+  const int w = hi - lo;
+  const long e = blockIdx.x * (long)blockDim.x + threadIdx.x;
+  if (e >= (long)B * w) return;
+  const int b = (int)(e / w), i = lo + (int)(e - (long)b * w);
+  const long p = (long)b * S + i;
+  if (tokens[p] == mask_id && force[p] == 1) tokens[p] = argmax[p];
+}
+
+hipError_t launch_unmask_forced(int32_t* tokens, const uint8_t* force, const int32_t* argmax, int B, int S,
+                                int mask_id, int lo, int hi, hipStream_t s) {
+  const long n = (long)B * (hi - lo);
+  if (n <= 0) return hipSuccess;
+  hipLaunchKernelGGL(k_unmask_forced, dim3((unsigned)((n + 255) / 256)), dim3(256), 0, s, tokens, force, argmax, B, S,
+                     mask_id, lo, hi);
   return hipGetLastError();
 }
 
