@@ -13,8 +13,9 @@ tokens / second.
 Prints ONE JSON line (rank 0, N = 1).  `roofline` describes the dominant
 kernel -- the gate/up + SwiGLU product of the skipped layers (128 active rows),
 timed live with HIP events bracketing each of its launches inside the timed
-region; `cpu_baseline` times the CPU oracle on a bounded sample (one dense
-layer, one sparse layer and the LM head) and extrapolates to a generation.
+region; `cpu_baseline` times the CPU oracle on a bounded sample (16 layers
+over all rows and over the active rows, scoring and selection, the LM head)
+and extrapolates to a generation.
 """
 from __future__ import annotations
 
@@ -99,41 +100,59 @@ def ffn_up_bytes(dims, rows: int) -> float:
     return (2 * dims.d_ff * dims.d + rows * dims.d + rows * dims.d_ff) * e
 
 
-def cpu_baseline(model_w_gpu, dims, k_sparse, boundary, steps):
-    """Time the oracle (float64 NumPy, bf16 storage rounding) on one dense layer, one sparse layer and the
-    LM head, then extrapolate to one generation."""
+def cpu_baseline(model_w_gpu, dims, k_sparse, boundary, steps, sample_layers=16):
+    """Time the oracle (float64 NumPy, bf16 storage rounding) on a bounded sample of the generation and
+    extrapolate to one generation.  The sample: `sample_layers` layers, each run once over all rows (as in
+    the full first iteration and the layers below the boundary) and once over the active rows (as in the
+    skipped regime); the importance score and top-k selection; the LM head with the confidence pass over
+    all rows and over the active rows."""
     import numpy as np
     from threadpoolctl import threadpool_info
 
-    from oracle.numerics import store_fn
-    from oracle.transformer import layer_rows, lm_logits
     import synth
+    from oracle.importance import VAR_L1N, importance_score
+    from oracle.numerics import store_fn
+    from oracle.selection import select_topk
+    from oracle.transformer import layer_rows, lm_logits
+    from oracle.vocab import conf_kl
 
     store = store_fn("bf16")
-    lw = {k: v.detach().to("cpu", torch.float64).numpy() for k, v in model_w_gpu["layers"][0].items()}
     B, S, d = dims.B, dims.S, dims.d
     x = synth.normal(synth.seed_of(900), (B * S, d), 1.0, torch.bfloat16).double().numpy()
+    xp = x + synth.normal(synth.seed_of(903), (B * S, d), 1e-3, torch.float32).double().numpy()
     kc = synth.normal(synth.seed_of(901), (B, S, dims.n_kv_heads, dims.head_dim), 1.0, torch.bfloat16).double().numpy()
     vc = synth.normal(synth.seed_of(902), (B, S, dims.n_kv_heads, dims.head_dim), 1.0, torch.bfloat16).double().numpy()
+    conf = synth.uniform01(synth.seed_of(904), (B * S,)).double().numpy()
     rows_all = np.arange(B * S)
+    n_layers = min(sample_layers, len(model_w_gpu["layers"]))
 
-    def t_layer(rows):
-        t0 = time.perf_counter()
-        layer_rows(lw, x[rows], rows % S, rows // S, kc, vc, n_heads=dims.n_heads, n_kv_heads=dims.n_kv_heads,
-                   rope_base=1e4, eps=1e-5, store=store)
-        return time.perf_counter() - t0
-
-    t_dense = t_layer(rows_all)
-    t_sparse = t_layer(rows_all[:k_sparse])
-    del lw
+    t_dense, t_sparse = [], []
+    for layer in range(n_layers):
+        lw = {k: v.detach().to("cpu", torch.float64).numpy() for k, v in model_w_gpu["layers"][layer].items()}
+        for rows, acc in ((rows_all, t_dense), (rows_all[:k_sparse], t_sparse)):
+            t0 = time.perf_counter()
+            layer_rows(lw, x[rows], rows % S, rows // S, kc, vc, n_heads=dims.n_heads, n_kv_heads=dims.n_kv_heads,
+                       rope_base=1e4, eps=1e-5, store=store)
+            acc.append(time.perf_counter() - t0)
+        del lw
+    t0 = time.perf_counter()
+    for b in range(B):
+        sc = importance_score(x[b * S:(b + 1) * S], xp[b * S:(b + 1) * S], conf[b * S:(b + 1) * S], None,
+                              alpha=0.5, var=VAR_L1N, conf_inverted=False)
+        select_topk(sc, np.zeros(S, dtype=np.uint8), k_sparse)
+    t_score = time.perf_counter() - t0
     head = model_w_gpu["lm_head"].detach().to("cpu", torch.float64).numpy()
     g = model_w_gpu["final_norm"].detach().to("cpu", torch.float64).numpy()
-    t0 = time.perf_counter()
-    lm_logits(x[:k_sparse], g, head, 1e-5, store)
-    t_head_sparse = time.perf_counter() - t0
-    t_head_dense = t_head_sparse * (B * S) / k_sparse
+    t_head = []
+    for rows in (rows_all, rows_all[:k_sparse]):
+        t0 = time.perf_counter()
+        conf_kl(lm_logits(x[rows], g, head, 1e-5, store), None, dims.mask_id)
+        t_head.append(time.perf_counter() - t0)
+    del head
     L = dims.n_layers
-    t_gen = (L * t_dense + t_head_dense) + (steps - 1) * (boundary * t_dense + (L - boundary) * t_sparse + t_head_sparse)
+    td, ts = sum(t_dense) / len(t_dense), sum(t_sparse) / len(t_sparse)
+    t_sample = sum(t_dense) + sum(t_sparse) + t_score + sum(t_head)
+    t_gen = (L * td + t_head[0]) + (steps - 1) * (boundary * td + (L - boundary) * ts + t_score + t_head[1])
     n_threads = max((p.get("num_threads", 1) for p in threadpool_info() if p.get("user_api") == "blas"), default=1)
     gen_tokens = B * (S - dims.prompt)
     return {
@@ -141,11 +160,37 @@ def cpu_baseline(model_w_gpu, dims, k_sparse, boundary, steps):
         "unit": "tokens/s",
         "cores": int(n_threads),
         "kind": "oracle",
-        "sample": (f"oracle (float64 NumPy, bf16 storage) timed on one dense layer ({B * S} rows, {t_dense:.2f} s), "
-                   f"one sparse layer ({k_sparse} rows, {t_sparse:.2f} s) and the LM head on {k_sparse} rows "
-                   f"({t_head_sparse:.2f} s); extrapolated to one {steps}-iteration generation "
-                   f"({t_gen:.1f} s); host os.cpu_count()={os.cpu_count()}"),
+        "sample": (f"oracle (float64 NumPy, bf16 storage rounding) timed for {t_sample:.1f} s: layers 0-{n_layers - 1} "
+                   f"each over all {B * S} rows ({td:.2f} s/layer) and over {k_sparse} active rows ({ts:.2f} s/layer), "
+                   f"importance score + top-{k_sparse} ({t_score:.2f} s), LM head + confidence over {B * S} rows "
+                   f"({t_head[0]:.2f} s) and {k_sparse} rows ({t_head[1]:.2f} s); extrapolated to one "
+                   f"{steps}-iteration generation ({t_gen:.0f} s); {n_threads} BLAS threads, "
+                   f"os.cpu_count()={os.cpu_count()}"),
     }
+
+
+DOMINANT_KERNEL = "dllm::k_gemm_lds<128, 128, 3, 1, 1>"
+TRAFFIC_PROFILE = os.path.join(ROOT, "profiles", "gemm_swiglu_llada_128rows_hbm_bytes.md")
+GEMM_SOURCE = os.path.join(ROOT, "token_skipping_denoise_amd", "csrc", "gemm.hip")
+
+
+def measured_traffic():
+    """HBM bytes per launch of the dominant kernel from its committed counter summary, or None when the
+    summary is missing or was taken from a different kernel source."""
+    import hashlib
+    import re
+
+    try:
+        text = open(TRAFFIC_PROFILE).read()
+    except OSError:
+        return None
+    m = re.search(r"traffic_bytes_per_launch:\s*(\d+)\s+gemm_source_sha256:\s*([0-9a-f]{64})", text)
+    if not m:
+        return None
+    with open(GEMM_SOURCE, "rb") as f:
+        if hashlib.sha256(f.read()).hexdigest() != m.group(2):
+            return None
+    return int(m.group(1))
 
 
 def main():
@@ -246,8 +291,8 @@ def main():
         bytes_per = ffn_up_bytes(dims, k_sparse * dims.B)
         achieved = bytes_per / (avg_ms * 1e-3) / 1e9
         roofline = {"bound": "hbm", "achieved": round(achieved, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
-                    "frac": round(achieved / HBM_PEAK_GBS, 4), "traffic": None,
-                    "kernel": "k_gemm_bf16<64,128,1> (gate/up + SwiGLU, 128 active rows)",
+                    "frac": round(achieved / HBM_PEAK_GBS, 4), "traffic": measured_traffic(),
+                    "kernel": DOMINANT_KERNEL + " (gate/up + SwiGLU of a skipped-regime layer, 128 active rows)",
                     "launches": timing.count, "avg_us": round(avg_ms * 1e3, 2),
                     "timed_in": ("eager generation right after the timed graph replays" if graph is not None
                                  else "timed region"),
