@@ -7,13 +7,22 @@
 // O(M_t * N * d) for M_t active rows (SureLock 2.1 item 4).
 //
 // bf16 kernel (gfx950 MFMA, flash style): a workgroup owns 128 queries of one
-// (sequence, KV head) -- the rows x the GQA heads that share that KV head --
-// and streams 64-key tiles of K and V through double-buffered LDS (K as
-// [key][d], V transposed to [d][key]).  Scores are formed transposed,
-// S^T = K Q^T, so each lane holds one query and its online-softmax state;
-// the exponentiated scores then serve directly as the B operand of
-// O^T += V^T P^T, with the key order inside a fragment chosen to match the
-// accumulator layout (any consistent k order gives the same contraction).
+// (sequence, KV head) -- the rows x the GQA heads that share that KV head.  Its
+// eight wavefronts form two groups of four; the groups take alternate 64-key
+// tiles and merge their softmax states through LDS at the end.  K and V tiles
+// stream from memory straight into LDS (buffer loads with an LDS destination,
+// range-checked so keys past S read as zero), two stages per group, in their
+// natural [key][d] layout with 16-byte chunks XOR-swizzled per row.  Scores are
+// formed transposed, S^T = K Q^T, so each lane holds one query and its online-
+// softmax state; the exponentiated scores then serve directly as the B operand
+// of O^T += V^T P^T.  The V^T operand is read with the gfx950 transposing LDS
+// read (ds_read_b64_tr_b16): in each 16-lane group, lane i receives column
+// n0 + i of four consecutive rows when lane j addresses row K0 + j/4 at column
+// n0 + 4 (j % 4).  The key order inside a fragment matches the accumulator
+// layout of the scores (any consistent k order gives the same contraction).
+// Only when few workgroups would cover a long key range is that range also
+// split across workgroups (split-KV), whose partial results a second kernel
+// merges.
 //
 // fp32 kernel (small fp32 models): one wavefront per (row, head), keys one at
 // a time with an online softmax.
@@ -25,6 +34,8 @@
 namespace dllm {
 
 typedef __bf16 bf16x8_t __attribute__((ext_vector_type(8)));
+typedef __bf16 bf16x2_t __attribute__((ext_vector_type(2)));
+typedef float f32x2_t __attribute__((ext_vector_type(2)));
 typedef float f32x16_t __attribute__((ext_vector_type(16)));
 
 // ---------------- fp32 ----------------
@@ -57,159 +68,226 @@ __global__ __launch_bounds__(256) void k_attn_f32(const float* __restrict__ q, c
 }
 
 // ---------------- bf16 MFMA ----------------
-constexpr int kKT = 64;           // keys per tile
-constexpr int kHD = 128;          // head dim
-constexpr int kLDK = kHD + 8;     // K tile row stride (elements)
-constexpr int kLDV = kKT + 4;     // V^T tile row stride (elements)
+constexpr int kKT = 64;                       // keys per tile
+constexpr int kHD = 128;                      // head dim
+constexpr int kRowBytes = kHD * 2;            // one key row of K or V
+constexpr int kTileBytes = kKT * kRowBytes;   // 16 KB per tensor
+constexpr int kStageBytes = 2 * kTileBytes;   // K tile, then V tile
+constexpr int kStages = 2;                    // per group
+// Fourth word of a raw buffer resource (CDNA): 32-bit data format, no swizzle; out-of-range
+// offsets read as zero.
+constexpr int kBufWord3 = 0x00020000;
+typedef __attribute__((address_space(3))) void lds_void;
+typedef short short4_t __attribute__((ext_vector_type(4)));
+typedef short short8_t __attribute__((ext_vector_type(8)));
+
+// 16-byte chunk c of tile row r sits in slot c ^ swz(r): the MFMA K reads (16 rows at one
+// chunk) and the transposing V reads (8 rows x 4 chunks) both touch every bank once per pass.
+__device__ __forceinline__ int swz(int r) { return ((r & 3) << 2) | ((r >> 2) & 3); }
+
+template <int N>
+__device__ __forceinline__ void wait_vm_attn() {
+  static_assert(N >= 0 && N < 64, "vmcnt is a 6-bit field");
+  __builtin_amdgcn_s_waitcnt((N & 15) | ((N >> 4) << 14) | (7 << 4) | (15 << 8));
+}
 
 // With nsplit > 1 the key tiles are divided among nsplit workgroups (split-KV): each writes
 // its unnormalised output and softmax statistics (max, sum, in the exp2 domain) to `part`,
 // and k_attn_merge combines them.
-__global__ __launch_bounds__(256, 2) void k_attn_bf16(const uint16_t* __restrict__ q, const uint16_t* __restrict__ kc,
+__global__ __launch_bounds__(512, 1) void k_attn_bf16(const uint16_t* __restrict__ q, const uint16_t* __restrict__ kc,
                                                       const uint16_t* __restrict__ vc, uint16_t* __restrict__ o,
                                                       const int32_t* __restrict__ n_active, int S, int k_max, int Hq,
                                                       int Hkv, float scale_log2e, int nsplit, float* __restrict__ part) {
-  __shared__ __attribute__((aligned(16))) uint16_t Ks[2][kKT * kLDK];
-  __shared__ __attribute__((aligned(16))) uint16_t Vt[2][kHD * kLDV];
+  __shared__ __attribute__((aligned(1024))) uint8_t smem[2 * kStages * kStageBytes];  // 128 KB
   const int b = blockIdx.z / nsplit, split = blockIdx.z - b * nsplit, hk = blockIdx.y;
   const int g = Hq / Hkv;
-  const int nq = n_active[b] * g;
   const int qb0 = blockIdx.x * 128;
-  if (qb0 >= nq) return;
-  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int grp = wave >> 2, gw = wave & 3;
   const int l32 = lane & 31, hi = lane >> 5;
+  uint8_t* gsm = smem + grp * kStages * kStageBytes;
 
-  // this lane's query
-  const int qi = qb0 + wave * 32 + l32;
-  const bool qvalid = qi < nq;
-  const int jrow = qvalid ? qi / g : 0, hg = qvalid ? qi - jrow * g : 0;
+  // this workgroup's key tiles [t_begin, t_end); group grp takes t_begin + grp, + 2, + 4, ...
+  const int ntiles_all = (S + kKT - 1) / kKT;
+  const int t_begin = (int)((long)split * ntiles_all / nsplit), t_end = (int)((long)(split + 1) * ntiles_all / nsplit);
+  const int n_steps = (t_end - t_begin + 1) / 2;  // tile pairs (the last may hold one tile)
+  const int n_my = (t_end - t_begin - grp + 1) / 2;
+
+  // K/V tile loads: 16 load instructions of 4 rows (1 KB) per tensor, 4 per wave.  Lane L of
+  // instruction qi fills row 4 qi + L / 16, slot L % 16, so it fetches chunk slot ^ swz(row).
+  const long head0 = ((long)b * S * Hkv + hk) * kHD;
+  const int nbytes = S * Hkv * kRowBytes;
+  const __amdgpu_buffer_rsrc_t rsk = __builtin_amdgcn_make_buffer_rsrc((void*)(kc + head0), (short)0, nbytes, kBufWord3);
+  const __amdgpu_buffer_rsrc_t rsv = __builtin_amdgcn_make_buffer_rsrc((void*)(vc + head0), (short)0, nbytes, kBufWord3);
+  int voff[4];
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    const int row = 4 * (gw * 4 + i) + (lane >> 4);
+    voff[i] = row * Hkv * kRowBytes + (((lane & 15) ^ swz(row)) << 4);
+  }
+  const int tile_bytes = kKT * Hkv * kRowBytes;
+  auto issue = [&](int t, int stage) {
+    uint8_t* st = gsm + stage * kStageBytes;
+    const int so = t * tile_bytes;  // in the per-lane offset, which the range check covers
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      const int qi = gw * 4 + i;
+      __builtin_amdgcn_raw_ptr_buffer_load_lds(rsk, (lds_void*)(st + qi * 1024), 16, voff[i] + so, 0, 0, 0);
+      __builtin_amdgcn_raw_ptr_buffer_load_lds(rsv, (lds_void*)(st + kTileBytes + qi * 1024), 16, voff[i] + so, 0, 0, 0);
+    }
+  };
+  // The first tile and the queries are requested before the active-row count is known (all
+  // addresses are valid either way): the three memory round trips overlap.
+  if (n_my > 0) issue(t_begin + grp, 0);
+  const int qi = qb0 + gw * 32 + l32;
+  const int qi_c = qi < k_max * g ? qi : k_max * g - 1;
+  const int jrow = qi_c / g, hg = qi_c - jrow * g;
   const long qrow = (long)b * k_max + jrow;
   const int h = hk * g + hg;
   bf16x8_t qf[kHD / 16];
   {
     const uint16_t* qp = q + (qrow * Hq + h) * kHD + 8 * hi;
 #pragma unroll
-    for (int t = 0; t < kHD / 16; ++t) {
-      uint4 v = qvalid ? *reinterpret_cast<const uint4*>(qp + 16 * t) : make_uint4(0, 0, 0, 0);
-      qf[t] = __builtin_bit_cast(bf16x8_t, v);
-    }
+    for (int t = 0; t < kHD / 16; ++t) qf[t] = __builtin_bit_cast(bf16x8_t, *reinterpret_cast<const uint4*>(qp + 16 * t));
   }
-
-  // tile loaders: 64 keys x 128 d = 1024 16-byte chunks per tensor, 4 per thread
-  uint4 rk[4], rv[4];
-  const long kv_row0 = (long)b * S;
-  auto load_global = [&](int key0) {
-#pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      const int c = tid + 256 * i, key = c >> 4, d0 = (c & 15) * 8;
-      const int gk = key0 + key;
-      if (gk < S) {
-        const long off = ((kv_row0 + gk) * Hkv + hk) * kHD + d0;
-        rk[i] = *reinterpret_cast<const uint4*>(kc + off);
-        rv[i] = *reinterpret_cast<const uint4*>(vc + off);
-      } else {
-        rk[i] = make_uint4(0, 0, 0, 0);
-        rv[i] = make_uint4(0, 0, 0, 0);
-      }
-    }
-  };
-  auto store_lds = [&](int buf) {
-#pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      const int c = tid + 256 * i, key = c >> 4, d0 = (c & 15) * 8;
-      *reinterpret_cast<uint4*>(&Ks[buf][key * kLDK + d0]) = rk[i];
-      const uint32_t w[4] = {rv[i].x, rv[i].y, rv[i].z, rv[i].w};
-#pragma unroll
-      for (int e = 0; e < 4; ++e) {
-        Vt[buf][(d0 + 2 * e) * kLDV + key] = (uint16_t)(w[e] & 0xffffu);
-        Vt[buf][(d0 + 2 * e + 1) * kLDV + key] = (uint16_t)(w[e] >> 16);
-      }
-    }
-  };
+  const int nq = n_active[b] * g;
+  if (qb0 >= nq) {
+    wait_vm_attn<0>();  // no load may still be writing this workgroup's LDS when it ends
+    return;
+  }
+  // a query slot past the live rows computes on whatever its row holds; its lanes never mix
+  // with other queries' lanes and are not written back
+  const bool qvalid = qi < nq;
 
   f32x16_t oacc[kHD / 32];
 #pragma unroll
   for (int db = 0; db < kHD / 32; ++db)
 #pragma unroll
     for (int e = 0; e < 16; ++e) oacc[db][e] = 0.f;
+  // running max of the raw scores q.k, and the softmax sum of 2^((s - m) * scale_log2e)
   float m_run = -INFINITY, l_run = 0.f;
 
-  const int ntiles_all = (S + kKT - 1) / kKT;
-  const int t_begin = (int)((long)split * ntiles_all / nsplit), t_end = (int)((long)(split + 1) * ntiles_all / nsplit);
-  load_global(t_begin * kKT);
-  store_lds(0);
-  __syncthreads();
-  for (int t = t_begin; t < t_end; ++t) {
-    const int buf = (t - t_begin) & 1;
-    const bool more = t + 1 < t_end;
-    if (more) load_global((t + 1) * kKT);
+  // per-lane parts of the fragment addresses
+  const int v_row = 4 * hi + ((lane & 15) >> 2);               // + kb2 * 32 + 16 hf (+ 8)
+  const int v_col = 16 * ((lane >> 4) & 1) + 4 * (lane & 3);  // + 32 db
+  for (int i = 0; i < n_steps; ++i) {
+    wait_vm_attn<0>();             // this wave's loads of tile i (and the query) have landed
+    __builtin_amdgcn_s_barrier();  // ... and every other wave's; stage (i + 1) % 2 is free
+    if (i + 1 < n_my) issue(t_begin + grp + 2 * (i + 1), (i + 1) & 1);
+    if (i < n_my) {
+      const int t = t_begin + grp + 2 * i;
+      const uint8_t* kst = gsm + (i & 1) * kStageBytes;
+      const uint8_t* vst = kst + kTileBytes;
+      // S^T for two 32-key blocks
+      f32x16_t sacc[2];
+#pragma unroll
+      for (int kb2 = 0; kb2 < 2; ++kb2) {
+        const int row = kb2 * 32 + l32;
+        const uint8_t* rp = kst + row * kRowBytes;
+        const int sw = swz(row);
+#pragma unroll
+        for (int e = 0; e < 16; ++e) sacc[kb2][e] = 0.f;
+#pragma unroll
+        for (int ts = 0; ts < kHD / 16; ++ts) {
+          const bf16x8_t a = *reinterpret_cast<const bf16x8_t*>(rp + (((2 * ts + hi) ^ sw) << 4));
+          sacc[kb2] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, qf[ts], sacc[kb2], 0, 0, 0);
+        }
+      }
+      // the last tile may be partial: keys past S score -inf
+      const int key0 = t * kKT;
+      if (key0 + kKT > S) {
+#pragma unroll
+        for (int kb2 = 0; kb2 < 2; ++kb2)
+#pragma unroll
+          for (int e = 0; e < 16; ++e)
+            if (key0 + kb2 * 32 + 8 * (e >> 2) + 4 * hi + (e & 3) >= S) sacc[kb2][e] = -INFINITY;
+      }
+      // online softmax (each query lives in lanes l and l^32)
+      float mt = -INFINITY;
+#pragma unroll
+      for (int kb2 = 0; kb2 < 2; ++kb2)
+#pragma unroll
+        for (int e = 0; e < 16; ++e) mt = fmaxf(mt, sacc[kb2][e]);
+      mt = fmaxf(mt, __shfl_xor(mt, 32, kWave));
+      const float m_new = fmaxf(m_run, mt);
+      const float corr = __builtin_amdgcn_exp2f((m_run - m_new) * scale_log2e);
+      const float mc = m_new * scale_log2e;
+      float rs = 0.f;
+#pragma unroll
+      for (int kb2 = 0; kb2 < 2; ++kb2)
+#pragma unroll
+        for (int e = 0; e < 16; ++e) {
+          const float p = __builtin_amdgcn_exp2f(fmaf(sacc[kb2][e], scale_log2e, -mc));
+          sacc[kb2][e] = p;
+          rs += p;
+        }
+      rs += __shfl_xor(rs, 32, kWave);
+      l_run = l_run * corr + rs;
+      m_run = m_new;
+#pragma unroll
+      for (int db = 0; db < kHD / 32; ++db)
+#pragma unroll
+        for (int e = 0; e < 16; ++e) oacc[db][e] *= corr;
 
-    // S^T for two 32-key blocks
-    f32x16_t sacc[2];
+      // O^T += V^T P^T over four 16-key steps; the V^T fragment (keys r0..r0+3, r0+8..r0+11 of
+      // column 32 db + l32) comes from two transposing reads of the [key][d] tile
 #pragma unroll
-    for (int kb = 0; kb < 2; ++kb) {
+      for (int s2 = 0; s2 < 4; ++s2) {
+        const int kb2 = s2 >> 1, hf = s2 & 1;
+        uint32_t pw[4];
 #pragma unroll
-      for (int e = 0; e < 16; ++e) sacc[kb][e] = 0.f;
+        for (int e = 0; e < 4; ++e) {
+          const f32x2_t pr = {sacc[kb2][8 * hf + 2 * e], sacc[kb2][8 * hf + 2 * e + 1]};
+          pw[e] = __builtin_bit_cast(uint32_t, __builtin_convertvector(pr, bf16x2_t));
+        }
+        const bf16x8_t pfrag = __builtin_bit_cast(bf16x8_t, make_uint4(pw[0], pw[1], pw[2], pw[3]));
+        const int r0 = kb2 * 32 + 16 * hf + v_row, r1 = r0 + 8;
+        const uint8_t* vp0 = vst + r0 * kRowBytes;
+        const uint8_t* vp1 = vst + r1 * kRowBytes;
+        const int sw0 = swz(r0), sw1 = swz(r1);
 #pragma unroll
-      for (int ts = 0; ts < kHD / 16; ++ts) {
-        const bf16x8_t a = *reinterpret_cast<const bf16x8_t*>(&Ks[buf][(kb * 32 + l32) * kLDK + ts * 16 + 8 * hi]);
-        sacc[kb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, qf[ts], sacc[kb], 0, 0, 0);
+        for (int db = 0; db < kHD / 32; ++db) {
+          const int col = 32 * db + v_col;       // element column of this lane's 8-byte read
+          const int inb = (col & 7) << 1;        // byte within the 16-byte chunk
+          const short4_t lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+              (__attribute__((address_space(3))) short4_t*)(vp0 + ((((col >> 3) ^ sw0) << 4) | inb)));
+          const short4_t hv = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+              (__attribute__((address_space(3))) short4_t*)(vp1 + ((((col >> 3) ^ sw1) << 4) | inb)));
+          const short8_t a8 = {lo[0], lo[1], lo[2], lo[3], hv[0], hv[1], hv[2], hv[3]};
+          oacc[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8_t, a8), pfrag, oacc[db], 0, 0, 0);
+        }
       }
     }
-    // scale, mask the tail, online softmax (each query lives in lanes l and l^32)
-    const int key0 = t * kKT;
-    float mt = -INFINITY;
-#pragma unroll
-    for (int kb = 0; kb < 2; ++kb)
-#pragma unroll
-      for (int e = 0; e < 16; ++e) {
-        const int key = key0 + kb * 32 + 8 * (e >> 2) + 4 * hi + (e & 3);
-        float sv = sacc[kb][e] * scale_log2e;
-        if (key >= S) sv = -INFINITY;
-        sacc[kb][e] = sv;
-        mt = fmaxf(mt, sv);
-      }
-    mt = fmaxf(mt, __shfl_xor(mt, 32, kWave));
-    const float m_new = fmaxf(m_run, mt);
-    const float corr = exp2f(m_run - m_new);
-    float rs = 0.f;
-#pragma unroll
-    for (int kb = 0; kb < 2; ++kb)
-#pragma unroll
-      for (int e = 0; e < 16; ++e) {
-        const float p = exp2f(sacc[kb][e] - m_new);
-        sacc[kb][e] = p;
-        rs += p;
-      }
-    rs += __shfl_xor(rs, 32, kWave);
-    l_run = l_run * corr + rs;
-    m_run = m_new;
+  }
+  __syncthreads();  // every wave is done with its tiles before the stages are reused below
+
+  // merge group 1 into group 0 through LDS: [wave][db][e][lane] floats, then (m, l) per wave lane
+  float* xs = reinterpret_cast<float*>(smem);
+  float* ml = xs + 4 * (kHD / 32) * 16 * 64;
+  if (grp == 1) {
 #pragma unroll
     for (int db = 0; db < kHD / 32; ++db)
 #pragma unroll
-      for (int e = 0; e < 16; ++e) oacc[db][e] *= corr;
-
-    // O^T += V^T P^T over four 16-key steps
+      for (int e = 0; e < 16; ++e) xs[((gw * (kHD / 32) + db) * 16 + e) * 64 + lane] = oacc[db][e];
+    ml[(gw * 2) * 64 + lane] = m_run;
+    ml[(gw * 2 + 1) * 64 + lane] = l_run;
+  }
+  __syncthreads();
+  if (grp == 1) return;
+  {
+    const float m1 = ml[(gw * 2) * 64 + lane], l1 = ml[(gw * 2 + 1) * 64 + lane];
+    const float M = fmaxf(m_run, m1);
+    // both -inf only for a group without keys; keep the merged state finite then
+    const float c0 = (m_run == -INFINITY) ? 0.f : exp2f((m_run - M) * scale_log2e);
+    const float c1 = (m1 == -INFINITY) ? 0.f : exp2f((m1 - M) * scale_log2e);
+    l_run = l_run * c0 + l1 * c1;
+    m_run = M;
 #pragma unroll
-    for (int s2 = 0; s2 < 4; ++s2) {
-      const int kb = s2 >> 1, hf = s2 & 1;
-      uint32_t pw[4];
+    for (int db = 0; db < kHD / 32; ++db)
 #pragma unroll
-      for (int e = 0; e < 4; ++e)
-        pw[e] = (uint32_t)f2bf(sacc[kb][8 * hf + 2 * e]) | ((uint32_t)f2bf(sacc[kb][8 * hf + 2 * e + 1]) << 16);
-      const bf16x8_t pfrag = __builtin_bit_cast(bf16x8_t, make_uint4(pw[0], pw[1], pw[2], pw[3]));
-      const int kofs = kb * 32 + 16 * hf + 4 * hi;
-#pragma unroll
-      for (int db = 0; db < kHD / 32; ++db) {
-        const uint16_t* vp = &Vt[buf][(db * 32 + l32) * kLDV + kofs];
-        const uint2 lo = *reinterpret_cast<const uint2*>(vp);
-        const uint2 hv = *reinterpret_cast<const uint2*>(vp + 8);
-        const bf16x8_t afrag = __builtin_bit_cast(bf16x8_t, make_uint4(lo.x, lo.y, hv.x, hv.y));
-        oacc[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(afrag, pfrag, oacc[db], 0, 0, 0);
-      }
-    }
-    if (more) store_lds(buf ^ 1);
-    __syncthreads();
+      for (int e = 0; e < 16; ++e)
+        oacc[db][e] = oacc[db][e] * c0 + xs[((gw * (kHD / 32) + db) * 16 + e) * 64 + lane] * c1;
   }
 
   if (!qvalid) return;
@@ -226,7 +304,7 @@ __global__ __launch_bounds__(256, 2) void k_attn_bf16(const uint16_t* __restrict
         *reinterpret_cast<float2*>(pp + d + 2) = make_float2(oacc[db][4 * e4 + 2], oacc[db][4 * e4 + 3]);
       }
     if (hi == 0) {
-      pp[kHD] = m_run;
+      pp[kHD] = m_run * scale_log2e;  // the merge works in the exp2 domain
       pp[kHD + 1] = l_run;
     }
     return;
@@ -264,13 +342,14 @@ __global__ __launch_bounds__(128) void k_attn_merge(const float* __restrict__ pa
   o[((long)r * Hq + h) * kHD + d] = f2bf(acc / L);
 }
 
+// Split-KV only pays when few workgroups would each stream a long key range: a split's
+// partial (128 queries x (D + 2) fp32) must stay small beside the K/V it summarises.
 int attention_splits(int dtype, int B, int S, int k_max, int Hq, int Hkv) {
   if (dtype == 0) return 1;
   const int g = Hq / Hkv;
   const long wgs = (long)((k_max * g + 127) / 128) * Hkv * B;
-  const int ntiles = (S + kKT - 1) / kKT;
   int ns = 1;
-  while (ns < 4 && wgs * ns < 256 && ntiles / (ns * 2) >= 2) ns *= 2;
+  while (ns < 8 && wgs * ns < 128 && S / (ns * 2) >= 512) ns *= 2;
   return ns;
 }
 
@@ -290,12 +369,13 @@ hipError_t launch_attention(int dtype, const void* q, const void* kc, const void
     return hipGetLastError();
   }
   if (D != kHD) return hipErrorInvalidValue;
+  if ((long)S * Hkv * kHD * 2 >= (1L << 31)) return hipErrorInvalidValue;  // 32-bit buffer offsets
   const int g = Hq / Hkv;
   const int qblocks = (k_max * g + 127) / 128;
   const float scale_log2e = (float)(1.0 / sqrt((double)D) * 1.4426950408889634);
   const int ns = attention_splits(dtype, B, S, k_max, Hq, Hkv);
   if (ns > 1 && !part) return hipErrorInvalidValue;
-  hipLaunchKernelGGL(k_attn_bf16, dim3(qblocks, Hkv, B * ns), dim3(256), 0, s, (const uint16_t*)q, (const uint16_t*)kc,
+  hipLaunchKernelGGL(k_attn_bf16, dim3(qblocks, Hkv, B * ns), dim3(512), 0, s, (const uint16_t*)q, (const uint16_t*)kc,
                      (const uint16_t*)vc, (uint16_t*)o, n_active, S, k_max, Hq, Hkv, scale_log2e, ns, part);
   if (ns > 1)
     hipLaunchKernelGGL(k_attn_merge, dim3(B * k_max, Hq), dim3(kHD), 0, s, part, ns, (long)B * k_max * Hq * (kHD + 2),

@@ -286,7 +286,7 @@ GemmPlan gemm_plan(int dtype, int M, int N, int K, bool swiglu) {
   GemmPlan p{64, 64, 1, 64, 2};
   if (dtype == 0) {
     const int tiles = ((M + 63) / 64) * ((N + 63) / 64);
-    while (!swiglu && tiles * p.splits < 256 && (K / 16) / (p.splits * 2) >= 8) p.splits *= 2;
+    while (!swiglu && tiles * p.splits < 256 && p.splits < 8 && (K / 16) / (p.splits * 2) >= 8) p.splits *= 2;
     return p;
   }
   // Direct-to-LDS kernel (pd = 10 + stages).  Rules from a tile sweep on the LLaDA-8B layer
@@ -302,6 +302,9 @@ GemmPlan gemm_plan(int dtype, int M, int N, int K, bool swiglu) {
   const long target = few ? 512 : 256;
   const int max_splits = 4;
   while (tiles * p.splits < target && p.splits < max_splits && K / (p.splits * 2) >= 1024) p.splits *= 2;
+  // 128x128 split-K grids of more than one workgroup per CU: two stages, so that two
+  // workgroups share each CU and the whole grid is resident at once
+  if (few && p.bn == 128 && p.splits > 1 && tiles * p.splits > 256 && tiles * p.splits <= 512) p.pd = 12;
   return p;
 }
 

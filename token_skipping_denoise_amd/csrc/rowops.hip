@@ -151,12 +151,14 @@ __device__ __forceinline__ float sum_splits(const float* __restrict__ p, int spl
   return v;
 }
 
-// One workgroup per row.  Columns of the QKV product: [Q: Hq*D | K: Hkv*D | V: Hkv*D].
-// Rotation angles i * theta_j, theta_j = base^(-2j/D), are formed in double and reduced
-// modulo 2 pi before the single-precision sine and cosine.  Each thread owns groups of four
-// rotation pairs (and four V columns); all of its 16-byte partial loads are issued before
-// any arithmetic, so a row costs about one memory round trip per split.
-constexpr int kQkvGroups = 8;  // 4-pair groups per thread: up to 8192 pairs per row
+// Columns of the QKV product: [Q: Hq*D | K: Hkv*D | V: Hkv*D].  A row's work is cut into
+// units of four rotation pairs of one Q or K head (columns j..j+3 and j+D/2..j+D/2+3) or four
+// V columns; a workgroup of 256 threads takes 256 consecutive units of one row, so a row
+// spreads over several workgroups.  Every 16-byte partial load of a thread (all SPLITS of
+// them) is issued before any arithmetic: a unit costs one memory round trip.  Rotation
+// angles i * theta_j, theta_j = base^(-2j/D), are formed in double and reduced modulo 2 pi
+// before the single-precision sine and cosine.
+constexpr int kQkvUnitsPerBlock = 256;
 
 template <typename T>
 __device__ __forceinline__ void store4(T* p, long off, const float* v) {
@@ -169,11 +171,12 @@ __device__ __forceinline__ void store4(T* p, long off, const float* v) {
   }
 }
 
-template <typename T>
-__global__ __launch_bounds__(256) void k_qkv_epilogue(const float* __restrict__ part, int splits, long sstride,
-                                                      const int32_t* __restrict__ row_pos, int S, int Hq, int Hkv,
-                                                      int D, double log2_base, T* __restrict__ q, T* __restrict__ kc,
-                                                      T* __restrict__ vc) {
+template <typename T, int SPLITS>
+__global__ __launch_bounds__(kQkvUnitsPerBlock) void k_qkv_epilogue(const float* __restrict__ part, long sstride,
+                                                                    const int32_t* __restrict__ row_pos, int S, int Hq,
+                                                                    int Hkv, int D, double log2_base,
+                                                                    T* __restrict__ q, T* __restrict__ kc,
+                                                                    T* __restrict__ vc) {
   __shared__ float cs[kMaxHalf], sn[kMaxHalf];
   const int r = blockIdx.x;
   const int pos = row_pos[r];
@@ -181,81 +184,94 @@ __global__ __launch_bounds__(256) void k_qkv_epilogue(const float* __restrict__ 
   const int i = pos % S;
   const int half = D / 2, g4 = half / 4;  // 4-pair groups per head
   const int NQ = Hq * D, NK = Hkv * D, N = NQ + 2 * NK;
-  for (int j = threadIdx.x; j < half; j += blockDim.x) {
-    const double a = (double)i * exp2(-2.0 * j / (double)D * log2_base);
-    const double red = a - 6.283185307179586 * rint(a * 0.15915494309189535);
-    float sv, cv;
-    sincosf((float)red, &sv, &cv);
-    cs[j] = cv;
-    sn[j] = sv;
+  const int ngroups = (Hq + Hkv) * g4;  // rotation units, then V units
+  const int u = blockIdx.y * kQkvUnitsPerBlock + threadIdx.x;
+  const bool rot = u < ngroups;
+  const bool val = !rot && u < ngroups + NK / 4;
+  const bool need_angles = blockIdx.y * kQkvUnitsPerBlock < ngroups;  // uniform per block
+  if (need_angles) {
+    for (int j = threadIdx.x; j < half; j += blockDim.x) {
+      const double a = (double)i * exp2(-2.0 * j / (double)D * log2_base);
+      const double red = a - 6.283185307179586 * rint(a * 0.15915494309189535);
+      float sv, cv;
+      sincosf((float)red, &sv, &cv);
+      cs[j] = cv;
+      sn[j] = sv;
+    }
   }
   const float* pr = part + (long)r * N;
-  const int ngroups = (Hq + Hkv) * g4;   // rotation groups
-  const int vgroups = NK / 4;            // V column groups
-  float x1[kQkvGroups][4], x2[kQkvGroups][4], xv[kQkvGroups][4];
-#pragma unroll
-  for (int k = 0; k < kQkvGroups; ++k)
-#pragma unroll
-    for (int e = 0; e < 4; ++e) x1[k][e] = x2[k][e] = xv[k][e] = 0.f;
-  for (int sp = 0; sp < splits; ++sp) {
-    const float* ps = pr + sp * sstride;
-#pragma unroll
-    for (int k = 0; k < kQkvGroups; ++k) {
-      const int gi = threadIdx.x + 256 * k;
-      if (gi < ngroups) {
-        const int hh = gi / g4, j0 = (gi - hh * g4) * 4;
-        const float4 a = *reinterpret_cast<const float4*>(ps + hh * D + j0);
-        const float4 b = *reinterpret_cast<const float4*>(ps + hh * D + j0 + half);
-        x1[k][0] += a.x; x1[k][1] += a.y; x1[k][2] += a.z; x1[k][3] += a.w;
-        x2[k][0] += b.x; x2[k][1] += b.y; x2[k][2] += b.z; x2[k][3] += b.w;
-      }
-      if (gi < vgroups) {
-        const float4 v = *reinterpret_cast<const float4*>(ps + NQ + NK + gi * 4);
-        xv[k][0] += v.x; xv[k][1] += v.y; xv[k][2] += v.z; xv[k][3] += v.w;
-      }
-    }
+  int hh = 0, j0 = 0;
+  long c1 = 0, c2 = 0;
+  if (rot) {
+    hh = u / g4;
+    j0 = (u - hh * g4) * 4;
+    c1 = hh * D + j0;
+    c2 = c1 + half;
+  } else if (val) {
+    c1 = NQ + NK + (long)(u - ngroups) * 4;
   }
-  __syncthreads();
+  float4 a[SPLITS], b[SPLITS];
 #pragma unroll
-  for (int k = 0; k < kQkvGroups; ++k) {
-    const int gi = threadIdx.x + 256 * k;
-    if (gi < ngroups) {
-      const int hh = gi / g4, j0 = (gi - hh * g4) * 4;
-      float y1[4], y2[4];
-#pragma unroll
-      for (int e = 0; e < 4; ++e) {
-        const float c = cs[j0 + e], sgn = sn[j0 + e];
-        y1[e] = x1[k][e] * c - x2[k][e] * sgn;
-        y2[e] = x2[k][e] * c + x1[k][e] * sgn;
-      }
-      if (hh < Hq) {
-        store4(q, (long)r * NQ + hh * D + j0, y1);
-        store4(q, (long)r * NQ + hh * D + j0 + half, y2);
-      } else {
-        const long o = ((long)pos * Hkv + (hh - Hq)) * D;
-        store4(kc, o + j0, y1);
-        store4(kc, o + j0 + half, y2);
-      }
-    }
-    if (gi < vgroups) store4(vc, (long)pos * NK + gi * 4, xv[k]);
+  for (int sp = 0; sp < SPLITS; ++sp) {
+    if (rot || val) a[sp] = *reinterpret_cast<const float4*>(pr + sp * sstride + c1);
+    if (rot) b[sp] = *reinterpret_cast<const float4*>(pr + sp * sstride + c2);
   }
+  if (need_angles) __syncthreads();
+  if (!rot && !val) return;
+  float x1[4] = {0.f, 0.f, 0.f, 0.f}, x2[4] = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+  for (int sp = 0; sp < SPLITS; ++sp) {
+    x1[0] += a[sp].x; x1[1] += a[sp].y; x1[2] += a[sp].z; x1[3] += a[sp].w;
+    if (rot) { x2[0] += b[sp].x; x2[1] += b[sp].y; x2[2] += b[sp].z; x2[3] += b[sp].w; }
+  }
+  if (val) {
+    store4(vc, (long)pos * NK + (u - ngroups) * 4, x1);
+    return;
+  }
+  float y1[4], y2[4];
+#pragma unroll
+  for (int e = 0; e < 4; ++e) {
+    const float c = cs[j0 + e], sg = sn[j0 + e];
+    y1[e] = x1[e] * c - x2[e] * sg;
+    y2[e] = x2[e] * c + x1[e] * sg;
+  }
+  if (hh < Hq) {
+    store4(q, (long)r * NQ + hh * D + j0, y1);
+    store4(q, (long)r * NQ + hh * D + j0 + half, y2);
+  } else {
+    const long o = ((long)pos * Hkv + (hh - Hq)) * D;
+    store4(kc, o + j0, y1);
+    store4(kc, o + j0 + half, y2);
+  }
+}
+
+template <typename T>
+static hipError_t qkv_epilogue_t(const float* part, int splits, long split_stride, const int32_t* row_pos, int R, int S,
+                                 int Hq, int Hkv, int D, double log2_base, void* q, void* kc, void* vc, hipStream_t s) {
+  const int units = (Hq + Hkv) * (D / 8) + Hkv * D / 4;
+  const dim3 grid(R, (units + kQkvUnitsPerBlock - 1) / kQkvUnitsPerBlock);
+  switch (splits) {
+#define DLLM_QKV_CASE(SP)                                                                                        \
+  case SP:                                                                                                       \
+    hipLaunchKernelGGL((k_qkv_epilogue<T, SP>), grid, dim3(kQkvUnitsPerBlock), 0, s, part, split_stride, row_pos, \
+                       S, Hq, Hkv, D, log2_base, (T*)q, (T*)kc, (T*)vc);                                         \
+    break;
+    DLLM_QKV_CASE(1) DLLM_QKV_CASE(2) DLLM_QKV_CASE(4) DLLM_QKV_CASE(8)
+#undef DLLM_QKV_CASE
+    default:
+      return hipErrorInvalidValue;
+  }
+  return hipGetLastError();
 }
 
 hipError_t launch_qkv_epilogue(int dtype, const float* part, int splits, long split_stride, const int32_t* row_pos,
                                int R, int S, int Hq, int Hkv, int D, float rope_base, void* q, void* kc, void* vc,
                                hipStream_t s) {
   if (R <= 0) return hipSuccess;
-  if (D / 2 > kMaxHalf || (D / 2) % 4 != 0 || (Hq + Hkv) * (D / 8) > 256 * kQkvGroups ||
-      Hkv * D / 4 > 256 * kQkvGroups)
-    return hipErrorInvalidValue;
+  if (D / 2 > kMaxHalf || (D / 2) % 4 != 0) return hipErrorInvalidValue;
   const double log2_base = log2((double)rope_base);
-  if (dtype == 0)
-    hipLaunchKernelGGL(k_qkv_epilogue<float>, dim3(R), dim3(256), 0, s, part, splits, split_stride, row_pos, S, Hq,
-                       Hkv, D, log2_base, (float*)q, (float*)kc, (float*)vc);
-  else
-    hipLaunchKernelGGL(k_qkv_epilogue<bf16>, dim3(R), dim3(256), 0, s, part, splits, split_stride, row_pos, S, Hq,
-                       Hkv, D, log2_base, (bf16*)q, (bf16*)kc, (bf16*)vc);
-  return hipGetLastError();
+  if (dtype == 0) return qkv_epilogue_t<float>(part, splits, split_stride, row_pos, R, S, Hq, Hkv, D, log2_base, q, kc, vc, s);
+  return qkv_epilogue_t<bf16>(part, splits, split_stride, row_pos, R, S, Hq, Hkv, D, log2_base, q, kc, vc, s);
 }
 
 // One workgroup per row: x += sum(partials) (rounded to storage), then xn = rmsnorm(x) * g.
