@@ -80,16 +80,21 @@ __device__ __forceinline__ void wait_stages(int ahead) {
 
 typedef __attribute__((address_space(3))) void lds_void;
 
-template <int BM, int BN, int NS, int EPI, int OCC>
-__global__ __launch_bounds__(256, OCC) void k_gemm_lds(const uint16_t* __restrict__ A, const uint16_t* __restrict__ W,
+template <int BM, int BN, int NS, int EPI, int OCC, int KG, int WM, int WN>
+__global__ __launch_bounds__(64 * WM * WN * KG, OCC) void k_gemm_lds(const uint16_t* __restrict__ A, const uint16_t* __restrict__ W,
                                                      float* __restrict__ C, uint16_t* __restrict__ H, int M, int N,
                                                      int K, int splits, int tiles_m, int tiles_n,
                                                      const int32_t* __restrict__ n_active, int k_max) {
   constexpr int BK = 64;
-  constexpr int TM = BM / 64, TN = BN / 64;
-  constexpr int LA = BM / 32, LB = BN / 32;  // load instructions per wave per stage (8 rows each)
+  constexpr int TM = BM / (32 * WM), TN = BN / (32 * WN);  // 32x32 blocks per wave
+  constexpr int NW = WM * WN * KG;           // wavefronts
+  constexpr int LA = BM / (8 * NW), LB = BN / (8 * NW);  // load instructions per wave per stage (8 rows each)
   constexpr int STAGE = (BM + BN) * BK;      // elements per stage
+  constexpr int KS = BK / 16 / KG;           // MFMA k-steps per stage for each k-group
+  static_assert(TM * 32 * WM == BM && TN * 32 * WN == BN, "wave tiles are whole 32x32 blocks");
   static_assert(EPI == 0 || TN % 2 == 0, "fused SwiGLU needs an even number of column blocks per wave");
+  static_assert(LA * 8 * NW == BM && LB * 8 * NW == BN, "every wave issues the same number of tile loads");
+  static_assert(KG == 1 || NS * STAGE * 2 >= BM * BN * 4, "the k-group reduction reuses the stage ring");
   __shared__ __attribute__((aligned(1024))) uint16_t smem[NS * STAGE];
 
   int tmi, tni, sp;
@@ -101,15 +106,21 @@ __global__ __launch_bounds__(256, OCC) void k_gemm_lds(const uint16_t* __restric
   const int nk = kb1 - kb0;
   const int tid = threadIdx.x, lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
-  const int wm = wave >> 1, wn = wave & 1;
+  // KG k-groups of WM x WN wavefronts over the tile: group kg multiplies k-steps
+  // [kg * KS, (kg + 1) * KS) of every stage; their sums meet in LDS at the end
+  const int kg = wave / (WM * WN), w4 = wave % (WM * WN);
+  const int wm = w4 / WN, wn = w4 % WN;
 
   const int F = N;
   const int h0 = tni * (BN / 2);
+  // SwiGLU: the tile's columns are WN wave slices of BN / WN; in each slice the first half
+  // holds gate rows and the second half the matching up rows
   auto w_row = [&](int c) -> int {
     if (EPI == 0) return tni * BN + c;
-    const int half = c / (BN / 2), lc = c % (BN / 2);
+    constexpr int SL = BN / WN;
+    const int sl = c / SL, lc = c % SL;
     const int jb = lc / 32, t = lc % 32;
-    return (jb < TN / 2) ? h0 + half * (BN / 4) + jb * 32 + t : F + h0 + half * (BN / 4) + (jb - TN / 2) * 32 + t;
+    return (jb < TN / 2) ? h0 + sl * (SL / 2) + jb * 32 + t : F + h0 + sl * (SL / 2) + (jb - TN / 2) * 32 + t;
   };
   const int w_rows = (EPI == 0) ? N : 2 * F;
   // A tile row is 128 bytes, half of the 64 banks: rows r and r+1 fall in opposite bank
@@ -120,13 +131,13 @@ __global__ __launch_bounds__(256, OCC) void k_gemm_lds(const uint16_t* __restric
   const uint16_t* gb[LB];
 #pragma unroll
   for (int i = 0; i < LA; ++i) {
-    const int row = (wave + 4 * i) * 8 + lrow;
+    const int row = (wave + NW * i) * 8 + lrow;
     const int chunk = (lane & 7) ^ ((row >> 1) & 7);
     ga[i] = A + (long)min(m0 + row, M - 1) * K + chunk * 8;
   }
 #pragma unroll
   for (int i = 0; i < LB; ++i) {
-    const int row = (wave + 4 * i) * 8 + lrow;
+    const int row = (wave + NW * i) * 8 + lrow;
     const int chunk = (lane & 7) ^ ((row >> 1) & 7);
     gb[i] = W + (long)min(w_row(row), w_rows - 1) * K + chunk * 8;
   }
@@ -135,10 +146,10 @@ __global__ __launch_bounds__(256, OCC) void k_gemm_lds(const uint16_t* __restric
     uint16_t* base = smem + stage * STAGE;
 #pragma unroll
     for (int i = 0; i < LA; ++i)
-      __builtin_amdgcn_global_load_lds((const void*)(ga[i] + k0), (lds_void*)(base + (wave + 4 * i) * 8 * BK), 16, 0, 0);
+      __builtin_amdgcn_global_load_lds((const void*)(ga[i] + k0), (lds_void*)(base + (wave + NW * i) * 8 * BK), 16, 0, 0);
 #pragma unroll
     for (int i = 0; i < LB; ++i)
-      __builtin_amdgcn_global_load_lds((const void*)(gb[i] + k0), (lds_void*)(base + BM * BK + (wave + 4 * i) * 8 * BK),
+      __builtin_amdgcn_global_load_lds((const void*)(gb[i] + k0), (lds_void*)(base + BM * BK + (wave + NW * i) * 8 * BK),
                                        16, 0, 0);
   };
 
@@ -156,18 +167,19 @@ __global__ __launch_bounds__(256, OCC) void k_gemm_lds(const uint16_t* __restric
     const int slot = ((ks * 2 + hi) ^ swz) * 8;
 #pragma unroll
     for (int i = 0; i < TM; ++i)
-      af[i] = *reinterpret_cast<const bf16x8_t*>(base + (wm * (BM / 2) + i * 32 + r32) * BK + slot);
+      af[i] = *reinterpret_cast<const bf16x8_t*>(base + (wm * (BM / WM) + i * 32 + r32) * BK + slot);
 #pragma unroll
     for (int j = 0; j < TN; ++j)
-      bfr[j] = *reinterpret_cast<const bf16x8_t*>(base + BM * BK + (wn * (BN / 2) + j * 32 + r32) * BK + slot);
+      bfr[j] = *reinterpret_cast<const bf16x8_t*>(base + BM * BK + (wn * (BN / WN) + j * 32 + r32) * BK + slot);
   };
   auto compute = [&](int stage) {
     const uint16_t* base = smem + stage * STAGE;
     bf16x8_t af[2][TM], bfr[2][TN];
-    load_frags(base, 0, af[0], bfr[0]);
+    load_frags(base, kg * KS, af[0], bfr[0]);
 #pragma unroll
-    for (int ks = 0; ks < BK / 16; ++ks) {
-      if (ks + 1 < BK / 16) load_frags(base, ks + 1, af[(ks + 1) & 1], bfr[(ks + 1) & 1]);
+    for (int kk = 0; kk < KS; ++kk) {
+      const int ks = kk;  // buffer parity; the LDS k-step is kg * KS + kk
+      if (kk + 1 < KS) load_frags(base, kg * KS + kk + 1, af[(ks + 1) & 1], bfr[(ks + 1) & 1]);
       // scheduling fence: the next step's LDS reads stay ahead of this step's MFMAs (the
       // scheduler would otherwise sink them behind the MFMAs and stall on their latency)
       __builtin_amdgcn_sched_barrier(0);
@@ -190,6 +202,27 @@ __global__ __launch_bounds__(256, OCC) void k_gemm_lds(const uint16_t* __restric
     if (t + NS - 1 < nk) issue((t + NS - 1) % NS, kb0 + t + NS - 1);
     compute(t % NS);
   }
+  if constexpr (KG == 2) {
+    // k-group 1 hands its sums to k-group 0 through the (now idle) stage ring
+    float* red = reinterpret_cast<float*>(smem);
+    __syncthreads();
+    if (kg == 1) {
+#pragma unroll
+      for (int i = 0; i < TM; ++i)
+#pragma unroll
+        for (int j = 0; j < TN; ++j)
+#pragma unroll
+          for (int e = 0; e < 16; ++e) red[(((w4 * TM + i) * TN + j) * 16 + e) * 64 + lane] = acc[i][j][e];
+    }
+    __syncthreads();
+    if (kg == 1) return;
+#pragma unroll
+    for (int i = 0; i < TM; ++i)
+#pragma unroll
+      for (int j = 0; j < TN; ++j)
+#pragma unroll
+        for (int e = 0; e < 16; ++e) acc[i][j][e] += red[(((w4 * TM + i) * TN + j) * 16 + e) * 64 + lane];
+  }
 
   if (EPI == 0) {
     float* Cs = C + (long)sp * M * N;
@@ -198,11 +231,11 @@ __global__ __launch_bounds__(256, OCC) void k_gemm_lds(const uint16_t* __restric
     for (int i = 0; i < TM; ++i)
 #pragma unroll
       for (int j = 0; j < TN; ++j) {
-        const int col = n0 + wn * (BN / 2) + j * 32 + (lane & 31);
+        const int col = n0 + wn * (BN / WN) + j * 32 + (lane & 31);
         if (col >= N) continue;
 #pragma unroll
         for (int e = 0; e < 16; ++e) {
-          const int row = m0 + wm * (BM / 2) + i * 32 + 8 * (e >> 2) + 4 * (lane >> 5) + (e & 3);
+          const int row = m0 + wm * (BM / WM) + i * 32 + 8 * (e >> 2) + 4 * (lane >> 5) + (e & 3);
           if (row < M) Cs[(long)row * N + col] = acc[i][j][e];
         }
       }
@@ -211,11 +244,11 @@ __global__ __launch_bounds__(256, OCC) void k_gemm_lds(const uint16_t* __restric
     for (int i = 0; i < TM; ++i)
 #pragma unroll
       for (int j = 0; j < TN / 2; ++j) {
-        const int col = h0 + wn * (BN / 4) + j * 32 + (lane & 31);
+        const int col = h0 + wn * (BN / WN / 2) + j * 32 + (lane & 31);
         if (col >= F) continue;
 #pragma unroll
         for (int e = 0; e < 16; ++e) {
-          const int row = m0 + wm * (BM / 2) + i * 32 + 8 * (e >> 2) + 4 * (lane >> 5) + (e & 3);
+          const int row = m0 + wm * (BM / WM) + i * 32 + 8 * (e >> 2) + 4 * (lane >> 5) + (e & 3);
           if (row >= M) continue;
           const float g = acc[i][j][e], u = acc[i][j + TN / 2][e];
           H[(long)row * F + col] = f2bf(g / (1.0f + expf(-g)) * u);
@@ -272,14 +305,12 @@ __global__ __launch_bounds__(256) void k_gemm_f32(const float* __restrict__ A, c
 
 #ifndef DLLM_LDS_CASES
 #define DLLM_LDS_CASES                                                                              \
-  DLLM_LDS_CASE(64, 64, 4) DLLM_LDS_CASE(64, 64, 6) DLLM_LDS_CASE(128, 64, 3) DLLM_LDS_CASE(128, 64, 4)    \
-  DLLM_LDS_CASE(64, 128, 4) DLLM_LDS_CASE(128, 128, 2) DLLM_LDS_CASE(128, 128, 3) DLLM_LDS_CASE(128, 128, 4) \
-  DLLM_LDS_CASE(256, 128, 2) DLLM_LDS_CASE(256, 128, 3)
+  DLLM_LDS_CASE(128, 64, 4, 1, 2, 2) DLLM_LDS_CASE(128, 128, 2, 1, 2, 2) DLLM_LDS_CASE(128, 128, 3, 1, 2, 2) \
+  DLLM_LDS_CASE(128, 256, 3, 1, 2, 4) DLLM_LDS_CASE(256, 256, 2, 1, 2, 4)
 #endif
 #ifndef DLLM_LDS_SWIGLU_CASES
 #define DLLM_LDS_SWIGLU_CASES                                                                       \
-  DLLM_LDS_CASE(64, 128, 4) DLLM_LDS_CASE(128, 128, 2) DLLM_LDS_CASE(128, 128, 3) DLLM_LDS_CASE(128, 128, 4) \
-  DLLM_LDS_CASE(256, 128, 2) DLLM_LDS_CASE(256, 128, 3)
+  DLLM_LDS_CASE(128, 128, 3, 1, 2, 2) DLLM_LDS_CASE(128, 128, 3, 2, 2, 2)
 #endif
 
 GemmPlan gemm_plan(int dtype, int M, int N, int K, bool swiglu) {
@@ -289,34 +320,66 @@ GemmPlan gemm_plan(int dtype, int M, int N, int K, bool swiglu) {
     while (!swiglu && tiles * p.splits < 256 && p.splits < 8 && (K / 16) / (p.splits * 2) >= 8) p.splits *= 2;
     return p;
   }
-  // Direct-to-LDS kernel (pd = 10 + stages).  Rules from a tile sweep on the LLaDA-8B layer
-  // shapes: few rows (HBM bound on the weights) -> 128-row tiles, 64 columns for narrow
-  // outputs, 3-4 stages in flight and split-K until ~512 workgroups; many rows (MFMA bound)
-  // -> 128x128 tiles, 2 stages so two workgroups share a CU.
+  // Direct-to-LDS kernel (pd = 10 + stages).  Rules from tile sweeps on the LLaDA-8B layer
+  // shapes.  Few rows (HBM bound on the weights): 128-row tiles; wide QKV-like outputs take
+  // 256 columns over 2 x 4 wavefronts, narrow ones 64 columns with 4 stages, and split-K
+  // fills the chip.  Many rows (MFMA bound): 256 x 256 tiles for wide outputs, otherwise
+  // 128 x 128 with 2 stages so that two workgroups share a CU; the fused SwiGLU product
+  // runs two k-groups of wavefronts.
   const bool few = M <= 192;
+  const bool wide = N > 8192 && N <= 32768;
   p.bm = 128;
-  p.bn = (swiglu || !few || N > 8192) ? 128 : 64;
-  p.pd = 10 + (few ? (p.bn == 64 ? 4 : 3) : 2);
-  if (swiglu) return p;  // the fused epilogue needs the whole reduction in one workgroup
+  p.bn = 128;
+  long target = 256;
+  if (few) {
+    if (swiglu) {
+      p.pd = 13;
+      return p;  // the fused epilogue needs the whole reduction in one workgroup
+    }
+    if (wide) {
+      p.bn = 256;
+      p.wm = 2;
+      p.wn = 4;
+      p.pd = 13;
+      target = 192;
+    } else if (N > 32768) {
+      p.pd = 13;
+    } else {
+      p.bn = 64;
+      p.pd = 14;
+    }
+  } else {
+    if (swiglu) {
+      p.pd = 13;
+      p.kg = 2;
+      return p;
+    }
+    if (wide) {
+      p.bm = 256;
+      p.bn = 256;
+      p.wm = 2;
+      p.wn = 4;
+      p.pd = 12;
+      target = 192;
+    } else {
+      p.pd = 12;
+    }
+  }
   const long tiles = (long)((M + p.bm - 1) / p.bm) * ((N + p.bn - 1) / p.bn);
-  const long target = few ? 512 : 256;
   const int max_splits = 4;
   while (tiles * p.splits < target && p.splits < max_splits && K / (p.splits * 2) >= 1024) p.splits *= 2;
-  // 128x128 split-K grids of more than one workgroup per CU: two stages, so that two
-  // workgroups share each CU and the whole grid is resident at once
-  if (few && p.bn == 128 && p.splits > 1 && tiles * p.splits > 256 && tiles * p.splits <= 512) p.pd = 12;
   return p;
 }
 
-template <int BM, int BN, int NS, int EPI>
+template <int BM, int BN, int NS, int EPI, int KG, int WM, int WN>
 static void launch_lds(const GemmPlan& p, const void* A, const void* W, float* C, void* H, int M, int N, int K,
                        const int32_t* n_active, int k_max, hipStream_t s) {
   const int ncols = EPI == 0 ? BN : BN / 2;
   const int tm = (M + BM - 1) / BM, tn = (N + ncols - 1) / ncols;
   constexpr int lds_bytes = NS * (BM + BN) * 64 * 2;
-  constexpr int occ = lds_bytes <= 80 * 1024 ? 2 : 1;
-  hipLaunchKernelGGL((k_gemm_lds<BM, BN, NS, EPI, occ>), dim3(tm * tn * p.splits), dim3(256), 0, s, (const uint16_t*)A,
-                     (const uint16_t*)W, C, (uint16_t*)H, M, N, K, p.splits, tm, tn, n_active, k_max);
+  constexpr int occ = (lds_bytes <= 80 * 1024 && KG * WM * WN == 4) ? 2 : 1;
+  hipLaunchKernelGGL((k_gemm_lds<BM, BN, NS, EPI, occ, KG, WM, WN>), dim3(tm * tn * p.splits), dim3(64 * KG * WM * WN), 0, s,
+                     (const uint16_t*)A, (const uint16_t*)W, C, (uint16_t*)H, M, N, K, p.splits, tm, tn, n_active, k_max);
 }
 
 hipError_t launch_gemm(int dtype, const GemmPlan& p, const void* A, const void* W, float* C, int M, int N, int K,
@@ -329,9 +392,10 @@ hipError_t launch_gemm(int dtype, const GemmPlan& p, const void* A, const void* 
     return hipGetLastError();
   }
   if (K % 64 != 0) return hipErrorInvalidValue;
-#define DLLM_LDS_CASE(BM_, BN_, NS_)                                                                \
-  if (p.bm == BM_ && p.bn == BN_ && p.bk == 64 && p.pd == 10 + NS_) {                               \
-    launch_lds<BM_, BN_, NS_, 0>(p, A, W, C, nullptr, M, N, K, n_active, k_max, s);                 \
+#define DLLM_LDS_CASE(BM_, BN_, NS_, KG_, WM_, WN_)                                                \
+  if (p.bm == BM_ && p.bn == BN_ && p.bk == 64 && p.pd == 10 + NS_ && p.kg == KG_ && p.wm == WM_ &&  \
+      p.wn == WN_) {                                                                                \
+    launch_lds<BM_, BN_, NS_, 0, KG_, WM_, WN_>(p, A, W, C, nullptr, M, N, K, n_active, k_max, s);  \
     return hipGetLastError();                                                                       \
   }
   DLLM_LDS_CASES
@@ -344,9 +408,10 @@ hipError_t launch_gemm_swiglu(const GemmPlan& p, const void* A, const void* W_ga
                               const int32_t* n_active, int k_max, hipStream_t s) {
   if (M <= 0 || F <= 0) return hipSuccess;
   if (K % 64 != 0 || F % (p.bn / 2) != 0 || p.splits != 1) return hipErrorInvalidValue;
-#define DLLM_LDS_CASE(BM_, BN_, NS_)                                                                \
-  if (p.bm == BM_ && p.bn == BN_ && p.bk == 64 && p.pd == 10 + NS_) {                               \
-    launch_lds<BM_, BN_, NS_, 1>(p, A, W_gate_up, nullptr, H, M, F, K, n_active, k_max, s);         \
+#define DLLM_LDS_CASE(BM_, BN_, NS_, KG_, WM_, WN_)                                                \
+  if (p.bm == BM_ && p.bn == BN_ && p.bk == 64 && p.pd == 10 + NS_ && p.kg == KG_ && p.wm == WM_ &&  \
+      p.wn == WN_) {                                                                                \
+    launch_lds<BM_, BN_, NS_, 1, KG_, WM_, WN_>(p, A, W_gate_up, nullptr, H, M, F, K, n_active, k_max, s); \
     return hipGetLastError();                                                                       \
   }
   DLLM_LDS_SWIGLU_CASES

@@ -40,6 +40,8 @@ hipError_t launch_copy(const void* src, void* dst, size_t bytes, hipStream_t s);
 // n_active == nullptr means every row is live.
 struct GemmPlan {
   int bm, bn, splits, bk, pd;  // tile rows, tile columns, K splits, K tile, 10 + LDS stages (bf16)
+  int kg = 1;                  // k-groups of wavefronts per workgroup (bf16)
+  int wm = 2, wn = 2;          // wavefronts along the tile's rows and columns (bf16)
 };
 GemmPlan gemm_plan(int dtype, int M, int N, int K, bool swiglu = false);
 hipError_t launch_gemm(int dtype, const GemmPlan& p, const void* A, const void* W, float* C, int M, int N, int K,
