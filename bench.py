@@ -169,7 +169,7 @@ def cpu_baseline(model_w_gpu, dims, k_sparse, boundary, steps, sample_layers=16)
     }
 
 
-DOMINANT_KERNEL = "dllm::k_gemm_lds<128, 128, 3, 1, 1, 1, 2, 2>"
+DOMINANT_KERNEL = "dllm::k_gemm_lds<128, 96, 4, 2, 1, 1, 4, 1>"
 TRAFFIC_PROFILE = os.path.join(ROOT, "profiles", "gemm_swiglu_llada_128rows_hbm_bytes.md")
 GEMM_SOURCE = os.path.join(ROOT, "token_skipping_denoise_amd", "csrc", "gemm.hip")
 

@@ -52,6 +52,10 @@ __device__ __forceinline__ void decode_tile(int nt, int tiles_m, int tiles_n, in
 //          in each wavefront's half of the tile the first TN/2 column blocks
 //          hold gate rows and the last TN/2 the matching up rows, so a lane
 //          holds both factors of its outputs.  splits must be 1.
+// EPI = 2: fused SwiGLU with gate and up rows interleaved in groups of 16: each 32-row
+//          block of the tile holds 16 gate rows and the matching 16 up rows, so the two
+//          factors sit in lanes t and t + 16 of one accumulator; any column count that is a
+//          multiple of 32 works (48 outputs for 96 columns).
 //
 // Direct-to-LDS variant (gfx950 global_load_lds_dwordx4): tiles stream from
 // memory straight into an NS-stage LDS ring with no register staging, so
@@ -92,7 +96,7 @@ __global__ __launch_bounds__(64 * WM * WN * KG, OCC) void k_gemm_lds(const uint1
   constexpr int STAGE = (BM + BN) * BK;      // elements per stage
   constexpr int KS = BK / 16 / KG;           // MFMA k-steps per stage for each k-group
   static_assert(TM * 32 * WM == BM && TN * 32 * WN == BN, "wave tiles are whole 32x32 blocks");
-  static_assert(EPI == 0 || TN % 2 == 0, "fused SwiGLU needs an even number of column blocks per wave");
+  static_assert(EPI != 1 || TN % 2 == 0, "fused SwiGLU needs an even number of column blocks per wave");
   static_assert(LA * 8 * NW == BM && LB * 8 * NW == BN, "every wave issues the same number of tile loads");
   static_assert(KG == 1 || NS * STAGE * 2 >= BM * BN * 4, "the k-group reduction reuses the stage ring");
   __shared__ __attribute__((aligned(1024))) uint16_t smem[NS * STAGE];
@@ -117,6 +121,10 @@ __global__ __launch_bounds__(64 * WM * WN * KG, OCC) void k_gemm_lds(const uint1
   // holds gate rows and the second half the matching up rows
   auto w_row = [&](int c) -> int {
     if (EPI == 0) return tni * BN + c;
+    if (EPI == 2) {  // every 32-row block: 16 gate rows, then the 16 matching up rows
+      const int o = h0 + (c >> 5) * 16 + (c & 15);
+      return (c & 16) ? F + o : o;
+    }
     constexpr int SL = BN / WN;
     const int sl = c / SL, lc = c % SL;
     const int jb = lc / 32, t = lc % 32;
@@ -239,6 +247,21 @@ __global__ __launch_bounds__(64 * WM * WN * KG, OCC) void k_gemm_lds(const uint1
           if (row < M) Cs[(long)row * N + col] = acc[i][j][e];
         }
       }
+  } else if (EPI == 2) {
+    // lane t < 16 of a column block holds gate output t, lane t + 16 the matching up value
+#pragma unroll
+    for (int i = 0; i < TM; ++i)
+#pragma unroll
+      for (int j = 0; j < TN; ++j) {
+        const int col = h0 + ((wn * (BN / WN) + j * 32) >> 1) + (lane & 15);
+#pragma unroll
+        for (int e = 0; e < 16; ++e) {
+          const float v = acc[i][j][e];
+          const float u = __shfl_xor(v, 16, kWave);
+          const int row = m0 + wm * (BM / WM) + i * 32 + 8 * (e >> 2) + 4 * (lane >> 5) + (e & 3);
+          if ((lane & 16) == 0 && col < F && row < M) H[(long)row * F + col] = f2bf(v / (1.0f + expf(-v)) * u);
+        }
+      }
   } else {
 #pragma unroll
     for (int i = 0; i < TM; ++i)
@@ -313,6 +336,10 @@ __global__ __launch_bounds__(256) void k_gemm_f32(const float* __restrict__ A, c
   DLLM_LDS_CASE(128, 128, 3, 1, 2, 2) DLLM_LDS_CASE(128, 128, 3, 2, 2, 2)
 #endif
 
+#ifndef DLLM_LDS_SWIGLU_ILV_CASES
+#define DLLM_LDS_SWIGLU_ILV_CASES DLLM_LDS_CASE(128, 96, 4, 1, 4, 1)
+#endif
+
 GemmPlan gemm_plan(int dtype, int M, int N, int K, bool swiglu) {
   GemmPlan p{64, 64, 1, 64, 2};
   if (dtype == 0) {
@@ -333,8 +360,18 @@ GemmPlan gemm_plan(int dtype, int M, int N, int K, bool swiglu) {
   long target = 256;
   if (few) {
     if (swiglu) {
-      p.pd = 13;
-      return p;  // the fused epilogue needs the whole reduction in one workgroup
+      // the fused epilogue needs whole sums, so no split-K: 48 outputs per tile (gate and up
+      // rows interleaved in 16s) give enough tiles to fill the chip when they divide F
+      if (N % 48 == 0 && N / 48 >= 192) {
+        p.bn = 96;
+        p.wm = 4;
+        p.wn = 1;
+        p.pd = 14;
+        p.ilv = 1;
+      } else {
+        p.pd = 13;
+      }
+      return p;
     }
     if (wide) {
       p.bn = 256;
@@ -410,11 +447,19 @@ hipError_t launch_gemm_swiglu(const GemmPlan& p, const void* A, const void* W_ga
   if (K % 64 != 0 || F % (p.bn / 2) != 0 || p.splits != 1) return hipErrorInvalidValue;
 #define DLLM_LDS_CASE(BM_, BN_, NS_, KG_, WM_, WN_)                                                \
   if (p.bm == BM_ && p.bn == BN_ && p.bk == 64 && p.pd == 10 + NS_ && p.kg == KG_ && p.wm == WM_ &&  \
-      p.wn == WN_) {                                                                                \
+      p.wn == WN_ && !p.ilv) {                                                                      \
     launch_lds<BM_, BN_, NS_, 1, KG_, WM_, WN_>(p, A, W_gate_up, nullptr, H, M, F, K, n_active, k_max, s); \
     return hipGetLastError();                                                                       \
   }
   DLLM_LDS_SWIGLU_CASES
+#undef DLLM_LDS_CASE
+#define DLLM_LDS_CASE(BM_, BN_, NS_, KG_, WM_, WN_)                                                \
+  if (p.bm == BM_ && p.bn == BN_ && p.bk == 64 && p.pd == 10 + NS_ && p.kg == KG_ && p.wm == WM_ &&  \
+      p.wn == WN_ && p.ilv) {                                                                       \
+    launch_lds<BM_, BN_, NS_, 2, KG_, WM_, WN_>(p, A, W_gate_up, nullptr, H, M, F, K, n_active, k_max, s); \
+    return hipGetLastError();                                                                       \
+  }
+  DLLM_LDS_SWIGLU_ILV_CASES
 #undef DLLM_LDS_CASE
 #undef DLLM_SWIGLU_CASE
   return hipErrorInvalidValue;

@@ -42,6 +42,7 @@ struct GemmPlan {
   int bm, bn, splits, bk, pd;  // tile rows, tile columns, K splits, K tile, 10 + LDS stages (bf16)
   int kg = 1;                  // k-groups of wavefronts per workgroup (bf16)
   int wm = 2, wn = 2;          // wavefronts along the tile's rows and columns (bf16)
+  int ilv = 0;                 // SwiGLU: gate/up rows interleaved in 16s inside each 32-row block
 };
 GemmPlan gemm_plan(int dtype, int M, int N, int K, bool swiglu = false);
 hipError_t launch_gemm(int dtype, const GemmPlan& p, const void* A, const void* W, float* C, int M, int N, int K,
