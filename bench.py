@@ -12,8 +12,10 @@ tokens / second.
 
 Prints ONE JSON line (rank 0, N = 1).  `roofline` describes the dominant
 kernel -- the gate/up + SwiGLU product of the skipped layers (128 active rows),
-timed live with HIP events bracketing each of its launches inside the timed
-region; `cpu_baseline` times the CPU oracle on a bounded sample (16 layers
+timed live with HIP events bracketing each of its launches; `kernels` gives the
+same for every kernel class of the skipped-regime iteration (its algorithmic
+bytes and flops over its average launch time, against the HBM or bf16 MFMA
+roof); `cpu_baseline` times the CPU oracle on a bounded sample (16 layers
 over all rows and over the active rows, scoring and selection, the LM head)
 and extrapolates to a generation.
 """
@@ -39,12 +41,17 @@ HBM_PEAK_GBS = 8000.0      # MI355X HBM3E, GB/s
 BF16_PEAK_TFLOPS = 2500.0  # MI355X dense bf16 MFMA
 
 
+HIP_EVENT_DISABLE_SYSTEM_FENCE = 0x20000000  # timing-only events: no cache writeback/invalidate
+
+
 class HipEvents:
-    """Raw hipEvent_t pairs (created through the HIP runtime) for the library's timing hook."""
+    """Raw hipEvent_t pairs (created through the HIP runtime) for the library's timing hook.  They
+    only time work and are read after a full device synchronisation, so they skip the
+    system-scope fence that would otherwise add cache maintenance inside the bracket."""
 
     def __init__(self, n: int):
         self.hip = ctypes.CDLL("libamdhip64.so")
-        self.hip.hipEventCreate.argtypes = [ctypes.POINTER(ctypes.c_void_p)]
+        self.hip.hipEventCreateWithFlags.argtypes = [ctypes.POINTER(ctypes.c_void_p), ctypes.c_uint]
         self.hip.hipEventElapsedTime.argtypes = [ctypes.POINTER(ctypes.c_float), ctypes.c_void_p, ctypes.c_void_p]
         self.hip.hipEventDestroy.argtypes = [ctypes.c_void_p]
         self.n = n
@@ -53,8 +60,8 @@ class HipEvents:
         for arr in (self.start, self.stop):
             for i in range(n):
                 ev = ctypes.c_void_p()
-                if self.hip.hipEventCreate(ctypes.byref(ev)) != 0:
-                    raise RuntimeError("hipEventCreate failed")
+                if self.hip.hipEventCreateWithFlags(ctypes.byref(ev), HIP_EVENT_DISABLE_SYSTEM_FENCE) != 0:
+                    raise RuntimeError("hipEventCreateWithFlags failed")
                 arr[i] = ev
 
     def elapsed_ms(self, count: int) -> list[float]:
@@ -98,6 +105,69 @@ def ffn_up_bytes(dims, rows: int) -> float:
     """Algorithmic HBM bytes of one gate/up + SwiGLU launch: weights + input rows + output rows."""
     e = 2
     return (2 * dims.d_ff * dims.d + rows * dims.d + rows * dims.d_ff) * e
+
+
+def kernel_work(dims, rows: int):
+    """Per kernel class: (timing class, rows filter, algorithmic bytes, flops) of one launch in an
+    early-skip iteration with `rows` active rows.  Bytes count what the method itself must move
+    (weights, input and output rows, caches it reads), not split-K partials or scratch."""
+    e, B, S, d, F, V = 2, dims.B, dims.S, dims.d, dims.d_ff, dims.vocab
+    hqd, hkvd = dims.n_heads * dims.head_dim, dims.n_kv_heads * dims.head_dim
+    nqkv = hqd + 2 * hkvd
+    R = rows
+
+    def gemm(n, k, out_e=e):
+        return (n * k + R * k) * e + R * n * out_e, 2.0 * R * n * k
+
+    return {
+        "qkv": (_ffi.TK_QKV, R) + gemm(nqkv, d),
+        "attention": (_ffi.TK_ATTN, R, (2 * R * hqd + 2 * B * S * hkvd) * e, 4.0 * R * S * hqd),
+        "o_proj": (_ffi.TK_O, R) + gemm(d, hqd),
+        "ffn_up_swiglu": (_ffi.TK_FFN_UP, R, ffn_up_bytes(dims, R), 2.0 * R * 2 * F * d),
+        "ffn_down": (_ffi.TK_FFN_DOWN, R) + gemm(d, F),
+        "lm_head": (_ffi.TK_LM_HEAD, R) + gemm(V, d, 4),
+        "vocab_conf": (_ffi.TK_VOCAB, R, 4.0 * R * V, 0.0),
+        "score": (_ffi.TK_SCORE, 0, 3.0 * B * S * d * e + 8.0 * B * S, 0.0),
+        "select": (_ffi.TK_SELECT, 0, 4.0 * B * S + 4.0 * B * rows, 0.0),
+    }
+
+
+def kernel_table(lib, model, state, tok0, plan, ws, dims, rows: int):
+    """Time every kernel class with HIP events around its launches over one eager generation each
+    and report its share of the HBM or MFMA roof."""
+    work = kernel_work(dims, rows)
+    cap = max(1, (len(plan) - 1) * dims.n_layers)
+    ev = HipEvents(cap)
+    out = []
+    try:
+        for name, (tk, max_rows, nbytes, flops) in work.items():
+            timing = _ffi.Timing(tk, max_rows, ev.n, 0, ctypes.cast(ev.start, ctypes.POINTER(ctypes.c_void_p)),
+                                 ctypes.cast(ev.stop, ctypes.POINTER(ctypes.c_void_p)))
+            lib.dllm_set_timing(ctypes.byref(timing))
+            try:
+                run_generation(model, state, tok0, plan, ws)
+                torch.cuda.synchronize()
+            finally:
+                lib.dllm_set_timing(None)
+            if timing.count == 0:
+                continue
+            durs = ev.elapsed_ms(timing.count)
+            us = sum(durs) / len(durs) * 1e3
+            gbps = nbytes / (us * 1e-6) / 1e9
+            tflops = flops / (us * 1e-6) / 1e12
+            ai = flops / nbytes if nbytes else 0.0
+            if name == "select":
+                bound, frac = "latency", None
+            elif ai > BF16_PEAK_TFLOPS * 1e12 / (HBM_PEAK_GBS * 1e9):
+                bound, frac = "mfma", tflops / BF16_PEAK_TFLOPS
+            else:
+                bound, frac = "hbm", gbps / HBM_PEAK_GBS
+            out.append({"kernel": name, "launches": timing.count, "avg_us": round(us, 2), "bytes": int(nbytes),
+                        "gbps": round(gbps, 1), "tflops": round(tflops, 2), "bound": bound,
+                        "frac": None if frac is None else round(frac, 4)})
+    finally:
+        ev.close()
+    return out
 
 
 def cpu_baseline(model_w_gpu, dims, k_sparse, boundary, steps, sample_layers=16):
@@ -299,6 +369,10 @@ def main():
                     "bytes_per_launch": int(bytes_per)}
         events.close()
 
+    kernels = None
+    if not args.no_kernel_timing:
+        kernels = kernel_table(lib, model, state, tok0, plan, ws, dims, k_sparse * dims.B)
+
     cpu = None
     if not args.no_cpu_baseline:
         cpu = cpu_baseline(w, dims, k_sparse, boundary, n_iter)
@@ -323,6 +397,7 @@ def main():
                    "iterations_per_step": n_iter, "setup_s": round(t_setup, 1),
                    "launch": "hip graph replay" if graph is not None else "eager"},
         "roofline": roofline,
+        "kernels": kernels,
         "cpu_baseline": cpu,
     }
     print(json.dumps(line), flush=True)
