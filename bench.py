@@ -263,6 +263,181 @@ def measured_traffic():
     return int(m.group(1))
 
 
+def dus_round_offsets(block: int, a: int = 2) -> list[list[int]]:
+    """Dilated unmasking rounds of one block (DUS summary, technical summary section 2): round r
+    takes the not yet planned offsets on the stride-a^(R-1-r) grid, R = ceil(log_a block), so the
+    first rounds are spread out and the last fills the neighbours."""
+    R = 1
+    while a ** R < block:
+        R += 1
+    done, rounds = set(), []
+    for r in range(R):
+        stride = a ** (R - 1 - r)
+        cur = [p for p in range(0, block, stride) if p not in done]
+        done.update(cur)
+        rounds.append(cur)
+    return rounds
+
+
+def dream_schedule(dims, device, n_steps=128, unmask=4, lock_max=0.8):
+    """SureLock-style run on the Dream-7B shapes: step 0 full, then every unlocked row is recomputed
+    (layers from 0, locked rows skip everything but stay attendable).  Random weights give
+    near-uniform posteriors that never lock by themselves, so a seeded per-sequence permutation
+    locks a growing share of all positions, f_t = lock_max * t / (n_steps - 1); the KL lock rule
+    stays active on top.  Four positions of the generated half are unmasked per step by confidence."""
+    import synth
+
+    perms = [synth.permutation(synth.seed_of(dims.cfg_id, 30_000, b), dims.S) for b in range(dims.B)]
+    lo, hi = dims.prompt, dims.S
+    steps = []
+    for t in range(n_steps):
+        n = int(round(lock_max * t / (n_steps - 1) * dims.S))
+        force = torch.zeros((dims.B, dims.S), dtype=torch.uint8)
+        for b in range(dims.B):
+            force[b, perms[b][:n]] = api.FORCE_EXCLUDED
+        if t == 0:
+            kw = dict(boundary_layer=0, full_step=True, score=None)
+        else:
+            kw = dict(boundary_layer=0, full_step=False,
+                      score=api.score_cfg(alpha=0.0, var=api.VAR_NONE, sel=api.SEL_UNLOCKED, k=dims.S))
+        kw.update(lock_kl_eps=1e-3, lock_conf_min=0.9, unmask_n=unmask, block_lo=lo, block_hi=hi)
+        steps.append((kw, force.to(device)))
+    return steps
+
+
+def long_schedule(dims, device, k_active=205, block=16, refresh_every=16):
+    """Long-context run on the LLaDA-8B shapes with a dilated schedule: the generated half is cut
+    into blocks of 16 decoded in ceil(log2 16) = 4 rounds (stride 8, 4, 2, 1); every step unmasks
+    exactly the round's planned positions.  Every 16th step refreshes everything (prompt
+    included); the others recompute the planned positions plus the response rows whose hidden
+    state at layer 0 changed most (1 - cos), k_active = 5% of S rows per sequence in all."""
+    rounds = dus_round_offsets(block)
+    n_blocks = (dims.S - dims.prompt) // block
+    steps = []
+    t = 0
+    for blk in range(n_blocks):
+        lo = dims.prompt + blk * block
+        for r in rounds:
+            force = torch.zeros((dims.B, dims.S), dtype=torch.uint8)
+            force[:, :dims.prompt] = api.FORCE_EXCLUDED
+            force[:, [lo + o for o in r]] = api.FORCE_ON
+            if t % refresh_every == 0:
+                kw = dict(boundary_layer=0, full_step=True, score=None)
+            else:
+                kw = dict(boundary_layer=0, full_step=False,
+                          score=api.score_cfg(alpha=0.0, var=api.VAR_COS, sel=api.SEL_TOPK, k=k_active))
+            kw.update(unmask_n=1, block_lo=lo, block_hi=lo + block, unmask_mode=api.UNMASK_FORCED)
+            steps.append((kw, force.to(device)))
+            t += 1
+    return steps
+
+
+def run_schedule(model, state, tok0, steps, ws):
+    state.tokens.copy_(tok0)
+    state.c.have_prev = 0
+    state.c.bnd_cur = 0
+    if state.force is not None:
+        state.force.zero_()
+    for kw, force in steps:
+        # the schedule's marks; rows the lock rule has already locked stay locked
+        torch.maximum(state.force, force, out=state.force)
+        if kw.get("unmask_mode") == api.UNMASK_FORCED:
+            state.force.copy_(force)
+        api.skip_step(model, state, api.step_cfg(ws=ws, **kw))
+
+
+def extra_workload(args):
+    """Dream-GQA lock ramp or long-context dilated run: one JSON line, eager launches (the
+    steps are long enough that launch overhead is noise)."""
+    dev = "cuda:0"
+    if args.workload == "dream":
+        dims, k_max = workloads.DREAM, workloads.DREAM.S
+        desc = ("Dream-7B-shaped 28-layer GQA 28/4 run, batch 8, prompt 512 + gen 512, 128 steps, locked share "
+                "ramped 0 -> 80% of positions (seeded), unlocked rows recomputed, KL lock rule on")
+    else:
+        dims, k_max = workloads.LLADA_LONG, 205
+        desc = ("LLaDA-8B-shaped 32-layer long-context run, batch 4, prompt 3584 + gen 512, dilated blocks of 16 "
+                "(4 rounds), 128 steps, refresh every 16 steps, else 205 active rows (5%)")
+    t0 = time.perf_counter()
+    w = workloads.model_weights(dims, device=dev)
+    model = api.Model(w, dims.n_heads, dims.n_kv_heads, dims.mask_id)
+    tok0 = workloads.initial_tokens(dims, device=dev)
+    track_kl = args.workload == "dream"
+    state = api.State(model, tok0.clone(), k_max=k_max, track_kl=track_kl)
+    ws = api.alloc_workspace(model, dims.B, dims.S, k_max)
+    steps = dream_schedule(dims, dev) if args.workload == "dream" else long_schedule(dims, dev)
+    torch.cuda.synchronize()
+    t_setup = time.perf_counter() - t0
+    for _ in range(args.warmup):
+        run_schedule(model, state, tok0, steps, ws)
+    torch.cuda.synchronize()
+    t_start = time.perf_counter()
+    for _ in range(args.steps):
+        run_schedule(model, state, tok0, steps, ws)
+    torch.cuda.synchronize()
+    elapsed = time.perf_counter() - t_start
+    gen_tokens = dims.B * (dims.S - dims.prompt)
+    kernels = None
+    if not args.no_kernel_timing and args.workload == "long":
+        lib = _ffi.load()
+        kernels = kernel_table_schedule(lib, model, state, tok0, steps, ws, dims, dims.B * k_max)
+    line = {
+        "metric": "denoised tokens/s at 8B shapes on 1 MI355X",
+        "value": round(gen_tokens * args.steps / elapsed, 2),
+        "unit": "tokens/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(elapsed / args.steps * 1e3, 3),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "bf16",
+        "data": "synthetic (seeded random-init weights N(0,0.02); prompt tokens uniform)",
+        "config": {"workload": desc, "batch": dims.B, "seq_len": dims.S, "layers": dims.n_layers,
+                   "hidden": dims.d, "vocab": dims.vocab, "iterations_per_step": len(steps),
+                   "setup_s": round(t_setup, 1), "launch": "eager"},
+        "kernels": kernels,
+    }
+    print(json.dumps(line), flush=True)
+
+
+def kernel_table_schedule(lib, model, state, tok0, steps, ws, dims, rows):
+    """kernel_table for an explicit schedule: rows = the padded active rows of a sparse step."""
+    work = kernel_work(dims, rows)
+    cap = max(1, len(steps) * dims.n_layers)
+    ev = HipEvents(cap)
+    out = []
+    try:
+        for name, (tk, max_rows, nbytes, flops) in work.items():
+            if name in ("score", "select"):
+                continue
+            timing = _ffi.Timing(tk, max_rows, ev.n, 0, ctypes.cast(ev.start, ctypes.POINTER(ctypes.c_void_p)),
+                                 ctypes.cast(ev.stop, ctypes.POINTER(ctypes.c_void_p)))
+            lib.dllm_set_timing(ctypes.byref(timing))
+            try:
+                run_schedule(model, state, tok0, steps, ws)
+                torch.cuda.synchronize()
+            finally:
+                lib.dllm_set_timing(None)
+            if timing.count == 0:
+                continue
+            durs = ev.elapsed_ms(timing.count)
+            us = sum(durs) / len(durs) * 1e3
+            gbps = nbytes / (us * 1e-6) / 1e9
+            tflops = flops / (us * 1e-6) / 1e12
+            ai = flops / nbytes if nbytes else 0.0
+            if ai > BF16_PEAK_TFLOPS * 1e12 / (HBM_PEAK_GBS * 1e9):
+                bound, frac = "mfma", tflops / BF16_PEAK_TFLOPS
+            else:
+                bound, frac = "hbm", gbps / HBM_PEAK_GBS
+            out.append({"kernel": name, "launches": timing.count, "avg_us": round(us, 2), "bytes": int(nbytes),
+                        "gbps": round(gbps, 1), "tflops": round(tflops, 2), "bound": bound, "frac": round(frac, 4)})
+    finally:
+        ev.close()
+    return out
+
+
 def main():
     ap = argparse.ArgumentParser(description=__doc__.split("\n")[0])
     ap.add_argument("--gpus", type=int, default=1)
@@ -271,6 +446,9 @@ def main():
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-kernel-timing", action="store_true")
     ap.add_argument("--no-graph", action="store_true", help="launch eagerly instead of replaying a HIP graph")
+    ap.add_argument("--workload", choices=("llada", "dream", "long"), default="llada",
+                    help="llada: the 32-layer early-skip generation (default); dream: Dream-GQA lock ramp; "
+                         "long: long-context dilated run")
     ap.add_argument("--calibrate-copy", action="store_true",
                     help="only copy a 1 GiB buffer once (reference for the HBM byte counters) and exit")
     args = ap.parse_args()
@@ -290,6 +468,9 @@ def main():
     if not torch.cuda.is_available():
         print("bench.py needs a GPU", file=sys.stderr)
         sys.exit(2)
+    if args.workload != "llada":
+        extra_workload(args)
+        return
 
     dims = workloads.LLADA
     dev = "cuda:0"

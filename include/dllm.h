@@ -220,7 +220,7 @@ int dllm_confidence_kl(const float *logits, float *logits_prev, const int32_t *r
  * below the boundary, score + select at the boundary, sparse layers,
  * final-hidden scatter, LM head on the active rows, confidence/KL, then the
  * SureLock lock update and/or confidence unmasking of [block_lo, block_hi).
- * On a full step every row is active (state->k_max must be >= S). */
+ * On a full step every row is active, whatever state->k_max is. */
 int dllm_skip_step(const dllm_model *model, dllm_state *state, const dllm_step_cfg *cfg, void *stream);
 
 /* Kernel classes the measurement hook can bracket. */

@@ -73,7 +73,7 @@ constexpr int kHD = 128;                      // head dim
 constexpr int kRowBytes = kHD * 2;            // one key row of K or V
 constexpr int kTileBytes = kKT * kRowBytes;   // 16 KB per tensor
 constexpr int kStageBytes = 2 * kTileBytes;   // K tile, then V tile
-constexpr int kStages = 2;                    // per group
+constexpr int kRing = 4;                      // stages shared by the workgroup
 // Fourth word of a raw buffer resource (CDNA): 32-bit data format, no swizzle; out-of-range
 // offsets read as zero.
 constexpr int kBufWord3 = 0x00020000;
@@ -84,6 +84,29 @@ typedef short short8_t __attribute__((ext_vector_type(8)));
 // 16-byte chunk c of tile row r sits in slot c ^ swz(r): the MFMA K reads (16 rows at one
 // chunk) and the transposing V reads (8 rows x 4 chunks) both touch every bank once per pass.
 __device__ __forceinline__ int swz(int r) { return ((r & 3) << 2) | ((r >> 2) & 3); }
+
+// Eight transposing 8-byte LDS reads, complete when the block ends.  Written out because the
+// compiler does not know which LDS bytes the builtin reads and so waits for every direct-to-LDS
+// load still in flight before it, the next tiles' included.
+__device__ __forceinline__ void tr_read8(short4_t (&d)[8], const uint32_t (&a)[8]) {
+  asm volatile(
+      "ds_read_b64_tr_b16 %0, %8\n\t"
+      "ds_read_b64_tr_b16 %1, %9\n\t"
+      "ds_read_b64_tr_b16 %2, %10\n\t"
+      "ds_read_b64_tr_b16 %3, %11\n\t"
+      "ds_read_b64_tr_b16 %4, %12\n\t"
+      "ds_read_b64_tr_b16 %5, %13\n\t"
+      "ds_read_b64_tr_b16 %6, %14\n\t"
+      "ds_read_b64_tr_b16 %7, %15\n\t"
+      "s_waitcnt lgkmcnt(0)"
+      : "=&v"(d[0]), "=&v"(d[1]), "=&v"(d[2]), "=&v"(d[3]), "=&v"(d[4]), "=&v"(d[5]), "=&v"(d[6]), "=&v"(d[7])
+      : "v"(a[0]), "v"(a[1]), "v"(a[2]), "v"(a[3]), "v"(a[4]), "v"(a[5]), "v"(a[6]), "v"(a[7])
+      : "memory");
+}
+
+__device__ __forceinline__ uint32_t lds_addr(const void* p) {
+  return (uint32_t)reinterpret_cast<uintptr_t>((const lds_void*)p);
+}
 
 template <int N>
 __device__ __forceinline__ void wait_vm_attn() {
@@ -98,7 +121,7 @@ __global__ __launch_bounds__(512, 1) void k_attn_bf16(const uint16_t* __restrict
                                                       const uint16_t* __restrict__ vc, uint16_t* __restrict__ o,
                                                       const int32_t* __restrict__ n_active, int S, int k_max, int Hq,
                                                       int Hkv, float scale_log2e, int nsplit, float* __restrict__ part) {
-  __shared__ __attribute__((aligned(1024))) uint8_t smem[2 * kStages * kStageBytes];  // 128 KB
+  __shared__ __attribute__((aligned(1024))) uint8_t smem[kRing * kStageBytes];  // 128 KB
   const int b = blockIdx.z / nsplit, split = blockIdx.z - b * nsplit, hk = blockIdx.y;
   const int g = Hq / Hkv;
   const int qb0 = blockIdx.x * 128;
@@ -106,56 +129,82 @@ __global__ __launch_bounds__(512, 1) void k_attn_bf16(const uint16_t* __restrict
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int grp = wave >> 2, gw = wave & 3;
   const int l32 = lane & 31, hi = lane >> 5;
-  uint8_t* gsm = smem + grp * kStages * kStageBytes;
 
-  // this workgroup's key tiles [t_begin, t_end); group grp takes t_begin + grp, + 2, + 4, ...
+  // this workgroup's key tiles [t_begin, t_end); key group grp takes keys 32 grp .. 32 grp + 31
+  // of every tile
   const int ntiles_all = (S + kKT - 1) / kKT;
   const int t_begin = (int)((long)split * ntiles_all / nsplit), t_end = (int)((long)(split + 1) * ntiles_all / nsplit);
-  const int n_steps = (t_end - t_begin + 1) / 2;  // tile pairs (the last may hold one tile)
-  const int n_my = (t_end - t_begin - grp + 1) / 2;
+  const int n_tiles = t_end - t_begin;
 
-  // K/V tile loads: 16 load instructions of 4 rows (1 KB) per tensor, 4 per wave.  Lane L of
+  // the queries first, straight into the ring's last stage (the prologue below fills the
+  // others; the tile loop first writes it after its first barrier): 128 query rows of 256 B, four
+  // 4-row load instructions per wave, chunk c of row r in slot c ^ swz(r) as for the tiles
+  const int kq = k_max * g;
+  uint8_t* qst = smem + (kRing - 1) * kStageBytes;
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    const int r = 4 * (wave * 4 + i) + (lane >> 4);
+    const int qs = min(qb0 + r, kq - 1);
+    const int jr = qs / g;
+    const long qrow_r = ((long)b * k_max + jr) * Hq + hk * g + (qs - jr * g);
+    const uint16_t* src = q + qrow_r * kHD + (((lane & 15) ^ swz(r)) << 3);
+    __builtin_amdgcn_global_load_lds((const void*)src, (lds_void*)(qst + (wave * 4 + i) * 1024), 16, 0, 0);
+  }
+  const int qi = qb0 + gw * 32 + l32;  // this lane's query slot
+
+  // K/V tile loads: 16 load instructions of 4 rows (1 KB) per tensor, 2 per wave.  Lane L of
   // instruction qi fills row 4 qi + L / 16, slot L % 16, so it fetches chunk slot ^ swz(row).
   const long head0 = ((long)b * S * Hkv + hk) * kHD;
   const int nbytes = S * Hkv * kRowBytes;
   const __amdgpu_buffer_rsrc_t rsk = __builtin_amdgcn_make_buffer_rsrc((void*)(kc + head0), (short)0, nbytes, kBufWord3);
   const __amdgpu_buffer_rsrc_t rsv = __builtin_amdgcn_make_buffer_rsrc((void*)(vc + head0), (short)0, nbytes, kBufWord3);
-  int voff[4];
+  int voff[2];
 #pragma unroll
-  for (int i = 0; i < 4; ++i) {
-    const int row = 4 * (gw * 4 + i) + (lane >> 4);
+  for (int i = 0; i < 2; ++i) {
+    const int row = 4 * (wave * 2 + i) + (lane >> 4);
     voff[i] = row * Hkv * kRowBytes + (((lane & 15) ^ swz(row)) << 4);
   }
   const int tile_bytes = kKT * Hkv * kRowBytes;
-  auto issue = [&](int t, int stage) {
-    uint8_t* st = gsm + stage * kStageBytes;
+  auto issue = [&](int t, int slot) {
+    uint8_t* st = smem + slot * kStageBytes;
     const int so = t * tile_bytes;  // in the per-lane offset, which the range check covers
 #pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      const int qi = gw * 4 + i;
-      __builtin_amdgcn_raw_ptr_buffer_load_lds(rsk, (lds_void*)(st + qi * 1024), 16, voff[i] + so, 0, 0, 0);
-      __builtin_amdgcn_raw_ptr_buffer_load_lds(rsv, (lds_void*)(st + kTileBytes + qi * 1024), 16, voff[i] + so, 0, 0, 0);
+    for (int i = 0; i < 2; ++i) {
+      const int qi2 = wave * 2 + i;
+      __builtin_amdgcn_raw_ptr_buffer_load_lds(rsk, (lds_void*)(st + qi2 * 1024), 16, voff[i] + so, 0, 0, 0);
+      __builtin_amdgcn_raw_ptr_buffer_load_lds(rsv, (lds_void*)(st + kTileBytes + qi2 * 1024), 16, voff[i] + so, 0, 0,
+                                               0);
     }
   };
-  // The first tile and the queries are requested before the active-row count is known (all
-  // addresses are valid either way): the three memory round trips overlap.
-  if (n_my > 0) issue(t_begin + grp, 0);
-  const int qi = qb0 + gw * 32 + l32;
-  const int qi_c = qi < k_max * g ? qi : k_max * g - 1;
-  const int jrow = qi_c / g, hg = qi_c - jrow * g;
-  const long qrow = (long)b * k_max + jrow;
-  const int h = hk * g + hg;
-  bf16x8_t qf[kHD / 16];
-  {
-    const uint16_t* qp = q + (qrow * Hq + h) * kHD + 8 * hi;
+  // the first tiles are requested before the active-row count is known (all addresses are valid
+  // either way), so those round trips overlap
 #pragma unroll
-    for (int t = 0; t < kHD / 16; ++t) qf[t] = __builtin_bit_cast(bf16x8_t, *reinterpret_cast<const uint4*>(qp + 16 * t));
-  }
+  for (int j = 0; j < kRing - 1; ++j)
+    if (j < n_tiles) issue(t_begin + j, j);
   const int nq = n_active[b] * g;
   if (qb0 >= nq) {
     wait_vm_attn<0>();  // no load may still be writing this workgroup's LDS when it ends
     return;
   }
+  // the query rows have landed once at most the prologue's tile loads are outstanding (loads
+  // complete in order); after the barrier every wave takes its B fragments from LDS
+  {
+    const int np = min(kRing - 1, n_tiles);
+    if (np >= 3) wait_vm_attn<12>();
+    else if (np == 2) wait_vm_attn<8>();
+    else if (np == 1) wait_vm_attn<4>();
+    else wait_vm_attn<0>();
+  }
+  __builtin_amdgcn_s_barrier();
+  bf16x8_t qf[kHD / 16];
+  {
+    const int r = gw * 32 + l32;
+    const uint8_t* rp = qst + r * kRowBytes;
+#pragma unroll
+    for (int t = 0; t < kHD / 16; ++t) qf[t] = *reinterpret_cast<const bf16x8_t*>(rp + (((2 * t + hi) ^ swz(r)) << 4));
+  }
+  // the reads are done before the first tile loop barrier lets a load overwrite the stage
+  __builtin_amdgcn_s_waitcnt(15 | (7 << 4) | (0 << 8) | (3 << 14));
   // a query slot past the live rows computes on whatever its row holds; its lanes never mix
   // with other queries' lanes and are not written back
   const bool qvalid = qi < nq;
@@ -167,100 +216,108 @@ __global__ __launch_bounds__(512, 1) void k_attn_bf16(const uint16_t* __restrict
     for (int e = 0; e < 16; ++e) oacc[db][e] = 0.f;
   // running max of the raw scores q.k, and the softmax sum of 2^((s - m) * scale_log2e)
   float m_run = -INFINITY, l_run = 0.f;
+  const float grow_thr = 8.f / scale_log2e;  // 2^8 in raw score units
 
   // per-lane parts of the fragment addresses
-  const int v_row = 4 * hi + ((lane & 15) >> 2);               // + kb2 * 32 + 16 hf (+ 8)
+  const int k_row = grp * 32 + l32;
+  const int k_sw = swz(k_row);
+  const int v_row = grp * 32 + 4 * hi + ((lane & 15) >> 2);    // + 16 hf (+ 8)
   const int v_col = 16 * ((lane >> 4) & 1) + 4 * (lane & 3);  // + 32 db
-  for (int i = 0; i < n_steps; ++i) {
-    wait_vm_attn<0>();             // this wave's loads of tile i (and the query) have landed
-    __builtin_amdgcn_s_barrier();  // ... and every other wave's; stage (i + 1) % 2 is free
-    if (i + 1 < n_my) issue(t_begin + grp + 2 * (i + 1), (i + 1) & 1);
-    if (i < n_my) {
-      const int t = t_begin + grp + 2 * i;
-      const uint8_t* kst = gsm + (i & 1) * kStageBytes;
-      const uint8_t* vst = kst + kTileBytes;
-      // S^T for two 32-key blocks
-      f32x16_t sacc[2];
+  for (int i = 0; i < n_tiles; ++i) {
+    // tiles after i may stay in flight (2 loads per tensor per wave each)
+    const int ahead = min(kRing - 2, n_tiles - 1 - i);
+    if (ahead >= 2) wait_vm_attn<8>();
+    else if (ahead == 1) wait_vm_attn<4>();
+    else wait_vm_attn<0>();
+    __builtin_amdgcn_s_barrier();  // every wave's loads of tile i have landed; slot (i - 1) is free
+    if (i + kRing - 1 < n_tiles) issue(t_begin + i + kRing - 1, (i + kRing - 1) % kRing);
+    const int t = t_begin + i;
+    const uint8_t* kst = smem + (i % kRing) * kStageBytes;
+    const uint8_t* vst = kst + kTileBytes;
+    // S^T for this group's 32 keys of the tile
+    f32x16_t sacc;
+    {
+      const uint8_t* rp = kst + k_row * kRowBytes;
 #pragma unroll
-      for (int kb2 = 0; kb2 < 2; ++kb2) {
-        const int row = kb2 * 32 + l32;
-        const uint8_t* rp = kst + row * kRowBytes;
-        const int sw = swz(row);
+      for (int e = 0; e < 16; ++e) sacc[e] = 0.f;
 #pragma unroll
-        for (int e = 0; e < 16; ++e) sacc[kb2][e] = 0.f;
-#pragma unroll
-        for (int ts = 0; ts < kHD / 16; ++ts) {
-          const bf16x8_t a = *reinterpret_cast<const bf16x8_t*>(rp + (((2 * ts + hi) ^ sw) << 4));
-          sacc[kb2] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, qf[ts], sacc[kb2], 0, 0, 0);
-        }
+      for (int ts = 0; ts < kHD / 16; ++ts) {
+        const bf16x8_t a = *reinterpret_cast<const bf16x8_t*>(rp + (((2 * ts + hi) ^ k_sw) << 4));
+        sacc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, qf[ts], sacc, 0, 0, 0);
       }
-      // the last tile may be partial: keys past S score -inf
-      const int key0 = t * kKT;
-      if (key0 + kKT > S) {
+    }
+    // the last tile may be partial: keys past S score -inf
+    const int key0 = t * kKT + grp * 32;
+    if (key0 + 32 > S) {
 #pragma unroll
-        for (int kb2 = 0; kb2 < 2; ++kb2)
+      for (int e = 0; e < 16; ++e)
+        if (key0 + 8 * (e >> 2) + 4 * hi + (e & 3) >= S) sacc[e] = -INFINITY;
+    }
+    // online softmax (each query lives in lanes l and l^32)
+    float mt = -INFINITY;
 #pragma unroll
-          for (int e = 0; e < 16; ++e)
-            if (key0 + kb2 * 32 + 8 * (e >> 2) + 4 * hi + (e & 3) >= S) sacc[kb2][e] = -INFINITY;
-      }
-      // online softmax (each query lives in lanes l and l^32)
-      float mt = -INFINITY;
-#pragma unroll
-      for (int kb2 = 0; kb2 < 2; ++kb2)
-#pragma unroll
-        for (int e = 0; e < 16; ++e) mt = fmaxf(mt, sacc[kb2][e]);
-      mt = fmaxf(mt, __shfl_xor(mt, 32, kWave));
+    for (int e = 0; e < 16; ++e) mt = fmaxf(mt, sacc[e]);
+    mt = fmaxf(mt, __shfl_xor(mt, 32, kWave));
+    // The reference max m_run only moves when some query of the wave would otherwise see a
+    // weight above 2^8; below that, numerator and sum keep using the old reference, which
+    // changes nothing but rounding and saves rescaling the accumulators on almost every tile.
+    if (__builtin_amdgcn_ballot_w64(mt > m_run + grow_thr) != 0) {
       const float m_new = fmaxf(m_run, mt);
-      const float corr = __builtin_amdgcn_exp2f((m_run - m_new) * scale_log2e);
-      const float mc = m_new * scale_log2e;
-      float rs = 0.f;
-#pragma unroll
-      for (int kb2 = 0; kb2 < 2; ++kb2)
-#pragma unroll
-        for (int e = 0; e < 16; ++e) {
-          const float p = __builtin_amdgcn_exp2f(fmaf(sacc[kb2][e], scale_log2e, -mc));
-          sacc[kb2][e] = p;
-          rs += p;
-        }
-      rs += __shfl_xor(rs, 32, kWave);
-      l_run = l_run * corr + rs;
+      // a lane without a finite score yet keeps the empty state (m = -inf, l = 0)
+      const float corr = (m_new == -INFINITY) ? 1.f : __builtin_amdgcn_exp2f((m_run - m_new) * scale_log2e);
+      l_run *= corr;
       m_run = m_new;
 #pragma unroll
       for (int db = 0; db < kHD / 32; ++db)
 #pragma unroll
         for (int e = 0; e < 16; ++e) oacc[db][e] *= corr;
+    }
+    // m_run = -inf only while every score seen is -inf, so every weight is 0 then
+    const float mc = (m_run == -INFINITY) ? 0.f : m_run * scale_log2e;
+    float rs = 0.f;
+#pragma unroll
+    for (int e = 0; e < 16; ++e) {
+      const float p = __builtin_amdgcn_exp2f(fmaf(sacc[e], scale_log2e, -mc));
+      sacc[e] = p;
+      rs += p;
+    }
+    rs += __shfl_xor(rs, 32, kWave);
+    l_run += rs;
 
-      // O^T += V^T P^T over four 16-key steps; the V^T fragment (keys r0..r0+3, r0+8..r0+11 of
-      // column 32 db + l32) comes from two transposing reads of the [key][d] tile
+    // O^T += V^T P^T over two 16-key steps; the V^T fragment (keys r0..r0+3, r0+8..r0+11 of
+    // column 32 db + l32) comes from two transposing reads of the [key][d] tile
 #pragma unroll
-      for (int s2 = 0; s2 < 4; ++s2) {
-        const int kb2 = s2 >> 1, hf = s2 & 1;
-        uint32_t pw[4];
+    for (int hf = 0; hf < 2; ++hf) {
+      uint32_t pw[4];
 #pragma unroll
-        for (int e = 0; e < 4; ++e) {
-          const f32x2_t pr = {sacc[kb2][8 * hf + 2 * e], sacc[kb2][8 * hf + 2 * e + 1]};
-          pw[e] = __builtin_bit_cast(uint32_t, __builtin_convertvector(pr, bf16x2_t));
-        }
-        const bf16x8_t pfrag = __builtin_bit_cast(bf16x8_t, make_uint4(pw[0], pw[1], pw[2], pw[3]));
-        const int r0 = kb2 * 32 + 16 * hf + v_row, r1 = r0 + 8;
-        const uint8_t* vp0 = vst + r0 * kRowBytes;
-        const uint8_t* vp1 = vst + r1 * kRowBytes;
-        const int sw0 = swz(r0), sw1 = swz(r1);
+      for (int e = 0; e < 4; ++e) {
+        const f32x2_t pr = {sacc[8 * hf + 2 * e], sacc[8 * hf + 2 * e + 1]};
+        pw[e] = __builtin_bit_cast(uint32_t, __builtin_convertvector(pr, bf16x2_t));
+      }
+      const bf16x8_t pfrag = __builtin_bit_cast(bf16x8_t, make_uint4(pw[0], pw[1], pw[2], pw[3]));
+      const int r0 = 16 * hf + v_row, r1 = r0 + 8;
+      const uint32_t vp0 = lds_addr(vst + r0 * kRowBytes);
+      const uint32_t vp1 = lds_addr(vst + r1 * kRowBytes);
+      const int sw0 = swz(r0), sw1 = swz(r1);
+      uint32_t ad[8];
 #pragma unroll
-        for (int db = 0; db < kHD / 32; ++db) {
-          const int col = 32 * db + v_col;       // element column of this lane's 8-byte read
-          const int inb = (col & 7) << 1;        // byte within the 16-byte chunk
-          const short4_t lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
-              (__attribute__((address_space(3))) short4_t*)(vp0 + ((((col >> 3) ^ sw0) << 4) | inb)));
-          const short4_t hv = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
-              (__attribute__((address_space(3))) short4_t*)(vp1 + ((((col >> 3) ^ sw1) << 4) | inb)));
-          const short8_t a8 = {lo[0], lo[1], lo[2], lo[3], hv[0], hv[1], hv[2], hv[3]};
-          oacc[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8_t, a8), pfrag, oacc[db], 0, 0, 0);
-        }
+      for (int db = 0; db < kHD / 32; ++db) {
+        const int col = 32 * db + v_col;  // element column of this lane's 8-byte read
+        const int inb = (col & 7) << 1;   // byte within the 16-byte chunk
+        ad[2 * db] = vp0 + ((((col >> 3) ^ sw0) << 4) | inb);
+        ad[2 * db + 1] = vp1 + ((((col >> 3) ^ sw1) << 4) | inb);
+      }
+      short4_t tv[8];
+      tr_read8(tv, ad);
+#pragma unroll
+      for (int db = 0; db < kHD / 32; ++db) {
+        const short4_t lo = tv[2 * db], hv = tv[2 * db + 1];
+        const short8_t a8 = {lo[0], lo[1], lo[2], lo[3], hv[0], hv[1], hv[2], hv[3]};
+        oacc[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8_t, a8), pfrag, oacc[db], 0, 0, 0);
       }
     }
   }
-  __syncthreads();  // every wave is done with its tiles before the stages are reused below
+  __syncthreads();  // every wave is done with the ring before it is reused below
 
   // merge group 1 into group 0 through LDS: [wave][db][e][lane] floats, then (m, l) per wave lane
   float* xs = reinterpret_cast<float*>(smem);
@@ -291,6 +348,9 @@ __global__ __launch_bounds__(512, 1) void k_attn_bf16(const uint16_t* __restrict
   }
 
   if (!qvalid) return;
+  const int jrow = qi / g;
+  const long qrow = (long)b * k_max + jrow;
+  const int h = hk * g + (qi - jrow * g);
   if (nsplit > 1) {
     // partial layout: [split][row][head][D + 2] = unnormalised O, then (m, l)
     const long n_rows = (long)(gridDim.z / nsplit) * k_max;  // B * k_max
