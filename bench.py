@@ -263,20 +263,13 @@ def measured_traffic():
     return int(m.group(1))
 
 
-def dus_round_offsets(block: int, a: int = 2) -> list[list[int]]:
-    """Dilated unmasking rounds of one block (DUS summary, technical summary section 2): round r
-    takes the not yet planned offsets on the stride-a^(R-1-r) grid, R = ceil(log_a block), so the
-    first rounds are spread out and the last fills the neighbours."""
-    R = 1
-    while a ** R < block:
+def n_dus_rounds(block: int, a: int = 2) -> int:
+    """Rounds of a dilated block (DUS summary, technical summary section 2): R = ceil(log_a block)."""
+    R, p = 0, 1
+    while p < block:
+        p *= a
         R += 1
-    done, rounds = set(), []
-    for r in range(R):
-        stride = a ** (R - 1 - r)
-        cur = [p for p in range(0, block, stride) if p not in done]
-        done.update(cur)
-        rounds.append(cur)
-    return rounds
+    return max(R, 1)
 
 
 def dream_schedule(dims, device, n_steps=128, unmask=4, lock_max=0.8):
@@ -301,33 +294,34 @@ def dream_schedule(dims, device, n_steps=128, unmask=4, lock_max=0.8):
             kw = dict(boundary_layer=0, full_step=False,
                       score=api.score_cfg(alpha=0.0, var=api.VAR_NONE, sel=api.SEL_UNLOCKED, k=dims.S))
         kw.update(lock_kl_eps=1e-3, lock_conf_min=0.9, unmask_n=unmask, block_lo=lo, block_hi=hi)
-        steps.append((kw, force.to(device)))
+        steps.append((kw, force.to(device), None))
     return steps
 
 
 def long_schedule(dims, device, k_active=205, block=16, refresh_every=16):
     """Long-context run on the LLaDA-8B shapes with a dilated schedule: the generated half is cut
     into blocks of 16 decoded in ceil(log2 16) = 4 rounds (stride 8, 4, 2, 1); every step unmasks
-    exactly the round's planned positions.  Every 16th step refreshes everything (prompt
-    included); the others recompute the planned positions plus the response rows whose hidden
-    state at layer 0 changed most (1 - cos), k_active = 5% of S rows per sequence in all."""
-    rounds = dus_round_offsets(block)
+    exactly the round's planned positions, which the library marks on the device
+    (dllm_dus_mark).  Every 16th step refreshes everything (prompt included); the others
+    recompute the planned positions plus the response rows whose hidden state at layer 0
+    changed most (1 - cos), k_active = 5% of S rows per sequence in all."""
+    n_rounds = n_dus_rounds(block)
     n_blocks = (dims.S - dims.prompt) // block
+    base = torch.zeros((dims.B, dims.S), dtype=torch.uint8)
+    base[:, :dims.prompt] = api.FORCE_EXCLUDED
+    base = base.to(device)
     steps = []
     t = 0
     for blk in range(n_blocks):
         lo = dims.prompt + blk * block
-        for r in rounds:
-            force = torch.zeros((dims.B, dims.S), dtype=torch.uint8)
-            force[:, :dims.prompt] = api.FORCE_EXCLUDED
-            force[:, [lo + o for o in r]] = api.FORCE_ON
+        for r in range(n_rounds):
             if t % refresh_every == 0:
                 kw = dict(boundary_layer=0, full_step=True, score=None)
             else:
                 kw = dict(boundary_layer=0, full_step=False,
                           score=api.score_cfg(alpha=0.0, var=api.VAR_COS, sel=api.SEL_TOPK, k=k_active))
             kw.update(unmask_n=1, block_lo=lo, block_hi=lo + block, unmask_mode=api.UNMASK_FORCED)
-            steps.append((kw, force.to(device)))
+            steps.append((kw, base, (lo, block, r)))
             t += 1
     return steps
 
@@ -338,11 +332,14 @@ def run_schedule(model, state, tok0, steps, ws):
     state.c.bnd_cur = 0
     if state.force is not None:
         state.force.zero_()
-    for kw, force in steps:
-        # the schedule's marks; rows the lock rule has already locked stay locked
-        torch.maximum(state.force, force, out=state.force)
-        if kw.get("unmask_mode") == api.UNMASK_FORCED:
+    for kw, force, plan in steps:
+        if plan is not None:
+            # a fresh base (prompt excluded), then this round's positions marked on the device
             state.force.copy_(force)
+            api.dus_mark(state.force, plan[0], plan[1], plan[2])
+        else:
+            # the schedule's marks; rows the lock rule has already locked stay locked
+            torch.maximum(state.force, force, out=state.force)
         api.skip_step(model, state, api.step_cfg(ws=ws, **kw))
 
 

@@ -216,6 +216,22 @@ int dllm_confidence_kl(const float *logits, float *logits_prev, const int32_t *r
                        int32_t V, int32_t exclude_id, int32_t have_prev, float *conf,
                        int32_t *argmax, float *kl, void *stream);
 
+/* Device planner of one dilated unmasking round ([DUS] technical summary
+ * section 2: a block of `block` positions is decoded in R = ceil(log_a block)
+ * rounds, round r taking the offsets that are multiples of a^(R-1-r) and were
+ * not taken by an earlier, coarser round).  For every sequence b and every
+ * offset o of round `round` of the block [lo, lo + block):
+ *     force[b*S + lo + o] = max(force[b*S + lo + o], mark).
+ * Other positions are untouched.  With mark = 1 the round's positions join the
+ * active set of the next dllm_skip_step (whatever their score) and are the ones
+ * DLLM_UNMASK_FORCED unmasks; a locked position (2) stays locked.
+ *  force: device [B, S] u8.  rounds: R, or 0 for ceil(log_a block) (1 for a
+ *  single position).  a >= 2, 0 <= round < R, 1 <= mark <= 255,
+ *  0 <= lo, lo + block <= S.  Invalid arguments return DLLM_EINVAL/ESHAPE
+ *  before any launch. */
+int dllm_dus_mark(uint8_t *force, int32_t B, int32_t S, int32_t lo, int32_t block, int32_t a,
+                  int32_t rounds, int32_t round, int32_t mark, void *stream);
+
 /* One full denoising iteration ([ES] 2.1; [SL] 2.1): embed, dense layers
  * below the boundary, score + select at the boundary, sparse layers,
  * final-hidden scatter, LM head on the active rows, confidence/KL, then the

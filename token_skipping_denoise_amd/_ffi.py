@@ -16,7 +16,7 @@ UNMASK_CONF, UNMASK_FORCED = 0, 1
 EXPORTED = (
     "dllm_workspace_size", "dllm_score_select", "dllm_gather_rows", "dllm_scatter_rows",
     "dllm_layer_sparse", "dllm_confidence_kl", "dllm_skip_step", "dllm_status_string", "dllm_version",
-    "dllm_set_timing",
+    "dllm_set_timing", "dllm_dus_mark",
 )
 TK_NONE, TK_QKV, TK_ATTN, TK_O, TK_FFN_UP, TK_FFN_DOWN, TK_LM_HEAD, TK_VOCAB, TK_SCORE, TK_SELECT = range(10)
 
@@ -87,6 +87,9 @@ def load(path: str = LIB_PATH) -> ctypes.CDLL:
     lib.dllm_confidence_kl.restype = c_int32
     lib.dllm_confidence_kl.argtypes = [c_void_p, c_void_p, c_void_p, c_int32, c_int32, c_int32, c_int32,
                                        c_void_p, c_void_p, c_void_p, c_void_p]
+    lib.dllm_dus_mark.restype = c_int32
+    lib.dllm_dus_mark.argtypes = [c_void_p, c_int32, c_int32, c_int32, c_int32, c_int32, c_int32, c_int32, c_int32,
+                                  c_void_p]
     lib.dllm_skip_step.restype = c_int32
     lib.dllm_skip_step.argtypes = [POINTER(ModelC), POINTER(StateC), POINTER(StepCfg), c_void_p]
     lib.dllm_status_string.restype = ctypes.c_char_p

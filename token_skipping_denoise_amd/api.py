@@ -103,6 +103,16 @@ def confidence_kl(logits, row_pos, conf, argmax, *, kl=None, logits_prev=None, e
     _check(st, "dllm_confidence_kl")
 
 
+def dus_mark(force, lo: int, block: int, round: int, *, a: int = 2, rounds: int = 0, mark: int = FORCE_ON):
+    """Marks the positions of one dilated unmasking round in force [B, S] u8 (device, in place)."""
+    if force.dtype != torch.uint8 or force.dim() != 2:
+        raise DllmError("force must be a [B, S] uint8 tensor")
+    B, S = force.shape
+    st = _lib().dllm_dus_mark(_ptr(force), B, S, int(lo), int(block), int(a), int(rounds), int(round), int(mark),
+                              _stream(force.device))
+    _check(st, "dllm_dus_mark")
+
+
 class Model:
     """Device weights in the C ABI layout plus the dllm_model struct.
 

@@ -328,6 +328,34 @@ int dllm_confidence_kl(const float* logits, float* logits_prev, const int32_t* r
   return DLLM_OK;
 }
 
+int dllm_dus_mark(uint8_t* force, int32_t B, int32_t S, int32_t lo, int32_t block, int32_t a, int32_t rounds,
+                  int32_t round, int32_t mark, void* stream) {
+  if (!force) return DLLM_EINVAL;
+  if (B < 1 || S < 1 || block < 1 || lo < 0 || (long)lo + block > S) return DLLM_ESHAPE;
+  if (a < 2 || rounds < 0 || mark < 1 || mark > 255) return DLLM_EINVAL;
+  // R = ceil(log_a block) rounds by default (one round for a single position)
+  int R = rounds;
+  if (R == 0) {
+    long p = 1;
+    while (p < block) {
+      p *= a;
+      ++R;
+    }
+    if (R == 0) R = 1;
+  }
+  if (round < 0 || round >= R) return DLLM_EINVAL;
+  // a^(R-1-round) and a^(R-round), clamped to the block length (no overflow for large R)
+  auto clamped_pow = [&](int e) -> int {
+    long p = 1;
+    for (int i = 0; i < e && p < block; ++i) p *= a;
+    return (int)(p < block ? p : block);
+  };
+  const int stride = clamped_pow(R - 1 - round);
+  const int stride_prev = round == 0 ? 0 : clamped_pow(R - round);
+  DLLM_TRY(launch_dus_mark(force, B, S, lo, block, stride, stride_prev, (uint8_t)mark, (hipStream_t)stream));
+  return DLLM_OK;
+}
+
 int dllm_skip_step(const dllm_model* model, dllm_state* state, const dllm_step_cfg* cfg, void* stream) {
   int st = check_model(model);
   if (st) return st;

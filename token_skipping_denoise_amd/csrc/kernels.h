@@ -83,5 +83,8 @@ hipError_t launch_unmask(int32_t* tokens, const float* conf, const int32_t* argm
 // tokens[b, i] = argmax[b, i] for masked i in [lo, hi) with force[b, i] == 1.
 hipError_t launch_unmask_forced(int32_t* tokens, const uint8_t* force, const int32_t* argmax, int B, int S,
                                 int mask_id, int lo, int hi, hipStream_t s);
+// force[b][lo + o] = max(force, mark) for the offsets o of one dilated round (post.hip).
+hipError_t launch_dus_mark(uint8_t* force, int B, int S, int lo, int block, int stride, int stride_prev, uint8_t mark,
+                           hipStream_t s);
 
 }  // namespace dllm

@@ -109,4 +109,28 @@ hipError_t launch_unmask_forced(int32_t* tokens, const uint8_t* force, const int
   return hipGetLastError();
 }
 
+// Dilated unmasking plan (DUS summary, technical summary section 2): round r of a block takes
+// the offsets on the stride-a^(R-1-r) grid that the coarser grid of round r-1 (stride a times
+// larger) did not already take.  `stride_prev` is 0 for round 0; both strides are clamped to the
+// block length, which keeps the membership test unchanged (only offset 0 is a multiple).
+__global__ void k_dus_mark(uint8_t* __restrict__ force, int B, int S, int lo, int block, int stride, int stride_prev,
+                           uint8_t mark) {
+  const long e = blockIdx.x * (long)blockDim.x + threadIdx.x;
+  if (e >= (long)B * block) return;
+  const int b = (int)(e / block), off = (int)(e - (long)b * block);
+  const bool in_round = off % stride == 0 && (stride_prev == 0 || off % stride_prev != 0);
+  if (!in_round) return;
+  uint8_t* f = force + (long)b * S + lo + off;
+  if (*f < mark) *f = mark;
+}
+
+hipError_t launch_dus_mark(uint8_t* force, int B, int S, int lo, int block, int stride, int stride_prev, uint8_t mark,
+                           hipStream_t s) {
+  const long n = (long)B * block;
+  if (n <= 0) return hipSuccess;
+  hipLaunchKernelGGL(k_dus_mark, dim3((unsigned)((n + 255) / 256)), dim3(256), 0, s, force, B, S, lo, block, stride,
+                     stride_prev, mark);
+  return hipGetLastError();
+}
+
 }  // namespace dllm
