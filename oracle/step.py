@@ -33,7 +33,7 @@ from .numerics import store_fn
 from .post import surelock_update, unmask_forced, unmask_topn
 from .selection import FORCE_EXCLUDED, select_thresh_cap, select_topk
 from .transformer import layer_rows, lm_logits
-from .vocab import conf_kl
+from .vocab import conf_kl, kl_state_value
 
 SEL_TOPK, SEL_THRESH_CAP, SEL_UNLOCKED = 0, 1, 2
 UNMASK_CONF, UNMASK_FORCED = 0, 1
@@ -90,16 +90,18 @@ class OracleState:
     logits_prev: np.ndarray | None
     force: np.ndarray
     have_prev: bool = False
+    kl_state_bf16: bool = False  # previous logits kept rounded to bf16 (compact KL state)
 
     def copy(self) -> "OracleState":
         return OracleState(
             self.tokens.copy(), [k.copy() for k in self.k_cache], [v.copy() for v in self.v_cache],
             None if self.h_bnd_prev is None else self.h_bnd_prev.copy(), self.h_fin.copy(),
             self.conf.copy(), self.kl.copy(), self.argmax.copy(),
-            None if self.logits_prev is None else self.logits_prev.copy(), self.force.copy(), self.have_prev)
+            None if self.logits_prev is None else self.logits_prev.copy(), self.force.copy(), self.have_prev,
+            self.kl_state_bf16)
 
 
-def new_state(model: OracleModel, tokens: np.ndarray, track_kl: bool) -> OracleState:
+def new_state(model: OracleModel, tokens: np.ndarray, track_kl: bool, kl_state_bf16: bool = False) -> OracleState:
     B, S = tokens.shape
     w = model.weights
     d = w["embed"].shape[1]
@@ -118,6 +120,7 @@ def new_state(model: OracleModel, tokens: np.ndarray, track_kl: bool) -> OracleS
         argmax=np.zeros((B, S), dtype=np.int64),
         logits_prev=np.zeros((B * S, V)) if track_kl else None,
         force=np.zeros((B, S), dtype=np.uint8),
+        kl_state_bf16=kl_state_bf16,
     )
 
 
@@ -178,12 +181,12 @@ def skip_step(model: OracleModel, st: OracleState, cfg: StepCfg) -> tuple[Oracle
     hf[rows] = x
     z = lm_logits(x, w["final_norm"], w["lm_head"], model.eps, store)
     zp = None if (st.logits_prev is None or not st.have_prev) else st.logits_prev[rows]
-    conf, arg, kl = conf_kl(z, zp, model.mask_id)
+    conf, arg, kl = conf_kl(z, zp, model.mask_id, st.kl_state_bf16)
     st.conf.reshape(-1)[rows] = conf
     st.argmax.reshape(-1)[rows] = arg
     st.kl.reshape(-1)[rows] = kl
     if st.logits_prev is not None:
-        st.logits_prev[rows] = z
+        st.logits_prev[rows] = kl_state_value(z, st.kl_state_bf16)
     if cfg.lock_kl_eps >= 0:
         st.force = surelock_update(st.force.reshape(-1), rows, st.conf.reshape(-1), st.kl.reshape(-1),
                                    st.have_prev, cfg.lock_kl_eps, cfg.lock_conf_min).reshape(B, S)

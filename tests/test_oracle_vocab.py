@@ -69,3 +69,55 @@ def test_identical_logits_kl_exactly_zero_batch():
     assert np.all(kl == 0.0)
     _, _, kl_none = conf_kl(z, None)
     assert np.all(np.isinf(kl_none))
+
+
+# ---- compact KL state: previous logits kept in bf16 -------------------------------------------
+
+def _bf16_grid(x):
+    from oracle.numerics import round_bf16
+    return round_bf16(x)
+
+
+def test_bf16_state_identical_logits_give_zero_kl():
+    """The state holds bf16(z); the next pass over the same fp32 logits compares bf16(z) with it: 0."""
+    from oracle.vocab import kl_state_value
+    for V in (2, 17, 1000):
+        z = RNG.normal(0, 3, V).astype(np.float32).astype(np.float64)
+        state = kl_state_value(z, prev_bf16=True)
+        _, _, kl = conf_kl_row(z, state, exclude_id=V // 2 if V > 2 else -1, prev_bf16=True)
+        assert kl == 0.0
+
+
+def test_bf16_state_reduces_to_fp32_path_on_bf16_logits():
+    """When every logit is a bf16 value the rounding is the identity: both state precisions agree exactly."""
+    for _ in range(5):
+        V = int(RNG.integers(2, 600))
+        z = _bf16_grid(RNG.normal(0, 2, V))
+        zp = _bf16_grid(RNG.normal(0, 2, V))
+        a = conf_kl_row(z, zp, exclude_id=-1, prev_bf16=False)
+        b = conf_kl_row(z, zp, exclude_id=-1, prev_bf16=True)
+        assert a == b
+
+
+def test_bf16_state_kl_matches_scipy_on_rounded_logits():
+    """KL(softmax(bf16(z)) || softmax(z')) computed by scipy's relative entropy; conf/argmax unrounded."""
+    for _ in range(5):
+        V = int(RNG.integers(3, 800))
+        z = RNG.normal(0, 2, V)
+        zp = _bf16_grid(RNG.normal(0, 2, V))
+        excl = int(RNG.integers(0, V))
+        conf, arg, kl = conf_kl_row(z, zp, exclude_id=excl, prev_bf16=True)
+        keep = np.arange(V) != excl
+        p = scipy.special.softmax(_bf16_grid(z[keep]))
+        q = scipy.special.softmax(zp[keep])
+        assert kl == pytest.approx(scipy.stats.entropy(p, q), rel=1e-9, abs=1e-13)
+        conf32, arg32, _ = conf_kl_row(z, zp, exclude_id=excl, prev_bf16=False)
+        assert conf == conf32 and arg == arg32
+
+
+def test_bf16_state_value_is_rne_rounding():
+    from oracle.vocab import kl_state_value
+    # 1 + 2^-8 is a tie between 1 and 1 + 2^-7 (bf16 spacing at 1): rounds to even (1.0)
+    z = np.array([1.0 + 2.0 ** -8, 1.0 + 3 * 2.0 ** -8, -2.5, 0.0])
+    assert kl_state_value(z, prev_bf16=True).tolist() == [1.0, 1.0 + 2.0 ** -6, -2.5, 0.0]
+    assert kl_state_value(z, prev_bf16=False).tolist() == z.tolist()
