@@ -326,7 +326,7 @@ def long_schedule(dims, device, k_active=205, block=16, refresh_every=16):
     return steps
 
 
-def run_schedule(model, state, tok0, steps, ws):
+def run_schedule(model, state, tok0, steps, ws, after_step=None):
     state.tokens.copy_(tok0)
     state.c.have_prev = 0
     state.c.bnd_cur = 0
@@ -341,6 +341,41 @@ def run_schedule(model, state, tok0, steps, ws):
             # the schedule's marks; rows the lock rule has already locked stay locked
             torch.maximum(state.force, force, out=state.force)
         api.skip_step(model, state, api.step_cfg(ws=ws, **kw))
+        if after_step is not None:
+            after_step(kw)
+
+
+def vocab_pass_stats(lib, model, state, tok0, steps, ws, dims, state_bytes):
+    """Times the confidence/KL vocabulary pass over one run of the schedule.  Its algorithmic
+    bytes per live row are 4 V (fp32 logits read) + 2 V state_bytes (previous logits read and
+    rewritten); live rows are all B*S on a full step, else the selected ones."""
+    ev = HipEvents(len(steps) + 1)
+    rows = []
+
+    def count_rows(kw):
+        if kw.get("full_step"):
+            rows.append(dims.B * dims.S)
+        else:
+            rows.append(int(state.n_active.sum()))
+
+    timing = _ffi.Timing(_ffi.TK_VOCAB, 0, ev.n, 0, ctypes.cast(ev.start, ctypes.POINTER(ctypes.c_void_p)),
+                         ctypes.cast(ev.stop, ctypes.POINTER(ctypes.c_void_p)))
+    lib.dllm_set_timing(ctypes.byref(timing))
+    try:
+        run_schedule(model, state, tok0, steps, ws, after_step=count_rows)
+        torch.cuda.synchronize()
+    finally:
+        lib.dllm_set_timing(None)
+    n = timing.count
+    durs = ev.elapsed_ms(n)
+    ev.close()
+    per_row = (4.0 + 2.0 * state_bytes) * dims.vocab
+    total_bytes = per_row * sum(rows[:n])
+    total_us = sum(durs) * 1e3
+    gbps = total_bytes / (total_us * 1e-6) / 1e9
+    return {"kernel": "vocab_conf_kl", "launches": n, "avg_us": round(total_us / max(n, 1), 2),
+            "live_rows": int(sum(rows[:n])), "bytes_per_row": int(per_row), "bytes": int(total_bytes),
+            "gbps": round(gbps, 1), "bound": "hbm", "frac": round(gbps / HBM_PEAK_GBS, 4)}
 
 
 def extra_workload(args):
@@ -360,7 +395,7 @@ def extra_workload(args):
     model = api.Model(w, dims.n_heads, dims.n_kv_heads, dims.mask_id)
     tok0 = workloads.initial_tokens(dims, device=dev)
     track_kl = args.workload == "dream"
-    state = api.State(model, tok0.clone(), k_max=k_max, track_kl=track_kl)
+    state = api.State(model, tok0.clone(), k_max=k_max, track_kl=track_kl, kl_state=args.kl_state)
     ws = api.alloc_workspace(model, dims.B, dims.S, k_max)
     steps = dream_schedule(dims, dev) if args.workload == "dream" else long_schedule(dims, dev)
     torch.cuda.synchronize()
@@ -378,6 +413,9 @@ def extra_workload(args):
     if not args.no_kernel_timing and args.workload == "long":
         lib = _ffi.load()
         kernels = kernel_table_schedule(lib, model, state, tok0, steps, ws, dims, dims.B * k_max)
+    elif not args.no_kernel_timing and args.workload == "dream":
+        lib = _ffi.load()
+        kernels = [vocab_pass_stats(lib, model, state, tok0, steps, ws, dims, 2 if args.kl_state == "bf16" else 4)]
     line = {
         "metric": "denoised tokens/s at 8B shapes on 1 MI355X",
         "value": round(gen_tokens * args.steps / elapsed, 2),
@@ -393,7 +431,8 @@ def extra_workload(args):
         "data": "synthetic (seeded random-init weights N(0,0.02); prompt tokens uniform)",
         "config": {"workload": desc, "batch": dims.B, "seq_len": dims.S, "layers": dims.n_layers,
                    "hidden": dims.d, "vocab": dims.vocab, "iterations_per_step": len(steps),
-                   "setup_s": round(t_setup, 1), "launch": "eager"},
+                   "setup_s": round(t_setup, 1), "launch": "eager",
+                   "kl_state": args.kl_state if track_kl else None},
         "kernels": kernels,
     }
     print(json.dumps(line), flush=True)
@@ -446,6 +485,8 @@ def main():
     ap.add_argument("--workload", choices=("llada", "dream", "long"), default="llada",
                     help="llada: the 32-layer early-skip generation (default); dream: Dream-GQA lock ramp; "
                          "long: long-context dilated run")
+    ap.add_argument("--kl-state", choices=("f32", "bf16"), default="f32",
+                    help="precision of the previous logits the KL lock rule compares against (dream workload)")
     ap.add_argument("--calibrate-copy", action="store_true",
                     help="only copy a 1 GiB buffer once (reference for the HBM byte counters) and exit")
     args = ap.parse_args()

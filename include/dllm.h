@@ -137,13 +137,18 @@ typedef struct {
   float *conf;            /* device [B, S] max softmax probability */
   float *kl;              /* device [B, S] local KL (+inf before a previous posterior exists) */
   int32_t *argmax;        /* device [B, S] most likely non-mask token */
-  float *logits_prev;     /* device [B*S, V] previous logits, or NULL (then KL is not tracked) */
+  void *logits_prev;      /* device [B*S, V] previous logits in logits_prev_dtype, or NULL (then KL is
+                             not tracked) */
   uint8_t *force;         /* device [B, S] dllm_force values, or NULL (all 0) */
   int32_t *idx;           /* device [B, k_max] out: active positions (ascending, -1 padded) */
   int32_t *n_active;      /* device [B] out */
   int32_t k_max;          /* row stride of idx and of the active-row buffers (1..S); a full
                              step leaves idx / n_active unchanged */
   int32_t have_prev;      /* 0 until the first step has run */
+  int32_t logits_prev_dtype; /* DLLM_F32, or DLLM_BF16 for the compact KL state: the previous logits
+                             are stored rounded to bf16 (RNE) and the KL compares the bf16-rounded
+                             current logits with them, so identical logits still give KL = 0;
+                             conf and argmax always come from the fp32 logits */
 } dllm_state;
 
 typedef struct {
@@ -208,11 +213,13 @@ int dllm_layer_sparse(const dllm_model *model, int32_t layer, void *x_act, const
  * item 1: D = KL(p_t || p_{t-1}); [ES] Eq. 1 confidence c).
  *  logits: device [R, V] fp32; row_pos: device [R], row r belongs to flat
  *  position row_pos[r] = b*S + i, or -1 (dead row, skipped).
- *  logits_prev: device [B*S, V] or NULL.  When non-NULL the row's previous
- *  logits are read (if have_prev) and then overwritten with logits[r].
+ *  logits_prev: device [B*S, V] of prev_dtype (DLLM_F32 or DLLM_BF16) or NULL.
+ *  When non-NULL the row's previous logits are read (if have_prev) and then
+ *  overwritten with logits[r] (rounded to bf16 for a bf16 state, where the
+ *  KL compares the bf16-rounded current logits with the stored ones).
  *  conf, argmax: device [B*S]; kl: device [B*S] or NULL (+inf without have_prev).
  *  exclude_id: vocabulary id treated as -inf (the mask token), or -1. */
-int dllm_confidence_kl(const float *logits, float *logits_prev, const int32_t *row_pos, int32_t R,
+int dllm_confidence_kl(const float *logits, void *logits_prev, int32_t prev_dtype, const int32_t *row_pos, int32_t R,
                        int32_t V, int32_t exclude_id, int32_t have_prev, float *conf,
                        int32_t *argmax, float *kl, void *stream);
 

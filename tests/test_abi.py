@@ -74,6 +74,14 @@ def test_argument_validation_returns_before_launch(lib):
     # k_max > S
     assert lib.dllm_gather_rows(fake, fake, fake, 1, 8, 9, 8, 1, fake, None) == 2
     # confidence pass with a bad exclude id
-    assert lib.dllm_confidence_kl(fake, None, fake, 4, 10, 10, 0, fake, fake, None, None) == 2
+    assert lib.dllm_confidence_kl(fake, None, 0, fake, 4, 10, 10, 0, fake, fake, None, None) == 2
+    # confidence pass with an unknown previous-logit precision
+    assert lib.dllm_confidence_kl(fake, fake, 7, fake, 4, 10, 3, 0, fake, fake, None, None) == 3
+    # dilated round planner: missing force map, block past S, base a < 2, round >= R, mark 0
+    assert lib.dllm_dus_mark(None, 1, 10, 0, 4, 2, 0, 0, 1, None) == 1
+    assert lib.dllm_dus_mark(fake, 1, 10, 8, 4, 2, 0, 0, 1, None) == 2
+    assert lib.dllm_dus_mark(fake, 1, 10, 0, 4, 1, 0, 0, 1, None) == 1
+    assert lib.dllm_dus_mark(fake, 1, 10, 0, 4, 2, 0, 2, 1, None) == 1
+    assert lib.dllm_dus_mark(fake, 1, 10, 0, 4, 2, 0, 0, 0, None) == 1
     # skip step without a model
     assert lib.dllm_skip_step(None, None, None, None) == 1

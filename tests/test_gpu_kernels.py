@@ -6,7 +6,7 @@ import torch
 import synth
 from oracle.importance import FLT_MAX, importance_score
 from oracle.selection import select_thresh_cap, select_topk
-from oracle.vocab import conf_kl
+from oracle.vocab import conf_kl, kl_state_value
 from tests.gpu_util import DEV, assert_close, np64, selection_gap
 from token_skipping_denoise_amd import api
 
@@ -172,3 +172,36 @@ def test_confidence_kl_parity(V, R, exclude):
     api.confidence_kl(zd, rpd, conf, arg, kl=kl, logits_prev=None, exclude_id=exclude, have_prev=False)
     torch.cuda.synchronize()
     assert torch.all(torch.isinf(kl.cpu()[pos]))
+
+
+@pytest.mark.parametrize("V,R,exclude", [(1024, 5, 1023), (126464, 6, 126463), (1001, 9, -1), (152064, 3, 7)])
+def test_confidence_kl_bf16_state_parity(V, R, exclude):
+    """Compact KL state: previous logits in bf16, KL between bf16(z) and the state; state written as bf16(z)."""
+    print(f"conf_kl bf16 state V={V} R={R}", flush=True)
+    B, S = 2, 8
+    z = synth.normal(synth.seed_of(V, 3), (R, V), 2.0, torch.float32)
+    zp_all = synth.normal(synth.seed_of(V, 4), (B * S, V), 2.0, torch.float32).to(torch.bfloat16)
+    row_pos = torch.tensor([(5 * r + 2) % (B * S) for r in range(R)], dtype=torch.int32)
+    row_pos[1] = -1                                     # a dead row
+    zp_all[row_pos[0]] = z[0].to(torch.bfloat16)        # the state of identical logits -> KL exactly 0
+    zp_all[row_pos[2]] = (z[2] + 3.0).to(torch.bfloat16)
+    zd, zpd, rpd = z.to(DEV), zp_all.clone().to(DEV), row_pos.to(DEV)
+    conf = torch.full((B * S,), -1.0, device=DEV)
+    arg = torch.full((B * S,), -1, dtype=torch.int32, device=DEV)
+    kl = torch.full((B * S,), -1.0, device=DEV)
+    api.confidence_kl(zd, rpd, conf, arg, kl=kl, logits_prev=zpd, exclude_id=exclude, have_prev=True)
+    torch.cuda.synchronize()
+    live = [r for r in range(R) if row_pos[r] >= 0]
+    pos = row_pos[live].long()
+    wc, wa, wk = conf_kl(np64(z)[live], np64(zp_all)[pos.numpy()], exclude, prev_bf16=True)
+    assert_close(np64(conf)[pos], wc, 1e-5, "conf")
+    assert np.array_equal(arg.cpu().numpy()[pos], wa)
+    np.testing.assert_allclose(np64(kl)[pos], wk, rtol=1e-4, atol=2e-5)
+    assert float(kl[row_pos[0]]) == 0.0
+    # the state now holds bf16(z) (RNE) bit for bit; the dead row's slot is untouched
+    zpc = zpd.cpu()
+    for r in live:
+        want = torch.from_numpy(kl_state_value(np64(z[r:r + 1]), prev_bf16=True)[0]).to(torch.bfloat16)
+        assert torch.equal(zpc[row_pos[r]].view(torch.int16), want.view(torch.int16))
+    untouched = sorted(set(range(B * S)) - set(pos.tolist()))
+    assert torch.equal(zpc[untouched].view(torch.int16), zp_all[untouched].view(torch.int16))

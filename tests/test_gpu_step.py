@@ -150,14 +150,18 @@ def test_bf16_early_skip_iteration(b_lay, vocab):
                  2e-2, "h_bnd")
 
 
-def test_bf16_gqa_surelock_iteration():
-    dims = workloads.shrink(workloads.DREAM, n_layers=2, d=256, n_heads=4, n_kv_heads=1, d_ff=384, vocab=1000,
+@pytest.mark.parametrize("kl_state,vocab", [("f32", 1000), ("bf16", 1000), ("bf16", 16384)])
+def test_bf16_gqa_surelock_iteration(kl_state, vocab):
+    """SureLock iteration; the previous logits kept in fp32 or in bf16 (with V = 16384 the vocabulary
+    pass splits every row into slices and merges them)."""
+    print(f"surelock kl_state={kl_state} V={vocab}", flush=True)
+    dims = workloads.shrink(workloads.DREAM, n_layers=2, d=256, n_heads=4, n_kv_heads=1, d_ff=384, vocab=vocab,
                             B=3, S=80, prompt=40)
     gm, om = _models(dims, std=0.05)
     tok = workloads.initial_tokens(dims)
-    gs = api.State(gm, tok.to(DEV), k_max=dims.S, track_kl=True)
+    gs = api.State(gm, tok.to(DEV), k_max=dims.S, track_kl=True, kl_state=kl_state)
     ws = api.alloc_workspace(gm, dims.B, dims.S, dims.S)
-    os_ = new_state(om, tok.numpy(), track_kl=True)
+    os_ = new_state(om, tok.numpy(), track_kl=True, kl_state_bf16=(kl_state == "bf16"))
     api.skip_step(gm, gs, api.step_cfg(0, True, ws=ws))
     os_, _ = skip_step(om, os_, StepCfg(boundary_layer=0, full_step=True))
     # lock a seeded 40% of positions per sequence on both sides; change three tokens

@@ -44,7 +44,8 @@ class StateC(Structure):
     _fields_ = [("tokens", c_void_p), ("k_cache", POINTER(c_void_p)), ("v_cache", POINTER(c_void_p)),
                 ("h_bnd", c_void_p * 2), ("bnd_cur", c_int32), ("h_fin", c_void_p), ("conf", c_void_p),
                 ("kl", c_void_p), ("argmax", c_void_p), ("logits_prev", c_void_p), ("force", c_void_p),
-                ("idx", c_void_p), ("n_active", c_void_p), ("k_max", c_int32), ("have_prev", c_int32)]
+                ("idx", c_void_p), ("n_active", c_void_p), ("k_max", c_int32), ("have_prev", c_int32),
+                ("logits_prev_dtype", c_int32)]
 
 
 class StepCfg(Structure):
@@ -85,7 +86,7 @@ def load(path: str = LIB_PATH) -> ctypes.CDLL:
     lib.dllm_layer_sparse.argtypes = [POINTER(ModelC), c_int32, c_void_p, c_void_p, c_void_p, c_int32, c_void_p,
                                       c_void_p, c_void_p, c_size_t, c_void_p]
     lib.dllm_confidence_kl.restype = c_int32
-    lib.dllm_confidence_kl.argtypes = [c_void_p, c_void_p, c_void_p, c_int32, c_int32, c_int32, c_int32,
+    lib.dllm_confidence_kl.argtypes = [c_void_p, c_void_p, c_int32, c_void_p, c_int32, c_int32, c_int32, c_int32,
                                        c_void_p, c_void_p, c_void_p, c_void_p]
     lib.dllm_dus_mark.restype = c_int32
     lib.dllm_dus_mark.argtypes = [c_void_p, c_int32, c_int32, c_int32, c_int32, c_int32, c_int32, c_int32, c_int32,

@@ -97,8 +97,14 @@ def scatter_rows(src, idx, n_active, dst):
 
 
 def confidence_kl(logits, row_pos, conf, argmax, *, kl=None, logits_prev=None, exclude_id=-1, have_prev=False):
+    """logits_prev: fp32 or bf16 [B*S, V] state (its dtype selects the state precision), or None."""
     R, V = logits.shape
-    st = _lib().dllm_confidence_kl(_ptr(logits), _ptr(logits_prev), _ptr(row_pos), R, V, int(exclude_id),
+    prev_dtype = DLLM_F32
+    if logits_prev is not None:
+        if logits_prev.dtype not in (torch.float32, torch.bfloat16):
+            raise DllmError("logits_prev must be float32 or bfloat16")
+        prev_dtype = _dtype_code(logits_prev)
+    st = _lib().dllm_confidence_kl(_ptr(logits), _ptr(logits_prev), prev_dtype, _ptr(row_pos), R, V, int(exclude_id),
                                    int(bool(have_prev)), _ptr(conf), _ptr(argmax), _ptr(kl), _stream(logits.device))
     _check(st, "dllm_confidence_kl")
 
@@ -187,7 +193,11 @@ def layer_sparse(model: Model, layer: int, x_act, idx, n_active, k_cache, v_cach
 class State:
     """Persistent device state of one generation run (tensors + dllm_state struct)."""
 
-    def __init__(self, model: Model, tokens: torch.Tensor, k_max: int, track_kl: bool = False, with_force: bool = True):
+    def __init__(self, model: Model, tokens: torch.Tensor, k_max: int, track_kl: bool = False, with_force: bool = True,
+                 kl_state: str = "f32"):
+        """kl_state: "f32" or "bf16", the precision the previous logits are kept in (with track_kl)."""
+        if kl_state not in ("f32", "bf16"):
+            raise DllmError("kl_state must be 'f32' or 'bf16'")
         B, S = tokens.shape
         V, d, Hq, Hkv, D, F, L = model.dims_tuple
         dev, dt = model.device, model.dtype
@@ -200,7 +210,8 @@ class State:
         self.conf = torch.zeros((B, S), dtype=torch.float32, device=dev)
         self.kl = torch.full((B, S), float("inf"), dtype=torch.float32, device=dev)
         self.argmax = torch.zeros((B, S), dtype=torch.int32, device=dev)
-        self.logits_prev = torch.zeros((B * S, V), dtype=torch.float32, device=dev) if track_kl else None
+        prev_dt = torch.bfloat16 if kl_state == "bf16" else torch.float32
+        self.logits_prev = torch.zeros((B * S, V), dtype=prev_dt, device=dev) if track_kl else None
         self.force = torch.zeros((B, S), dtype=torch.uint8, device=dev) if with_force else None
         self.idx = torch.full((B, k_max), -1, dtype=torch.int32, device=dev)
         self.n_active = torch.zeros((B,), dtype=torch.int32, device=dev)
@@ -223,6 +234,7 @@ class State:
         self.c.n_active = _ptr(self.n_active)
         self.c.k_max = int(k_max)
         self.c.have_prev = 0
+        self.c.logits_prev_dtype = DLLM_BF16 if kl_state == "bf16" else DLLM_F32
 
     @property
     def h_bnd_prev(self) -> torch.Tensor:

@@ -319,12 +319,14 @@ int dllm_layer_sparse(const dllm_model* model, int32_t layer, void* x_act, const
   return run_layer(c, layer, x_act, n_active, row_pos, k_max, k_cache, v_cache, nullptr);
 }
 
-int dllm_confidence_kl(const float* logits, float* logits_prev, const int32_t* row_pos, int32_t R, int32_t V,
-                       int32_t exclude_id, int32_t have_prev, float* conf, int32_t* argmax, float* kl, void* stream) {
+int dllm_confidence_kl(const float* logits, void* logits_prev, int32_t prev_dtype, const int32_t* row_pos, int32_t R,
+                       int32_t V, int32_t exclude_id, int32_t have_prev, float* conf, int32_t* argmax, float* kl,
+                       void* stream) {
   if (!logits || !row_pos || !conf || !argmax) return DLLM_EINVAL;
+  if (prev_dtype != DLLM_F32 && prev_dtype != DLLM_BF16) return DLLM_EDTYPE;
   if (R < 0 || V < 2 || exclude_id >= V) return DLLM_ESHAPE;
-  DLLM_TRY(launch_conf_kl(logits, logits_prev, row_pos, R, V, exclude_id, have_prev, conf, argmax, kl, nullptr,
-                          (hipStream_t)stream));
+  DLLM_TRY(launch_conf_kl(logits, logits_prev, prev_dtype, row_pos, R, V, exclude_id, have_prev, conf, argmax, kl,
+                          nullptr, (hipStream_t)stream));
   return DLLM_OK;
 }
 
@@ -360,6 +362,7 @@ int dllm_skip_step(const dllm_model* model, dllm_state* state, const dllm_step_c
   int st = check_model(model);
   if (st) return st;
   if (!state || !cfg) return DLLM_EINVAL;
+  if (state->logits_prev_dtype != DLLM_F32 && state->logits_prev_dtype != DLLM_BF16) return DLLM_EDTYPE;
   const dllm_dims& d = model->dims;
   const int L = d.n_layers, B = d.B, S = d.S;
   const int full = cfg->full_step ? 1 : 0;
@@ -471,8 +474,8 @@ int dllm_skip_step(const dllm_model* model, dllm_state* state, const dllm_step_c
   }
   {
     TimedRegion t(DLLM_TK_VOCAB, R, c.s);
-    DLLM_TRY(launch_conf_kl(logits, state->logits_prev, rp, R, d.vocab, model->mask_id, state->have_prev,
-                            state->conf, state->argmax, state->kl, c.ws + c.L.vpart, c.s));
+    DLLM_TRY(launch_conf_kl(logits, state->logits_prev, state->logits_prev_dtype, rp, R, d.vocab, model->mask_id,
+                            state->have_prev, state->conf, state->argmax, state->kl, c.ws + c.L.vpart, c.s));
   }
   if (cfg->lock_kl_eps >= 0.f && state->have_prev)
     DLLM_TRY(launch_lock_update(rp, R, state->conf, state->kl, cfg->lock_kl_eps, cfg->lock_conf_min, state->force,

@@ -71,8 +71,9 @@ hipError_t launch_select(const float* score, const uint8_t* force, int B, int S,
 // Rows are split into vocabulary slices when few rows are active; `partial` needs
 // conf_kl_part_bytes(R, V) bytes (may be null when that is 0).
 size_t conf_kl_part_bytes(int R, int V);
-hipError_t launch_conf_kl(const float* logits, float* logits_prev, const int32_t* row_pos, int R, int V,
-                          int exclude_id, int have_prev, float* conf, int32_t* argmax, float* kl, void* partial,
+// logits_prev holds fp32 (prev_dtype 0) or bf16 (prev_dtype 1) previous logits, or is null.
+hipError_t launch_conf_kl(const float* logits, void* logits_prev, int prev_dtype, const int32_t* row_pos, int R,
+                          int V, int exclude_id, int have_prev, float* conf, int32_t* argmax, float* kl, void* partial,
                           hipStream_t s);
 
 // ---------------- post-step (post.hip) ----------------
