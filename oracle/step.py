@@ -17,10 +17,20 @@ Order of operations (ES-dLLM technical summary 2.1; SureLock 2.1):
   6. SureLock lock update and/or unmasking of the current block (by
      confidence, or the positions a dilated schedule plans for this round).
 
-Readings where the pages leave a step open: one boundary per iteration; the
-mask id is the last vocabulary entry and is excluded from softmax and argmax;
-a locked row (force == 2) skips every layer and the LM head, its cached K/V
-stay attendable; step 0 has no previous posterior, so its KL is +inf.
+Nested boundaries (ES-dLLM technical summary 2.1 item 2 selects at the start of
+a layer with a per-layer score I_{l,i}): optionally, at later layers
+n_1 < n_2 < ... the active rows are scored again, from the change of the hidden
+state entering that layer since it was last computed for the row (a per-layer
+cache, filled by full steps and updated for every row that reaches the layer),
+and only the top k_j of them continue.  A row dropped at layer n_j keeps the
+K/V it wrote below n_j; from n_j on it is skipped like any other row (cached
+K/V, final hidden state and statistics reused).
+
+Readings where the pages leave a step open: the mask id is the last vocabulary
+entry and is excluded from softmax and argmax; a locked row (force == 2) skips
+every layer and the LM head, its cached K/V stay attendable; step 0 has no
+previous posterior, so its KL is +inf; a nested selection is a top-k with the
+step's score settings (alpha, change term), forced rows kept first.
 """
 from __future__ import annotations
 
@@ -75,6 +85,7 @@ class StepCfg:
     block_lo: int = 0
     block_hi: int = 0
     unmask_mode: int = UNMASK_CONF
+    nested: tuple = ()             # ((layer, k), ...): later layers that narrow the active set
 
 
 @dataclass
@@ -91,6 +102,7 @@ class OracleState:
     force: np.ndarray
     have_prev: bool = False
     kl_state_bf16: bool = False  # previous logits kept rounded to bf16 (compact KL state)
+    h_nested: list = field(default_factory=list)  # per nested boundary: [B, S, d] hidden state entering it
 
     def copy(self) -> "OracleState":
         return OracleState(
@@ -98,10 +110,11 @@ class OracleState:
             None if self.h_bnd_prev is None else self.h_bnd_prev.copy(), self.h_fin.copy(),
             self.conf.copy(), self.kl.copy(), self.argmax.copy(),
             None if self.logits_prev is None else self.logits_prev.copy(), self.force.copy(), self.have_prev,
-            self.kl_state_bf16)
+            self.kl_state_bf16, [h.copy() for h in self.h_nested])
 
 
-def new_state(model: OracleModel, tokens: np.ndarray, track_kl: bool, kl_state_bf16: bool = False) -> OracleState:
+def new_state(model: OracleModel, tokens: np.ndarray, track_kl: bool, kl_state_bf16: bool = False,
+              n_nested: int = 0) -> OracleState:
     B, S = tokens.shape
     w = model.weights
     d = w["embed"].shape[1]
@@ -121,6 +134,7 @@ def new_state(model: OracleModel, tokens: np.ndarray, track_kl: bool, kl_state_b
         logits_prev=np.zeros((B * S, V)) if track_kl else None,
         force=np.zeros((B, S), dtype=np.uint8),
         kl_state_bf16=kl_state_bf16,
+        h_nested=[np.zeros((B, S, d)) for _ in range(n_nested)],
     )
 
 
@@ -148,6 +162,14 @@ def skip_step(model: OracleModel, st: OracleState, cfg: StepCfg) -> tuple[Oracle
     full = bool(cfg.full_step)
     if not full and st.h_bnd_prev is None:
         raise ValueError("a sparse step needs the previous boundary hidden state")
+    nested = [(int(nl), int(nk)) for nl, nk in cfg.nested]
+    if len(nested) > len(st.h_nested):
+        raise ValueError("the state holds fewer nested caches than the step names")
+    prev_layer = b_lay
+    for nl, nk in nested:
+        if not (prev_layer < nl < L) or nk < 0:
+            raise ValueError("nested layers must increase strictly after the boundary, below L; k >= 0")
+        prev_layer = nl
 
     x = w["embed"][st.tokens.reshape(-1)].reshape(B * S, d).copy()
     rows = np.arange(B * S)                   # flat b*S + i of the rows being computed
@@ -166,9 +188,37 @@ def skip_step(model: OracleModel, st: OracleState, cfg: StepCfg) -> tuple[Oracle
         rows = np.concatenate(sel).astype(np.int64)
         x = x[rows].copy()
 
+    nested_rows = []
+
+    def nested_boundary(j, k):
+        nonlocal rows, x
+        hn = st.h_nested[j].reshape(B * S, d)
+        if full:
+            hn[rows] = x
+            return
+        s = importance_score(x, hn[rows], st.conf.reshape(-1)[rows], st.kl.reshape(-1)[rows],
+                             alpha=cfg.score.alpha, var=cfg.score.var, conf_inverted=cfg.score.conf_inverted)
+        hn[rows] = x            # the hidden state entering this layer, kept for the next iteration
+        keep = []
+        for b in range(B):
+            in_b = (rows // S) == b
+            pos = rows[in_b] % S
+            sc = np.zeros(S)
+            sc[pos] = s[in_b]
+            fo = np.full(S, FORCE_EXCLUDED, dtype=np.uint8)   # only the active rows compete
+            fo[pos] = np.minimum(st.force[b, pos], 1)
+            keep.append(b * S + select_topk(sc, fo, k))
+        new_rows = np.concatenate(keep).astype(np.int64)
+        x = x[np.searchsorted(rows, new_rows)].copy()
+        rows = new_rows
+        nested_rows.append(rows.copy())
+
     for l in range(L):
         if l == b_lay:
             boundary()
+        for j, (nl, nk) in enumerate(nested):
+            if l == nl:
+                nested_boundary(j, nk)
         lw = w["layers"][l]
         x = layer_rows(lw, x, rows % S, rows // S, st.k_cache[l], st.v_cache[l],
                        n_heads=model.n_heads, n_kv_heads=model.n_kv_heads,
@@ -197,4 +247,4 @@ def skip_step(model: OracleModel, st: OracleState, cfg: StepCfg) -> tuple[Oracle
             st.tokens = unmask_topn(st.tokens, st.conf, st.argmax, model.mask_id,
                                     cfg.block_lo, cfg.block_hi, cfg.unmask_n)
     st.have_prev = True
-    return st, {"rows": rows, "scores": scores, "logits": z}
+    return st, {"rows": rows, "scores": scores, "logits": z, "nested_rows": nested_rows}

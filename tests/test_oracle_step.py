@@ -210,3 +210,96 @@ def test_bf16_mode_close_to_exact():
     sb, _ = full_step(mb, tok, 1)
     err = np.abs(sb.h_fin - se.h_fin).max() / np.abs(se.h_fin).max()
     assert 0 < err < 2e-2
+
+
+# ---- nested boundaries: later layers narrow the active set (ES-dLLM 2.1 item 2, I_{l,i}) -------
+
+def test_nested_full_step_fills_cache_with_layer_input():
+    """A full step stores, for every row, the hidden state entering each nested layer (= dense pass)."""
+    m = tiny_model(21)
+    tok = tokens(22)
+    st = new_state(m, tok, True, n_nested=2)
+    st2, _ = skip_step(m, st, StepCfg(boundary_layer=0, full_step=True, nested=((1, 3), (2, 2))))
+    for j, nl in enumerate((1, 2)):
+        np.testing.assert_allclose(st2.h_nested[j], dense(m, tok, nl)["h_bnd"], rtol=1e-12, atol=1e-12)
+
+
+def test_nested_keeping_every_row_equals_single_boundary():
+    m = tiny_model(23)
+    tok = tokens(24)
+    st = new_state(m, tok, True, n_nested=1)
+    st, _ = skip_step(m, st, StepCfg(boundary_layer=1, full_step=True, nested=((2, 5),)))
+    st.tokens[:, 9] = 4
+    sc = ScoreCfg(alpha=0.5, var=VAR_L1N, k=5)
+    a, ia = skip_step(m, st, StepCfg(boundary_layer=1, full_step=False, score=sc))
+    b, ib = skip_step(m, st, StepCfg(boundary_layer=1, full_step=False, score=sc, nested=((2, 5),)))
+    assert np.array_equal(ia["rows"], ib["rows"]) and np.array_equal(ib["nested_rows"][0], ib["rows"])
+    for name in ("h_fin", "conf", "kl", "argmax"):
+        assert np.array_equal(getattr(a, name), getattr(b, name)), name
+    for l in range(L):
+        assert np.array_equal(a.k_cache[l], b.k_cache[l]) and np.array_equal(a.v_cache[l], b.v_cache[l])
+
+
+def test_nested_unchanged_input_selects_by_confidence():
+    """Nothing changed since the caches were filled: every change term is 0 (P5), so each nested
+    stage keeps the k most confident rows of the previous stage (ties to the lower position),
+    checked here by a brute-force ordering."""
+    m = tiny_model(25)
+    tok = tokens(26)
+    st = new_state(m, tok, True, n_nested=2)
+    st, _ = skip_step(m, st, StepCfg(boundary_layer=0, full_step=True, nested=((1, 8), (2, 3))))
+    alpha = 0.7
+    cfg = StepCfg(boundary_layer=0, full_step=False, score=ScoreCfg(alpha=alpha, var=VAR_COS, k=8),
+                  nested=((1, 5), (2, 3)))
+    st2, info = skip_step(m, st, cfg)
+    conf = st.conf.reshape(-1)
+    prev = info["nested_rows"][0]
+    stages = [np.concatenate([b * S + np.array(sorted(sorted(range(S), key=lambda i: (-conf[b * S + i], i))[:8]))
+                              for b in range(B)])]
+    for k in (5, 3):
+        keep = []
+        for b in range(B):
+            cand = [r for r in stages[-1] if r // S == b]
+            keep += sorted(sorted(cand, key=lambda r: (-np.float32(alpha * conf[r]), r))[:k])
+        stages.append(np.array(keep))
+    assert np.array_equal(prev, stages[1])
+    assert np.array_equal(info["nested_rows"][1], stages[2])
+    assert np.array_equal(info["rows"], stages[2])
+
+
+def test_nested_dropped_rows_are_skipped_from_their_layer_on():
+    m = tiny_model(27)
+    tok = tokens(28)
+    st = new_state(m, tok, True, n_nested=1)
+    st, _ = skip_step(m, st, StepCfg(boundary_layer=0, full_step=True, nested=((2, 4),)))
+    st.tokens[:, 7] = 2
+    st.tokens[:, 10] = 3
+    cfg = StepCfg(boundary_layer=0, full_step=False, score=ScoreCfg(alpha=0.5, var=VAR_L1N, k=7), nested=((2, 3),))
+    st2, info = skip_step(m, st, cfg)
+    before = info["nested_rows"][0]
+    final = info["rows"]
+    assert np.array_equal(before, final) and len(final) == B * 3
+    # rows that reached layer 2 (the boundary selection) vs the ones that continued past it
+    reached = np.nonzero(np.any(st2.h_nested[0].reshape(B * S, d) != st.h_nested[0].reshape(B * S, d), axis=1))[0]
+    assert set(final) <= set(reached) and len(reached) == B * 7
+    dropped = np.setdiff1d(reached, final)
+    for name in ("h_fin", "conf", "kl", "argmax"):
+        fb = getattr(st, name).reshape(B * S, -1)
+        fa = getattr(st2, name).reshape(B * S, -1)
+        assert np.array_equal(fb[dropped], fa[dropped]), name
+        assert not np.array_equal(fb[final], fa[final]), name
+    for l in range(L):
+        kb, ka = st.k_cache[l].reshape(B * S, -1), st2.k_cache[l].reshape(B * S, -1)
+        if l == 1:  # layer 1 ran on every row selected at the boundary, and attention mixed in the change
+            assert not np.any(np.all(kb[dropped] == ka[dropped], axis=1))
+        elif l >= 2:  # from layer 2 on the dropped rows are skipped
+            assert np.array_equal(kb[dropped], ka[dropped])
+
+
+@pytest.mark.parametrize("nested", [((0, 2),), ((2, 2), (2, 1)), ((3, 2),), ((2, -1),)])
+def test_nested_layers_validated(nested):
+    m = tiny_model(29)
+    tok = tokens(30)
+    st = new_state(m, tok, True, n_nested=2)
+    with pytest.raises(ValueError):
+        skip_step(m, st, StepCfg(boundary_layer=0, full_step=True, nested=nested))
