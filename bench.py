@@ -79,17 +79,21 @@ class HipEvents:
                 self.hip.hipEventDestroy(arr[i])
 
 
-def llada_generation(dims, k_sparse=128, boundary=4, steps=64, block=32):
-    """Per-iteration (cfg kwargs) of the semi-autoregressive early-skip generation."""
+def llada_generation(dims, k_sparse=128, boundary=4, steps=64, block=32, nested=()):
+    """Per-iteration (cfg kwargs) of the semi-autoregressive early-skip generation; `nested` adds
+    later layers that narrow the active set ((layer, k), ...), on every iteration (a full step
+    fills their caches)."""
     per_block = steps // ((dims.S - dims.prompt) // block)
     out = []
     for t in range(steps):
         lo = dims.prompt + (t // per_block) * block
         if t == 0:
-            out.append(dict(boundary_layer=boundary, full_step=True, score=None, unmask_n=4, block_lo=lo, block_hi=lo + block))
+            out.append(dict(boundary_layer=boundary, full_step=True, score=None, unmask_n=4, block_lo=lo,
+                            block_hi=lo + block, nested=nested))
         else:
             sc = api.score_cfg(alpha=0.5, conf_inverted=False, var=api.VAR_L1N, sel=api.SEL_TOPK, k=k_sparse)
-            out.append(dict(boundary_layer=boundary, full_step=False, score=sc, unmask_n=4, block_lo=lo, block_hi=lo + block))
+            out.append(dict(boundary_layer=boundary, full_step=False, score=sc, unmask_n=4, block_lo=lo,
+                            block_hi=lo + block, nested=nested))
     return out
 
 
@@ -485,6 +489,9 @@ def main():
     ap.add_argument("--workload", choices=("llada", "dream", "long"), default="llada",
                     help="llada: the 32-layer early-skip generation (default); dream: Dream-GQA lock ramp; "
                          "long: long-context dilated run")
+    ap.add_argument("--nested", default="",
+                    help="llada workload: nested boundaries 'layer:k[,layer:k]' that narrow the 128 active rows "
+                         "at later layers (ES-dLLM per-layer selection), e.g. 16:64")
     ap.add_argument("--kl-state", choices=("f32", "bf16"), default="f32",
                     help="precision of the previous logits the KL lock rule compares against (dream workload)")
     ap.add_argument("--calibrate-copy", action="store_true",
@@ -519,9 +526,10 @@ def main():
     torch.cuda.synchronize()
     t_setup = time.perf_counter() - t0
     tok0 = workloads.initial_tokens(dims, device=dev)
-    state = api.State(model, tok0.clone(), k_max=k_sparse, track_kl=False)
+    nested = tuple(tuple(int(v) for v in item.split(":")) for item in args.nested.split(",")) if args.nested else ()
+    state = api.State(model, tok0.clone(), k_max=k_sparse, track_kl=False, n_nested=len(nested))
     ws = api.alloc_workspace(model, dims.B, dims.S, k_sparse)
-    plan = llada_generation(dims, k_sparse, boundary, n_iter)
+    plan = llada_generation(dims, k_sparse, boundary, n_iter, nested=nested)
 
     # one eager generation first (first-touch of every buffer and kernel)
     run_generation(model, state, tok0, plan, ws)
@@ -610,11 +618,13 @@ def main():
         "dtype": "bf16",
         "data": "synthetic (seeded random-init weights N(0,0.02); prompt tokens uniform)",
         "config": {"workload": "LLaDA-8B-shaped 32-layer early-skip generation (prompt 256 + gen 256, blocks of 32, "
-                               "64 iterations, layers 4-31 on top-128 rows)",
+                               "64 iterations, layers 4-31 on top-128 rows)"
+                               + ("".join(f"; from layer {nl} on the top {nk}" for nl, nk in nested)),
                    "batch": dims.B, "seq_len": dims.S, "layers": dims.n_layers, "hidden": dims.d,
                    "vocab": dims.vocab, "active_rows": k_sparse, "boundary_layer": boundary,
                    "iterations_per_step": n_iter, "setup_s": round(t_setup, 1),
-                   "launch": "hip graph replay" if graph is not None else "eager"},
+                   "launch": "hip graph replay" if graph is not None else "eager",
+                   "nested": [list(x) for x in nested] or None},
         "roofline": roofline,
         "kernels": kernels,
         "cpu_baseline": cpu,

@@ -82,6 +82,9 @@ typedef enum {
                              dilated schedule plans for this round ([DUS] sec. 2) */
 } dllm_unmask_mode;
 
+/* Most nested boundaries a step may name (dllm_step_cfg.nested_layer). */
+#define DLLM_MAX_NESTED 3
+
 /* force[] values: per position. */
 enum { DLLM_FORCE_NONE = 0, DLLM_FORCE_ON = 1, DLLM_FORCE_EXCLUDED = 2 };
 
@@ -149,6 +152,9 @@ typedef struct {
                              are stored rounded to bf16 (RNE) and the KL compares the bf16-rounded
                              current logits with them, so identical logits still give KL = 0;
                              conf and argmax always come from the fp32 logits */
+  void *h_nested[DLLM_MAX_NESTED]; /* device [B, S, d] each, or NULL: the hidden state entering
+                             nested layer j the last time each position was computed there
+                             (written by full steps and by every row reaching that layer) */
 } dllm_state;
 
 typedef struct {
@@ -162,6 +168,17 @@ typedef struct {
   int32_t unmask_mode;      /* dllm_unmask_mode */
   void *ws;                 /* device workspace */
   size_t ws_bytes;
+  /* Nested boundaries ([ES] 2.1 item 2: selection at the start of a layer with the per-layer
+   * score I_{l,i}).  At layers boundary_layer < nested_layer[0] < ... < L the rows still active
+   * are scored again with `score`'s alpha / change term, the change taken between the hidden state
+   * entering that layer and state->h_nested[j] at the row's position; the top nested_k[j] of
+   * them (forced rows first, ties to the lower position) continue, the others are skipped from
+   * that layer on (they keep the K/V written below it; their final hidden state and statistics
+   * stay cached).  h_nested[j] is then updated for every row that reached the layer.  A full
+   * step fills h_nested[j] for every row.  idx / n_active report the last set. */
+  int32_t n_nested;                       /* 0..DLLM_MAX_NESTED */
+  int32_t nested_layer[DLLM_MAX_NESTED];
+  int32_t nested_k[DLLM_MAX_NESTED];      /* 0 <= k <= state->k_max */
 } dllm_step_cfg;
 
 /* Bytes of device workspace needed by dllm_skip_step / dllm_layer_sparse for

@@ -188,7 +188,7 @@ def skip_step(model: OracleModel, st: OracleState, cfg: StepCfg) -> tuple[Oracle
         rows = np.concatenate(sel).astype(np.int64)
         x = x[rows].copy()
 
-    nested_rows = []
+    nested_rows, nested_scores = [], []
 
     def nested_boundary(j, k):
         nonlocal rows, x
@@ -199,6 +199,7 @@ def skip_step(model: OracleModel, st: OracleState, cfg: StepCfg) -> tuple[Oracle
         s = importance_score(x, hn[rows], st.conf.reshape(-1)[rows], st.kl.reshape(-1)[rows],
                              alpha=cfg.score.alpha, var=cfg.score.var, conf_inverted=cfg.score.conf_inverted)
         hn[rows] = x            # the hidden state entering this layer, kept for the next iteration
+        nested_scores.append((rows.copy(), s.copy()))
         keep = []
         for b in range(B):
             in_b = (rows // S) == b
@@ -247,4 +248,5 @@ def skip_step(model: OracleModel, st: OracleState, cfg: StepCfg) -> tuple[Oracle
             st.tokens = unmask_topn(st.tokens, st.conf, st.argmax, model.mask_id,
                                     cfg.block_lo, cfg.block_hi, cfg.unmask_n)
     st.have_prev = True
-    return st, {"rows": rows, "scores": scores, "logits": z, "nested_rows": nested_rows}
+    return st, {"rows": rows, "scores": scores, "logits": z, "nested_rows": nested_rows,
+                "nested_scores": nested_scores}

@@ -85,3 +85,35 @@ def test_argument_validation_returns_before_launch(lib):
     assert lib.dllm_dus_mark(fake, 1, 10, 0, 4, 2, 0, 0, 0, None) == 1
     # skip step without a model
     assert lib.dllm_skip_step(None, None, None, None) == 1
+
+
+def test_struct_layouts_match_header(tmp_path):
+    """Every ctypes struct of the binding has the header's size and field offsets (gcc, CPU only)."""
+    import shutil
+    import subprocess
+    gcc = shutil.which("gcc") or shutil.which("cc")
+    if gcc is None:
+        pytest.skip("no C compiler")
+    structs = {"dllm_dims": _ffi.Dims, "dllm_score_cfg": _ffi.ScoreCfg, "dllm_state": _ffi.StateC,
+               "dllm_step_cfg": _ffi.StepCfg, "dllm_timing": _ffi.Timing, "dllm_layer_w": _ffi.LayerW,
+               "dllm_model": _ffi.ModelC}
+    lines = ["#include <stdio.h>", "#include <stddef.h>", '#include "dllm.h"', "int main(void) {"]
+    for cname, py in structs.items():
+        lines.append(f'  printf("{cname} size %zu\\n", sizeof({cname}));')
+        for fname, _ in py._fields_:
+            lines.append(f'  printf("{cname} {fname} %zu\\n", offsetof({cname}, {fname}));')
+    lines += ["  return 0;", "}"]
+    src = tmp_path / "layout.c"
+    src.write_text("\n".join(lines) + "\n")
+    exe = tmp_path / "layout"
+    subprocess.run([gcc, "-std=c99", "-I", os.path.dirname(HEADER), str(src), "-o", str(exe)], check=True)
+    out = subprocess.run([str(exe)], check=True, capture_output=True, text=True).stdout.split("\n")
+    got = {}
+    for line in out:
+        if line:
+            parts = line.split()
+            got[(parts[0], parts[1])] = int(parts[2])
+    for cname, py in structs.items():
+        assert got[(cname, "size")] == ctypes.sizeof(py), cname
+        for fname, _ in py._fields_:
+            assert got[(cname, fname)] == getattr(py, fname).offset, f"{cname}.{fname}"

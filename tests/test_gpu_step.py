@@ -310,3 +310,78 @@ def test_all_rows_active_equals_full_step_on_gpu():
     assert torch.equal(outs[0][1], outs[1][1])
     for a, b in zip(outs[0][2], outs[1][2]):
         assert torch.equal(a, b)
+
+
+def _tiered_conf(B, S, tiers, forced_top, seed):
+    """Confidences in separated tiers: tiers = [n_1, n_2, ...] rows per sequence in bands
+    [0.92, 1.0], [0.75, 0.83], [0.55, 0.63], ...; `forced_top` positions always in the top band;
+    every other row in [0, 0.3]."""
+    u = synth.uniform01(synth.seed_of(seed), (B, S)).numpy().astype(np.float64)
+    conf = 0.3 * u
+    for b in range(B):
+        perm = [int(i) for i in synth.permutation(synth.seed_of(seed, b), S).numpy() if int(i) not in forced_top]
+        order = list(forced_top) + perm
+        start = 0
+        for t, n in enumerate(tiers):
+            lo = [0.92, 0.75, 0.55, 0.40][t]
+            for i in order[start:start + n]:
+                conf[b, i] = lo + 0.08 * u[b, i]
+            start += n
+    return conf.astype(np.float32)
+
+
+def test_bf16_nested_boundaries():
+    """Boundary at layer 1 (24 rows), nested boundaries at layers 2 (12 rows) and 3 (6 rows)."""
+    dims = workloads.shrink(workloads.LLADA, n_layers=4, d=256, n_heads=2, n_kv_heads=2, d_ff=512, vocab=1000,
+                            B=2, S=96, prompt=48)
+    k, nested = 24, ((2, 12), (3, 6))
+    gm, om = _models(dims, std=0.05)
+    tok = workloads.initial_tokens(dims)
+    gs = api.State(gm, tok.to(DEV), k_max=k, track_kl=True, n_nested=2)
+    ws = api.alloc_workspace(gm, dims.B, dims.S, k)
+    os_ = new_state(om, tok.numpy(), track_kl=True, n_nested=2)
+    api.skip_step(gm, gs, api.step_cfg(1, True, ws=ws, nested=nested))
+    os_, _ = skip_step(om, os_, StepCfg(boundary_layer=1, full_step=True, nested=nested))
+    torch.cuda.synchronize()
+    BS = dims.B * dims.S
+    for j in range(2):   # a full step fills the nested caches for every row
+        assert_close(np64(gs.h_nested[j]).reshape(BS, -1), os_.h_nested[j].reshape(BS, -1), 2e-2, f"h_nested {j}")
+    conf = _tiered_conf(dims.B, dims.S, [6, 6, 12], [50, 51, 52], 91)
+    gs.conf.copy_(torch.from_numpy(conf))
+    os_.conf = conf.astype(np.float64)
+    new_tok = tok.clone()
+    new_tok[:, 50:53] = torch.tensor([5, 6, 7], dtype=torch.int32)
+    gs.tokens.copy_(new_tok)
+    os_.tokens = new_tok.numpy().astype(np.int64)
+    k_before = [t.cpu().clone() for t in gs.k_cache]
+    hn_before = [t.cpu().clone() for t in gs.h_nested]
+    hf_before = gs.h_fin.cpu().clone()
+    gsc, osc = _score_cfg_pair(0.8, VAR_L1N, SEL_TOPK, k)
+    api.skip_step(gm, gs, api.step_cfg(1, False, gsc, ws=ws, nested=nested))
+    os_, info = skip_step(om, os_, StepCfg(boundary_layer=1, full_step=False, score=osc, nested=nested))
+    torch.cuda.synchronize()
+    # every selection is well separated, so both sides must take the same rows
+    assert min(selection_gap(info["scores"][b], os_.force[b], k) for b in range(dims.B)) > 0.02
+    for (rows_j, s_j), (_, kk) in zip(info["nested_scores"], nested):
+        for b in range(dims.B):
+            sb = np.sort(s_j[rows_j // dims.S == b])[::-1]
+            assert sb[kk - 1] - sb[kk] > 0.02
+    stage = [info["nested_scores"][0][0], info["nested_scores"][1][0], info["rows"]]  # rows entering 2, 3, final
+    got_rows = [b * dims.S + int(i) for b in range(dims.B) for i in gs.idx[b, :int(gs.n_active[b])].cpu()]
+    assert got_rows == info["rows"].tolist()
+    final = info["rows"]
+    _compare_state(gs, os_, final, 2e-2, "nested")
+    others = np.setdiff1d(np.arange(BS), final)
+    assert torch.equal(gs.h_fin.cpu().reshape(BS, -1)[others], hf_before.reshape(BS, -1)[others])
+    for l in range(dims.n_layers):
+        active = np.arange(BS) if l < 1 else (stage[0] if l < 2 else (stage[1] if l < 3 else final))
+        kc = gs.k_cache[l].cpu().reshape(BS, -1)
+        assert_close(np64(kc)[active], os_.k_cache[l].reshape(BS, -1)[active], 2e-2, f"K {l}")
+        idle = np.setdiff1d(np.arange(BS), active)
+        assert torch.equal(kc[idle], k_before[l].reshape(BS, -1)[idle]), f"layer {l} skipped rows"
+    for j in range(2):   # caches refreshed exactly for the rows that reached the layer
+        hn = gs.h_nested[j].cpu().reshape(BS, -1)
+        reached = stage[j]
+        assert_close(np64(hn)[reached], os_.h_nested[j].reshape(BS, -1)[reached], 2e-2, f"h_nested {j} rows")
+        idle = np.setdiff1d(np.arange(BS), reached)
+        assert torch.equal(hn[idle], hn_before[j].reshape(BS, -1)[idle])

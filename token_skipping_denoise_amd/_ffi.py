@@ -12,6 +12,7 @@ VAR_L1N, VAR_COS, VAR_L2REL, VAR_KL, VAR_NONE = 0, 1, 2, 3, 4
 SEL_TOPK, SEL_THRESH_CAP, SEL_UNLOCKED = 0, 1, 2
 FORCE_NONE, FORCE_ON, FORCE_EXCLUDED = 0, 1, 2
 UNMASK_CONF, UNMASK_FORCED = 0, 1
+MAX_NESTED = 3
 
 EXPORTED = (
     "dllm_workspace_size", "dllm_score_select", "dllm_gather_rows", "dllm_scatter_rows",
@@ -45,14 +46,15 @@ class StateC(Structure):
                 ("h_bnd", c_void_p * 2), ("bnd_cur", c_int32), ("h_fin", c_void_p), ("conf", c_void_p),
                 ("kl", c_void_p), ("argmax", c_void_p), ("logits_prev", c_void_p), ("force", c_void_p),
                 ("idx", c_void_p), ("n_active", c_void_p), ("k_max", c_int32), ("have_prev", c_int32),
-                ("logits_prev_dtype", c_int32)]
+                ("logits_prev_dtype", c_int32), ("h_nested", c_void_p * MAX_NESTED)]
 
 
 class StepCfg(Structure):
     _fields_ = [("boundary_layer", c_int32), ("full_step", c_int32), ("score", ScoreCfg),
                 ("lock_kl_eps", c_float), ("lock_conf_min", c_float), ("unmask_n", c_int32),
                 ("block_lo", c_int32), ("block_hi", c_int32), ("unmask_mode", c_int32), ("ws", c_void_p),
-                ("ws_bytes", c_size_t)]
+                ("ws_bytes", c_size_t), ("n_nested", c_int32), ("nested_layer", c_int32 * MAX_NESTED),
+                ("nested_k", c_int32 * MAX_NESTED)]
 
 
 class Timing(Structure):

@@ -194,10 +194,13 @@ class State:
     """Persistent device state of one generation run (tensors + dllm_state struct)."""
 
     def __init__(self, model: Model, tokens: torch.Tensor, k_max: int, track_kl: bool = False, with_force: bool = True,
-                 kl_state: str = "f32"):
-        """kl_state: "f32" or "bf16", the precision the previous logits are kept in (with track_kl)."""
+                 kl_state: str = "f32", n_nested: int = 0):
+        """kl_state: "f32" or "bf16", the precision the previous logits are kept in (with track_kl).
+        n_nested: hidden-state caches for that many nested boundaries."""
         if kl_state not in ("f32", "bf16"):
             raise DllmError("kl_state must be 'f32' or 'bf16'")
+        if not 0 <= n_nested <= _ffi.MAX_NESTED:
+            raise DllmError(f"n_nested must be 0..{_ffi.MAX_NESTED}")
         B, S = tokens.shape
         V, d, Hq, Hkv, D, F, L = model.dims_tuple
         dev, dt = model.device, model.dtype
@@ -207,6 +210,7 @@ class State:
         self.v_cache = [torch.zeros((B, S, Hkv, D), dtype=dt, device=dev) for _ in range(L)]
         self.h_bnd = [torch.zeros((B, S, d), dtype=dt, device=dev) for _ in range(2)]
         self.h_fin = torch.zeros((B, S, d), dtype=dt, device=dev)
+        self.h_nested = [torch.zeros((B, S, d), dtype=dt, device=dev) for _ in range(n_nested)]
         self.conf = torch.zeros((B, S), dtype=torch.float32, device=dev)
         self.kl = torch.full((B, S), float("inf"), dtype=torch.float32, device=dev)
         self.argmax = torch.zeros((B, S), dtype=torch.int32, device=dev)
@@ -235,6 +239,8 @@ class State:
         self.c.k_max = int(k_max)
         self.c.have_prev = 0
         self.c.logits_prev_dtype = DLLM_BF16 if kl_state == "bf16" else DLLM_F32
+        for j, t in enumerate(self.h_nested):
+            self.c.h_nested[j] = _ptr(t)
 
     @property
     def h_bnd_prev(self) -> torch.Tensor:
@@ -244,7 +250,10 @@ class State:
 
 def step_cfg(boundary_layer: int, full_step: bool, score: _ffi.ScoreCfg | None = None, *, lock_kl_eps=-1.0,
              lock_conf_min=0.9, unmask_n=0, block_lo=0, block_hi=0, unmask_mode=UNMASK_CONF,
-             ws=None) -> _ffi.StepCfg:
+             ws=None, nested=()) -> _ffi.StepCfg:
+    """nested: ((layer, k), ...) later layers that narrow the active set (at most MAX_NESTED)."""
+    if len(nested) > _ffi.MAX_NESTED:
+        raise DllmError(f"at most {_ffi.MAX_NESTED} nested boundaries")
     c = _ffi.StepCfg()
     c.boundary_layer = int(boundary_layer)
     c.full_step = int(bool(full_step))
@@ -258,6 +267,10 @@ def step_cfg(boundary_layer: int, full_step: bool, score: _ffi.ScoreCfg | None =
     if ws is not None:
         c.ws = _ptr(ws)
         c.ws_bytes = ws.numel() * ws.element_size()
+    c.n_nested = len(nested)
+    for j, (nl, nk) in enumerate(nested):
+        c.nested_layer[j] = int(nl)
+        c.nested_k[j] = int(nk)
     return c
 
 

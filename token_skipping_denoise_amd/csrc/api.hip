@@ -48,7 +48,8 @@ struct TimedRegion {
 
 // Workspace layout for (dims, dtype, k_max).
 struct WsLayout {
-  size_t xfull, xact, xn, q, o, h, part, attn, vpart, logits, scores, idx_id, nact_full, rowpos_d, rowpos_s, total;
+  size_t xfull, xact, xn, q, o, h, part, attn, vpart, logits, scores, idx_id, nact_full, rowpos_d, rowpos_s,
+      nforce, row_of, old_row, total;
 };
 
 long max_part_floats(const dllm_dims& d, int dtype, long M) {
@@ -90,6 +91,9 @@ bool plan_ws(const dllm_dims& d, int dtype, int k_max, WsLayout& L) {
   L.nact_full = take(d.B * sizeof(int32_t));
   L.rowpos_d = take(Rd * sizeof(int32_t));
   L.rowpos_s = take(Rs * sizeof(int32_t));
+  L.nforce = take(Rd);                     // nested boundaries: candidate marks per position
+  L.row_of = take(Rd * sizeof(int32_t));   //   active row of each position
+  L.old_row = take(Rs * sizeof(int32_t));  //   row before narrowing of each row after it
   L.total = off;
   return true;
 }
@@ -390,6 +394,13 @@ int dllm_skip_step(const dllm_model* model, dllm_state* state, const dllm_step_c
   if (cfg->unmask_n > 0 && (cfg->block_lo < 0 || cfg->block_hi > S || cfg->block_lo > cfg->block_hi))
     return DLLM_EINVAL;
   if (cfg->lock_kl_eps >= 0.f && !state->force) return DLLM_EINVAL;
+  const int n_nested = cfg->n_nested;
+  if (n_nested < 0 || n_nested > DLLM_MAX_NESTED) return DLLM_EINVAL;
+  for (int j = 0, prev = b_lay; j < n_nested; prev = cfg->nested_layer[j], ++j) {
+    if (cfg->nested_layer[j] <= prev || cfg->nested_layer[j] >= L) return DLLM_EINVAL;
+    if (cfg->nested_k[j] < 0 || cfg->nested_k[j] > kx) return DLLM_EINVAL;
+    if (!state->h_nested[j] || !aligned16(state->h_nested[j])) return DLLM_EINVAL;
+  }
 
   Ctx c{model, &d, model->dtype, (char*)cfg->ws, {}, (hipStream_t)stream};
   plan_ws(d, c.dtype, kx, c.L);
@@ -436,15 +447,50 @@ int dllm_skip_step(const dllm_model* model, dllm_state* state, const dllm_step_c
     return DLLM_OK;
   };
 
+  // nested boundary j at layer nl: re-score the active rows against the layer's cache, keep the
+  // top nested_k[j], refresh the cache for every row that got here, compact the survivors
+  auto nested = [&](int j, int nl) -> int {
+    void* hc = state->h_nested[j];
+    if (full) {
+      DLLM_TRY(launch_copy(xfull, hc, (size_t)Rd * row_bytes, c.s));
+      return DLLM_OK;
+    }
+    float* scores = c.at<float>(c.L.scores);
+    uint8_t* nforce = c.at<uint8_t>(c.L.nforce);
+    int32_t* row_of = c.at<int32_t>(c.L.row_of);
+    int32_t* old_row = c.at<int32_t>(c.L.old_row);
+    DLLM_TRY(launch_score_rows(c.dtype, xact, rp_s, Rs, hc, state->conf, state->kl, state->force, (long)Rd, d.d,
+                               sc.alpha, sc.conf_inverted, sc.var, scores, nforce, row_of, c.s));
+    DLLM_TRY(launch_select(scores, nforce, B, S, DLLM_SEL_TOPK, cfg->nested_k[j], 0.f, kx, state->idx,
+                           state->n_active, c.s));
+    DLLM_TRY(launch_scatter_norm(c.dtype, xact, rp_s, Rs, d.d, hc, nullptr, eps, nullptr, c.s));
+    DLLM_TRY(launch_copy(xact, xfull, (size_t)Rs * row_bytes, c.s));  // xfull is idle past the boundary
+    DLLM_TRY(launch_row_pos(state->idx, state->n_active, B, S, kx, rp_s, c.s));
+    DLLM_TRY(launch_compose_rows(rp_s, row_of, Rs, old_row, c.s));
+    DLLM_TRY(launch_gather_norm(c.dtype, xfull, old_row, Rs, d.d, xact, model->layers[nl].attn_norm, eps, xn, c.s));
+    return DLLM_OK;
+  };
+  auto nested_at = [&](int l) -> int {
+    for (int j = 0; j < n_nested; ++j)
+      if (cfg->nested_layer[j] == l) return j;
+    return -1;
+  };
+
   for (int l = 0; l < L; ++l) {
     if (l == b_lay) {
       st = boundary();
       if (st) return st;
     }
+    const int jn = nested_at(l);
+    if (jn >= 0) {
+      st = nested(jn, l);
+      if (st) return st;
+    }
     const bool dense = full || l < b_lay;
     const void* next_g;
     if (l + 1 == L) next_g = model->final_norm;
-    else if (!full && l + 1 == b_lay) next_g = nullptr;  // the boundary gather normalises the active rows
+    else if (!full && (l + 1 == b_lay || nested_at(l + 1) >= 0))
+      next_g = nullptr;  // the boundary (or nested) gather normalises the active rows
     else next_g = model->layers[l + 1].attn_norm;
     if (dense)
       st = run_layer(c, l, xfull, nact_full, rp_d, S, state->k_cache[l], state->v_cache[l], next_g);

@@ -64,6 +64,15 @@ hipError_t launch_attention(int dtype, const void* q, const void* kc, const void
 hipError_t launch_score(int dtype, const void* h_cur, const void* h_prev, void* h_next, const float* conf_prev,
                         const float* kl_prev, const uint8_t* force, int rows, int width, float alpha,
                         int conf_inverted, int var, float* score, hipStream_t s);
+// Nested boundary: score of the active rows (x_act row r at position row_pos[r]) against the
+// per-layer cache h_cache [positions, width]; force_nested [positions] is set to excluded except
+// at the active positions, row_of [positions] maps an active position to its row (score_select.hip).
+hipError_t launch_score_rows(int dtype, const void* x_act, const int32_t* row_pos, int R, const void* h_cache,
+                             const float* conf_prev, const float* kl_prev, const uint8_t* force, long positions,
+                             int width, float alpha, int conf_inverted, int var, float* score, uint8_t* force_nested,
+                             int32_t* row_of, hipStream_t s);
+// old_row[r] = row_of[row_pos[r]] (or -1 for a dead row).
+hipError_t launch_compose_rows(const int32_t* row_pos, const int32_t* row_of, int R, int32_t* old_row, hipStream_t s);
 hipError_t launch_select(const float* score, const uint8_t* force, int B, int S, int sel, int k, float tau,
                          int k_max, int32_t* idx, int32_t* n_active, hipStream_t s);
 

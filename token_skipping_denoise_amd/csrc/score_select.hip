@@ -25,20 +25,13 @@ enum { kSelTopK = 0, kSelThreshCap = 1, kSelUnlocked = 2 };
 
 // One wavefront per row.  Sums are accumulated per lane in index order and
 // combined by a fixed butterfly, so the result is deterministic.
+// Change term of one row pair (the whole wave): L1 / sqrt(w) / |b|, |a - b| / |b| or 1 - cos
+// (stable form 0.5 || a/|a| - b/|b| ||^2).  With n4 the wave also copies row a there.
 template <typename T>
-__global__ __launch_bounds__(256) void k_score(const T* __restrict__ h_cur, const T* __restrict__ h_prev,
-                                               T* __restrict__ h_next, const float* __restrict__ conf_prev,
-                                               const float* __restrict__ kl_prev, const uint8_t* __restrict__ force,
-                                               int rows, int w, float alpha, int conf_inverted, int var,
-                                               float* __restrict__ score) {
+__device__ __forceinline__ float change_term(const uint4* a4, const uint4* b4, uint4* n4, int w, int var) {
   using E = Elem<T>;
   const int lane = threadIdx.x & 63;
-  const int r = blockIdx.x * 4 + (threadIdx.x >> 6);
-  if (r >= rows) return;
   const int nchunk = w / E::kVec;
-  const uint4* a4 = reinterpret_cast<const uint4*>(h_cur + (long)r * w);
-  const uint4* b4 = reinterpret_cast<const uint4*>(h_prev + (long)r * w);
-  uint4* n4 = h_next ? reinterpret_cast<uint4*>(h_next + (long)r * w) : nullptr;
   float l1 = 0.f, l2 = 0.f, na = 0.f, nb = 0.f;
   int diff = 0;
   const bool need_rows = (var == kVarL1N || var == kVarCos || var == kVarL2Rel);
@@ -62,58 +55,131 @@ __global__ __launch_bounds__(256) void k_score(const T* __restrict__ h_cur, cons
       }
     }
   }
-  float psi = 0.f;
-  if (var == kVarKL) {
-    psi = kl_prev[r];
-  } else if (need_rows) {
-    l1 = wave_sum(l1);
-    l2 = wave_sum(l2);
-    na = wave_sum(na);
-    nb = wave_sum(nb);
-    diff = wave_or(diff);
-    if (var == kVarL1N) {
-      psi = (nb == 0.f) ? (diff ? FLT_MAX : 0.f) : l1 / (sqrtf((float)w) * sqrtf(nb));
-    } else if (var == kVarL2Rel) {
-      psi = (nb == 0.f) ? (diff ? FLT_MAX : 0.f) : sqrtf(l2) / sqrtf(nb);
-    } else {  // cosine change, stable form 0.5 * || a/|a| - b/|b| ||^2
-      if (na == 0.f || nb == 0.f) {
-        psi = diff ? FLT_MAX : 0.f;
-      } else {
-        const float ia = 1.0f / sqrtf(na), ib = 1.0f / sqrtf(nb);
-        float c2 = 0.f;
-        for (int c = lane; c < nchunk; c += kWave) {
-          float fa[E::kVec], fb[E::kVec];
-          E::unpack(a4[c], fa);
-          E::unpack(b4[c], fb);
+  if (!need_rows) return 0.f;
+  l1 = wave_sum(l1);
+  l2 = wave_sum(l2);
+  na = wave_sum(na);
+  nb = wave_sum(nb);
+  diff = wave_or(diff);
+  if (var == kVarL1N) return (nb == 0.f) ? (diff ? FLT_MAX : 0.f) : l1 / (sqrtf((float)w) * sqrtf(nb));
+  if (var == kVarL2Rel) return (nb == 0.f) ? (diff ? FLT_MAX : 0.f) : sqrtf(l2) / sqrtf(nb);
+  if (na == 0.f || nb == 0.f) return diff ? FLT_MAX : 0.f;
+  const float ia = 1.0f / sqrtf(na), ib = 1.0f / sqrtf(nb);
+  float c2 = 0.f;
+  for (int c = lane; c < nchunk; c += kWave) {
+    float fa[E::kVec], fb[E::kVec];
+    E::unpack(a4[c], fa);
+    E::unpack(b4[c], fb);
 #pragma unroll
-          for (int e = 0; e < E::kVec; ++e) {
-            const float t = fa[e] * ia - fb[e] * ib;
-            c2 += t * t;
-          }
-        }
-        psi = 0.5f * wave_sum(c2);
-      }
+    for (int e = 0; e < E::kVec; ++e) {
+      const float t = fa[e] * ia - fb[e] * ib;
+      c2 += t * t;
     }
   }
+  return 0.5f * wave_sum(c2);
+}
+
+__device__ __forceinline__ float importance(float c, float psi, float alpha, int conf_inverted) {
+  const float phi = conf_inverted ? 1.0f - c : c;
+  return alpha * phi + (1.0f - alpha) * psi;
+}
+
+// ES-dLLM Eq. 1 (and variants) for every position: one wave per row.
+template <typename T>
+__global__ __launch_bounds__(256) void k_score(const T* __restrict__ h_cur, const T* __restrict__ h_prev,
+                                               T* __restrict__ h_next, const float* __restrict__ conf_prev,
+                                               const float* __restrict__ kl_prev, int rows, int w, float alpha,
+                                               int conf_inverted, int var, float* __restrict__ score) {
+  const int lane = threadIdx.x & 63;
+  const int r = blockIdx.x * 4 + (threadIdx.x >> 6);
+  if (r >= rows) return;
+  const uint4* a4 = reinterpret_cast<const uint4*>(h_cur + (long)r * w);
+  const uint4* b4 = reinterpret_cast<const uint4*>(h_prev + (long)r * w);
+  uint4* n4 = h_next ? reinterpret_cast<uint4*>(h_next + (long)r * w) : nullptr;
+  float psi = change_term<T>(a4, b4, n4, w, var == kVarKL ? kVarNone : var);
+  if (var == kVarKL) psi = kl_prev[r];
+  if (lane == 0) score[r] = importance(conf_prev[r], psi, alpha, conf_inverted);
+}
+
+// Nested boundary: the same score for the active rows only, from the row's current hidden state
+// (x_act row r) and the per-layer cache at its position p = row_pos[r].  Marks the active
+// positions as candidates in force_nested (the caller set every position to excluded first;
+// a forced row stays forced) and records the row of each active position in row_of.
+template <typename T>
+__global__ __launch_bounds__(256) void k_score_rows(const T* __restrict__ x_act, const int32_t* __restrict__ row_pos,
+                                                    const T* __restrict__ h_cache, const float* __restrict__ conf_prev,
+                                                    const float* __restrict__ kl_prev,
+                                                    const uint8_t* __restrict__ force, int R, int w, float alpha,
+                                                    int conf_inverted, int var, float* __restrict__ score,
+                                                    uint8_t* __restrict__ force_nested, int32_t* __restrict__ row_of) {
+  const int lane = threadIdx.x & 63;
+  const int r = blockIdx.x * 4 + (threadIdx.x >> 6);
+  if (r >= R) return;
+  const int p = row_pos[r];
+  if (p < 0) return;
+  const uint4* a4 = reinterpret_cast<const uint4*>(x_act + (long)r * w);
+  const uint4* b4 = reinterpret_cast<const uint4*>(h_cache + (long)p * w);
+  float psi = change_term<T>(a4, b4, nullptr, w, var == kVarKL ? kVarNone : var);
+  if (var == kVarKL) psi = kl_prev[p];
   if (lane == 0) {
-    const float c = conf_prev[r];
-    const float phi = conf_inverted ? 1.0f - c : c;
-    score[r] = alpha * phi + (1.0f - alpha) * psi;
+    score[p] = importance(conf_prev[p], psi, alpha, conf_inverted);
+    force_nested[p] = (force && force[p] == 1) ? 1 : 0;
+    row_of[p] = r;
   }
-  (void)force;
+}
+
+__global__ void k_fill_excluded(uint8_t* __restrict__ force_nested, int32_t* __restrict__ row_of, long n) {
+  const long i = blockIdx.x * (long)blockDim.x + threadIdx.x;
+  if (i >= n) return;
+  force_nested[i] = 2;
+  row_of[i] = -1;
+}
+
+// old_row[r] = row_of[row_pos[r]] for the rows of the narrowed set (-1 for dead rows)
+__global__ void k_compose_rows(const int32_t* __restrict__ row_pos, const int32_t* __restrict__ row_of, int R,
+                               int32_t* __restrict__ old_row) {
+  const int r = blockIdx.x * blockDim.x + threadIdx.x;
+  if (r >= R) return;
+  const int p = row_pos[r];
+  old_row[r] = p < 0 ? -1 : row_of[p];
 }
 
 hipError_t launch_score(int dtype, const void* h_cur, const void* h_prev, void* h_next, const float* conf_prev,
                         const float* kl_prev, const uint8_t* force, int rows, int width, float alpha,
                         int conf_inverted, int var, float* score, hipStream_t s) {
+  (void)force;  // forced and excluded rows are handled by the selection
   if (rows <= 0) return hipSuccess;
   dim3 grid((rows + 3) / 4), block(256);
   if (dtype == 0)
     hipLaunchKernelGGL(k_score<float>, grid, block, 0, s, (const float*)h_cur, (const float*)h_prev, (float*)h_next,
-                       conf_prev, kl_prev, force, rows, width, alpha, conf_inverted, var, score);
+                       conf_prev, kl_prev, rows, width, alpha, conf_inverted, var, score);
   else
     hipLaunchKernelGGL(k_score<bf16>, grid, block, 0, s, (const bf16*)h_cur, (const bf16*)h_prev, (bf16*)h_next,
-                       conf_prev, kl_prev, force, rows, width, alpha, conf_inverted, var, score);
+                       conf_prev, kl_prev, rows, width, alpha, conf_inverted, var, score);
+  return hipGetLastError();
+}
+
+hipError_t launch_score_rows(int dtype, const void* x_act, const int32_t* row_pos, int R, const void* h_cache,
+                             const float* conf_prev, const float* kl_prev, const uint8_t* force, long positions,
+                             int width, float alpha, int conf_inverted, int var, float* score, uint8_t* force_nested,
+                             int32_t* row_of, hipStream_t s) {
+  if (positions > 0)
+    hipLaunchKernelGGL(k_fill_excluded, dim3((unsigned)((positions + 255) / 256)), dim3(256), 0, s, force_nested,
+                       row_of, positions);
+  if (R <= 0) return hipGetLastError();
+  dim3 grid((R + 3) / 4), block(256);
+  if (dtype == 0)
+    hipLaunchKernelGGL(k_score_rows<float>, grid, block, 0, s, (const float*)x_act, row_pos, (const float*)h_cache,
+                       conf_prev, kl_prev, force, R, width, alpha, conf_inverted, var, score, force_nested, row_of);
+  else
+    hipLaunchKernelGGL(k_score_rows<bf16>, grid, block, 0, s, (const bf16*)x_act, row_pos, (const bf16*)h_cache,
+                       conf_prev, kl_prev, force, R, width, alpha, conf_inverted, var, score, force_nested, row_of);
+  return hipGetLastError();
+}
+
+hipError_t launch_compose_rows(const int32_t* row_pos, const int32_t* row_of, int R, int32_t* old_row, hipStream_t s) {
+  if (R <= 0) return hipSuccess;
+  hipLaunchKernelGGL(k_compose_rows, dim3((R + 255) / 256), dim3(256), 0, s, row_pos, row_of, R, old_row);
   return hipGetLastError();
 }
 
