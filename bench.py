@@ -243,9 +243,9 @@ def cpu_baseline(model_w_gpu, dims, k_sparse, boundary, steps, sample_layers=16)
     }
 
 
-DOMINANT_KERNEL = "dllm::k_gemm_lds<128, 96, 4, 2, 1, 1, 4, 1>"
-TRAFFIC_PROFILE = os.path.join(ROOT, "profiles", "gemm_swiglu_llada_128rows_hbm_bytes.md")
-GEMM_SOURCE = os.path.join(ROOT, "token_skipping_denoise_amd", "csrc", "gemm.hip")
+DOMINANT_KERNEL = "dllm::(anonymous namespace)::k_gemm_packed<3, 64, 2>"
+TRAFFIC_PROFILE = os.path.join(ROOT, "profiles", "gemm_packed_swiglu_llada_128rows_hbm_bytes.md")
+GEMM_SOURCE = os.path.join(ROOT, "token_skipping_denoise_amd", "csrc", "gemm_packed.hip")
 
 
 def measured_traffic():
@@ -589,7 +589,8 @@ def main():
         achieved = bytes_per / (avg_ms * 1e-3) / 1e9
         roofline = {"bound": "hbm", "achieved": round(achieved, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
                     "frac": round(achieved / HBM_PEAK_GBS, 4), "traffic": measured_traffic(),
-                    "kernel": DOMINANT_KERNEL + " (gate/up + SwiGLU of a skipped-regime layer, 128 active rows)",
+                    "kernel": DOMINANT_KERNEL + " (gate/up + SwiGLU of a skipped-regime layer, 128 active rows, "
+                              "fragment-packed weights)",
                     "launches": timing.count, "avg_us": round(avg_ms * 1e3, 2),
                     "timed_in": ("eager generation right after the timed graph replays" if graph is not None
                                  else "timed region"),

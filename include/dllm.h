@@ -105,6 +105,12 @@ typedef struct {
   const void *ffn_norm;   /* device [d] */
   const void *w_gate_up;  /* device [2F, d]: gate rows, then up rows */
   const void *w_down;     /* device [d, F] */
+  /* Optional second copies in MFMA fragment order (dllm_pack_weight), or NULL.  When present,
+   * the active-row products they fit (at most 128 rows; the gate/up product over d = 4096 and
+   * the down projection over F = 12288 in 8 K splits) stream them straight into registers
+   * instead of the row-major copies above, which stay in use for every other product. */
+  const void *w_gate_up_packed; /* w_gate_up packed with gate/up interleave F */
+  const void *w_down_packed;    /* w_down packed without interleave */
 } dllm_layer_w;
 
 typedef struct {
@@ -239,6 +245,19 @@ int dllm_layer_sparse(const dllm_model *model, int32_t layer, void *x_act, const
 int dllm_confidence_kl(const float *logits, void *logits_prev, int32_t prev_dtype, const int32_t *row_pos, int32_t R,
                        int32_t V, int32_t exclude_id, int32_t have_prev, float *conf,
                        int32_t *argmax, float *kl, void *stream);
+
+/* Repacks a bf16 weight W [N, K] (nn.Linear layout) into MFMA B-fragment order for the
+ * active-row products ([ES] 2.1 item 2: at batch 1 they stream the weights): fragment
+ * (nb, ks) -- 32 output columns x 16 reduction elements -- is 1 KB at element
+ * ((ks / 4) * (N / 32) + nb) * 2048 + (ks % 4) * 512 (stage-major: the 64-element stages of all
+ * column blocks one after the other), lane l element e holding
+ * W[row(32 nb + l % 32)][16 ks + 8 (l / 32) + e].
+ * With interleave_f = F > 0, W is the stacked [gate; up] [2F, K] and packed row 32 nb + r is
+ * gate row 16 nb + r (r < 16) or up row F + 16 nb + r - 16, so each output's two factors meet
+ * in one accumulator.
+ *  w: device [N, K] bf16; w_packed: device, N*K bf16 elements, caller-owned, not aliasing w.
+ *  N % 32 == 0, K % 64 == 0; interleave_f is 0 or N / 2 (then a multiple of 16). */
+int dllm_pack_weight(const void *w, void *w_packed, int32_t N, int32_t K, int32_t interleave_f, void *stream);
 
 /* Device planner of one dilated unmasking round ([DUS] technical summary
  * section 2: a block of `block` positions is decoded in R = ceil(log_a block)

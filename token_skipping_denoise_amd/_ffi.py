@@ -17,7 +17,7 @@ MAX_NESTED = 3
 EXPORTED = (
     "dllm_workspace_size", "dllm_score_select", "dllm_gather_rows", "dllm_scatter_rows",
     "dllm_layer_sparse", "dllm_confidence_kl", "dllm_skip_step", "dllm_status_string", "dllm_version",
-    "dllm_set_timing", "dllm_dus_mark",
+    "dllm_set_timing", "dllm_dus_mark", "dllm_pack_weight",
 )
 TK_NONE, TK_QKV, TK_ATTN, TK_O, TK_FFN_UP, TK_FFN_DOWN, TK_LM_HEAD, TK_VOCAB, TK_SCORE, TK_SELECT = range(10)
 
@@ -27,7 +27,8 @@ class Dims(Structure):
 
 
 class LayerW(Structure):
-    _fields_ = [(n, c_void_p) for n in ("attn_norm", "w_qkv", "w_o", "ffn_norm", "w_gate_up", "w_down")]
+    _fields_ = [(n, c_void_p) for n in ("attn_norm", "w_qkv", "w_o", "ffn_norm", "w_gate_up", "w_down",
+                                        "w_gate_up_packed", "w_down_packed")]
 
 
 class ModelC(Structure):
@@ -90,6 +91,8 @@ def load(path: str = LIB_PATH) -> ctypes.CDLL:
     lib.dllm_confidence_kl.restype = c_int32
     lib.dllm_confidence_kl.argtypes = [c_void_p, c_void_p, c_int32, c_void_p, c_int32, c_int32, c_int32, c_int32,
                                        c_void_p, c_void_p, c_void_p, c_void_p]
+    lib.dllm_pack_weight.restype = c_int32
+    lib.dllm_pack_weight.argtypes = [c_void_p, c_void_p, c_int32, c_int32, c_int32, c_void_p]
     lib.dllm_dus_mark.restype = c_int32
     lib.dllm_dus_mark.argtypes = [c_void_p, c_int32, c_int32, c_int32, c_int32, c_int32, c_int32, c_int32, c_int32,
                                   c_void_p]

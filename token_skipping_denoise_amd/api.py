@@ -119,15 +119,30 @@ def dus_mark(force, lo: int, block: int, round: int, *, a: int = 2, rounds: int 
     _check(st, "dllm_dus_mark")
 
 
+def pack_weight(w, interleave_f: int = 0):
+    """A [N, K] bf16 weight repacked into MFMA fragment order (new tensor, same device)."""
+    if w.dtype != torch.bfloat16 or w.dim() != 2:
+        raise DllmError("pack_weight takes a [N, K] bfloat16 tensor")
+    N, K = w.shape
+    out = torch.empty_like(w)
+    st = _lib().dllm_pack_weight(_ptr(w), _ptr(out), N, K, int(interleave_f), _stream(w.device))
+    _check(st, "dllm_pack_weight")
+    return out
+
+
 class Model:
     """Device weights in the C ABI layout plus the dllm_model struct.
 
     ``weights`` holds per-layer tensors wq/wk/wv/wo/wg/wu/wd and norms (as
     produced by synth.workloads); Q/K/V and gate/up are concatenated once
-    here into the fused row layout the library expects.
+    here into the fused row layout the library expects.  With ``pack`` (bf16
+    only) the gate/up and down weights are also stored in MFMA fragment order
+    (dllm_pack_weight), which the library streams for the active-row products
+    those copies fit.
     """
 
-    def __init__(self, weights: dict, n_heads: int, n_kv_heads: int, mask_id: int, rope_base=1e4, rms_eps=1e-5):
+    def __init__(self, weights: dict, n_heads: int, n_kv_heads: int, mask_id: int, rope_base=1e4, rms_eps=1e-5,
+                 pack: bool = True):
         emb = weights["embed"]
         self.dtype = emb.dtype
         self.device = emb.device
@@ -149,9 +164,14 @@ class Model:
                 "w_gate_up": torch.cat([lw["wg"], lw["wu"]], 0).contiguous(),
                 "w_down": lw["wd"].contiguous(),
             })
+        if pack and emb.dtype == torch.bfloat16 and F % 16 == 0 and d % 64 == 0 and F % 64 == 0:
+            for t in self.layers:
+                t["w_gate_up_packed"] = pack_weight(t["w_gate_up"], interleave_f=F)
+                t["w_down_packed"] = pack_weight(t["w_down"])
         self._lw = (_ffi.LayerW * L)()
+        names = ("attn_norm", "w_qkv", "w_o", "ffn_norm", "w_gate_up", "w_down", "w_gate_up_packed", "w_down_packed")
         for i, t in enumerate(self.layers):
-            self._lw[i] = _ffi.LayerW(*[_ptr(t[k]) for k in ("attn_norm", "w_qkv", "w_o", "ffn_norm", "w_gate_up", "w_down")])
+            self._lw[i] = _ffi.LayerW(*[_ptr(t.get(k)) for k in names])
         self.dims_tuple = (V, d, n_heads, n_kv_heads, D, F, L)
         self.mask_id = mask_id
         self.c = _ffi.ModelC()

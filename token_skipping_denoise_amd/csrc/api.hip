@@ -62,6 +62,8 @@ long max_part_floats(const dllm_dims& d, int dtype, long M) {
     const GemmPlan p = gemm_plan(dtype, (int)M, Ns[i], Ks[i]);
     best = std::max(best, (long)p.splits * M * Ns[i]);
   }
+  const PackedPlan pd = packed_plan((int)M, d.d, d.d_ff, false);  // the packed down projection
+  if (dtype == DLLM_BF16 && pd.ok) best = std::max(best, (long)pd.splits * M * d.d);
   return best;
 }
 
@@ -170,9 +172,13 @@ int run_layer(const Ctx& c, int l, void* x, const int32_t* nact, const int32_t* 
   }
   DLLM_TRY(launch_resid_norm(c.dtype, part, p.splits, (long)R * d.d, row_pos, R, d.d, x, w.ffn_norm, eps, xn, c.s));
   if (c.dtype == DLLM_BF16) {
+    const PackedPlan pp = w.w_gate_up_packed ? packed_plan(R, 2 * d.d_ff, d.d, true) : PackedPlan{};
     p = gemm_plan(c.dtype, R, d.d_ff, d.d, true);
     TimedRegion t(DLLM_TK_FFN_UP, R, c.s);
-    DLLM_TRY(launch_gemm_swiglu(p, xn, w.w_gate_up, h, R, d.d_ff, d.d, nact, kx, c.s));
+    if (pp.ok)
+      DLLM_TRY(launch_gemm_packed(pp, xn, w.w_gate_up_packed, nullptr, h, R, 2 * d.d_ff, d.d, d.d_ff, nact, kx, c.s));
+    else
+      DLLM_TRY(launch_gemm_swiglu(p, xn, w.w_gate_up, h, R, d.d_ff, d.d, nact, kx, c.s));
   } else {
     p = gemm_plan(c.dtype, R, 2 * d.d_ff, d.d);
     TimedRegion t(DLLM_TK_FFN_UP, R, c.s);
@@ -181,8 +187,15 @@ int run_layer(const Ctx& c, int l, void* x, const int32_t* nact, const int32_t* 
   }
   p = gemm_plan(c.dtype, R, d.d, d.d_ff);
   {
+    const PackedPlan pp = (c.dtype == DLLM_BF16 && w.w_down_packed) ? packed_plan(R, d.d, d.d_ff, false)
+                                                                     : PackedPlan{};
     TimedRegion t(DLLM_TK_FFN_DOWN, R, c.s);
-    DLLM_TRY(launch_gemm(c.dtype, p, h, w.w_down, part, R, d.d, d.d_ff, nact, kx, c.s));
+    if (pp.ok) {
+      DLLM_TRY(launch_gemm_packed(pp, h, w.w_down_packed, part, nullptr, R, d.d, d.d_ff, 0, nact, kx, c.s));
+      p.splits = pp.splits;
+    } else {
+      DLLM_TRY(launch_gemm(c.dtype, p, h, w.w_down, part, R, d.d, d.d_ff, nact, kx, c.s));
+    }
   }
   DLLM_TRY(launch_resid_norm(c.dtype, part, p.splits, (long)R * d.d, row_pos, R, d.d, x, next_g, eps, xn, c.s));
   return DLLM_OK;
@@ -331,6 +344,15 @@ int dllm_confidence_kl(const float* logits, void* logits_prev, int32_t prev_dtyp
   if (R < 0 || V < 2 || exclude_id >= V) return DLLM_ESHAPE;
   DLLM_TRY(launch_conf_kl(logits, logits_prev, prev_dtype, row_pos, R, V, exclude_id, have_prev, conf, argmax, kl,
                           nullptr, (hipStream_t)stream));
+  return DLLM_OK;
+}
+
+int dllm_pack_weight(const void* w, void* w_packed, int32_t N, int32_t K, int32_t interleave_f, void* stream) {
+  if (!w || !w_packed || w == w_packed) return DLLM_EINVAL;
+  if (!aligned16(w) || !aligned16(w_packed)) return DLLM_EINVAL;
+  if (N < 32 || K < 64 || N % 32 || K % 64) return DLLM_ESHAPE;
+  if (interleave_f != 0 && (2L * interleave_f != N || interleave_f % 16)) return DLLM_ESHAPE;
+  DLLM_TRY(launch_pack_frag(w, w_packed, N, K, interleave_f, (hipStream_t)stream));
   return DLLM_OK;
 }
 

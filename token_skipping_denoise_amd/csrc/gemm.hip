@@ -259,7 +259,7 @@ __global__ __launch_bounds__(64 * WM * WN * KG, OCC) void k_gemm_lds(const uint1
           const float v = acc[i][j][e];
           const float u = __shfl_xor(v, 16, kWave);
           const int row = m0 + wm * (BM / WM) + i * 32 + 8 * (e >> 2) + 4 * (lane >> 5) + (e & 3);
-          if ((lane & 16) == 0 && col < F && row < M) H[(long)row * F + col] = f2bf(v / (1.0f + expf(-v)) * u);
+          if ((lane & 16) == 0 && col < F && row < M) H[(long)row * F + col] = f2bf(silu_fast(v) * u);
         }
       }
   } else {
@@ -274,7 +274,7 @@ __global__ __launch_bounds__(64 * WM * WN * KG, OCC) void k_gemm_lds(const uint1
           const int row = m0 + wm * (BM / WM) + i * 32 + 8 * (e >> 2) + 4 * (lane >> 5) + (e & 3);
           if (row >= M) continue;
           const float g = acc[i][j][e], u = acc[i][j + TN / 2][e];
-          H[(long)row * F + col] = f2bf(g / (1.0f + expf(-g)) * u);
+          H[(long)row * F + col] = f2bf(silu_fast(g) * u);
         }
       }
   }
@@ -329,7 +329,7 @@ __global__ __launch_bounds__(256) void k_gemm_f32(const float* __restrict__ A, c
 #ifndef DLLM_LDS_CASES
 #define DLLM_LDS_CASES                                                                              \
   DLLM_LDS_CASE(128, 64, 4, 1, 2, 2) DLLM_LDS_CASE(128, 128, 2, 1, 2, 2) DLLM_LDS_CASE(128, 128, 3, 1, 2, 2) \
-  DLLM_LDS_CASE(128, 256, 3, 1, 2, 4) DLLM_LDS_CASE(256, 256, 2, 1, 2, 4)
+  DLLM_LDS_CASE(128, 256, 3, 1, 2, 4) DLLM_LDS_CASE(256, 256, 2, 1, 2, 4) DLLM_LDS_CASE(128, 128, 4, 2, 2, 2)
 #endif
 #ifndef DLLM_LDS_SWIGLU_CASES
 #define DLLM_LDS_SWIGLU_CASES                                                                       \
@@ -381,6 +381,13 @@ GemmPlan gemm_plan(int dtype, int M, int N, int K, bool swiglu) {
       target = 192;
     } else if (N > 32768) {
       p.pd = 13;
+    } else if (K >= 2 * N && K % (8 * 64 * 4) == 0 && N % 128 == 0) {
+      // long reductions into narrow outputs (the down projection): 128 x 128 tiles with two
+      // k-groups of wavefronts (two waves per SIMD) and an 8-way K split to fill the chip
+      p.pd = 14;
+      p.kg = 2;
+      p.splits = 8;
+      return p;
     } else {
       p.bn = 64;
       p.pd = 14;

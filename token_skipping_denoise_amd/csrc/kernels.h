@@ -51,6 +51,23 @@ hipError_t launch_gemm(int dtype, const GemmPlan& p, const void* A, const void* 
 hipError_t launch_gemm_swiglu(const GemmPlan& p, const void* A, const void* W_gate_up, void* H, int M, int F, int K,
                               const int32_t* n_active, int k_max, hipStream_t s);
 
+// ---------------- products on fragment-packed weights (gemm_packed.hip) ----------------
+// W [N, K] repacked into 1 KB MFMA B fragments (32 columns x 16 reduction elements); with
+// F > 0 (the stacked [gate; up] [2F, K]) gate and up rows interleave in 16s.
+hipError_t launch_pack_frag(const void* W, void* Wp, int N, int K, int F, hipStream_t s);
+struct PackedPlan {
+  bool ok = false;
+  int nw = 0;      // waves per workgroup, one 32-column block each
+  int splits = 1;  // K splits (fp32 partials)
+  int nkc = 0;     // 64-element stages per split
+};
+// Whether the packed path covers an M x N x K product (M <= 128; compiled stage counts only).
+PackedPlan packed_plan(int M, int N, int K, bool swiglu);
+// swiglu (H non-null): H[m][f] = silu(A Wg^T) * (A Wu^T), N = 2F packed columns; else fp32 partials
+// C[sp][m][n].
+hipError_t launch_gemm_packed(const PackedPlan& p, const void* A, const void* Wp, float* C, void* H, int M, int N,
+                              int K, int F, const int32_t* n_active, int k_max, hipStream_t s);
+
 // ---------------- attention (attention.hip) ----------------
 // o[r, h, :] = softmax(q[r, h] . Kc[b, :, h/g] / sqrt(D)) Vc[b, :, h/g] over all S keys.
 // Split-KV (bf16, few query blocks): `part` needs attention_part_bytes(...) bytes.
