@@ -34,8 +34,6 @@
 namespace dllm {
 
 typedef __bf16 bf16x8_t __attribute__((ext_vector_type(8)));
-typedef __bf16 bf16x2_t __attribute__((ext_vector_type(2)));
-typedef float f32x2_t __attribute__((ext_vector_type(2)));
 typedef float f32x16_t __attribute__((ext_vector_type(16)));
 
 // ---------------- fp32 ----------------
@@ -104,8 +102,56 @@ __device__ __forceinline__ void tr_read8(short4_t (&d)[8], const uint32_t (&a)[8
       : "memory");
 }
 
+// The same for sixteen reads (both 16-key halves of a tile's V^T fragments).
+__device__ __forceinline__ void tr_read16(short4_t (&d)[16], const uint32_t (&a)[16]) {
+  asm volatile(
+      "ds_read_b64_tr_b16 %0, %16\n\t"
+      "ds_read_b64_tr_b16 %1, %17\n\t"
+      "ds_read_b64_tr_b16 %2, %18\n\t"
+      "ds_read_b64_tr_b16 %3, %19\n\t"
+      "ds_read_b64_tr_b16 %4, %20\n\t"
+      "ds_read_b64_tr_b16 %5, %21\n\t"
+      "ds_read_b64_tr_b16 %6, %22\n\t"
+      "ds_read_b64_tr_b16 %7, %23\n\t"
+      "ds_read_b64_tr_b16 %8, %24\n\t"
+      "ds_read_b64_tr_b16 %9, %25\n\t"
+      "ds_read_b64_tr_b16 %10, %26\n\t"
+      "ds_read_b64_tr_b16 %11, %27\n\t"
+      "ds_read_b64_tr_b16 %12, %28\n\t"
+      "ds_read_b64_tr_b16 %13, %29\n\t"
+      "ds_read_b64_tr_b16 %14, %30\n\t"
+      "ds_read_b64_tr_b16 %15, %31\n\t"
+      "s_waitcnt lgkmcnt(0)"
+      : "=&v"(d[0]), "=&v"(d[1]), "=&v"(d[2]), "=&v"(d[3]), "=&v"(d[4]), "=&v"(d[5]), "=&v"(d[6]), "=&v"(d[7]),
+        "=&v"(d[8]), "=&v"(d[9]), "=&v"(d[10]), "=&v"(d[11]), "=&v"(d[12]), "=&v"(d[13]), "=&v"(d[14]),
+        "=&v"(d[15])
+      : "v"(a[0]), "v"(a[1]), "v"(a[2]), "v"(a[3]), "v"(a[4]), "v"(a[5]), "v"(a[6]), "v"(a[7]), "v"(a[8]),
+        "v"(a[9]), "v"(a[10]), "v"(a[11]), "v"(a[12]), "v"(a[13]), "v"(a[14]), "v"(a[15])
+      : "memory");
+}
+
 __device__ __forceinline__ uint32_t lds_addr(const void* p) {
   return (uint32_t)reinterpret_cast<uintptr_t>((const lds_void*)p);
+}
+
+// Combine lanes l and l ^ 32 without an LDS round trip: v_permlane32_swap exchanges the
+// upper half of one register with the lower half of another, so afterwards the two results
+// hold (x[l % 32], x[l % 32 + 32]) in the same order on every lane.
+__device__ __forceinline__ void half_pair(float x, float& lo, float& hi) {
+  const auto r = __builtin_amdgcn_permlane32_swap(__builtin_bit_cast(unsigned, x), __builtin_bit_cast(unsigned, x),
+                                                  false, false);
+  lo = __builtin_bit_cast(float, (unsigned)r[0]);
+  hi = __builtin_bit_cast(float, (unsigned)r[1]);
+}
+__device__ __forceinline__ float half_swap_max(float x) {
+  float a, b;
+  half_pair(x, a, b);
+  return fmaxf(a, b);
+}
+__device__ __forceinline__ float half_swap_sum(float x) {
+  float a, b;
+  half_pair(x, a, b);
+  return a + b;
 }
 
 template <int N>
@@ -223,6 +269,21 @@ __global__ __launch_bounds__(512, 1) void k_attn_bf16(const uint16_t* __restrict
   const int k_sw = swz(k_row);
   const int v_row = grp * 32 + 4 * hi + ((lane & 15) >> 2);    // + 16 hf (+ 8)
   const int v_col = 16 * ((lane >> 4) & 1) + 4 * (lane & 3);  // + 32 db
+  // byte offsets (within a stage's V tile) of the sixteen transposing reads: half hf of the
+  // tile's 32 keys, column block db, rows r0 (keys +0..3) and r0 + 8 (keys +8..11)
+  uint32_t v_off[16];
+#pragma unroll
+  for (int hf = 0; hf < 2; ++hf) {
+    const int r0 = 16 * hf + v_row, r1 = r0 + 8;
+    const int sw0 = swz(r0), sw1 = swz(r1);
+#pragma unroll
+    for (int db = 0; db < kHD / 32; ++db) {
+      const int col = 32 * db + v_col;  // element column of this lane's 8-byte read
+      const int inb = (col & 7) << 1;   // byte within the 16-byte chunk
+      v_off[8 * hf + 2 * db] = r0 * kRowBytes + ((((col >> 3) ^ sw0) << 4) | inb);
+      v_off[8 * hf + 2 * db + 1] = r1 * kRowBytes + ((((col >> 3) ^ sw1) << 4) | inb);
+    }
+  }
   for (int i = 0; i < n_tiles; ++i) {
     // tiles after i may stay in flight (2 loads per tensor per wave each)
     const int ahead = min(kRing - 2, n_tiles - 1 - i);
@@ -236,15 +297,24 @@ __global__ __launch_bounds__(512, 1) void k_attn_bf16(const uint16_t* __restrict
     const uint8_t* vst = kst + kTileBytes;
     // S^T for this group's 32 keys of the tile
     f32x16_t sacc;
+    short4_t tv[16];
     {
       const uint8_t* rp = kst + k_row * kRowBytes;
 #pragma unroll
       for (int e = 0; e < 16; ++e) sacc[e] = 0.f;
+      // every LDS read of the tile in one batch, so the wave waits for LDS once per tile: the
+      // eight K fragments, then the sixteen transposing V^T reads, whose block ends with the wait
+      bf16x8_t kf[kHD / 16];
 #pragma unroll
-      for (int ts = 0; ts < kHD / 16; ++ts) {
-        const bf16x8_t a = *reinterpret_cast<const bf16x8_t*>(rp + (((2 * ts + hi) ^ k_sw) << 4));
-        sacc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, qf[ts], sacc, 0, 0, 0);
-      }
+      for (int ts = 0; ts < kHD / 16; ++ts) kf[ts] = *reinterpret_cast<const bf16x8_t*>(rp + (((2 * ts + hi) ^ k_sw) << 4));
+      const uint32_t vb = lds_addr(vst);
+      uint32_t ad[16];
+#pragma unroll
+      for (int j = 0; j < 16; ++j) ad[j] = vb + v_off[j];
+      tr_read16(tv, ad);
+      __builtin_amdgcn_sched_barrier(0);  // keep the reads together (the scheduler would spread them)
+#pragma unroll
+      for (int ts = 0; ts < kHD / 16; ++ts) sacc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kf[ts], qf[ts], sacc, 0, 0, 0);
     }
     // the last tile may be partial: keys past S score -inf
     const int key0 = t * kKT + grp * 32;
@@ -257,7 +327,7 @@ __global__ __launch_bounds__(512, 1) void k_attn_bf16(const uint16_t* __restrict
     float mt = -INFINITY;
 #pragma unroll
     for (int e = 0; e < 16; ++e) mt = fmaxf(mt, sacc[e]);
-    mt = fmaxf(mt, __shfl_xor(mt, 32, kWave));
+    mt = half_swap_max(mt);
     // The reference max m_run only moves when some query of the wave would otherwise see a
     // weight above 2^8; below that, numerator and sum keep using the old reference, which
     // changes nothing but rounding and saves rescaling the accumulators on almost every tile.
@@ -281,11 +351,12 @@ __global__ __launch_bounds__(512, 1) void k_attn_bf16(const uint16_t* __restrict
       sacc[e] = p;
       rs += p;
     }
-    rs += __shfl_xor(rs, 32, kWave);
+    rs = half_swap_sum(rs);
     l_run += rs;
 
-    // O^T += V^T P^T over two 16-key steps; the V^T fragment (keys r0..r0+3, r0+8..r0+11 of
-    // column 32 db + l32) comes from two transposing reads of the [key][d] tile
+    // O^T += V^T P^T over two 16-key steps; the V^T fragment of half hf and column block db
+    // (keys r0..r0+3 and r0+8..r0+11 of column 32 db + l32) is the pair of transposing reads
+    // 8 hf + 2 db and 8 hf + 2 db + 1 made above
 #pragma unroll
     for (int hf = 0; hf < 2; ++hf) {
       uint32_t pw[4];
@@ -295,23 +366,9 @@ __global__ __launch_bounds__(512, 1) void k_attn_bf16(const uint16_t* __restrict
         pw[e] = __builtin_bit_cast(uint32_t, __builtin_convertvector(pr, bf16x2_t));
       }
       const bf16x8_t pfrag = __builtin_bit_cast(bf16x8_t, make_uint4(pw[0], pw[1], pw[2], pw[3]));
-      const int r0 = 16 * hf + v_row, r1 = r0 + 8;
-      const uint32_t vp0 = lds_addr(vst + r0 * kRowBytes);
-      const uint32_t vp1 = lds_addr(vst + r1 * kRowBytes);
-      const int sw0 = swz(r0), sw1 = swz(r1);
-      uint32_t ad[8];
 #pragma unroll
       for (int db = 0; db < kHD / 32; ++db) {
-        const int col = 32 * db + v_col;  // element column of this lane's 8-byte read
-        const int inb = (col & 7) << 1;   // byte within the 16-byte chunk
-        ad[2 * db] = vp0 + ((((col >> 3) ^ sw0) << 4) | inb);
-        ad[2 * db + 1] = vp1 + ((((col >> 3) ^ sw1) << 4) | inb);
-      }
-      short4_t tv[8];
-      tr_read8(tv, ad);
-#pragma unroll
-      for (int db = 0; db < kHD / 32; ++db) {
-        const short4_t lo = tv[2 * db], hv = tv[2 * db + 1];
+        const short4_t lo = tv[8 * hf + 2 * db], hv = tv[8 * hf + 2 * db + 1];
         const short8_t a8 = {lo[0], lo[1], lo[2], lo[3], hv[0], hv[1], hv[2], hv[3]};
         oacc[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8_t, a8), pfrag, oacc[db], 0, 0, 0);
       }
@@ -319,14 +376,17 @@ __global__ __launch_bounds__(512, 1) void k_attn_bf16(const uint16_t* __restrict
   }
   __syncthreads();  // every wave is done with the ring before it is reused below
 
-  // merge group 1 into group 0 through LDS: [wave][db][e][lane] floats, then (m, l) per wave lane
-  float* xs = reinterpret_cast<float*>(smem);
-  float* ml = xs + 4 * (kHD / 32) * 16 * 64;
+  // merge group 1 into group 0 through LDS: float4 [wave][db][e4][lane] (64 KB), then (m, l)
+  // per wave lane
+  float4* xs = reinterpret_cast<float4*>(smem);
+  float* ml = reinterpret_cast<float*>(smem + 4 * (kHD / 32) * 4 * 64 * sizeof(float4));
   if (grp == 1) {
 #pragma unroll
     for (int db = 0; db < kHD / 32; ++db)
 #pragma unroll
-      for (int e = 0; e < 16; ++e) xs[((gw * (kHD / 32) + db) * 16 + e) * 64 + lane] = oacc[db][e];
+      for (int e4 = 0; e4 < 4; ++e4)
+        xs[((gw * (kHD / 32) + db) * 4 + e4) * 64 + lane] =
+            make_float4(oacc[db][4 * e4], oacc[db][4 * e4 + 1], oacc[db][4 * e4 + 2], oacc[db][4 * e4 + 3]);
     ml[(gw * 2) * 64 + lane] = m_run;
     ml[(gw * 2 + 1) * 64 + lane] = l_run;
   }
@@ -336,22 +396,27 @@ __global__ __launch_bounds__(512, 1) void k_attn_bf16(const uint16_t* __restrict
     const float m1 = ml[(gw * 2) * 64 + lane], l1 = ml[(gw * 2 + 1) * 64 + lane];
     const float M = fmaxf(m_run, m1);
     // both -inf only for a group without keys; keep the merged state finite then
-    const float c0 = (m_run == -INFINITY) ? 0.f : exp2f((m_run - M) * scale_log2e);
-    const float c1 = (m1 == -INFINITY) ? 0.f : exp2f((m1 - M) * scale_log2e);
+    const float c0 = (m_run == -INFINITY) ? 0.f : __builtin_amdgcn_exp2f((m_run - M) * scale_log2e);
+    const float c1 = (m1 == -INFINITY) ? 0.f : __builtin_amdgcn_exp2f((m1 - M) * scale_log2e);
     l_run = l_run * c0 + l1 * c1;
     m_run = M;
 #pragma unroll
     for (int db = 0; db < kHD / 32; ++db)
 #pragma unroll
-      for (int e = 0; e < 16; ++e)
-        oacc[db][e] = oacc[db][e] * c0 + xs[((gw * (kHD / 32) + db) * 16 + e) * 64 + lane] * c1;
+      for (int e4 = 0; e4 < 4; ++e4) {
+        const float4 x = xs[((gw * (kHD / 32) + db) * 4 + e4) * 64 + lane];
+        oacc[db][4 * e4] = oacc[db][4 * e4] * c0 + x.x * c1;
+        oacc[db][4 * e4 + 1] = oacc[db][4 * e4 + 1] * c0 + x.y * c1;
+        oacc[db][4 * e4 + 2] = oacc[db][4 * e4 + 2] * c0 + x.z * c1;
+        oacc[db][4 * e4 + 3] = oacc[db][4 * e4 + 3] * c0 + x.w * c1;
+      }
   }
 
-  if (!qvalid) return;
-  const int jrow = qi / g;
-  const long qrow = (long)b * k_max + jrow;
-  const int h = hk * g + (qi - jrow * g);
   if (nsplit > 1) {
+    if (!qvalid) return;
+    const int jrow = qi / g;
+    const long qrow = (long)b * k_max + jrow;
+    const int h = hk * g + (qi - jrow * g);
     // partial layout: [split][row][head][D + 2] = unnormalised O, then (m, l)
     const long n_rows = (long)(gridDim.z / nsplit) * k_max;  // B * k_max
     float* pp = part + (((long)split * n_rows + qrow) * Hq + h) * (kHD + 2);
@@ -369,6 +434,10 @@ __global__ __launch_bounds__(512, 1) void k_attn_bf16(const uint16_t* __restrict
     }
     return;
   }
+  if (!qvalid) return;
+  const int jrow = qi / g;
+  const long qrow = (long)b * k_max + jrow;
+  const int h = hk * g + (qi - jrow * g);
   const float inv_l = 1.0f / l_run;
   uint16_t* op = o + (qrow * Hq + h) * kHD;
 #pragma unroll
@@ -376,8 +445,8 @@ __global__ __launch_bounds__(512, 1) void k_attn_bf16(const uint16_t* __restrict
 #pragma unroll
     for (int e4 = 0; e4 < 4; ++e4) {
       const int d = db * 32 + 8 * e4 + 4 * hi;
-      const uint32_t w0 = (uint32_t)f2bf(oacc[db][4 * e4] * inv_l) | ((uint32_t)f2bf(oacc[db][4 * e4 + 1] * inv_l) << 16);
-      const uint32_t w1 = (uint32_t)f2bf(oacc[db][4 * e4 + 2] * inv_l) | ((uint32_t)f2bf(oacc[db][4 * e4 + 3] * inv_l) << 16);
+      const uint32_t w0 = pack_bf16x2(oacc[db][4 * e4] * inv_l, oacc[db][4 * e4 + 1] * inv_l);
+      const uint32_t w1 = pack_bf16x2(oacc[db][4 * e4 + 2] * inv_l, oacc[db][4 * e4 + 3] * inv_l);
       *reinterpret_cast<uint2*>(op + d) = make_uint2(w0, w1);
     }
 }

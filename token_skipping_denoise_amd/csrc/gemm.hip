@@ -329,7 +329,8 @@ __global__ __launch_bounds__(256) void k_gemm_f32(const float* __restrict__ A, c
 #ifndef DLLM_LDS_CASES
 #define DLLM_LDS_CASES                                                                              \
   DLLM_LDS_CASE(128, 64, 4, 1, 2, 2) DLLM_LDS_CASE(128, 128, 2, 1, 2, 2) DLLM_LDS_CASE(128, 128, 3, 1, 2, 2) \
-  DLLM_LDS_CASE(128, 256, 3, 1, 2, 4) DLLM_LDS_CASE(256, 256, 2, 1, 2, 4) DLLM_LDS_CASE(128, 128, 4, 2, 2, 2)
+  DLLM_LDS_CASE(128, 256, 3, 1, 2, 4) DLLM_LDS_CASE(256, 256, 2, 1, 2, 4) DLLM_LDS_CASE(128, 128, 4, 2, 2, 2) \
+  DLLM_LDS_CASE(256, 192, 2, 1, 2, 2) DLLM_LDS_CASE(256, 128, 3, 1, 2, 2)
 #endif
 #ifndef DLLM_LDS_SWIGLU_CASES
 #define DLLM_LDS_SWIGLU_CASES                                                                       \
@@ -337,7 +338,7 @@ __global__ __launch_bounds__(256) void k_gemm_f32(const float* __restrict__ A, c
 #endif
 
 #ifndef DLLM_LDS_SWIGLU_ILV_CASES
-#define DLLM_LDS_SWIGLU_ILV_CASES DLLM_LDS_CASE(128, 96, 4, 1, 4, 1)
+#define DLLM_LDS_SWIGLU_ILV_CASES DLLM_LDS_CASE(128, 96, 4, 1, 4, 1) DLLM_LDS_CASE(256, 192, 2, 1, 2, 2)
 #endif
 
 GemmPlan gemm_plan(int dtype, int M, int N, int K, bool swiglu) {
@@ -350,9 +351,10 @@ GemmPlan gemm_plan(int dtype, int M, int N, int K, bool swiglu) {
   // Direct-to-LDS kernel (pd = 10 + stages).  Rules from tile sweeps on the LLaDA-8B layer
   // shapes.  Few rows (HBM bound on the weights): 128-row tiles; wide QKV-like outputs take
   // 256 columns over 2 x 4 wavefronts, narrow ones 64 columns with 4 stages, and split-K
-  // fills the chip.  Many rows (MFMA bound): 256 x 256 tiles for wide outputs, otherwise
-  // 128 x 128 with 2 stages so that two workgroups share a CU; the fused SwiGLU product
-  // runs two k-groups of wavefronts.
+  // fills the chip.  Many rows (MFMA bound): 256-row tiles over 2 x 2 wavefronts where the
+  // shape allows (256 x 192 for the fused SwiGLU product and QKV-like outputs, 256 x 128 with
+  // a 4-way K split for the down projection), otherwise 128 x 128 with 2 stages, so that two
+  // workgroups share a CU, and split-K up to 4.
   const bool few = M <= 192;
   const bool wide = N > 8192 && N <= 32768;
   p.bm = 128;
@@ -393,20 +395,40 @@ GemmPlan gemm_plan(int dtype, int M, int N, int K, bool swiglu) {
       p.pd = 14;
     }
   } else {
+    // 256-row tiles over 2 x 2 wavefronts keep 128 x 96 (or 128 x 64) wave tiles, which read
+    // fewer fragment bytes from LDS per MFMA than 64 x 64 ones
     if (swiglu) {
-      p.pd = 13;
-      p.kg = 2;
+      if (N % 96 == 0) {  // 96 outputs (192 interleaved gate/up rows) per tile
+        p.bm = 256;
+        p.bn = 192;
+        p.wm = 2;
+        p.wn = 2;
+        p.pd = 12;
+        p.ilv = 1;
+      } else {
+        p.pd = 13;
+        p.kg = 2;
+      }
       return p;
     }
     if (wide) {
       p.bm = 256;
-      p.bn = 256;
+      p.bn = (N % 192 == 0) ? 192 : 256;
       p.wm = 2;
-      p.wn = 4;
+      p.wn = (p.bn == 192) ? 2 : 4;
       p.pd = 12;
       target = 192;
+    } else if (K >= 2 * N && N % 128 == 0 && K / (64 * 4) >= 3) {
+      // long reductions into narrow outputs (the down projection)
+      p.bm = 256;
+      p.wm = 2;
+      p.wn = 2;
+      p.pd = 13;
+      p.splits = 4;
+      return p;
     } else {
       p.pd = 12;
+      target = 512;
     }
   }
   const long tiles = (long)((M + p.bm - 1) / p.bm) * ((N + p.bn - 1) / p.bn);

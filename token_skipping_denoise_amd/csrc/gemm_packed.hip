@@ -178,8 +178,7 @@ __device__ __forceinline__ void packed_body(const uint16_t* __restrict__ A, cons
 #pragma unroll
         for (int h = 0; h < 2; ++h) {
           const int e = 4 * g + 2 * h;
-          w2[h] = (uint32_t)f2bf(silu_fast(acc[i][e]) * acc[i][e + 8]) |
-                  ((uint32_t)f2bf(silu_fast(acc[i][e + 1]) * acc[i][e + 9]) << 16);
+          w2[h] = pack_bf16x2(silu_fast(acc[i][e]) * acc[i][e + 8], silu_fast(acc[i][e + 1]) * acc[i][e + 9]);
         }
         *reinterpret_cast<uint2*>(H + (long)row * F + nb * 16 + 8 * g + 4 * hi) = make_uint2(w2[0], w2[1]);
       }

@@ -165,8 +165,8 @@ __device__ __forceinline__ void store4(T* p, long off, const float* v) {
   if constexpr (sizeof(T) == 4) {
     *reinterpret_cast<float4*>(p + off) = make_float4(v[0], v[1], v[2], v[3]);
   } else {
-    const uint32_t w0 = (uint32_t)f2bf(v[0]) | ((uint32_t)f2bf(v[1]) << 16);
-    const uint32_t w1 = (uint32_t)f2bf(v[2]) | ((uint32_t)f2bf(v[3]) << 16);
+    const uint32_t w0 = pack_bf16x2(v[0], v[1]);
+    const uint32_t w1 = pack_bf16x2(v[2], v[3]);
     *reinterpret_cast<uint2*>(p + off) = make_uint2(w0, w1);
   }
 }

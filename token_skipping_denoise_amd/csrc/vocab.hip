@@ -20,15 +20,6 @@ namespace dllm {
 
 constexpr int kVT = 256;
 
-typedef __bf16 bf16x2_t __attribute__((ext_vector_type(2)));
-typedef float f32x2_t __attribute__((ext_vector_type(2)));
-
-// two floats to two bf16 (RNE, the hardware conversion), packed low-first
-__device__ __forceinline__ uint32_t pack_bf16x2(float a, float b) {
-  const f32x2_t v = {a, b};
-  return __builtin_bit_cast(uint32_t, __builtin_convertvector(v, bf16x2_t));
-}
-
 // Online state of a vocabulary slice: max / sum-exp / argmax of the logits (m, s, am); of the
 // logits the KL compares (mk, sk, with the KL numerator t relative to mk); of the previous
 // logits (mp, sp).  With an fp32 KL state the compared logits are the logits themselves, so
