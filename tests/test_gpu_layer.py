@@ -22,10 +22,14 @@ CASES = {
     "bf16_full_rows": (workloads.shrink(workloads.LLADA, n_layers=1, d=512, n_heads=4, n_kv_heads=4, d_ff=1024,
                                         vocab=1000, B=1, S=192, prompt=96), 0.05, [192], 192),
     "f32_tiny": (workloads.shrink(workloads.TINY, n_layers=1, B=2, S=70), 0.1, [17, 30], 30),
-    # one query block over 34 key tiles (ragged): the key range is split across 4 workgroups
-    "bf16_split_kv": (workloads.shrink(workloads.DREAM, n_layers=1, d=256, n_heads=2, n_kv_heads=1, d_ff=384,
+    # 65 KV heads of one 128-query block over 34 key tiles (ragged): too few workgroups for the
+    # chip, so each key range is split across 2 workgroups (split-KV + merge)
+    "bf16_split_kv": (workloads.shrink(workloads.LLADA, n_layers=1, d=256, n_heads=65, n_kv_heads=65, d_ff=384,
                                        vocab=1000, B=1, S=2120, prompt=1024), 0.1, [40], 40),
-    # a single (partial) key tile: one of the two key groups of a workgroup has no keys
+    # 4 x 17 query blocks of 128: enough workgroups for the 128-query kernel without a split
+    "bf16_q128": (workloads.shrink(workloads.LLADA, n_layers=1, d=256, n_heads=17, n_kv_heads=17, d_ff=384,
+                                   vocab=1000, B=4, S=100, prompt=50), 0.1, [37, 20, 1, 9], 37),
+    # two key tiles, one partial, over four waves: two waves of each workgroup have no keys
     "bf16_one_tile": (workloads.shrink(workloads.LLADA, n_layers=1, d=256, n_heads=2, n_kv_heads=2, d_ff=512,
                                        vocab=1000, B=2, S=40, prompt=20), 0.1, [13, 40], 40),
 }

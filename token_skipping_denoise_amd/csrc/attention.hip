@@ -451,6 +451,243 @@ __global__ __launch_bounds__(512, 1) void k_attn_bf16(const uint16_t* __restrict
     }
 }
 
+// ---- short key ranges: 32 query slots per workgroup, keys split among its waves ----
+// With a few hundred keys, a workgroup of 128 queries spends most of its time in the latency
+// of one tile after the next while most CUs have nothing to do.  Here a workgroup owns 32
+// query slots of one (sequence, KV head) -- four times the workgroups -- and each of its four
+// wavefronts takes a contiguous quarter of the 32-key tiles through a two-stage LDS ring of its
+// own, so no wave waits for another until the four softmax states are merged at the end (each
+// wave then finishes one 32-column block of the output).  The per-tile arithmetic is that of
+// k_attn_bf16.
+constexpr int kQT = 32;                       // keys per tile
+constexpr int kQTileBytes = kQT * kRowBytes;  // 8 KB per tensor
+constexpr int kQStage = 2 * kQTileBytes;      // K tile, then V tile
+constexpr int kQRing = 2;                     // stages per wave
+constexpr int kQWaves = 4;
+
+__global__ __launch_bounds__(256, 1) void k_attn_q32(const uint16_t* __restrict__ q, const uint16_t* __restrict__ kc,
+                                                     const uint16_t* __restrict__ vc, uint16_t* __restrict__ o,
+                                                     const int32_t* __restrict__ n_active, int S, int k_max, int Hq,
+                                                     int Hkv, float scale_log2e) {
+  // four per-wave rings (128 KB), then the 32 query rows (8 KB)
+  __shared__ __attribute__((aligned(1024))) uint8_t smem[kQWaves * kQRing * kQStage + kQT * kRowBytes];
+  const int b = blockIdx.z, hk = blockIdx.y;
+  const int g = Hq / Hkv;
+  const int qb0 = blockIdx.x * 32;
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int l32 = lane & 31, hi = lane >> 5;
+  const int ntiles_all = (S + kQT - 1) / kQT;
+  const int t_begin = wave * ntiles_all / kQWaves, t_end = (wave + 1) * ntiles_all / kQWaves;
+  const int n_tiles = t_end - t_begin;
+  uint8_t* ring = smem + wave * kQRing * kQStage;
+  uint8_t* qst = smem + kQWaves * kQRing * kQStage;
+
+  // the 32 query rows: eight 4-row load instructions, two per wave, chunk c of row r in slot
+  // c ^ swz(r)
+  const int kq = k_max * g;
+#pragma unroll
+  for (int i = 0; i < 2; ++i) {
+    const int r = 4 * (wave * 2 + i) + (lane >> 4);
+    const int qs = min(qb0 + r, kq - 1);
+    const int jr = qs / g;
+    const long qrow_r = ((long)b * k_max + jr) * Hq + hk * g + (qs - jr * g);
+    const uint16_t* src = q + qrow_r * kHD + (((lane & 15) ^ swz(r)) << 3);
+    __builtin_amdgcn_global_load_lds((const void*)src, (lds_void*)(qst + (wave * 2 + i) * 1024), 16, 0, 0);
+  }
+
+  // K/V tiles: eight 4-row load instructions per tensor, all issued by the owning wave; lane L
+  // of instruction i fills row 4 i + L / 16, slot L % 16, so it fetches chunk slot ^ swz(row)
+  const long head0 = ((long)b * S * Hkv + hk) * kHD;
+  const int nbytes = S * Hkv * kRowBytes;
+  const __amdgpu_buffer_rsrc_t rsk = __builtin_amdgcn_make_buffer_rsrc((void*)(kc + head0), (short)0, nbytes, kBufWord3);
+  const __amdgpu_buffer_rsrc_t rsv = __builtin_amdgcn_make_buffer_rsrc((void*)(vc + head0), (short)0, nbytes, kBufWord3);
+  int voff[8];
+#pragma unroll
+  for (int i = 0; i < 8; ++i) {
+    const int row = 4 * i + (lane >> 4);
+    voff[i] = row * Hkv * kRowBytes + (((lane & 15) ^ swz(row)) << 4);
+  }
+  const int tile_bytes = kQT * Hkv * kRowBytes;
+  auto issue = [&](int t, int slot) {
+    uint8_t* st = ring + slot * kQStage;
+    const int so = t * tile_bytes;  // in the per-lane offset, which the range check covers
+#pragma unroll
+    for (int i = 0; i < 8; ++i) {
+      __builtin_amdgcn_raw_ptr_buffer_load_lds(rsk, (lds_void*)(st + i * 1024), 16, voff[i] + so, 0, 0, 0);
+      __builtin_amdgcn_raw_ptr_buffer_load_lds(rsv, (lds_void*)(st + kQTileBytes + i * 1024), 16, voff[i] + so, 0, 0,
+                                               0);
+    }
+  };
+#pragma unroll
+  for (int j = 0; j < kQRing; ++j)
+    if (j < n_tiles) issue(t_begin + j, j);
+  const int nq = n_active[b] * g;
+  if (qb0 >= nq) {
+    wait_vm_attn<0>();  // no load may still be writing this workgroup's LDS when it ends
+    return;
+  }
+  // the query rows have landed once at most the tile loads (16 per tile) are outstanding
+  {
+    const int np = min(kQRing, n_tiles);
+    if (np >= 2) wait_vm_attn<32>();
+    else if (np == 1) wait_vm_attn<16>();
+    else wait_vm_attn<0>();
+  }
+  __builtin_amdgcn_s_barrier();
+  bf16x8_t qf[kHD / 16];
+  {
+    const uint8_t* rp = qst + l32 * kRowBytes;
+#pragma unroll
+    for (int t = 0; t < kHD / 16; ++t) qf[t] = *reinterpret_cast<const bf16x8_t*>(rp + (((2 * t + hi) ^ swz(l32)) << 4));
+  }
+  const int qi = qb0 + l32;  // this lane's query slot
+  const bool qvalid = qi < nq;
+
+  f32x16_t oacc[kHD / 32];
+#pragma unroll
+  for (int db = 0; db < kHD / 32; ++db)
+#pragma unroll
+    for (int e = 0; e < 16; ++e) oacc[db][e] = 0.f;
+  float m_run = -INFINITY, l_run = 0.f;
+  const float grow_thr = 8.f / scale_log2e;  // 2^8 in raw score units
+
+  const int k_sw = swz(l32);
+  const int v_row = 4 * hi + ((lane & 15) >> 2);              // + 16 hf (+ 8)
+  const int v_col = 16 * ((lane >> 4) & 1) + 4 * (lane & 3);  // + 32 db
+  uint32_t v_off[16];
+#pragma unroll
+  for (int hf = 0; hf < 2; ++hf) {
+    const int r0 = 16 * hf + v_row, r1 = r0 + 8;
+    const int sw0 = swz(r0), sw1 = swz(r1);
+#pragma unroll
+    for (int db = 0; db < kHD / 32; ++db) {
+      const int col = 32 * db + v_col;
+      const int inb = (col & 7) << 1;
+      v_off[8 * hf + 2 * db] = r0 * kRowBytes + ((((col >> 3) ^ sw0) << 4) | inb);
+      v_off[8 * hf + 2 * db + 1] = r1 * kRowBytes + ((((col >> 3) ^ sw1) << 4) | inb);
+    }
+  }
+  for (int i = 0; i < n_tiles; ++i) {
+    if (i + 1 < n_tiles) wait_vm_attn<16>();  // tile i + 1 may stay in flight
+    else wait_vm_attn<0>();
+    const int t = t_begin + i;
+    const uint8_t* kst = ring + (i % kQRing) * kQStage;
+    f32x16_t sacc;
+    short4_t tv[16];
+    bf16x8_t kf[kHD / 16];
+    {
+      const uint8_t* rp = kst + l32 * kRowBytes;
+#pragma unroll
+      for (int ts = 0; ts < kHD / 16; ++ts) kf[ts] = *reinterpret_cast<const bf16x8_t*>(rp + (((2 * ts + hi) ^ k_sw) << 4));
+      const uint32_t vb = lds_addr(kst + kQTileBytes);
+      uint32_t ad[16];
+#pragma unroll
+      for (int j = 0; j < 16; ++j) ad[j] = vb + v_off[j];
+      tr_read16(tv, ad);  // ends with the LDS wait, so the stage is free afterwards
+      __builtin_amdgcn_sched_barrier(0);
+    }
+    if (i + kQRing < n_tiles) issue(t + kQRing, i % kQRing);
+#pragma unroll
+    for (int e = 0; e < 16; ++e) sacc[e] = 0.f;
+#pragma unroll
+    for (int ts = 0; ts < kHD / 16; ++ts) sacc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kf[ts], qf[ts], sacc, 0, 0, 0);
+    const int key0 = t * kQT;
+    if (key0 + kQT > S) {
+#pragma unroll
+      for (int e = 0; e < 16; ++e)
+        if (key0 + 8 * (e >> 2) + 4 * hi + (e & 3) >= S) sacc[e] = -INFINITY;
+    }
+    float mt = -INFINITY;
+#pragma unroll
+    for (int e = 0; e < 16; ++e) mt = fmaxf(mt, sacc[e]);
+    mt = half_swap_max(mt);
+    if (__builtin_amdgcn_ballot_w64(mt > m_run + grow_thr) != 0) {
+      const float m_new = fmaxf(m_run, mt);
+      const float corr = (m_new == -INFINITY) ? 1.f : __builtin_amdgcn_exp2f((m_run - m_new) * scale_log2e);
+      l_run *= corr;
+      m_run = m_new;
+#pragma unroll
+      for (int db = 0; db < kHD / 32; ++db)
+#pragma unroll
+        for (int e = 0; e < 16; ++e) oacc[db][e] *= corr;
+    }
+    const float mc = (m_run == -INFINITY) ? 0.f : m_run * scale_log2e;
+    float rs = 0.f;
+#pragma unroll
+    for (int e = 0; e < 16; ++e) {
+      const float p = __builtin_amdgcn_exp2f(fmaf(sacc[e], scale_log2e, -mc));
+      sacc[e] = p;
+      rs += p;
+    }
+    rs = half_swap_sum(rs);
+    l_run += rs;
+#pragma unroll
+    for (int hf = 0; hf < 2; ++hf) {
+      uint32_t pw[4];
+#pragma unroll
+      for (int e = 0; e < 4; ++e) pw[e] = pack_bf16x2(sacc[8 * hf + 2 * e], sacc[8 * hf + 2 * e + 1]);
+      const bf16x8_t pfrag = __builtin_bit_cast(bf16x8_t, make_uint4(pw[0], pw[1], pw[2], pw[3]));
+#pragma unroll
+      for (int db = 0; db < kHD / 32; ++db) {
+        const short4_t lo = tv[8 * hf + 2 * db], hv = tv[8 * hf + 2 * db + 1];
+        const short8_t a8 = {lo[0], lo[1], lo[2], lo[3], hv[0], hv[1], hv[2], hv[3]};
+        oacc[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8_t, a8), pfrag, oacc[db], 0, 0, 0);
+      }
+    }
+  }
+  __syncthreads();  // every wave is done with its ring before the rings are reused below
+
+  // merge: every wave leaves its O^T fragments (float4 [wave][db][e4][lane], 64 KB) and (m, l);
+  // wave w then combines the four states for column block w
+  float4* xs = reinterpret_cast<float4*>(smem);
+  float* ml = reinterpret_cast<float*>(smem + kQWaves * (kHD / 32) * 4 * 64 * sizeof(float4));
+#pragma unroll
+  for (int db = 0; db < kHD / 32; ++db)
+#pragma unroll
+    for (int e4 = 0; e4 < 4; ++e4)
+      xs[((wave * (kHD / 32) + db) * 4 + e4) * 64 + lane] =
+          make_float4(oacc[db][4 * e4], oacc[db][4 * e4 + 1], oacc[db][4 * e4 + 2], oacc[db][4 * e4 + 3]);
+  ml[(wave * 2) * 64 + lane] = m_run;
+  ml[(wave * 2 + 1) * 64 + lane] = l_run;
+  __syncthreads();
+  float mw[kQWaves], M = -INFINITY;
+#pragma unroll
+  for (int w = 0; w < kQWaves; ++w) {
+    mw[w] = ml[(w * 2) * 64 + lane];
+    M = fmaxf(M, mw[w]);
+  }
+  float cw[kQWaves], L = 0.f;
+#pragma unroll
+  for (int w = 0; w < kQWaves; ++w) {
+    // a wave without keys (or with only masked ones) keeps m = -inf and contributes nothing
+    cw[w] = (mw[w] == -INFINITY) ? 0.f : __builtin_amdgcn_exp2f((mw[w] - M) * scale_log2e);
+    L += ml[(w * 2 + 1) * 64 + lane] * cw[w];
+  }
+  if (!qvalid) return;
+  const int jrow = qi / g;
+  const long qrow = (long)b * k_max + jrow;
+  const int h = hk * g + (qi - jrow * g);
+  const float inv_l = 1.0f / L;
+  uint16_t* op = o + (qrow * Hq + h) * kHD;
+  const int db = wave;
+#pragma unroll
+  for (int e4 = 0; e4 < 4; ++e4) {
+    float4 acc = make_float4(0.f, 0.f, 0.f, 0.f);
+#pragma unroll
+    for (int w = 0; w < kQWaves; ++w) {
+      const float4 x = xs[((w * (kHD / 32) + db) * 4 + e4) * 64 + lane];
+      acc.x += x.x * cw[w];
+      acc.y += x.y * cw[w];
+      acc.z += x.z * cw[w];
+      acc.w += x.w * cw[w];
+    }
+    const int d = db * 32 + 8 * e4 + 4 * hi;
+    *reinterpret_cast<uint2*>(op + d) =
+        make_uint2(pack_bf16x2(acc.x * inv_l, acc.y * inv_l), pack_bf16x2(acc.z * inv_l, acc.w * inv_l));
+  }
+}
+
 // Combine split-KV partials: O = sum_s O_s 2^(m_s - M) / sum_s l_s 2^(m_s - M).
 __global__ __launch_bounds__(128) void k_attn_merge(const float* __restrict__ part, int nsplit, long split_stride,
                                                     const int32_t* __restrict__ n_active, int k_max, int Hq,
@@ -471,10 +708,17 @@ __global__ __launch_bounds__(128) void k_attn_merge(const float* __restrict__ pa
   o[((long)r * Hq + h) * kHD + d] = f2bf(acc / L);
 }
 
+// The 32-query kernel when 128-query workgroups would occupy at most a quarter of the CUs
+// (measured on the LLaDA-8B shapes: 128 active rows of 32 heads, S 256 .. 2048).
+static bool attention_q32(int B, int k_max, int Hq, int Hkv) {
+  const long wgs128 = (long)((k_max * (Hq / Hkv) + 127) / 128) * Hkv * B;
+  return wgs128 <= 64;
+}
+
 // Split-KV only pays when few workgroups would each stream a long key range: a split's
 // partial (128 queries x (D + 2) fp32) must stay small beside the K/V it summarises.
 int attention_splits(int dtype, int B, int S, int k_max, int Hq, int Hkv) {
-  if (dtype == 0) return 1;
+  if (dtype == 0 || attention_q32(B, k_max, Hq, Hkv)) return 1;
   const int g = Hq / Hkv;
   const long wgs = (long)((k_max * g + 127) / 128) * Hkv * B;
   int ns = 1;
@@ -502,6 +746,11 @@ hipError_t launch_attention(int dtype, const void* q, const void* kc, const void
   const int g = Hq / Hkv;
   const int qblocks = (k_max * g + 127) / 128;
   const float scale_log2e = (float)(1.0 / sqrt((double)D) * 1.4426950408889634);
+  if (attention_q32(B, k_max, Hq, Hkv)) {
+    hipLaunchKernelGGL(k_attn_q32, dim3((k_max * g + 31) / 32, Hkv, B), dim3(256), 0, s, (const uint16_t*)q,
+                       (const uint16_t*)kc, (const uint16_t*)vc, (uint16_t*)o, n_active, S, k_max, Hq, Hkv, scale_log2e);
+    return hipGetLastError();
+  }
   const int ns = attention_splits(dtype, B, S, k_max, Hq, Hkv);
   if (ns > 1 && !part) return hipErrorInvalidValue;
   hipLaunchKernelGGL(k_attn_bf16, dim3(qblocks, Hkv, B * ns), dim3(512), 0, s, (const uint16_t*)q, (const uint16_t*)kc,
