@@ -154,6 +154,20 @@ __device__ __forceinline__ float half_swap_sum(float x) {
   return a + b;
 }
 
+// Workgroup coordinates with the query blocks of one (sequence, KV head) kept on one XCD.
+// Workgroups are dealt to the eight XCDs in turn by linear id; when the grid is a multiple of 8,
+// XCD x takes the x-th contiguous eighth of the (query block fastest) work list instead, so the
+// query blocks that stream the same K/V share that XCD's L2 rather than each fetching it.
+__device__ __forceinline__ void attn_block(int& bx, int& by, int& bz) {
+  const int nx = gridDim.x, ny = gridDim.y;
+  const int n = nx * ny * gridDim.z;
+  int lin = blockIdx.x + nx * (blockIdx.y + ny * blockIdx.z);
+  if ((n & 7) == 0) lin = (lin & 7) * (n >> 3) + (lin >> 3);
+  bx = lin % nx;
+  by = (lin / nx) % ny;
+  bz = lin / (nx * ny);
+}
+
 template <int N>
 __device__ __forceinline__ void wait_vm_attn() {
   static_assert(N >= 0 && N < 64, "vmcnt is a 6-bit field");
@@ -168,9 +182,11 @@ __global__ __launch_bounds__(512, 1) void k_attn_bf16(const uint16_t* __restrict
                                                       const int32_t* __restrict__ n_active, int S, int k_max, int Hq,
                                                       int Hkv, float scale_log2e, int nsplit, float* __restrict__ part) {
   __shared__ __attribute__((aligned(1024))) uint8_t smem[kRing * kStageBytes];  // 128 KB
-  const int b = blockIdx.z / nsplit, split = blockIdx.z - b * nsplit, hk = blockIdx.y;
+  int bx, by, bz;
+  attn_block(bx, by, bz);
+  const int b = bz / nsplit, split = bz - b * nsplit, hk = by;
   const int g = Hq / Hkv;
-  const int qb0 = blockIdx.x * 128;
+  const int qb0 = bx * 128;
   const int tid = threadIdx.x, lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int grp = wave >> 2, gw = wave & 3;
@@ -471,9 +487,11 @@ __global__ __launch_bounds__(256, 1) void k_attn_q32(const uint16_t* __restrict_
                                                      int Hkv, float scale_log2e) {
   // four per-wave rings (128 KB), then the 32 query rows (8 KB)
   __shared__ __attribute__((aligned(1024))) uint8_t smem[kQWaves * kQRing * kQStage + kQT * kRowBytes];
-  const int b = blockIdx.z, hk = blockIdx.y;
+  int bx, by, bz;
+  attn_block(bx, by, bz);
+  const int b = bz, hk = by;
   const int g = Hq / Hkv;
-  const int qb0 = blockIdx.x * 32;
+  const int qb0 = bx * 32;
   const int tid = threadIdx.x, lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int l32 = lane & 31, hi = lane >> 5;
