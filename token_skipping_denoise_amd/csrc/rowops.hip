@@ -15,13 +15,19 @@ namespace dllm {
 
 enum RowMode { kEmbed = 0, kGather = 1, kScatter = 2 };
 
-constexpr int kRowChunks = 4;  // 16-byte chunks per thread: rows up to 1024 chunks
+constexpr int kRowThreads = 512;                  // threads of a row-norm workgroup
+constexpr int kRowChunks = 1024 / kRowThreads;    // 16-byte chunks per thread: rows up to 1024 chunks
 
-__device__ __forceinline__ float block_sum256(float v, float* red) {
+// Sum over the workgroup: butterfly within each wave, then the wave sums in wave order.
+template <int NT>
+__device__ __forceinline__ float block_sum(float v, float* red) {
   v = wave_sum(v);
   if ((threadIdx.x & 63) == 0) red[threadIdx.x >> 6] = v;
   __syncthreads();
-  return red[0] + red[1] + red[2] + red[3];
+  float t = red[0];
+#pragma unroll
+  for (int w = 1; w < NT / 64; ++w) t += red[w];
+  return t;
 }
 
 
@@ -29,13 +35,14 @@ __device__ __forceinline__ float block_sum256(float v, float* red) {
 // One workgroup per row: copy a row (by token id, gather or scatter) and optionally write
 // its RMSNorm * g.  The sum of squares uses the same chunk assignment and reduction order
 // as k_resid_norm, so a row normalised here and one normalised there are bit-identical.
-template <typename T, int MODE>
-__global__ __launch_bounds__(256) void k_rows_norm(const T* __restrict__ src, const int32_t* __restrict__ map,
+template <typename T, int MODE, int NT = kRowThreads>
+__global__ __launch_bounds__(NT) void k_rows_norm(const T* __restrict__ src, const int32_t* __restrict__ map,
                                                    int V, int rows, int w, T* __restrict__ dst,
                                                    const T* __restrict__ g, float eps, T* __restrict__ dst_norm) {
   using E = Elem<T>;
   constexpr int VE = E::kVec;
-  __shared__ float red[4];
+  constexpr int CH = 1024 / NT;  // 16-byte chunks per thread
+  __shared__ float red[NT / 64];
   const int r = blockIdx.x;
   long src_row, dst_row;
   if (MODE == kEmbed) {
@@ -52,11 +59,11 @@ __global__ __launch_bounds__(256) void k_rows_norm(const T* __restrict__ src, co
   const int nchunk = w / VE;
   const uint4* s4 = reinterpret_cast<const uint4*>(src + src_row * (long)w);
   uint4* d4 = dst ? reinterpret_cast<uint4*>(dst + dst_row * (long)w) : nullptr;
-  float f[kRowChunks][VE];
+  float f[CH][VE];
   float ss = 0.f;
 #pragma unroll
-  for (int k = 0; k < kRowChunks; ++k) {
-    const int c = threadIdx.x + 256 * k;
+  for (int k = 0; k < CH; ++k) {
+    const int c = threadIdx.x + NT * k;
     if (c >= nchunk) break;
     const uint4 v = s4[c];
     if (d4) d4[c] = v;
@@ -65,13 +72,13 @@ __global__ __launch_bounds__(256) void k_rows_norm(const T* __restrict__ src, co
     for (int e = 0; e < VE; ++e) ss += f[k][e] * f[k][e];
   }
   if (!g) return;
-  ss = block_sum256(ss, red);
+  ss = block_sum<NT>(ss, red);
   const float inv = 1.0f / sqrtf(ss / (float)w + eps);
   const uint4* g4 = reinterpret_cast<const uint4*>(g);
   uint4* n4 = reinterpret_cast<uint4*>(dst_norm + (long)r * w);
 #pragma unroll
-  for (int k = 0; k < kRowChunks; ++k) {
-    const int c = threadIdx.x + 256 * k;
+  for (int k = 0; k < CH; ++k) {
+    const int c = threadIdx.x + NT * k;
     if (c >= nchunk) break;
     float gf[VE];
     E::unpack(g4[c], gf);
@@ -85,8 +92,8 @@ template <int MODE>
 static hipError_t rows_norm(int dtype, const void* src, const int32_t* map, int V, int rows, int w, void* dst,
                             const void* g, float eps, void* dst_norm, hipStream_t s) {
   if (rows <= 0) return hipSuccess;
-  if (w / (dtype == 0 ? 4 : 8) > 256 * kRowChunks) return hipErrorInvalidValue;
-  dim3 grid(rows), block(256);
+  if (w / (dtype == 0 ? 4 : 8) > kRowThreads * kRowChunks) return hipErrorInvalidValue;
+  dim3 grid(rows), block(kRowThreads);
   if (dtype == 0)
     hipLaunchKernelGGL((k_rows_norm<float, MODE>), grid, block, 0, s, (const float*)src, map, V, rows, w,
                        (float*)dst, (const float*)g, eps, (float*)dst_norm);
@@ -277,24 +284,25 @@ hipError_t launch_qkv_epilogue(int dtype, const float* part, int splits, long sp
 // One workgroup per row: x += sum(partials) (rounded to storage), then xn = rmsnorm(x) * g.
 // Every load of the row is issued up front (values stay in registers), so the row costs
 // about one memory round trip.
-template <typename T, int SPLITS>
-__global__ __launch_bounds__(256) void k_resid_norm(const float* __restrict__ part, int splits_unused, long sstride,
+template <typename T, int SPLITS, int NT = kRowThreads>
+__global__ __launch_bounds__(NT) void k_resid_norm(const float* __restrict__ part, int splits_unused, long sstride,
                                                     const int32_t* __restrict__ row_pos, int R, int d,
                                                     T* __restrict__ x, const T* __restrict__ g, float eps,
                                                     T* __restrict__ xn) {
   using E = Elem<T>;
   constexpr int V = E::kVec;
-  __shared__ float red[4];
+  constexpr int CH = 1024 / NT;  // 16-byte chunks per thread
+  __shared__ float red[NT / 64];
   const int r = blockIdx.x;
   if (row_pos[r] < 0) return;
   const int nchunk = d / V;
   uint4* x4 = reinterpret_cast<uint4*>(x + (long)r * d);
   const float* pr = part + (long)r * d;
-  float f[kRowChunks][V];
+  float f[CH][V];
   float ss = 0.f;
 #pragma unroll
-  for (int k = 0; k < kRowChunks; ++k) {
-    const int c = threadIdx.x + 256 * k;
+  for (int k = 0; k < CH; ++k) {
+    const int c = threadIdx.x + NT * k;
     if (c >= nchunk) break;
     E::unpack(x4[c], f[k]);
 #pragma unroll
@@ -316,13 +324,13 @@ __global__ __launch_bounds__(256) void k_resid_norm(const float* __restrict__ pa
     for (int e = 0; e < V; ++e) ss += f[k][e] * f[k][e];
   }
   if (!g) return;
-  ss = block_sum256(ss, red);
+  ss = block_sum<NT>(ss, red);
   const float inv = 1.0f / sqrtf(ss / (float)d + eps);
   const uint4* g4 = reinterpret_cast<const uint4*>(g);
   uint4* n4 = reinterpret_cast<uint4*>(xn + (long)r * d);
 #pragma unroll
-  for (int k = 0; k < kRowChunks; ++k) {
-    const int c = threadIdx.x + 256 * k;
+  for (int k = 0; k < CH; ++k) {
+    const int c = threadIdx.x + NT * k;
     if (c >= nchunk) break;
     float gf[V];
     E::unpack(g4[c], gf);
@@ -336,9 +344,9 @@ hipError_t launch_resid_norm(int dtype, const float* part, int splits, long spli
                              int R, int d, void* x, const void* g, float eps, void* xn, hipStream_t s) {
   if (R <= 0) return hipSuccess;
   const int vec = dtype == 0 ? 4 : 8;
-  if (d % vec != 0 || d / vec > 256 * kRowChunks) return hipErrorInvalidValue;
+  if (d % vec != 0 || d / vec > kRowThreads * kRowChunks) return hipErrorInvalidValue;
 #define DLLM_RN(T_, SP_)                                                                              \
-  hipLaunchKernelGGL((k_resid_norm<T_, SP_>), dim3(R), dim3(256), 0, s, part, splits, split_stride, row_pos, R, d, \
+  hipLaunchKernelGGL((k_resid_norm<T_, SP_>), dim3(R), dim3(kRowThreads), 0, s, part, splits, split_stride, row_pos, R, d, \
                      (T_*)x, (const T_*)g, eps, (T_*)xn)
 #define DLLM_RN_SPLITS(T_)                          \
   switch (splits) {                                 \
