@@ -330,7 +330,7 @@ __global__ __launch_bounds__(256) void k_gemm_f32(const float* __restrict__ A, c
 #define DLLM_LDS_CASES                                                                              \
   DLLM_LDS_CASE(128, 64, 4, 1, 2, 2) DLLM_LDS_CASE(128, 128, 2, 1, 2, 2) DLLM_LDS_CASE(128, 128, 3, 1, 2, 2) \
   DLLM_LDS_CASE(128, 256, 3, 1, 2, 4) DLLM_LDS_CASE(256, 256, 2, 1, 2, 4) DLLM_LDS_CASE(128, 128, 4, 2, 2, 2) \
-  DLLM_LDS_CASE(256, 192, 2, 1, 2, 2) DLLM_LDS_CASE(256, 128, 3, 1, 2, 2) DLLM_LDS_CASE(128, 192, 3, 1, 2, 2)
+  DLLM_LDS_CASE(256, 192, 2, 1, 4, 2) DLLM_LDS_CASE(256, 128, 3, 1, 4, 2) DLLM_LDS_CASE(128, 192, 3, 1, 2, 2)
 #endif
 #ifndef DLLM_LDS_SWIGLU_CASES
 #define DLLM_LDS_SWIGLU_CASES                                                                       \
@@ -338,7 +338,7 @@ __global__ __launch_bounds__(256) void k_gemm_f32(const float* __restrict__ A, c
 #endif
 
 #ifndef DLLM_LDS_SWIGLU_ILV_CASES
-#define DLLM_LDS_SWIGLU_ILV_CASES DLLM_LDS_CASE(128, 96, 4, 1, 4, 1) DLLM_LDS_CASE(256, 192, 2, 1, 2, 2)
+#define DLLM_LDS_SWIGLU_ILV_CASES DLLM_LDS_CASE(128, 96, 4, 1, 4, 1) DLLM_LDS_CASE(256, 192, 2, 1, 4, 2)
 #endif
 
 GemmPlan gemm_plan(int dtype, int M, int N, int K, bool swiglu) {
@@ -397,13 +397,13 @@ GemmPlan gemm_plan(int dtype, int M, int N, int K, bool swiglu) {
       p.pd = 14;
     }
   } else {
-    // 256-row tiles over 2 x 2 wavefronts keep 128 x 96 (or 128 x 64) wave tiles, which read
-    // fewer fragment bytes from LDS per MFMA than 64 x 64 ones
+    // 256-row tiles over 4 x 2 wavefronts: 64 x 96 (or 64 x 64) wave tiles, and eight waves
+    // issuing the tile loads (the loads in flight per CU, not the MFMAs, bound these tiles)
     if (swiglu) {
       if (N % 96 == 0) {  // 96 outputs (192 interleaved gate/up rows) per tile
         p.bm = 256;
         p.bn = 192;
-        p.wm = 2;
+        p.wm = 4;
         p.wn = 2;
         p.pd = 12;
         p.ilv = 1;
@@ -416,14 +416,14 @@ GemmPlan gemm_plan(int dtype, int M, int N, int K, bool swiglu) {
     if (wide) {
       p.bm = 256;
       p.bn = (N % 192 == 0) ? 192 : 256;
-      p.wm = 2;
+      p.wm = (p.bn == 192) ? 4 : 2;
       p.wn = (p.bn == 192) ? 2 : 4;
       p.pd = 12;
       target = 192;
     } else if (K >= 2 * N && N % 128 == 0 && K / (64 * 4) >= 3) {
       // long reductions into narrow outputs (the down projection)
       p.bm = 256;
-      p.wm = 2;
+      p.wm = 4;
       p.wn = 2;
       p.pd = 13;
       p.splits = 4;
