@@ -330,7 +330,8 @@ __global__ __launch_bounds__(256) void k_gemm_f32(const float* __restrict__ A, c
 #define DLLM_LDS_CASES                                                                              \
   DLLM_LDS_CASE(128, 64, 4, 1, 2, 2) DLLM_LDS_CASE(128, 128, 2, 1, 2, 2) DLLM_LDS_CASE(128, 128, 3, 1, 2, 2) \
   DLLM_LDS_CASE(128, 256, 3, 1, 2, 4) DLLM_LDS_CASE(256, 256, 2, 1, 2, 4) DLLM_LDS_CASE(128, 128, 4, 2, 2, 2) \
-  DLLM_LDS_CASE(256, 192, 2, 1, 4, 2) DLLM_LDS_CASE(256, 128, 3, 1, 4, 2) DLLM_LDS_CASE(128, 192, 3, 1, 2, 2)
+  DLLM_LDS_CASE(256, 192, 2, 1, 4, 2) DLLM_LDS_CASE(256, 128, 3, 1, 4, 2) DLLM_LDS_CASE(128, 192, 3, 1, 4, 2) \
+  DLLM_LDS_CASE(128, 64, 4, 1, 4, 2) DLLM_LDS_CASE(128, 128, 3, 1, 4, 2)
 #endif
 #ifndef DLLM_LDS_SWIGLU_CASES
 #define DLLM_LDS_SWIGLU_CASES                                                                       \
@@ -349,9 +350,10 @@ GemmPlan gemm_plan(int dtype, int M, int N, int K, bool swiglu) {
     return p;
   }
   // Direct-to-LDS kernel (pd = 10 + stages).  Rules from tile sweeps on the LLaDA-8B layer
-  // shapes.  Few rows (HBM bound on the weights): 128-row tiles; wide QKV-like outputs take
-  // 192 columns over 2 x 2 wavefronts (256 over 2 x 4 when 192 does not divide them), narrow
-  // ones 64 columns with 4 stages, and split-K fills the chip.  Many rows (MFMA bound): 256-row tiles over 2 x 2 wavefronts where the
+  // shapes.  Few rows (HBM bound on the weights): 128-row tiles over eight wavefronts (more
+  // waves issuing loads keep more bytes in flight per CU); wide QKV-like outputs take 192
+  // columns (256 over 2 x 4 when 192 does not divide them), narrow ones 64 columns with 4
+  // stages, and split-K fills the chip.  Many rows (MFMA bound): 256-row tiles over 2 x 2 wavefronts where the
   // shape allows (256 x 192 for the fused SwiGLU product and QKV-like outputs, 256 x 128 with
   // a 4-way K split for the down projection), otherwise 128 x 128 with 2 stages, so that two
   // workgroups share a CU, and split-K up to 4.
@@ -379,11 +381,12 @@ GemmPlan gemm_plan(int dtype, int M, int N, int K, bool swiglu) {
       // 128 x 192 tiles over 2 x 2 wavefronts when they divide the width: 4-way split-K then
       // gives 256 workgroups, one per CU
       p.bn = (N % 192 == 0) ? 192 : 256;
-      p.wm = 2;
+      p.wm = (p.bn == 192) ? 4 : 2;
       p.wn = (p.bn == 192) ? 2 : 4;
       p.pd = 13;
       target = 192;
     } else if (N > 32768) {
+      p.wm = 4;
       p.pd = 13;
     } else if (K >= 2 * N && K % (8 * 64 * 4) == 0 && N % 128 == 0) {
       // long reductions into narrow outputs (the down projection): 128 x 128 tiles with two
@@ -394,6 +397,7 @@ GemmPlan gemm_plan(int dtype, int M, int N, int K, bool swiglu) {
       return p;
     } else {
       p.bn = 64;
+      p.wm = 4;
       p.pd = 14;
     }
   } else {
