@@ -22,7 +22,10 @@
 // layout of the scores (any consistent k order gives the same contraction).
 // Only when few workgroups would cover a long key range is that range also
 // split across workgroups (split-KV), whose partial results a second kernel
-// merges.
+// merges.  When 128-query workgroups would leave most CUs idle (the 128 active
+// rows of an early-skip layer), k_attn_q32 serves 32 query slots per workgroup
+// instead, its four waves splitting the keys (see there).  Both remap workgroup
+// ids so that the query blocks of one (sequence, KV head) share an XCD's L2.
 //
 // fp32 kernel (small fp32 models): one wavefront per (row, head), keys one at
 // a time with an online softmax.

@@ -6,12 +6,14 @@
 // [M, K], nn.Linear weights [N, K]), which is the natural layout for the
 // CDNA matrix cores.
 //
-// bf16 path: v_mfma_f32_32x32x16_bf16 (gfx950), fp32 accumulation,
-// 256 threads = 2x2 wavefronts, BK = 64, tiles streamed from memory straight
-// into a multi-stage LDS ring with global_load_lds_dwordx4 (no register
-// staging), XOR-swizzled so MFMA fragment reads are conflict-free.  Split-K
-// writes fp32 partials that the row epilogues reduce; row tiles with no live
-// row exit at once.
+// bf16 path: v_mfma_f32_32x32x16_bf16 (gfx950), fp32 accumulation, WM x WN
+// wavefronts (times KG k-groups) per tile, BK = 64, tiles streamed from memory
+// straight into a multi-stage LDS ring with global_load_lds_dwordx4 (no
+// register staging), XOR-swizzled so MFMA fragment reads are conflict-free.
+// Most plans use eight wavefronts: these kernels are bound by the loads each CU
+// keeps in flight, and more waves issue more of them.  Split-K writes fp32
+// partials that the row epilogues reduce; row tiles with no live row exit at
+// once.
 // Workgroup ids are remapped so that each XCD works on a contiguous range of
 // tiles, m-tile fastest, so tiles sharing a weight panel share that XCD's L2.
 //
