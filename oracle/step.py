@@ -26,6 +26,18 @@ and only the top k_j of them continue.  A row dropped at layer n_j keeps the
 K/V it wrote below n_j; from n_j on it is skipped like any other row (cached
 K/V, final hidden state and statistics reused).
 
+Per-layer caching (dLLM-Cache summary section 3, f2): with layer_cache set, every layer
+l >= b runs a partial update instead of the single selection at b.  Entering layer l, each
+row's hidden state is compared with the one it had when the row was last computed at l (a
+per-layer input cache); the top k rows of each sequence by the step's score settings
+(alpha 0 and the cosine change term give the feature-similarity test) are computed through
+the layer, their K/V overwrite the cache rows, and every other row takes the output it had
+when it was last computed at l (a per-layer output cache).  Both caches keep the new values of
+the computed rows.  A full step computes every row at every layer and fills both caches.  The
+long-interval prompt cache is the caller's force == 2 on prompt positions between full steps.
+After the last layer the rows computed there get the LM head; all others keep their
+statistics (their final hidden state is the cached one).
+
 Readings where the pages leave a step open: the mask id is the last vocabulary
 entry and is excluded from softmax and argmax; a locked row (force == 2) skips
 every layer and the LM head, its cached K/V stay attendable; step 0 has no
@@ -86,6 +98,7 @@ class StepCfg:
     block_hi: int = 0
     unmask_mode: int = UNMASK_CONF
     nested: tuple = ()             # ((layer, k), ...): later layers that narrow the active set
+    layer_cache: bool = False      # per-layer partial update from layer b on (dLLM-Cache)
 
 
 @dataclass
@@ -103,6 +116,8 @@ class OracleState:
     have_prev: bool = False
     kl_state_bf16: bool = False  # previous logits kept rounded to bf16 (compact KL state)
     h_nested: list = field(default_factory=list)  # per nested boundary: [B, S, d] hidden state entering it
+    x_in: list = field(default_factory=list)      # per layer (layer cache): [B, S, d] input when last computed
+    x_out: list = field(default_factory=list)     # per layer (layer cache): [B, S, d] output when last computed
 
     def copy(self) -> "OracleState":
         return OracleState(
@@ -110,11 +125,12 @@ class OracleState:
             None if self.h_bnd_prev is None else self.h_bnd_prev.copy(), self.h_fin.copy(),
             self.conf.copy(), self.kl.copy(), self.argmax.copy(),
             None if self.logits_prev is None else self.logits_prev.copy(), self.force.copy(), self.have_prev,
-            self.kl_state_bf16, [h.copy() for h in self.h_nested])
+            self.kl_state_bf16, [h.copy() for h in self.h_nested], [h.copy() for h in self.x_in],
+            [h.copy() for h in self.x_out])
 
 
 def new_state(model: OracleModel, tokens: np.ndarray, track_kl: bool, kl_state_bf16: bool = False,
-              n_nested: int = 0) -> OracleState:
+              n_nested: int = 0, layer_cache: bool = False) -> OracleState:
     B, S = tokens.shape
     w = model.weights
     d = w["embed"].shape[1]
@@ -135,6 +151,8 @@ def new_state(model: OracleModel, tokens: np.ndarray, track_kl: bool, kl_state_b
         force=np.zeros((B, S), dtype=np.uint8),
         kl_state_bf16=kl_state_bf16,
         h_nested=[np.zeros((B, S, d)) for _ in range(n_nested)],
+        x_in=[np.zeros((B, S, d)) for _ in range(L)] if layer_cache else [],
+        x_out=[np.zeros((B, S, d)) for _ in range(L)] if layer_cache else [],
     )
 
 
@@ -160,7 +178,15 @@ def skip_step(model: OracleModel, st: OracleState, cfg: StepCfg) -> tuple[Oracle
     if not (0 <= b_lay <= L):
         raise ValueError("boundary layer out of range")
     full = bool(cfg.full_step)
-    if not full and st.h_bnd_prev is None:
+    lcache = bool(cfg.layer_cache)
+    if lcache:
+        if len(st.x_in) != L or len(st.x_out) != L:
+            raise ValueError("a layer-cache step needs the per-layer caches in the state")
+        if cfg.nested:
+            raise ValueError("nested boundaries and the layer cache do not combine")
+        if not full and not st.have_prev:
+            raise ValueError("a sparse layer-cache step needs caches filled by an earlier step")
+    elif not full and st.h_bnd_prev is None:
         raise ValueError("a sparse step needs the previous boundary hidden state")
     nested = [(int(nl), int(nk)) for nl, nk in cfg.nested]
     if len(nested) > len(st.h_nested):
@@ -214,20 +240,49 @@ def skip_step(model: OracleModel, st: OracleState, cfg: StepCfg) -> tuple[Oracle
         rows = new_rows
         nested_rows.append(rows.copy())
 
+    layer_sel, layer_scores = [], []
+
+    def cached_layer(l, lw):
+        """Partial update of layer l over every row (x: all B*S rows in, all rows out)."""
+        nonlocal x, rows
+        xi, xo = st.x_in[l].reshape(B * S, d), st.x_out[l].reshape(B * S, d)
+        if full:
+            xi[:] = x
+            x = layer_rows(lw, x, rows % S, rows // S, st.k_cache[l], st.v_cache[l], n_heads=model.n_heads,
+                           n_kv_heads=model.n_kv_heads, rope_base=model.rope_base, eps=model.eps, store=store)
+            xo[:] = x
+            return
+        s = importance_score(x, xi, st.conf.reshape(-1), st.kl.reshape(-1), alpha=cfg.score.alpha,
+                             var=cfg.score.var, conf_inverted=cfg.score.conf_inverted).reshape(B, S)
+        sel = np.concatenate([b * S + _select(cfg.score, s[b], st.force[b]) for b in range(B)]).astype(np.int64)
+        layer_scores.append(s)
+        layer_sel.append(sel)
+        xi[sel] = x[sel]
+        xo[sel] = layer_rows(lw, x[sel], sel % S, sel // S, st.k_cache[l], st.v_cache[l], n_heads=model.n_heads,
+                             n_kv_heads=model.n_kv_heads, rope_base=model.rope_base, eps=model.eps, store=store)
+        x = xo.copy()
+        rows = sel
+
     for l in range(L):
-        if l == b_lay:
+        if l == b_lay and not lcache:
             boundary()
         for j, (nl, nk) in enumerate(nested):
             if l == nl:
                 nested_boundary(j, nk)
         lw = w["layers"][l]
+        if lcache and l >= b_lay:
+            cached_layer(l, lw)
+            continue
         x = layer_rows(lw, x, rows % S, rows // S, st.k_cache[l], st.v_cache[l],
                        n_heads=model.n_heads, n_kv_heads=model.n_kv_heads,
                        rope_base=model.rope_base, eps=model.eps, store=store)
-    if b_lay == L:
+    if b_lay == L and not lcache:
         boundary()
 
-    st.h_bnd_prev = h_bnd_new
+    if not lcache:
+        st.h_bnd_prev = h_bnd_new
+    if x.shape[0] != len(rows):          # layer cache: x holds every row, the last layer computed `rows`
+        x = x[rows]
     hf = st.h_fin.reshape(B * S, d)
     hf[rows] = x
     z = lm_logits(x, w["final_norm"], w["lm_head"], model.eps, store)
@@ -249,4 +304,4 @@ def skip_step(model: OracleModel, st: OracleState, cfg: StepCfg) -> tuple[Oracle
                                     cfg.block_lo, cfg.block_hi, cfg.unmask_n)
     st.have_prev = True
     return st, {"rows": rows, "scores": scores, "logits": z, "nested_rows": nested_rows,
-                "nested_scores": nested_scores}
+                "nested_scores": nested_scores, "layer_rows": layer_sel, "layer_scores": layer_scores}

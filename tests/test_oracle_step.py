@@ -303,3 +303,121 @@ def test_nested_layers_validated(nested):
     st = new_state(m, tok, True, n_nested=2)
     with pytest.raises(ValueError):
         skip_step(m, st, StepCfg(boundary_layer=0, full_step=True, nested=nested))
+
+
+# ---- per-layer cache (dLLM-Cache summary section 3) ----
+
+def _lc_full(m, tok, b):
+    st = new_state(m, tok, True, layer_cache=True)
+    return skip_step(m, st, StepCfg(boundary_layer=b, full_step=True, layer_cache=True))
+
+
+@pytest.mark.parametrize("b", [0, 1])
+def test_layer_cache_full_step_fills_caches_with_dense_layer_io(b):
+    """Full step: the cache of layer l >= b holds the dense pass's hidden state entering layer l
+    (input) and entering layer l + 1 (output; the final hidden state after the last layer)."""
+    m = tiny_model(21)
+    tok = tokens(22)
+    st, _ = _lc_full(m, tok, b)
+    for l in range(L):
+        if l < b:
+            assert not st.x_in[l].any() and not st.x_out[l].any()
+            continue
+        np.testing.assert_allclose(st.x_in[l], dense(m, tok, l)["h_bnd"], rtol=1e-12, atol=1e-12)
+        want_out = dense(m, tok, l + 1)["h_bnd"] if l + 1 < L else dense(m, tok)["h_fin"]
+        np.testing.assert_allclose(st.x_out[l], want_out, rtol=1e-12, atol=1e-12)
+
+
+@pytest.mark.parametrize("b", [0, 2])
+def test_layer_cache_every_row_equals_dense(b):
+    """k = S: every row recomputed at every layer, so the step is the dense recompute of the new
+    tokens (K/V of every layer, final hidden state, logits)."""
+    m = tiny_model(23)
+    tok = tokens(24)
+    st, _ = _lc_full(m, tok, b)
+    st.tokens[0, 7] = 3
+    st.tokens[1, 10] = 5
+    st2, info = skip_step(m, st, StepCfg(boundary_layer=b, full_step=False, layer_cache=True,
+                                         score=ScoreCfg(alpha=0.0, var=VAR_COS, k=S)))
+    ref = dense(m, st.tokens)
+    for l in range(L):
+        np.testing.assert_allclose(st2.k_cache[l], ref["k"][l], rtol=1e-11, atol=1e-12)
+        np.testing.assert_allclose(st2.v_cache[l], ref["v"][l], rtol=1e-11, atol=1e-12)
+    np.testing.assert_allclose(st2.h_fin, ref["h_fin"], rtol=1e-11, atol=1e-12)
+    np.testing.assert_allclose(info["logits"], ref["logits"].reshape(B * S, V), rtol=1e-10, atol=1e-11)
+    assert len(info["layer_rows"]) == L - b
+
+
+def test_layer_cache_unchanged_tokens_reproduce_dense_and_tie_on_index():
+    """Nothing changed since the full step: every change term is 0, so each layer keeps the first
+    k positions of every sequence, and reused and recomputed rows both equal the dense values."""
+    m = tiny_model(25)
+    tok = tokens(26)
+    st, _ = _lc_full(m, tok, 0)
+    k = 3
+    st2, info = skip_step(m, st, StepCfg(boundary_layer=0, full_step=False, layer_cache=True,
+                                         score=ScoreCfg(alpha=0.0, var=VAR_COS, k=k)))
+    want = np.concatenate([bb * S + np.arange(k) for bb in range(B)])
+    for sel in info["layer_rows"]:
+        np.testing.assert_array_equal(sel, want)
+    for sc in info["layer_scores"]:
+        assert np.all(np.abs(sc) < 1e-12)
+    ref = dense(m, tok)
+    np.testing.assert_allclose(st2.h_fin, ref["h_fin"], rtol=1e-11, atol=1e-12)
+    for l in range(L):
+        np.testing.assert_allclose(st2.x_out[l], st.x_out[l], rtol=1e-11, atol=1e-12)
+
+
+def test_layer_cache_selects_the_changed_row_and_reuses_the_rest():
+    """One token changes: at layer 0 only its row's input differs from the cache, so with k = 1 and
+    the cosine change term that row is recomputed; every other row keeps its cached layer output
+    and K/V, and rows not recomputed at the last layer keep their statistics."""
+    m = tiny_model(27)
+    tok = tokens(28)
+    st, _ = _lc_full(m, tok, 0)
+    p = 8
+    st.tokens[1, p] = 4
+    st2, info = skip_step(m, st, StepCfg(boundary_layer=0, full_step=False, layer_cache=True,
+                                         score=ScoreCfg(alpha=0.0, var=VAR_COS, k=1)))
+    sel0 = info["layer_rows"][0]
+    assert sel0[1] == S + p                                     # sequence 1: the changed position
+    assert info["layer_scores"][0][1, p] > 0 and np.all(np.delete(info["layer_scores"][0][1], p) < 1e-12)
+    others = np.setdiff1d(np.arange(B * S), sel0)
+    np.testing.assert_array_equal(st2.x_out[0].reshape(B * S, d)[others], st.x_out[0].reshape(B * S, d)[others])
+    kc0, kc1 = st.k_cache[0].reshape(B * S, -1), st2.k_cache[0].reshape(B * S, -1)
+    np.testing.assert_array_equal(kc1[others], kc0[others])
+    assert not np.allclose(kc1[S + p], kc0[S + p])
+    np.testing.assert_array_equal(st2.x_in[0].reshape(B * S, d)[S + p], m.weights["embed"][4])
+    last = info["rows"]
+    keep = np.setdiff1d(np.arange(B * S), last)
+    np.testing.assert_array_equal(st2.h_fin.reshape(B * S, d)[keep], st.h_fin.reshape(B * S, d)[keep])
+    np.testing.assert_array_equal(st2.conf.reshape(-1)[keep], st.conf.reshape(-1)[keep])
+    np.testing.assert_array_equal(st2.argmax.reshape(-1)[keep], st.argmax.reshape(-1)[keep])
+    np.testing.assert_array_equal(st2.h_fin.reshape(B * S, d)[last], st2.x_out[L - 1].reshape(B * S, d)[last])
+
+
+def test_layer_cache_locked_prompt_rows_are_never_recomputed():
+    """Long-interval prompt cache: prompt positions locked (force 2) between full steps are never
+    selected and keep their cached K/V at every layer."""
+    m = tiny_model(29)
+    tok = tokens(30)
+    st, _ = _lc_full(m, tok, 0)
+    st.force[:, :6] = 2
+    st.tokens[0, 9] = 2
+    st2, info = skip_step(m, st, StepCfg(boundary_layer=0, full_step=False, layer_cache=True,
+                                         score=ScoreCfg(alpha=0.0, var=VAR_COS, k=4)))
+    for sel in info["layer_rows"]:
+        assert np.all(sel % S >= 6)
+    for l in range(L):
+        np.testing.assert_array_equal(st2.k_cache[l][:, :6], st.k_cache[l][:, :6])
+
+
+def test_layer_cache_validated():
+    m = tiny_model(31)
+    tok = tokens(32)
+    st = new_state(m, tok, True)                       # no per-layer caches
+    with pytest.raises(ValueError):
+        skip_step(m, st, StepCfg(boundary_layer=0, full_step=True, layer_cache=True))
+    st, _ = _lc_full(m, tok, 0)
+    with pytest.raises(ValueError):
+        skip_step(m, st, StepCfg(boundary_layer=1, full_step=False, layer_cache=True, nested=((2, 1),)))
