@@ -161,6 +161,10 @@ typedef struct {
   void *h_nested[DLLM_MAX_NESTED]; /* device [B, S, d] each, or NULL: the hidden state entering
                              nested layer j the last time each position was computed there
                              (written by full steps and by every row reaching that layer) */
+  void **x_in_cache;      /* per-layer cache (step cfg layer_cache), or NULL: host array [L] of device
+                             [B, S, d], the hidden state entering layer l when each position was last
+                             computed there; entries below the boundary layer may be NULL */
+  void **x_out_cache;     /* the same for the hidden state leaving layer l */
 } dllm_state;
 
 typedef struct {
@@ -185,6 +189,16 @@ typedef struct {
   int32_t n_nested;                       /* 0..DLLM_MAX_NESTED */
   int32_t nested_layer[DLLM_MAX_NESTED];
   int32_t nested_k[DLLM_MAX_NESTED];      /* 0 <= k <= state->k_max */
+  /* Per-layer cache ([DC] section 3: partial response update gated by feature similarity; the
+   * long-interval prompt cache is force == 2 on prompt positions between full steps).  With
+   * layer_cache = 1, every layer l >= boundary_layer replaces the single selection: each
+   * position's hidden state entering l is scored against x_in_cache[l] with `score` (alpha 0 and
+   * DLLM_VAR_COS give the cosine-similarity test), the top score.k per sequence (forced first,
+   * locked excluded, ties to the lower position) are computed through layer l and written to
+   * both caches, and every other position takes x_out_cache[l] as its output.  The rows computed
+   * at the last layer get the LM head; idx / n_active report them.  A full step fills both caches
+   * of layers >= boundary_layer for every position.  Needs n_nested = 0. */
+  int32_t layer_cache;
 } dllm_step_cfg;
 
 /* Bytes of device workspace needed by dllm_skip_step / dllm_layer_sparse for

@@ -180,6 +180,8 @@ def skip_step(model: OracleModel, st: OracleState, cfg: StepCfg) -> tuple[Oracle
     full = bool(cfg.full_step)
     lcache = bool(cfg.layer_cache)
     if lcache:
+        if b_lay >= L:
+            raise ValueError("the layer cache needs a layer at or above the boundary")
         if len(st.x_in) != L or len(st.x_out) != L:
             raise ValueError("a layer-cache step needs the per-layer caches in the state")
         if cfg.nested:

@@ -87,6 +87,57 @@ def test_argument_validation_returns_before_launch(lib):
     assert lib.dllm_skip_step(None, None, None, None) == 1
 
 
+def _fake_step_args(n_layers=2):
+    """A model / state / step config whose pointers are never dereferenced (validation fails
+    first), keeping the host arrays alive on the returned tuple."""
+    F = 0x1000                                         # 16-byte aligned, never read
+    lw = (_ffi.LayerW * n_layers)(*[_ffi.LayerW(*([F] * 6), None, None) for _ in range(n_layers)])
+    m = _ffi.ModelC(_ffi.Dims(1, 8, 128, 1, 1, 128, 128, 16, n_layers), 1, 1e4, 1e-5, 15, F,
+                    ctypes.cast(lw, ctypes.POINTER(_ffi.LayerW)), F, F)
+    kv = (ctypes.c_void_p * n_layers)(*([F] * n_layers))
+    st = _ffi.StateC()
+    for f in ("tokens", "h_fin", "conf", "kl", "argmax", "idx", "n_active", "force"):
+        setattr(st, f, F)
+    st.k_cache = ctypes.cast(kv, ctypes.POINTER(ctypes.c_void_p))
+    st.v_cache = ctypes.cast(kv, ctypes.POINTER(ctypes.c_void_p))
+    st.h_bnd[0] = st.h_bnd[1] = F
+    st.k_max = 4
+    st.have_prev = 1
+    cfg = _ffi.StepCfg()
+    cfg.boundary_layer = 0
+    cfg.full_step = 0
+    cfg.score = _ffi.ScoreCfg(0.0, 0, 1, 0, 2, 0.0)
+    cfg.lock_kl_eps = -1.0
+    cfg.layer_cache = 1
+    return m, st, cfg, (lw, kv)
+
+
+def test_layer_cache_validation_returns_before_launch(lib):
+    m, st, cfg, keep = _fake_step_args()
+    # per-layer caches missing
+    assert lib.dllm_skip_step(ctypes.byref(m), ctypes.byref(st), ctypes.byref(cfg), None) == 1
+    caches = (ctypes.c_void_p * 2)(0x1000, 0x1000)
+    st.x_in_cache = ctypes.cast(caches, ctypes.POINTER(ctypes.c_void_p))
+    st.x_out_cache = ctypes.cast(caches, ctypes.POINTER(ctypes.c_void_p))
+    # the boundary must leave a cached layer; nested boundaries do not combine with the cache
+    cfg.boundary_layer = 2
+    assert lib.dllm_skip_step(ctypes.byref(m), ctypes.byref(st), ctypes.byref(cfg), None) == 1
+    cfg.boundary_layer = 0
+    cfg.n_nested = 1
+    cfg.nested_layer[0] = 1
+    cfg.nested_k[0] = 1
+    st.h_nested[0] = 0x1000
+    assert lib.dllm_skip_step(ctypes.byref(m), ctypes.byref(st), ctypes.byref(cfg), None) == 1
+    cfg.n_nested = 0
+    # a misaligned cache row buffer
+    bad = (ctypes.c_void_p * 2)(0x1000, 0x1004)
+    st.x_out_cache = ctypes.cast(bad, ctypes.POINTER(ctypes.c_void_p))
+    assert lib.dllm_skip_step(ctypes.byref(m), ctypes.byref(st), ctypes.byref(cfg), None) == 1
+    # everything valid but no workspace: still no launch
+    st.x_out_cache = ctypes.cast(caches, ctypes.POINTER(ctypes.c_void_p))
+    assert lib.dllm_skip_step(ctypes.byref(m), ctypes.byref(st), ctypes.byref(cfg), None) == 4
+
+
 def test_struct_layouts_match_header(tmp_path):
     """Every ctypes struct of the binding has the header's size and field offsets (gcc, CPU only)."""
     import shutil

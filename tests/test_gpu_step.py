@@ -385,3 +385,79 @@ def test_bf16_nested_boundaries():
         assert_close(np64(hn)[reached], os_.h_nested[j].reshape(BS, -1)[reached], 2e-2, f"h_nested {j} rows")
         idle = np.setdiff1d(np.arange(BS), reached)
         assert torch.equal(hn[idle], hn_before[j].reshape(BS, -1)[idle])
+
+
+@pytest.mark.parametrize("case", ["tiers_b1", "changed_b0"])
+def test_bf16_layer_cache(case):
+    """Per-layer cache steps ([DC] section 3) against the oracle, prompt rows locked between full
+    steps.  tiers_b1: layer 0 dense, layers 1-3 cached, alpha 0.8 with two separated confidence
+    tiers (8 rows per sequence recomputed at every cached layer).  changed_b0: every layer cached,
+    alpha 0 (cosine change only), k = the 3 positions whose tokens changed."""
+    dims = workloads.shrink(workloads.LLADA, n_layers=4, d=256, n_heads=2, n_kv_heads=2, d_ff=512, vocab=1000,
+                            B=2, S=96, prompt=48)
+    B, S, L = dims.B, dims.S, dims.n_layers
+    BS = B * S
+    b, k, alpha = (1, 8, 0.8) if case == "tiers_b1" else (0, 3, 0.0)
+    print(f"layer cache {case}", flush=True)
+    gm, om = _models(dims, std=0.05)
+    tok = workloads.initial_tokens(dims)
+    gs = api.State(gm, tok.to(DEV), k_max=k, track_kl=True, layer_cache=True)
+    ws = api.alloc_workspace(gm, B, S, k)
+    os_ = new_state(om, tok.numpy(), track_kl=True, layer_cache=True)
+    api.skip_step(gm, gs, api.step_cfg(b, True, ws=ws, layer_cache=True))
+    os_, _ = skip_step(om, os_, StepCfg(boundary_layer=b, full_step=True, layer_cache=True))
+    torch.cuda.synchronize()
+    for l in range(b, L):   # a full step fills both caches of every cached layer
+        assert_close(np64(gs.x_in[l]).reshape(BS, -1), os_.x_in[l].reshape(BS, -1), 2e-2, f"x_in {l}")
+        assert_close(np64(gs.x_out[l]).reshape(BS, -1), os_.x_out[l].reshape(BS, -1), 2e-2, f"x_out {l}")
+    if case == "tiers_b1":
+        # 8 response positions per sequence well above every other (the prompt rows are locked)
+        u = synth.uniform01(synth.seed_of(93), (B, S)).numpy().astype(np.float64)
+        conf = 0.3 * u
+        for bb in range(B):
+            for i in [50, 51, 52, 60 + bb, 66, 71, 77 + bb, 84]:
+                conf[bb, i] = 0.75 + 0.25 * u[bb, i]
+        conf = conf.astype(np.float32)
+        gs.conf.copy_(torch.from_numpy(conf))
+        os_.conf = conf.astype(np.float64)
+    force = np.zeros((B, S), dtype=np.uint8)
+    force[:, :dims.prompt] = 2                                  # long-interval prompt cache
+    gs.force.copy_(torch.from_numpy(force))
+    os_.force = force.copy()
+    new_tok = tok.clone()
+    new_tok[:, 50:53] = torch.tensor([5, 6, 7], dtype=torch.int32)
+    gs.tokens.copy_(new_tok)
+    os_.tokens = new_tok.numpy().astype(np.int64)
+    kv_before = [(a.cpu().clone(), v.cpu().clone()) for a, v in zip(gs.k_cache, gs.v_cache)]
+    xi_before = [t.cpu().clone() for t in gs.x_in]
+    xo_before = [t.cpu().clone() for t in gs.x_out]
+    hf_before = gs.h_fin.cpu().clone()
+    gsc, osc = _score_cfg_pair(alpha, VAR_COS, SEL_TOPK, k)
+    api.skip_step(gm, gs, api.step_cfg(b, False, gsc, ws=ws, layer_cache=True))
+    os_, info = skip_step(om, os_, StepCfg(boundary_layer=b, full_step=False, score=osc, layer_cache=True))
+    torch.cuda.synchronize()
+    assert len(info["layer_rows"]) == L - b
+    for s in info["layer_scores"]:        # every layer's selection is well separated
+        assert min(selection_gap(s[bb], force[bb], k) for bb in range(B)) > 0.02
+    got_rows = [bb * S + int(i) for bb in range(B) for i in gs.idx[bb, :int(gs.n_active[bb])].cpu()]
+    assert got_rows == info["rows"].tolist()
+    for l in range(L):
+        rows_l = np.arange(BS) if l < b else info["layer_rows"][l - b]
+        assert np.all(rows_l % S >= dims.prompt) or l < b
+        idle = np.setdiff1d(np.arange(BS), rows_l)
+        for t_g, t_o, t_b, nm in ((gs.k_cache[l], os_.k_cache[l], kv_before[l][0], "K"),
+                                  (gs.v_cache[l], os_.v_cache[l], kv_before[l][1], "V")):
+            g2 = t_g.cpu().reshape(BS, -1)
+            assert_close(np64(g2)[rows_l], t_o.reshape(BS, -1)[rows_l], 2e-2, f"{nm} {l}")
+            assert torch.equal(g2[idle], t_b.reshape(BS, -1)[idle]), f"{nm} layer {l} idle rows"
+        if l >= b:
+            for t_g, t_o, t_b, nm in ((gs.x_in[l], os_.x_in[l], xi_before[l], "x_in"),
+                                      (gs.x_out[l], os_.x_out[l], xo_before[l], "x_out")):
+                g2 = t_g.cpu().reshape(BS, -1)
+                assert_close(np64(g2)[rows_l], t_o.reshape(BS, -1)[rows_l], 2e-2, f"{nm} {l}")
+                assert torch.equal(g2[idle], t_b.reshape(BS, -1)[idle]), f"{nm} layer {l} idle rows"
+    final = info["rows"]
+    _compare_state(gs, os_, final, 2e-2, "layer cache")
+    _argmax_ok(gs, os_, final, 0.05)
+    others = np.setdiff1d(np.arange(BS), final)
+    assert torch.equal(gs.h_fin.cpu().reshape(BS, -1)[others], hf_before.reshape(BS, -1)[others])

@@ -47,7 +47,8 @@ class StateC(Structure):
                 ("h_bnd", c_void_p * 2), ("bnd_cur", c_int32), ("h_fin", c_void_p), ("conf", c_void_p),
                 ("kl", c_void_p), ("argmax", c_void_p), ("logits_prev", c_void_p), ("force", c_void_p),
                 ("idx", c_void_p), ("n_active", c_void_p), ("k_max", c_int32), ("have_prev", c_int32),
-                ("logits_prev_dtype", c_int32), ("h_nested", c_void_p * MAX_NESTED)]
+                ("logits_prev_dtype", c_int32), ("h_nested", c_void_p * MAX_NESTED),
+                ("x_in_cache", POINTER(c_void_p)), ("x_out_cache", POINTER(c_void_p))]
 
 
 class StepCfg(Structure):
@@ -55,7 +56,7 @@ class StepCfg(Structure):
                 ("lock_kl_eps", c_float), ("lock_conf_min", c_float), ("unmask_n", c_int32),
                 ("block_lo", c_int32), ("block_hi", c_int32), ("unmask_mode", c_int32), ("ws", c_void_p),
                 ("ws_bytes", c_size_t), ("n_nested", c_int32), ("nested_layer", c_int32 * MAX_NESTED),
-                ("nested_k", c_int32 * MAX_NESTED)]
+                ("nested_k", c_int32 * MAX_NESTED), ("layer_cache", c_int32)]
 
 
 class Timing(Structure):

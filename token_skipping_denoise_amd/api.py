@@ -214,9 +214,10 @@ class State:
     """Persistent device state of one generation run (tensors + dllm_state struct)."""
 
     def __init__(self, model: Model, tokens: torch.Tensor, k_max: int, track_kl: bool = False, with_force: bool = True,
-                 kl_state: str = "f32", n_nested: int = 0):
+                 kl_state: str = "f32", n_nested: int = 0, layer_cache: bool = False):
         """kl_state: "f32" or "bf16", the precision the previous logits are kept in (with track_kl).
-        n_nested: hidden-state caches for that many nested boundaries."""
+        n_nested: hidden-state caches for that many nested boundaries.
+        layer_cache: per-layer input/output hidden-state caches for the per-layer cache steps."""
         if kl_state not in ("f32", "bf16"):
             raise DllmError("kl_state must be 'f32' or 'bf16'")
         if not 0 <= n_nested <= _ffi.MAX_NESTED:
@@ -231,6 +232,8 @@ class State:
         self.h_bnd = [torch.zeros((B, S, d), dtype=dt, device=dev) for _ in range(2)]
         self.h_fin = torch.zeros((B, S, d), dtype=dt, device=dev)
         self.h_nested = [torch.zeros((B, S, d), dtype=dt, device=dev) for _ in range(n_nested)]
+        self.x_in = [torch.zeros((B, S, d), dtype=dt, device=dev) for _ in range(L)] if layer_cache else []
+        self.x_out = [torch.zeros((B, S, d), dtype=dt, device=dev) for _ in range(L)] if layer_cache else []
         self.conf = torch.zeros((B, S), dtype=torch.float32, device=dev)
         self.kl = torch.full((B, S), float("inf"), dtype=torch.float32, device=dev)
         self.argmax = torch.zeros((B, S), dtype=torch.int32, device=dev)
@@ -261,6 +264,11 @@ class State:
         self.c.logits_prev_dtype = DLLM_BF16 if kl_state == "bf16" else DLLM_F32
         for j, t in enumerate(self.h_nested):
             self.c.h_nested[j] = _ptr(t)
+        if layer_cache:
+            self._xi = (ctypes.c_void_p * L)(*[_ptr(t) for t in self.x_in])
+            self._xo = (ctypes.c_void_p * L)(*[_ptr(t) for t in self.x_out])
+            self.c.x_in_cache = ctypes.cast(self._xi, ctypes.POINTER(ctypes.c_void_p))
+            self.c.x_out_cache = ctypes.cast(self._xo, ctypes.POINTER(ctypes.c_void_p))
 
     @property
     def h_bnd_prev(self) -> torch.Tensor:
@@ -270,8 +278,9 @@ class State:
 
 def step_cfg(boundary_layer: int, full_step: bool, score: _ffi.ScoreCfg | None = None, *, lock_kl_eps=-1.0,
              lock_conf_min=0.9, unmask_n=0, block_lo=0, block_hi=0, unmask_mode=UNMASK_CONF,
-             ws=None, nested=()) -> _ffi.StepCfg:
-    """nested: ((layer, k), ...) later layers that narrow the active set (at most MAX_NESTED)."""
+             ws=None, nested=(), layer_cache=False) -> _ffi.StepCfg:
+    """nested: ((layer, k), ...) later layers that narrow the active set (at most MAX_NESTED).
+    layer_cache: per-layer partial update from the boundary layer on (needs State(layer_cache=True))."""
     if len(nested) > _ffi.MAX_NESTED:
         raise DllmError(f"at most {_ffi.MAX_NESTED} nested boundaries")
     c = _ffi.StepCfg()
@@ -291,6 +300,7 @@ def step_cfg(boundary_layer: int, full_step: bool, score: _ffi.ScoreCfg | None =
     for j, (nl, nk) in enumerate(nested):
         c.nested_layer[j] = int(nl)
         c.nested_k[j] = int(nk)
+    c.layer_cache = int(bool(layer_cache))
     return c
 
 

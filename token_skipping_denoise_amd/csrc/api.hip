@@ -423,6 +423,14 @@ int dllm_skip_step(const dllm_model* model, dllm_state* state, const dllm_step_c
     if (cfg->nested_k[j] < 0 || cfg->nested_k[j] > kx) return DLLM_EINVAL;
     if (!state->h_nested[j] || !aligned16(state->h_nested[j])) return DLLM_EINVAL;
   }
+  const bool lcache = cfg->layer_cache != 0;
+  if (lcache) {
+    if (n_nested != 0 || b_lay >= L || !state->x_in_cache || !state->x_out_cache) return DLLM_EINVAL;
+    for (int l = b_lay; l < L; ++l)
+      if (!state->x_in_cache[l] || !state->x_out_cache[l] || !aligned16(state->x_in_cache[l]) ||
+          !aligned16(state->x_out_cache[l]))
+        return DLLM_EINVAL;
+  }
 
   Ctx c{model, &d, model->dtype, (char*)cfg->ws, {}, (hipStream_t)stream};
   plan_ws(d, c.dtype, kx, c.L);
@@ -498,7 +506,40 @@ int dllm_skip_step(const dllm_model* model, dllm_state* state, const dllm_step_c
     return -1;
   };
 
+  // per-layer cache at layer l >= b: score every position against the layer's input cache,
+  // compute the top k through the layer (refreshing both caches for them), every other position
+  // takes its cached output; a full step computes every row and fills both caches
+  auto cached_layer = [&](int l) -> int {
+    void* ci = state->x_in_cache[l];
+    void* co = state->x_out_cache[l];
+    const void* next_g = (l + 1 == L) ? model->final_norm : (full ? model->layers[l + 1].attn_norm : nullptr);
+    if (full) {
+      DLLM_TRY(launch_copy(xfull, ci, (size_t)Rd * row_bytes, c.s));
+      const int r = run_layer(c, l, xfull, nact_full, rp_d, S, state->k_cache[l], state->v_cache[l], next_g);
+      if (r) return r;
+      DLLM_TRY(launch_copy(xfull, co, (size_t)Rd * row_bytes, c.s));
+      return DLLM_OK;
+    }
+    float* scores = c.at<float>(c.L.scores);
+    DLLM_TRY(launch_score(c.dtype, xfull, ci, nullptr, state->conf, state->kl, state->force, Rd, d.d, sc.alpha,
+                          sc.conf_inverted, sc.var, scores, c.s));
+    DLLM_TRY(launch_select(scores, state->force, B, S, sc.sel, sc.k, sc.tau, kx, state->idx, state->n_active, c.s));
+    DLLM_TRY(launch_row_pos(state->idx, state->n_active, B, S, kx, rp_s, c.s));
+    DLLM_TRY(launch_gather_norm(c.dtype, xfull, rp_s, Rs, d.d, xact, model->layers[l].attn_norm, eps, xn, c.s));
+    DLLM_TRY(launch_scatter_norm(c.dtype, xact, rp_s, Rs, d.d, ci, nullptr, eps, nullptr, c.s));
+    const int r = run_layer(c, l, xact, state->n_active, rp_s, kx, state->k_cache[l], state->v_cache[l], next_g);
+    if (r) return r;
+    DLLM_TRY(launch_scatter_norm(c.dtype, xact, rp_s, Rs, d.d, co, nullptr, eps, nullptr, c.s));
+    if (l + 1 < L) DLLM_TRY(launch_copy(co, xfull, (size_t)Rd * row_bytes, c.s));
+    return DLLM_OK;
+  };
+
   for (int l = 0; l < L; ++l) {
+    if (lcache && l >= b_lay) {
+      st = cached_layer(l);
+      if (st) return st;
+      continue;
+    }
     if (l == b_lay) {
       st = boundary();
       if (st) return st;
@@ -512,7 +553,7 @@ int dllm_skip_step(const dllm_model* model, dllm_state* state, const dllm_step_c
     const void* next_g;
     if (l + 1 == L) next_g = model->final_norm;
     else if (!full && (l + 1 == b_lay || nested_at(l + 1) >= 0))
-      next_g = nullptr;  // the boundary (or nested) gather normalises the active rows
+      next_g = nullptr;  // the boundary (or nested, or per-layer cache) gather normalises the active rows
     else next_g = model->layers[l + 1].attn_norm;
     if (dense)
       st = run_layer(c, l, xfull, nact_full, rp_d, S, state->k_cache[l], state->v_cache[l], next_g);
