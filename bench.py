@@ -330,6 +330,31 @@ def long_schedule(dims, device, k_active=205, block=16, refresh_every=16):
     return steps
 
 
+def dcache_schedule(dims, device, k_active=64, refresh_every=16, block=32, unmask=4):
+    """Per-layer cache run on the LLaDA-8B shapes (dLLM-Cache summary section 3): every 16th step
+    is a full step that refreshes every layer's caches (prompt included); the others lock the
+    prompt rows (long-interval prompt cache) and, at every layer, recompute the k_active = 25% of
+    the 256 response rows whose hidden state entering the layer changed most (1 - cos) since
+    they were last computed there, the rest taking their cached layer outputs.  Blocks of 32
+    generated positions, four unmasked per step by confidence, 64 steps."""
+    base = torch.zeros((dims.B, dims.S), dtype=torch.uint8)
+    base[:, :dims.prompt] = api.FORCE_EXCLUDED
+    base = base.to(device)
+    n_steps = (dims.S - dims.prompt) // unmask
+    per_block = block // unmask
+    steps = []
+    for t in range(n_steps):
+        lo = dims.prompt + (t // per_block) * block
+        if t % refresh_every == 0:
+            kw = dict(boundary_layer=0, full_step=True, score=None)
+        else:
+            kw = dict(boundary_layer=0, full_step=False,
+                      score=api.score_cfg(alpha=0.0, var=api.VAR_COS, sel=api.SEL_TOPK, k=k_active))
+        kw.update(unmask_n=unmask, block_lo=lo, block_hi=lo + block, layer_cache=True)
+        steps.append((kw, base, None))
+    return steps
+
+
 def run_schedule(model, state, tok0, steps, ws, after_step=None):
     state.tokens.copy_(tok0)
     state.c.have_prev = 0
@@ -390,6 +415,11 @@ def extra_workload(args):
         dims, k_max = workloads.DREAM, workloads.DREAM.S
         desc = ("Dream-7B-shaped 28-layer GQA 28/4 run, batch 8, prompt 512 + gen 512, 128 steps, locked share "
                 "ramped 0 -> 80% of positions (seeded), unlocked rows recomputed, KL lock rule on")
+    elif args.workload == "dcache":
+        dims, k_max = workloads.LLADA, 64
+        desc = ("LLaDA-8B-shaped 32-layer per-layer cache run, batch 1, prompt 256 + gen 256, blocks of 32, 64 steps: "
+                "full refresh every 16 steps, else prompt rows cached and at every layer the 64 response rows "
+                "(25%) with the largest input change (1 - cos) recomputed, the rest reusing cached outputs")
     else:
         dims, k_max = workloads.LLADA_LONG, 205
         desc = ("LLaDA-8B-shaped 32-layer long-context run, batch 4, prompt 3584 + gen 512, dilated blocks of 16 "
@@ -399,9 +429,15 @@ def extra_workload(args):
     model = api.Model(w, dims.n_heads, dims.n_kv_heads, dims.mask_id)
     tok0 = workloads.initial_tokens(dims, device=dev)
     track_kl = args.workload == "dream"
-    state = api.State(model, tok0.clone(), k_max=k_max, track_kl=track_kl, kl_state=args.kl_state)
+    state = api.State(model, tok0.clone(), k_max=k_max, track_kl=track_kl, kl_state=args.kl_state,
+                      layer_cache=args.workload == "dcache")
     ws = api.alloc_workspace(model, dims.B, dims.S, k_max)
-    steps = dream_schedule(dims, dev) if args.workload == "dream" else long_schedule(dims, dev)
+    if args.workload == "dream":
+        steps = dream_schedule(dims, dev)
+    elif args.workload == "dcache":
+        steps = dcache_schedule(dims, dev, k_active=k_max)
+    else:
+        steps = long_schedule(dims, dev)
     torch.cuda.synchronize()
     t_setup = time.perf_counter() - t0
     for _ in range(args.warmup):
@@ -414,7 +450,7 @@ def extra_workload(args):
     elapsed = time.perf_counter() - t_start
     gen_tokens = dims.B * (dims.S - dims.prompt)
     kernels = None
-    if not args.no_kernel_timing and args.workload == "long":
+    if not args.no_kernel_timing and args.workload in ("long", "dcache"):
         lib = _ffi.load()
         kernels = kernel_table_schedule(lib, model, state, tok0, steps, ws, dims, dims.B * k_max)
     elif not args.no_kernel_timing and args.workload == "dream":
@@ -486,9 +522,9 @@ def main():
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-kernel-timing", action="store_true")
     ap.add_argument("--no-graph", action="store_true", help="launch eagerly instead of replaying a HIP graph")
-    ap.add_argument("--workload", choices=("llada", "dream", "long"), default="llada",
+    ap.add_argument("--workload", choices=("llada", "dream", "long", "dcache"), default="llada",
                     help="llada: the 32-layer early-skip generation (default); dream: Dream-GQA lock ramp; "
-                         "long: long-context dilated run")
+                         "long: long-context dilated run; dcache: per-layer cache (dLLM-Cache) run")
     ap.add_argument("--nested", default="",
                     help="llada workload: nested boundaries 'layer:k[,layer:k]' that narrow the 128 active rows "
                          "at later layers (ES-dLLM per-layer selection), e.g. 16:64")
