@@ -8,7 +8,7 @@
 //
 // bf16 path: v_mfma_f32_32x32x16_bf16 (gfx950), fp32 accumulation, WM x WN
 // wavefronts (times KG k-groups) per tile, BK = 64, tiles streamed from memory
-// straight into a multi-stage LDS ring with global_load_lds_dwordx4 (no
+// straight into a multi-stage LDS ring with 16-byte buffer loads to LDS (no
 // register staging), XOR-swizzled so MFMA fragment reads are conflict-free.
 // Most plans use eight wavefronts: these kernels are bound by the loads each CU
 // keeps in flight, and more waves issue more of them.  Split-K writes fp32
@@ -59,7 +59,7 @@ __device__ __forceinline__ void decode_tile(int nt, int tiles_m, int tiles_n, in
 //          factors sit in lanes t and t + 16 of one accumulator; any column count that is a
 //          multiple of 32 works (48 outputs for 96 columns).
 //
-// Direct-to-LDS variant (gfx950 global_load_lds_dwordx4): tiles stream from
+// Direct-to-LDS variant (gfx950 buffer_load_dwordx4 ... lds): tiles stream from
 // memory straight into an NS-stage LDS ring with no register staging, so
 // NS-1 tiles stay in flight while one is multiplied.  BK = 64: a tile row is
 // 128 bytes = 8 chunks of 16 bytes; one wave load instruction fills 8 rows
@@ -85,6 +85,26 @@ __device__ __forceinline__ void wait_stages(int ahead) {
 }
 
 typedef __attribute__((address_space(3))) void lds_void;
+
+// Tile loads go through buffer resources based at the tile's first row, so that
+// every offset is a 32-bit byte count within the tile (the launcher checks the
+// span) and the address arithmetic is one VGPR add per load.  A buffer load to LDS
+// issues faster than the flat global_load_lds form on gfx950.  Word 3 of the
+// descriptor is the raw 32-bit-element format with no swizzle.
+template <int LA, int LB, int NW, int BM, int BK>
+__device__ __forceinline__ void issue_tile(const uint16_t* a_base, int a_bytes, const int* oa, const uint16_t* w_base,
+                                           int w_bytes, const int* ob, int k0_bytes, uint16_t* stage, int wave) {
+  const __amdgpu_buffer_rsrc_t ra = __builtin_amdgcn_make_buffer_rsrc((void*)a_base, (short)0, a_bytes, 0x00020000);
+  const __amdgpu_buffer_rsrc_t rw = __builtin_amdgcn_make_buffer_rsrc((void*)w_base, (short)0, w_bytes, 0x00020000);
+#pragma unroll
+  for (int i = 0; i < LA; ++i)
+    __builtin_amdgcn_raw_ptr_buffer_load_lds(ra, (lds_void*)(stage + (wave + NW * i) * 8 * BK), 16, oa[i] + k0_bytes, 0,
+                                             0, 0);
+#pragma unroll
+  for (int i = 0; i < LB; ++i)
+    __builtin_amdgcn_raw_ptr_buffer_load_lds(rw, (lds_void*)(stage + BM * BK + (wave + NW * i) * 8 * BK), 16,
+                                             ob[i] + k0_bytes, 0, 0, 0);
+}
 
 template <int BM, int BN, int NS, int EPI, int OCC, int KG, int WM, int WN>
 __global__ __launch_bounds__(64 * WM * WN * KG, OCC) void k_gemm_lds(const uint16_t* __restrict__ A, const uint16_t* __restrict__ W,
@@ -136,31 +156,29 @@ __global__ __launch_bounds__(64 * WM * WN * KG, OCC) void k_gemm_lds(const uint1
   // A tile row is 128 bytes, half of the 64 banks: rows r and r+1 fall in opposite bank
   // halves, so the chunk slot is swizzled by (r >> 1) & 7 and any 16 consecutive rows read at
   // one chunk index touch all 64 banks once.
+  // per-tile bases: A from row m0, W from the tile's lowest weight row (every row the
+  // tile reads, clamped rows included, lies at or above it)
+  const int wr0 = (EPI == 0) ? tni * BN : h0;
+  const uint16_t* a_base = A + (long)m0 * K;
+  const uint16_t* w_base = W + (long)wr0 * K;
+  const int a_bytes = (int)min((long)(M - m0) * K * 2, 0x7fffffffL);
+  const int w_bytes = (int)min((long)(w_rows - wr0) * K * 2, 0x7fffffffL);
   const int lrow = lane >> 3;
-  const uint16_t* ga[LA];
-  const uint16_t* gb[LB];
+  int oa[LA], ob[LB];  // byte offsets of this lane's chunk in each load, k excluded
 #pragma unroll
   for (int i = 0; i < LA; ++i) {
     const int row = (wave + NW * i) * 8 + lrow;
     const int chunk = (lane & 7) ^ ((row >> 1) & 7);
-    ga[i] = A + (long)min(m0 + row, M - 1) * K + chunk * 8;
+    oa[i] = ((min(m0 + row, M - 1) - m0) * K + chunk * 8) * 2;
   }
 #pragma unroll
   for (int i = 0; i < LB; ++i) {
     const int row = (wave + NW * i) * 8 + lrow;
     const int chunk = (lane & 7) ^ ((row >> 1) & 7);
-    gb[i] = W + (long)min(w_row(row), w_rows - 1) * K + chunk * 8;
+    ob[i] = ((min(w_row(row), w_rows - 1) - wr0) * K + chunk * 8) * 2;
   }
   auto issue = [&](int stage, int kb) {
-    const long k0 = (long)kb * BK;
-    uint16_t* base = smem + stage * STAGE;
-#pragma unroll
-    for (int i = 0; i < LA; ++i)
-      __builtin_amdgcn_global_load_lds((const void*)(ga[i] + k0), (lds_void*)(base + (wave + NW * i) * 8 * BK), 16, 0, 0);
-#pragma unroll
-    for (int i = 0; i < LB; ++i)
-      __builtin_amdgcn_global_load_lds((const void*)(gb[i] + k0), (lds_void*)(base + BM * BK + (wave + NW * i) * 8 * BK),
-                                       16, 0, 0);
+    issue_tile<LA, LB, NW, BM, BK>(a_base, a_bytes, oa, w_base, w_bytes, ob, kb * BK * 2, smem + stage * STAGE, wave);
   };
 
   f32x16_t acc[TM][TN];
@@ -446,14 +464,19 @@ GemmPlan gemm_plan(int dtype, int M, int N, int K, bool swiglu) {
 }
 
 template <int BM, int BN, int NS, int EPI, int KG, int WM, int WN>
-static void launch_lds(const GemmPlan& p, const void* A, const void* W, float* C, void* H, int M, int N, int K,
-                       const int32_t* n_active, int k_max, hipStream_t s) {
+static hipError_t launch_lds(const GemmPlan& p, const void* A, const void* W, float* C, void* H, int M, int N, int K,
+                             const int32_t* n_active, int k_max, hipStream_t s) {
+  // the kernel's buffer offsets are 32-bit bytes within one tile: BM rows of A, and
+  // BN weight rows (plain) or the gate..up span F + BN / 2 rows (SwiGLU)
+  const long w_span = EPI == 0 ? BN : (long)N + BN / 2;
+  if ((long)BM * K * 2 > 0x7fffffffL || w_span * K * 2 > 0x7fffffffL) return hipErrorInvalidValue;
   const int ncols = EPI == 0 ? BN : BN / 2;
   const int tm = (M + BM - 1) / BM, tn = (N + ncols - 1) / ncols;
   constexpr int lds_bytes = NS * (BM + BN) * 64 * 2;
   constexpr int occ = (lds_bytes <= 80 * 1024 && KG * WM * WN == 4) ? 2 : 1;
   hipLaunchKernelGGL((k_gemm_lds<BM, BN, NS, EPI, occ, KG, WM, WN>), dim3(tm * tn * p.splits), dim3(64 * KG * WM * WN), 0, s,
                      (const uint16_t*)A, (const uint16_t*)W, C, (uint16_t*)H, M, N, K, p.splits, tm, tn, n_active, k_max);
+  return hipGetLastError();
 }
 
 hipError_t launch_gemm(int dtype, const GemmPlan& p, const void* A, const void* W, float* C, int M, int N, int K,
@@ -469,8 +492,7 @@ hipError_t launch_gemm(int dtype, const GemmPlan& p, const void* A, const void* 
 #define DLLM_LDS_CASE(BM_, BN_, NS_, KG_, WM_, WN_)                                                \
   if (p.bm == BM_ && p.bn == BN_ && p.bk == 64 && p.pd == 10 + NS_ && p.kg == KG_ && p.wm == WM_ &&  \
       p.wn == WN_) {                                                                                \
-    launch_lds<BM_, BN_, NS_, 0, KG_, WM_, WN_>(p, A, W, C, nullptr, M, N, K, n_active, k_max, s);  \
-    return hipGetLastError();                                                                       \
+    return launch_lds<BM_, BN_, NS_, 0, KG_, WM_, WN_>(p, A, W, C, nullptr, M, N, K, n_active, k_max, s); \
   }
   DLLM_LDS_CASES
 #undef DLLM_LDS_CASE
@@ -485,16 +507,14 @@ hipError_t launch_gemm_swiglu(const GemmPlan& p, const void* A, const void* W_ga
 #define DLLM_LDS_CASE(BM_, BN_, NS_, KG_, WM_, WN_)                                                \
   if (p.bm == BM_ && p.bn == BN_ && p.bk == 64 && p.pd == 10 + NS_ && p.kg == KG_ && p.wm == WM_ &&  \
       p.wn == WN_ && !p.ilv) {                                                                      \
-    launch_lds<BM_, BN_, NS_, 1, KG_, WM_, WN_>(p, A, W_gate_up, nullptr, H, M, F, K, n_active, k_max, s); \
-    return hipGetLastError();                                                                       \
+    return launch_lds<BM_, BN_, NS_, 1, KG_, WM_, WN_>(p, A, W_gate_up, nullptr, H, M, F, K, n_active, k_max, s); \
   }
   DLLM_LDS_SWIGLU_CASES
 #undef DLLM_LDS_CASE
 #define DLLM_LDS_CASE(BM_, BN_, NS_, KG_, WM_, WN_)                                                \
   if (p.bm == BM_ && p.bn == BN_ && p.bk == 64 && p.pd == 10 + NS_ && p.kg == KG_ && p.wm == WM_ &&  \
       p.wn == WN_ && p.ilv) {                                                                       \
-    launch_lds<BM_, BN_, NS_, 2, KG_, WM_, WN_>(p, A, W_gate_up, nullptr, H, M, F, K, n_active, k_max, s); \
-    return hipGetLastError();                                                                       \
+    return launch_lds<BM_, BN_, NS_, 2, KG_, WM_, WN_>(p, A, W_gate_up, nullptr, H, M, F, K, n_active, k_max, s); \
   }
   DLLM_LDS_SWIGLU_ILV_CASES
 #undef DLLM_LDS_CASE

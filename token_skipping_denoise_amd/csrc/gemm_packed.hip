@@ -84,6 +84,18 @@ __global__ void k_pack_frag(const uint16_t* __restrict__ W, uint16_t* __restrict
   }
 }
 
+// Activation tile DMA through a buffer resource over A (a buffer load to LDS issues
+// faster than the flat global_load_lds form); word 3 is the raw 32-bit format.
+template <int LAW, int NW, int BK>
+__device__ __forceinline__ void act_dma(const uint16_t* A, int a_bytes, const int* oa, int k0_bytes, uint16_t* stage,
+                                        int wave) {
+  const __amdgpu_buffer_rsrc_t ra = __builtin_amdgcn_make_buffer_rsrc((void*)A, (short)0, a_bytes, 0x00020000);
+#pragma unroll
+  for (int i = 0; i < LAW; ++i)
+    __builtin_amdgcn_raw_ptr_buffer_load_lds(ra, (lds_void*)(stage + (wave + NW * i) * 8 * BK), 16, oa[i] + k0_bytes, 0,
+                                             0, 0);
+}
+
 // EPI 0: fp32 split-K partials C[sp][m][n].  EPI 2: H[m][f] = silu(gate) * up (bf16), F outputs.
 template <int NW, int NKC, int EPI, int LAW>
 __device__ __forceinline__ void packed_body(const uint16_t* __restrict__ A, const uint16_t* __restrict__ Wp,
@@ -99,23 +111,21 @@ __device__ __forceinline__ void packed_body(const uint16_t* __restrict__ A, cons
   const int hi = lane >> 5, r32 = lane & 31;
   // activation DMA: 16 instructions of 8 rows (1 KB) per stage, instruction q = wave + NW i;
   // chunk c of row r sits in slot c ^ ((r >> 1) & 7) so the fragment reads are conflict-free
-  const uint16_t* ga[LAW];
+  // (buffer loads: byte offsets within A, which the launcher keeps under 2^31 bytes)
+  int oa[LAW];
 #pragma unroll
   for (int i = 0; i < LAW; ++i) {
     const int row = (wave + NW * i) * 8 + (lane >> 3);
     const int chunk = (lane & 7) ^ ((row >> 1) & 7);
-    ga[i] = A + (long)min(row, M - 1) * K + chunk * 8;
+    oa[i] = (min(row, M - 1) * K + chunk * 8) * 2;
   }
+  const int a_bytes = M * K * 2;
   const int nb = tn * NW + wave;  // this wave's 32-column block
   const long stage_stride = (long)(N / 32) * 2048;  // one stage of every column block
   const uint16_t* gw = Wp + (long)nb * 2048 + lane * 8;
   bf16x8_t wb[D + 1][4];
   auto issue = [&](int slot, int kb, bf16x8_t* wdst) {
-    uint16_t* base = smem + slot * ASTAGE;
-#pragma unroll
-    for (int i = 0; i < LAW; ++i)
-      __builtin_amdgcn_global_load_lds((const void*)(ga[i] + (long)kb * BK), (lds_void*)(base + (wave + NW * i) * 8 * BK),
-                                       16, 0, 0);
+    act_dma<LAW, NW, BK>(A, a_bytes, oa, kb * BK * 2, smem + slot * ASTAGE, wave);
 #pragma unroll
     for (int s = 0; s < 4; ++s) wdst[s] = *reinterpret_cast<const bf16x8_t*>(gw + kb * stage_stride + s * 512);
   };
@@ -231,7 +241,7 @@ PackedPlan packed_plan(int M, int N, int K, bool swiglu) {
 
 hipError_t launch_gemm_packed(const PackedPlan& p, const void* A, const void* Wp, float* C, void* H, int M, int N,
                               int K, int F, const int32_t* n_active, int k_max, hipStream_t s) {
-  if (!p.ok) return hipErrorInvalidValue;
+  if (!p.ok || M <= 0 || M > kPkRows || (long)M * K * 2 > 0x7fffffffL) return hipErrorInvalidValue;
   const int tiles_n = N / (32 * p.nw);
   const dim3 grid(tiles_n * p.splits), block(64 * p.nw);
   if (H && p.nw == 3 && p.nkc == 64)
