@@ -29,6 +29,11 @@ CASES = {
     # 4 x 17 query blocks of 128: enough workgroups for the 128-query kernel without a split
     "bf16_q128": (workloads.shrink(workloads.LLADA, n_layers=1, d=256, n_heads=17, n_kv_heads=17, d_ff=384,
                                    vocab=1000, B=4, S=100, prompt=50), 0.1, [37, 20, 1, 9], 37),
+    # 600 rows (two sequences of k_max 300, the second with 7 live rows): the many-row plans
+    # (256 x 192 interleaved SwiGLU, 256 x 128 split-K down, 128 x 128 QKV and O) over a
+    # ragged last tile and whole dead tiles; attention in 32-query workgroups over 300 slots
+    "bf16_ragged_256_tiles": (workloads.shrink(workloads.LLADA, n_layers=1, d=256, n_heads=2, n_kv_heads=2, d_ff=768,
+                                               vocab=1000, B=2, S=400, prompt=200), 0.05, [300, 7], 300),
     # two key tiles, one partial, over four waves: two waves of each workgroup have no keys
     "bf16_one_tile": (workloads.shrink(workloads.LLADA, n_layers=1, d=256, n_heads=2, n_kv_heads=2, d_ff=512,
                                        vocab=1000, B=2, S=40, prompt=20), 0.1, [13, 40], 40),

@@ -373,10 +373,10 @@ GemmPlan gemm_plan(int dtype, int M, int N, int K, bool swiglu) {
   // shapes.  Few rows (HBM bound on the weights): 128-row tiles over eight wavefronts (more
   // waves issuing loads keep more bytes in flight per CU); wide QKV-like outputs take 192
   // columns (256 over 2 x 4 when 192 does not divide them), narrow ones 64 columns with 4
-  // stages, and split-K fills the chip.  Many rows (MFMA bound): 256-row tiles over 2 x 2 wavefronts where the
-  // shape allows (256 x 192 for the fused SwiGLU product and QKV-like outputs, 256 x 128 with
-  // a 4-way K split for the down projection), otherwise 128 x 128 with 2 stages, so that two
-  // workgroups share a CU, and split-K up to 4.
+  // stages, and split-K fills the chip.  Many rows: 256-row tiles over 4 x 2 wavefronts where
+  // the shape allows (256 x 192 for the fused SwiGLU product and QKV-like outputs, 256 x 128
+  // with a 4-way K split for the down projection), otherwise 128 x 128 with 2 stages, so that
+  // two workgroups share a CU, and split-K up to 4.
   const bool few = M <= 192;
   const bool wide = N > 8192 && N <= 32768;
   p.bm = 128;
@@ -398,7 +398,7 @@ GemmPlan gemm_plan(int dtype, int M, int N, int K, bool swiglu) {
       return p;
     }
     if (wide) {
-      // 128 x 192 tiles over 2 x 2 wavefronts when they divide the width: 4-way split-K then
+      // 128 x 192 tiles over 4 x 2 wavefronts when they divide the width: 4-way split-K then
       // gives 256 workgroups, one per CU
       p.bn = (N % 192 == 0) ? 192 : 256;
       p.wm = (p.bn == 192) ? 4 : 2;
