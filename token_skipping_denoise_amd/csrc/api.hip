@@ -140,7 +140,7 @@ struct Ctx {
 
 // One layer on rows r = b*kx + j (live iff j < nact[b]); xn holds rmsnorm(x) * attn_norm on entry.
 int run_layer(const Ctx& c, int l, void* x, const int32_t* nact, const int32_t* row_pos, int kx, void* kc, void* vc,
-              const void* next_g) {
+              const void* next_g, void* out_scatter = nullptr) {
   const dllm_dims& d = *c.d;
   const dllm_layer_w& w = c.m->layers[l];
   const int R = d.B * kx;
@@ -197,7 +197,8 @@ int run_layer(const Ctx& c, int l, void* x, const int32_t* nact, const int32_t* 
       DLLM_TRY(launch_gemm(c.dtype, p, h, w.w_down, part, R, d.d, d.d_ff, nact, kx, c.s));
     }
   }
-  DLLM_TRY(launch_resid_norm(c.dtype, part, p.splits, (long)R * d.d, row_pos, R, d.d, x, next_g, eps, xn, c.s));
+  DLLM_TRY(launch_resid_norm(c.dtype, part, p.splits, (long)R * d.d, row_pos, R, d.d, x, next_g, eps, xn, c.s,
+                             out_scatter));
   return DLLM_OK;
 }
 
@@ -509,6 +510,9 @@ int dllm_skip_step(const dllm_model* model, dllm_state* state, const dllm_step_c
   // per-layer cache at layer l >= b: score every position against the layer's input cache,
   // compute the top k through the layer (refreshing both caches for them), every other position
   // takes its cached output; a full step computes every row and fills both caches
+  // input rows of the next cached layer: the boundary's input, then each sparse layer's
+  // output cache, which holds the current output of every row (no copy back into xfull)
+  const void* xin = xfull;
   auto cached_layer = [&](int l) -> int {
     void* ci = state->x_in_cache[l];
     void* co = state->x_out_cache[l];
@@ -521,16 +525,16 @@ int dllm_skip_step(const dllm_model* model, dllm_state* state, const dllm_step_c
       return DLLM_OK;
     }
     float* scores = c.at<float>(c.L.scores);
-    DLLM_TRY(launch_score(c.dtype, xfull, ci, nullptr, state->conf, state->kl, state->force, Rd, d.d, sc.alpha,
+    DLLM_TRY(launch_score(c.dtype, xin, ci, nullptr, state->conf, state->kl, state->force, Rd, d.d, sc.alpha,
                           sc.conf_inverted, sc.var, scores, c.s));
     DLLM_TRY(launch_select(scores, state->force, B, S, sc.sel, sc.k, sc.tau, kx, state->idx, state->n_active, c.s));
     DLLM_TRY(launch_row_pos(state->idx, state->n_active, B, S, kx, rp_s, c.s));
-    DLLM_TRY(launch_gather_norm(c.dtype, xfull, rp_s, Rs, d.d, xact, model->layers[l].attn_norm, eps, xn, c.s));
-    DLLM_TRY(launch_scatter_norm(c.dtype, xact, rp_s, Rs, d.d, ci, nullptr, eps, nullptr, c.s));
-    const int r = run_layer(c, l, xact, state->n_active, rp_s, kx, state->k_cache[l], state->v_cache[l], next_g);
+    // the selected rows, normalised for the layer, and their inputs recorded in the input cache
+    DLLM_TRY(launch_gather_norm(c.dtype, xin, rp_s, Rs, d.d, xact, model->layers[l].attn_norm, eps, xn, c.s, ci));
+    // the layer's outputs go to the output cache from its last residual kernel
+    const int r = run_layer(c, l, xact, state->n_active, rp_s, kx, state->k_cache[l], state->v_cache[l], next_g, co);
     if (r) return r;
-    DLLM_TRY(launch_scatter_norm(c.dtype, xact, rp_s, Rs, d.d, co, nullptr, eps, nullptr, c.s));
-    if (l + 1 < L) DLLM_TRY(launch_copy(co, xfull, (size_t)Rd * row_bytes, c.s));
+    xin = co;
     return DLLM_OK;
   };
 

@@ -10,9 +10,10 @@ namespace dllm {
 // x[r] = embed[tok[r]] for r < rows; if g: xn[r] = rmsnorm(x[r]) * g.
 hipError_t launch_embed_norm(int dtype, const void* embed, const int32_t* tokens, int V, int rows, int d,
                              const void* g, float eps, void* x, void* xn, hipStream_t s);
-// dst[r] = src[row_pos[r]] for live rows; if g: dst_norm[r] = rmsnorm(dst[r]) * g.
+// dst[r] = src[row_pos[r]] for live rows; if g: dst_norm[r] = rmsnorm(dst[r]) * g; if dst_at_src:
+// dst_at_src[row_pos[r]] = src[row_pos[r]] as well (the same rows copied in place to another buffer).
 hipError_t launch_gather_norm(int dtype, const void* src, const int32_t* row_pos, int R, int w, void* dst,
-                              const void* g, float eps, void* dst_norm, hipStream_t s);
+                              const void* g, float eps, void* dst_norm, hipStream_t s, void* dst_at_src = nullptr);
 // dst[row_pos[r]] = src[r] for live rows; if g: dst_norm[r] = rmsnorm(src[r]) * g.
 hipError_t launch_scatter_norm(int dtype, const void* src, const int32_t* row_pos, int R, int w, void* dst,
                                const void* g, float eps, void* dst_norm, hipStream_t s);
@@ -26,9 +27,11 @@ hipError_t launch_identity_rows(int B, int S, int32_t* idx, int32_t* n_active, h
 hipError_t launch_qkv_epilogue(int dtype, const float* part, int splits, long split_stride,
                                const int32_t* row_pos, int R, int S, int Hq, int Hkv, int D, float rope_base,
                                void* q, void* kc, void* vc, hipStream_t s);
-// x[r] += sum of partials; if g: xn[r] = rmsnorm(x[r]) * g.
+// x[r] += sum of partials; if g: xn[r] = rmsnorm(x[r]) * g; if x_scatter: x_scatter[row_pos[r]] = x[r]
+// as well (the new rows also written to their positions in a full-height buffer).
 hipError_t launch_resid_norm(int dtype, const float* part, int splits, long split_stride, const int32_t* row_pos,
-                             int R, int d, void* x, const void* g, float eps, void* xn, hipStream_t s);
+                             int R, int d, void* x, const void* g, float eps, void* xn, hipStream_t s,
+                             void* x_scatter = nullptr);
 // h[r, c] = silu(P[r, c]) * P[r, F + c] with P the summed partials [R, 2F].
 hipError_t launch_swiglu(int dtype, const float* part, int splits, long split_stride, const int32_t* row_pos,
                          int R, int F, void* h, hipStream_t s);

@@ -38,7 +38,8 @@ __device__ __forceinline__ float block_sum(float v, float* red) {
 template <typename T, int MODE, int NT = kRowThreads>
 __global__ __launch_bounds__(NT) void k_rows_norm(const T* __restrict__ src, const int32_t* __restrict__ map,
                                                    int V, int rows, int w, T* __restrict__ dst,
-                                                   const T* __restrict__ g, float eps, T* __restrict__ dst_norm) {
+                                                   const T* __restrict__ g, float eps, T* __restrict__ dst_norm,
+                                                   T* __restrict__ dst_at_src) {
   using E = Elem<T>;
   constexpr int VE = E::kVec;
   constexpr int CH = 1024 / NT;  // 16-byte chunks per thread
@@ -59,6 +60,7 @@ __global__ __launch_bounds__(NT) void k_rows_norm(const T* __restrict__ src, con
   const int nchunk = w / VE;
   const uint4* s4 = reinterpret_cast<const uint4*>(src + src_row * (long)w);
   uint4* d4 = dst ? reinterpret_cast<uint4*>(dst + dst_row * (long)w) : nullptr;
+  uint4* m4 = dst_at_src ? reinterpret_cast<uint4*>(dst_at_src + src_row * (long)w) : nullptr;  // gather only
   float f[CH][VE];
   float ss = 0.f;
 #pragma unroll
@@ -67,6 +69,7 @@ __global__ __launch_bounds__(NT) void k_rows_norm(const T* __restrict__ src, con
     if (c >= nchunk) break;
     const uint4 v = s4[c];
     if (d4) d4[c] = v;
+    if (m4) m4[c] = v;
     E::unpack(v, f[k]);
 #pragma unroll
     for (int e = 0; e < VE; ++e) ss += f[k][e] * f[k][e];
@@ -90,16 +93,16 @@ __global__ __launch_bounds__(NT) void k_rows_norm(const T* __restrict__ src, con
 
 template <int MODE>
 static hipError_t rows_norm(int dtype, const void* src, const int32_t* map, int V, int rows, int w, void* dst,
-                            const void* g, float eps, void* dst_norm, hipStream_t s) {
+                            const void* g, float eps, void* dst_norm, hipStream_t s, void* dst_at_src = nullptr) {
   if (rows <= 0) return hipSuccess;
   if (w / (dtype == 0 ? 4 : 8) > kRowThreads * kRowChunks) return hipErrorInvalidValue;
   dim3 grid(rows), block(kRowThreads);
   if (dtype == 0)
     hipLaunchKernelGGL((k_rows_norm<float, MODE>), grid, block, 0, s, (const float*)src, map, V, rows, w,
-                       (float*)dst, (const float*)g, eps, (float*)dst_norm);
+                       (float*)dst, (const float*)g, eps, (float*)dst_norm, (float*)dst_at_src);
   else
     hipLaunchKernelGGL((k_rows_norm<bf16, MODE>), grid, block, 0, s, (const bf16*)src, map, V, rows, w,
-                       (bf16*)dst, (const bf16*)g, eps, (bf16*)dst_norm);
+                       (bf16*)dst, (const bf16*)g, eps, (bf16*)dst_norm, (bf16*)dst_at_src);
   return hipGetLastError();
 }
 
@@ -108,8 +111,8 @@ hipError_t launch_embed_norm(int dtype, const void* embed, const int32_t* tokens
   return rows_norm<kEmbed>(dtype, embed, tokens, V, rows, d, x, g, eps, xn, s);
 }
 hipError_t launch_gather_norm(int dtype, const void* src, const int32_t* row_pos, int R, int w, void* dst,
-                              const void* g, float eps, void* dst_norm, hipStream_t s) {
-  return rows_norm<kGather>(dtype, src, row_pos, 0, R, w, dst, g, eps, dst_norm, s);
+                              const void* g, float eps, void* dst_norm, hipStream_t s, void* dst_at_src) {
+  return rows_norm<kGather>(dtype, src, row_pos, 0, R, w, dst, g, eps, dst_norm, s, dst_at_src);
 }
 hipError_t launch_scatter_norm(int dtype, const void* src, const int32_t* row_pos, int R, int w, void* dst,
                                const void* g, float eps, void* dst_norm, hipStream_t s) {
@@ -288,7 +291,7 @@ template <typename T, int SPLITS, int NT = kRowThreads>
 __global__ __launch_bounds__(NT) void k_resid_norm(const float* __restrict__ part, int splits_unused, long sstride,
                                                     const int32_t* __restrict__ row_pos, int R, int d,
                                                     T* __restrict__ x, const T* __restrict__ g, float eps,
-                                                    T* __restrict__ xn) {
+                                                    T* __restrict__ xn, T* __restrict__ x_scat) {
   using E = Elem<T>;
   constexpr int V = E::kVec;
   constexpr int CH = 1024 / NT;  // 16-byte chunks per thread
@@ -297,6 +300,7 @@ __global__ __launch_bounds__(NT) void k_resid_norm(const float* __restrict__ par
   if (row_pos[r] < 0) return;
   const int nchunk = d / V;
   uint4* x4 = reinterpret_cast<uint4*>(x + (long)r * d);
+  uint4* s4 = x_scat ? reinterpret_cast<uint4*>(x_scat + (long)row_pos[r] * d) : nullptr;
   const float* pr = part + (long)r * d;
   float f[CH][V];
   float ss = 0.f;
@@ -319,6 +323,7 @@ __global__ __launch_bounds__(NT) void k_resid_norm(const float* __restrict__ par
     }
     const uint4 packed = E::pack(f[k]);
     x4[c] = packed;
+    if (s4) s4[c] = packed;
     E::unpack(packed, f[k]);  // the stored (rounded) values feed the norm
 #pragma unroll
     for (int e = 0; e < V; ++e) ss += f[k][e] * f[k][e];
@@ -341,13 +346,14 @@ __global__ __launch_bounds__(NT) void k_resid_norm(const float* __restrict__ par
 }
 
 hipError_t launch_resid_norm(int dtype, const float* part, int splits, long split_stride, const int32_t* row_pos,
-                             int R, int d, void* x, const void* g, float eps, void* xn, hipStream_t s) {
+                             int R, int d, void* x, const void* g, float eps, void* xn, hipStream_t s,
+                             void* x_scatter) {
   if (R <= 0) return hipSuccess;
   const int vec = dtype == 0 ? 4 : 8;
   if (d % vec != 0 || d / vec > kRowThreads * kRowChunks) return hipErrorInvalidValue;
 #define DLLM_RN(T_, SP_)                                                                              \
   hipLaunchKernelGGL((k_resid_norm<T_, SP_>), dim3(R), dim3(kRowThreads), 0, s, part, splits, split_stride, row_pos, R, d, \
-                     (T_*)x, (const T_*)g, eps, (T_*)xn)
+                     (T_*)x, (const T_*)g, eps, (T_*)xn, (T_*)x_scatter)
 #define DLLM_RN_SPLITS(T_)                          \
   switch (splits) {                                 \
     case 1: DLLM_RN(T_, 1); break;                  \
