@@ -470,9 +470,9 @@ int dllm_skip_step(const dllm_model* model, dllm_state* state, const dllm_step_c
     }
     {
       TimedRegion t(DLLM_TK_SELECT, Rd, c.s);
-      DLLM_TRY(launch_select(scores, state->force, B, S, sc.sel, sc.k, sc.tau, kx, state->idx, state->n_active, c.s));
+      DLLM_TRY(launch_select(scores, state->force, B, S, sc.sel, sc.k, sc.tau, kx, state->idx, state->n_active, c.s,
+                             rp_s));
     }
-    DLLM_TRY(launch_row_pos(state->idx, state->n_active, B, S, kx, rp_s, c.s));
     const void* g = (b_lay < L) ? model->layers[b_lay].attn_norm : model->final_norm;
     DLLM_TRY(launch_gather_norm(c.dtype, xfull, rp_s, Rs, d.d, xact, g, eps, xn, c.s));
     return DLLM_OK;
@@ -527,8 +527,8 @@ int dllm_skip_step(const dllm_model* model, dllm_state* state, const dllm_step_c
     float* scores = c.at<float>(c.L.scores);
     DLLM_TRY(launch_score(c.dtype, xin, ci, nullptr, state->conf, state->kl, state->force, Rd, d.d, sc.alpha,
                           sc.conf_inverted, sc.var, scores, c.s));
-    DLLM_TRY(launch_select(scores, state->force, B, S, sc.sel, sc.k, sc.tau, kx, state->idx, state->n_active, c.s));
-    DLLM_TRY(launch_row_pos(state->idx, state->n_active, B, S, kx, rp_s, c.s));
+    DLLM_TRY(launch_select(scores, state->force, B, S, sc.sel, sc.k, sc.tau, kx, state->idx, state->n_active, c.s,
+                           rp_s));
     // the selected rows, normalised for the layer, and their inputs recorded in the input cache
     DLLM_TRY(launch_gather_norm(c.dtype, xin, rp_s, Rs, d.d, xact, model->layers[l].attn_norm, eps, xn, c.s, ci));
     // the layer's outputs go to the output cache from its last residual kernel

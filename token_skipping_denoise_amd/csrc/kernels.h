@@ -94,7 +94,7 @@ hipError_t launch_score_rows(int dtype, const void* x_act, const int32_t* row_po
 // old_row[r] = row_of[row_pos[r]] (or -1 for a dead row).
 hipError_t launch_compose_rows(const int32_t* row_pos, const int32_t* row_of, int R, int32_t* old_row, hipStream_t s);
 hipError_t launch_select(const float* score, const uint8_t* force, int B, int S, int sel, int k, float tau,
-                         int k_max, int32_t* idx, int32_t* n_active, hipStream_t s);
+                         int k_max, int32_t* idx, int32_t* n_active, hipStream_t s, int32_t* row_pos = nullptr);
 
 // ---------------- vocabulary pass (vocab.hip) ----------------
 // Rows are split into vocabulary slices when few rows are active; `partial` needs

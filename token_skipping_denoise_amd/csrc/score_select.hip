@@ -229,7 +229,7 @@ __device__ __forceinline__ int block_count(bool flag, BlockScan& sh) {
 __global__ __launch_bounds__(kSelThreads) void k_select(const float* __restrict__ score,
                                                         const uint8_t* __restrict__ force, int S, int sel, int k,
                                                         float tau, int k_max, int32_t* __restrict__ idx,
-                                                        int32_t* __restrict__ n_active) {
+                                                        int32_t* __restrict__ n_active, int32_t* __restrict__ row_pos) {
   __shared__ BlockScan sh;
   __shared__ int hist[256];
   __shared__ int bcast[2];
@@ -304,6 +304,7 @@ __global__ __launch_bounds__(kSelThreads) void k_select(const float* __restrict_
   // stable compaction in ascending index order
   int carry_eq = 0, carry_sel = 0;
   int32_t* out = idx + (long)b * k_max;
+  int32_t* rpo = row_pos ? row_pos + (long)b * k_max : nullptr;  // b S + i beside each index
   for (int i0 = 0; i0 < S; i0 += kSelThreads) {
     const int i = i0 + tid;
     bool gt = false, eq = false;
@@ -324,19 +325,26 @@ __global__ __launch_bounds__(kSelThreads) void k_select(const float* __restrict_
     const bool flag = gt || (eq && eq_rank < take_eq);
     int tot_sel;
     const int opos = carry_sel + block_excl_count(flag, sh, tot_sel);
-    if (flag && opos < k_max) out[opos] = i;
+    if (flag && opos < k_max) {
+      out[opos] = i;
+      if (rpo) rpo[opos] = b * S + i;
+    }
     carry_eq += tot_eq;
     carry_sel += tot_sel;
   }
   const int n = min(carry_sel, k_max);
-  for (int j = n + tid; j < k_max; j += kSelThreads) out[j] = -1;
+  for (int j = n + tid; j < k_max; j += kSelThreads) {
+    out[j] = -1;
+    if (rpo) rpo[j] = -1;
+  }
   if (tid == 0) n_active[b] = n;
 }
 
 hipError_t launch_select(const float* score, const uint8_t* force, int B, int S, int sel, int k, float tau,
-                         int k_max, int32_t* idx, int32_t* n_active, hipStream_t s) {
+                         int k_max, int32_t* idx, int32_t* n_active, hipStream_t s, int32_t* row_pos) {
   if (B <= 0) return hipSuccess;
-  hipLaunchKernelGGL(k_select, dim3(B), dim3(kSelThreads), 0, s, score, force, S, sel, k, tau, k_max, idx, n_active);
+  hipLaunchKernelGGL(k_select, dim3(B), dim3(kSelThreads), 0, s, score, force, S, sel, k, tau, k_max, idx, n_active,
+                     row_pos);
   return hipGetLastError();
 }
 
