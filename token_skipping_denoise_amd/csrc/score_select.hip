@@ -27,11 +27,82 @@ enum { kSelTopK = 0, kSelThreshCap = 1, kSelUnlocked = 2 };
 // combined by a fixed butterfly, so the result is deterministic.
 // Change term of one row pair (the whole wave): L1 / sqrt(w) / |b|, |a - b| / |b| or 1 - cos
 // (stable form 0.5 || a/|a| - b/|b| ||^2).  With n4 the wave also copies row a there.
+// Rows of up to kChunkRegs * 64 chunks (4096 bf16 or 2048 fp32 values) take a path with every
+// load of the lane issued before the first use and both rows kept in registers for the cosine
+// pass; the per-lane sums run over the same chunks in the same order as the general loop, so
+// both paths give bit-identical results.
+constexpr int kChunkRegs = 8;
+
+template <typename T>
+__device__ __forceinline__ float change_term_regs(const uint4* a4, const uint4* b4, uint4* n4, int w, int var) {
+  using E = Elem<T>;
+  const int lane = threadIdx.x & 63;
+  const int nchunk = w / E::kVec;
+  const bool need_rows = (var == kVarL1N || var == kVarCos || var == kVarL2Rel);
+  uint4 va[kChunkRegs], vb[kChunkRegs];
+#pragma unroll
+  for (int i = 0; i < kChunkRegs; ++i) {
+    const int c = lane + kWave * i;
+    if (c < nchunk) {
+      va[i] = a4[c];
+      if (need_rows) vb[i] = b4[c];
+    }
+  }
+  if (n4) {
+#pragma unroll
+    for (int i = 0; i < kChunkRegs; ++i)
+      if (lane + kWave * i < nchunk) n4[lane + kWave * i] = va[i];
+  }
+  if (!need_rows) return 0.f;
+  float l1 = 0.f, l2 = 0.f, na = 0.f, nb = 0.f;
+  int diff = 0;
+#pragma unroll
+  for (int i = 0; i < kChunkRegs; ++i) {
+    if (lane + kWave * i >= nchunk) break;
+    float fa[E::kVec], fb[E::kVec];
+    E::unpack(va[i], fa);
+    E::unpack(vb[i], fb);
+#pragma unroll
+    for (int e = 0; e < E::kVec; ++e) {
+      const float dlt = fa[e] - fb[e];
+      diff |= (fa[e] != fb[e]);
+      l1 += fabsf(dlt);
+      l2 += dlt * dlt;
+      na += fa[e] * fa[e];
+      nb += fb[e] * fb[e];
+    }
+  }
+  l1 = wave_sum(l1);
+  l2 = wave_sum(l2);
+  na = wave_sum(na);
+  nb = wave_sum(nb);
+  diff = wave_or(diff);
+  if (var == kVarL1N) return (nb == 0.f) ? (diff ? FLT_MAX : 0.f) : l1 / (sqrtf((float)w) * sqrtf(nb));
+  if (var == kVarL2Rel) return (nb == 0.f) ? (diff ? FLT_MAX : 0.f) : sqrtf(l2) / sqrtf(nb);
+  if (na == 0.f || nb == 0.f) return diff ? FLT_MAX : 0.f;
+  const float ia = 1.0f / sqrtf(na), ib = 1.0f / sqrtf(nb);
+  float c2 = 0.f;
+#pragma unroll
+  for (int i = 0; i < kChunkRegs; ++i) {
+    if (lane + kWave * i >= nchunk) break;
+    float fa[E::kVec], fb[E::kVec];
+    E::unpack(va[i], fa);
+    E::unpack(vb[i], fb);
+#pragma unroll
+    for (int e = 0; e < E::kVec; ++e) {
+      const float t = fa[e] * ia - fb[e] * ib;
+      c2 += t * t;
+    }
+  }
+  return 0.5f * wave_sum(c2);
+}
+
 template <typename T>
 __device__ __forceinline__ float change_term(const uint4* a4, const uint4* b4, uint4* n4, int w, int var) {
   using E = Elem<T>;
   const int lane = threadIdx.x & 63;
   const int nchunk = w / E::kVec;
+  if (nchunk <= kChunkRegs * kWave) return change_term_regs<T>(a4, b4, n4, w, var);
   float l1 = 0.f, l2 = 0.f, na = 0.f, nb = 0.f;
   int diff = 0;
   const bool need_rows = (var == kVarL1N || var == kVarCos || var == kVarL2Rel);
@@ -86,12 +157,12 @@ __device__ __forceinline__ float importance(float c, float psi, float alpha, int
 
 // ES-dLLM Eq. 1 (and variants) for every position: one wave per row.
 template <typename T>
-__global__ __launch_bounds__(256) void k_score(const T* __restrict__ h_cur, const T* __restrict__ h_prev,
-                                               T* __restrict__ h_next, const float* __restrict__ conf_prev,
-                                               const float* __restrict__ kl_prev, int rows, int w, float alpha,
-                                               int conf_inverted, int var, float* __restrict__ score) {
+__global__ __launch_bounds__(64) void k_score(const T* __restrict__ h_cur, const T* __restrict__ h_prev,
+                                              T* __restrict__ h_next, const float* __restrict__ conf_prev,
+                                              const float* __restrict__ kl_prev, int rows, int w, float alpha,
+                                              int conf_inverted, int var, float* __restrict__ score) {
   const int lane = threadIdx.x & 63;
-  const int r = blockIdx.x * 4 + (threadIdx.x >> 6);
+  const int r = blockIdx.x;  // one row per single-wave workgroup: the rows spread over every CU
   if (r >= rows) return;
   const uint4* a4 = reinterpret_cast<const uint4*>(h_cur + (long)r * w);
   const uint4* b4 = reinterpret_cast<const uint4*>(h_prev + (long)r * w);
@@ -149,7 +220,7 @@ hipError_t launch_score(int dtype, const void* h_cur, const void* h_prev, void* 
                         int conf_inverted, int var, float* score, hipStream_t s) {
   (void)force;  // forced and excluded rows are handled by the selection
   if (rows <= 0) return hipSuccess;
-  dim3 grid((rows + 3) / 4), block(256);
+  dim3 grid(rows), block(64);
   if (dtype == 0)
     hipLaunchKernelGGL(k_score<float>, grid, block, 0, s, (const float*)h_cur, (const float*)h_prev, (float*)h_next,
                        conf_prev, kl_prev, rows, width, alpha, conf_inverted, var, score);
