@@ -258,6 +258,7 @@ hipError_t launch_compose_rows(const int32_t* row_pos, const int32_t* row_of, in
 // Selection
 // ---------------------------------------------------------------------------
 constexpr int kSelThreads = 1024;
+constexpr int kSelCache = 4096;  // positions whose keys a selection keeps in LDS
 constexpr int kSelWaves = kSelThreads / kWave;
 
 // Order-preserving key: larger key = selected earlier.  NaN -> 0 (below -inf),
@@ -304,10 +305,25 @@ __global__ __launch_bounds__(kSelThreads) void k_select(const float* __restrict_
   __shared__ BlockScan sh;
   __shared__ int hist[256];
   __shared__ int bcast[2];
+  // keys of up to kSelCache positions, read from memory once (the radix passes and the
+  // compaction then read LDS); a non-candidate position is marked in cflag
+  __shared__ uint32_t kkey[kSelCache];
+  __shared__ uint8_t kcand[kSelCache];
   const int b = blockIdx.x;
   const float* sc = score + (long)b * S;
   const uint8_t* fo = force ? force + (long)b * S : nullptr;
   const int tid = threadIdx.x;
+  const bool cached = S <= kSelCache;
+  // candidate flag and key of position i: f = 2 excluded, f = 1 forced (largest key)
+  auto cand_key = [&](int i, uint32_t& key) -> bool {
+    if (cached) {
+      key = kkey[i];
+      return kcand[i] != 0;
+    }
+    const int f = fo ? fo[i] : 0;
+    key = (f == 1) ? 0xffffffffu : score_key(sc[i]);
+    return f != 2;
+  };
 
   // candidates and threshold qualifiers
   int n_cand = 0, n_q = 0;
@@ -316,10 +332,15 @@ __global__ __launch_bounds__(kSelThreads) void k_select(const float* __restrict_
     bool cand = false, q = false;
     if (i < S) {
       const int f = fo ? fo[i] : 0;
+      const float v = sc[i];
       cand = (f != 2);
-      q = cand && (f == 1 || sc[i] > tau);
+      q = cand && (f == 1 || v > tau);
+      if (cached) {
+        kkey[i] = (f == 1) ? 0xffffffffu : score_key(v);
+        kcand[i] = cand ? 1 : 0;
+      }
     }
-    n_cand += block_count(cand, sh);
+    n_cand += block_count(cand, sh);  // its barrier also publishes the cached keys
     n_q += block_count(q, sh);
   }
   int k_eff = (sel == kSelUnlocked) ? n_cand : (sel == kSelThreshCap ? min(k, n_q) : min(k, n_cand));
@@ -336,9 +357,8 @@ __global__ __launch_bounds__(kSelThreads) void k_select(const float* __restrict_
       for (int t = tid; t < 256; t += kSelThreads) hist[t] = 0;
       __syncthreads();
       for (int i = tid; i < S; i += kSelThreads) {
-        const int f = fo ? fo[i] : 0;
-        if (f == 2) continue;
-        const uint32_t key = (f == 1) ? 0xffffffffu : score_key(sc[i]);
+        uint32_t key;
+        if (!cand_key(i, key)) continue;
         if ((key & hmask) == prefix) atomicAdd(&hist[(key >> shift) & 255u], 1);
       }
       __syncthreads();
@@ -380,12 +400,11 @@ __global__ __launch_bounds__(kSelThreads) void k_select(const float* __restrict_
     const int i = i0 + tid;
     bool gt = false, eq = false;
     if (i < S) {
-      const int f = fo ? fo[i] : 0;
-      if (f != 2) {
+      uint32_t key;
+      if (cand_key(i, key)) {
         if (take_all) {
           gt = true;
         } else if (k_eff > 0) {
-          const uint32_t key = (f == 1) ? 0xffffffffu : score_key(sc[i]);
           gt = key > kth;
           eq = key == kth;
         }
