@@ -561,8 +561,9 @@ int dllm_skip_step(const dllm_model* model, dllm_state* state, const dllm_step_c
     else next_g = model->layers[l + 1].attn_norm;
     if (dense)
       st = run_layer(c, l, xfull, nact_full, rp_d, S, state->k_cache[l], state->v_cache[l], next_g);
-    else
-      st = run_layer(c, l, xact, state->n_active, rp_s, kx, state->k_cache[l], state->v_cache[l], next_g);
+    else  // the last layer's residual kernel also writes the final hidden state of its rows
+      st = run_layer(c, l, xact, state->n_active, rp_s, kx, state->k_cache[l], state->v_cache[l], next_g,
+                     l + 1 == L ? state->h_fin : nullptr);
     if (st) return st;
   }
   if (b_lay == L) {
@@ -576,7 +577,8 @@ int dllm_skip_step(const dllm_model* model, dllm_state* state, const dllm_step_c
   const int32_t* nact = full ? nact_full : state->n_active;
   const int kk = full ? S : kx;
   if (full) DLLM_TRY(launch_copy(xfull, state->h_fin, (size_t)Rd * row_bytes, c.s));
-  else DLLM_TRY(launch_scatter_norm(c.dtype, xact, rp_s, Rs, d.d, state->h_fin, nullptr, eps, nullptr, c.s));
+  else if (lcache || b_lay == L)  // otherwise the last sparse layer wrote them
+    DLLM_TRY(launch_scatter_norm(c.dtype, xact, rp_s, Rs, d.d, state->h_fin, nullptr, eps, nullptr, c.s));
 
   float* logits = c.at<float>(c.L.logits);
   GemmPlan p = gemm_plan(c.dtype, R, d.vocab, d.d);
