@@ -450,8 +450,7 @@ int dllm_skip_step(const dllm_model* model, dllm_state* state, const dllm_step_c
   void* h_next = state->h_bnd[1 - state->bnd_cur];
   const float eps = model->rms_eps;
 
-  DLLM_TRY(launch_identity_rows(B, S, idx_id, nact_full, c.s));
-  DLLM_TRY(launch_row_pos(idx_id, nact_full, B, S, S, rp_d, c.s));
+  DLLM_TRY(launch_identity_rows(B, S, idx_id, nact_full, c.s, rp_d));  // every row, and its row position
   // embedding (+ first layer's norm when layer 0 runs dense)
   const bool l0_dense = full || b_lay > 0;
   DLLM_TRY(launch_embed_norm(c.dtype, model->embed, state->tokens, d.vocab, Rd, d.d,

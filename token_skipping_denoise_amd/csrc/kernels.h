@@ -20,8 +20,9 @@ hipError_t launch_scatter_norm(int dtype, const void* src, const int32_t* row_po
 // row_pos[b*k_max + j] = b*S + idx[b*k_max + j] if j < n_active[b], else -1.
 hipError_t launch_row_pos(const int32_t* idx, const int32_t* n_active, int B, int S, int k_max,
                           int32_t* row_pos, hipStream_t s);
-// idx[b*S + i] = i, n_active[b] = S.
-hipError_t launch_identity_rows(int B, int S, int32_t* idx, int32_t* n_active, hipStream_t s);
+// idx[b*S + i] = i, n_active[b] = S; if row_pos: row_pos[b*S + i] = b*S + i.
+hipError_t launch_identity_rows(int B, int S, int32_t* idx, int32_t* n_active, hipStream_t s,
+                                int32_t* row_pos = nullptr);
 // Sum split-K partials of the QKV GEMM, apply RoPE at position row_pos % S, write Q [R, Hq*D]
 // and K/V rows into the caches [B, S, Hkv, D].
 hipError_t launch_qkv_epilogue(int dtype, const float* part, int splits, long split_stride,

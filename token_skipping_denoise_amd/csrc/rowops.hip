@@ -140,15 +140,19 @@ hipError_t launch_row_pos(const int32_t* idx, const int32_t* n_active, int B, in
   return hipGetLastError();
 }
 
-__global__ void k_identity_rows(int B, int S, int32_t* __restrict__ idx, int32_t* __restrict__ n_active) {
+__global__ void k_identity_rows(int B, int S, int32_t* __restrict__ idx, int32_t* __restrict__ n_active,
+                                int32_t* __restrict__ row_pos) {
   const int r = blockIdx.x * blockDim.x + threadIdx.x;
-  if (r < B * S) idx[r] = r % S;
+  if (r < B * S) {
+    idx[r] = r % S;
+    if (row_pos) row_pos[r] = r;  // b S + i
+  }
   if (r < B) n_active[r] = S;
 }
 
-hipError_t launch_identity_rows(int B, int S, int32_t* idx, int32_t* n_active, hipStream_t s) {
+hipError_t launch_identity_rows(int B, int S, int32_t* idx, int32_t* n_active, hipStream_t s, int32_t* row_pos) {
   const int n = B * S;
-  hipLaunchKernelGGL(k_identity_rows, dim3((n + 255) / 256), dim3(256), 0, s, B, S, idx, n_active);
+  hipLaunchKernelGGL(k_identity_rows, dim3((n + 255) / 256), dim3(256), 0, s, B, S, idx, n_active, row_pos);
   return hipGetLastError();
 }
 
