@@ -37,6 +37,11 @@
  *    with j >= n_active[b] are dead and their contents are unspecified.
  *  - Calls on one stream are ordered; calls that share a workspace or state
  *    must not overlap on different streams.
+ *  - bf16 shapes: d, n_heads * head_dim and d_ff are multiples of 64,
+ *    head_dim is 128, and the kernels address memory with 32-bit offsets, so
+ *    the SwiGLU weight ((d_ff + 128) x d elements), 256 rows of any GEMM input
+ *    and one sequence's K/V cache of one layer (S x n_kv_heads x 128) must each
+ *    stay under 2 GiB; other shapes return DLLM_ESHAPE before any launch.
  */
 #ifndef DLLM_H
 #define DLLM_H

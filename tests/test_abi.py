@@ -56,6 +56,18 @@ def test_workspace_size_planning(lib):
     assert lib.dllm_workspace_size(ctypes.byref(tiny), _ffi.DLLM_F32, 32) > 0
 
 
+def test_bf16_shapes_past_32_bit_offsets_are_rejected(lib):
+    """bf16 kernels address with 32-bit byte offsets: the shapes whose SwiGLU weight, GEMM
+    tile or per-sequence K/V cache would reach 2 GiB are refused before any launch."""
+    ok = _ffi.Dims(1, 4096, 8192, 64, 8, 128, 65536 - 128, 32000, 1)  # (d_ff + 128) d 2 B = 2^30
+    assert lib.dllm_workspace_size(ctypes.byref(ok), _ffi.DLLM_BF16, 64) > 0
+    wide_ffn = _ffi.Dims(1, 4096, 8192, 64, 8, 128, 131072, 32000, 1)  # SwiGLU span 2^31 B
+    long_kv = _ffi.Dims(1, 1 << 20, 4096, 64, 8, 128, 12288, 32000, 1)  # K/V of one sequence 2 GiB
+    big_k = _ffi.Dims(1, 512, 4096 * 1024, 32, 32, 128, 12288, 32000, 1)  # 256 rows x 4M x 2 B = 2 GiB
+    for bad in (wide_ffn, long_kv, big_k):
+        assert lib.dllm_workspace_size(ctypes.byref(bad), _ffi.DLLM_BF16, 64) == 0
+
+
 def test_argument_validation_returns_before_launch(lib):
     cfg = _ffi.ScoreCfg(0.5, 0, 0, 0, 4, 0.0)
     fake = ctypes.c_void_p(16)   # never dereferenced: validation fails first

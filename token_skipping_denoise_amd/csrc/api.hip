@@ -111,6 +111,15 @@ int check_dims(const dllm_dims* d, int dtype) {
   if (dtype == DLLM_BF16) {
     // MFMA GEMM: every reduction dim a multiple of 64; attention head dim 128
     if (d->head_dim != 128 || d->d % 64 || (d->n_heads * d->head_dim) % 64 || d->d_ff % 64) return DLLM_ESHAPE;
+    // 32-bit buffer offsets: a GEMM tile (up to 256 activation rows, or the gate..up span of
+    // the SwiGLU weight) and one sequence's K/V cache of a layer stay under 2 GiB
+    long kmax = d->d;
+    if ((long)d->n_heads * d->head_dim > kmax) kmax = (long)d->n_heads * d->head_dim;
+    if (d->d_ff > kmax) kmax = d->d_ff;
+    const long lim = 1L << 31;
+    if (256L * kmax * 2 >= lim || ((long)d->d_ff + 128) * d->d * 2 >= lim ||
+        (long)d->S * d->n_kv_heads * d->head_dim * 2 >= lim)
+      return DLLM_ESHAPE;
   } else {
     if ((d->head_dim != 64 && d->head_dim != 128) || d->d % 4 || d->d_ff % 4) return DLLM_ESHAPE;
   }
