@@ -180,3 +180,30 @@ def test_struct_layouts_match_header(tmp_path):
         assert got[(cname, "size")] == ctypes.sizeof(py), cname
         for fname, _ in py._fields_:
             assert got[(cname, fname)] == getattr(py, fname).offset, f"{cname}.{fname}"
+
+
+def test_product_path_never_touches_the_oracle():
+    """The package (binding and HIP sources) neither imports nor names the CPU oracle: only the
+    tests, smoke() and the bench's CPU-baseline leg may use it."""
+    pkg = os.path.join(os.path.dirname(os.path.dirname(os.path.abspath(__file__))), "token_skipping_denoise_amd")
+    offenders = []
+    for root, _, files in os.walk(pkg):
+        if "_build" in root or "__pycache__" in root:
+            continue
+        for f in files:
+            if f.endswith((".py", ".hip", ".h", ".cpp")):
+                text = open(os.path.join(root, f)).read()
+                if re.search(r"^\s*(from|import)\s+oracle\b|\boracle[./]", text, flags=re.M):
+                    offenders.append(f)
+    assert offenders == []
+
+
+def test_binding_fails_loudly_without_the_library(tmp_path):
+    """No fallback path: loading a missing library raises instead of computing anything else."""
+    saved = _ffi._LIB
+    _ffi._LIB = None
+    try:
+        with pytest.raises(RuntimeError, match="missing"):
+            _ffi.load(str(tmp_path / "libdllm.so"))
+    finally:
+        _ffi._LIB = saved
