@@ -375,8 +375,10 @@ GemmPlan gemm_plan(int dtype, int M, int N, int K, bool swiglu) {
   // columns (256 over 2 x 4 when 192 does not divide them), narrow ones 64 columns with 4
   // stages, and split-K fills the chip.  Many rows: 256-row tiles over 4 x 2 wavefronts where
   // the shape allows (256 x 192 for the fused SwiGLU product and QKV-like outputs, 256 x 128
-  // with a 4-way K split for the down projection), otherwise 128 x 128 with 2 stages, so that
-  // two workgroups share a CU, and split-K up to 4.
+  // with a 4- or 2-way K split for the down projection), otherwise 128 x 128 with 2 stages, so
+  // that two workgroups share a CU, and split-K up to 4.  With rows padded per sequence, dead
+  // rows fill more of a 256-row tile than of a 128-row one, so the 128-row plans stay where
+  // 256-row tiles measured faster only on fully live rows (Dream-7B's F = 18944 gate/up).
   const bool few = M <= 192;
   const bool wide = N > 8192 && N <= 32768;
   p.bm = 128;
@@ -445,12 +447,13 @@ GemmPlan gemm_plan(int dtype, int M, int N, int K, bool swiglu) {
       p.pd = 12;
       target = 192;
     } else if (K >= 2 * N && N % 128 == 0 && K / (64 * 4) >= 3) {
-      // long reductions into narrow outputs (the down projection)
+      // long reductions into narrow outputs (the down projection): a 4-way K split, 2-way
+      // once the row tiles alone give three workgroups per CU
       p.bm = 256;
       p.wm = 4;
       p.wn = 2;
       p.pd = 13;
-      p.splits = 4;
+      p.splits = ((long)((M + 255) / 256) * ((N + 127) / 128) >= 768) ? 2 : 4;
       return p;
     } else {
       p.pd = 12;
