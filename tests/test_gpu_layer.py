@@ -34,9 +34,12 @@ CASES = {
     # ragged last tile and whole dead tiles; attention in 32-query workgroups over 300 slots
     "bf16_ragged_256_tiles": (workloads.shrink(workloads.LLADA, n_layers=1, d=256, n_heads=2, n_kv_heads=2, d_ff=768,
                                                vocab=1000, B=2, S=400, prompt=200), 0.05, [300, 7], 300),
-    # F = 640 (not a multiple of 96) over 560 rows: the many-row SwiGLU fallback (128 x 128
-    # tiles, gate and up in the two halves of each wave's columns, two k-groups)
+    # F = 640 (a multiple of 128, not of 96) over 560 rows: interleaved 128 x 256 SwiGLU tiles
     "bf16_ffn640_many_rows": (workloads.shrink(workloads.LLADA, n_layers=1, d=256, n_heads=2, n_kv_heads=2, d_ff=640,
+                                               vocab=1000, B=2, S=300, prompt=150), 0.05, [280, 151], 280),
+    # F = 320 (a multiple of neither 96 nor 128) over 560 rows: the many-row SwiGLU fallback
+    # (128 x 128 tiles, gate and up in the two halves of each wave's columns, two k-groups)
+    "bf16_ffn320_many_rows": (workloads.shrink(workloads.LLADA, n_layers=1, d=256, n_heads=2, n_kv_heads=2, d_ff=320,
                                                vocab=1000, B=2, S=300, prompt=150), 0.05, [280, 151], 280),
     # two key tiles, one partial, over four waves: two waves of each workgroup have no keys
     "bf16_one_tile": (workloads.shrink(workloads.LLADA, n_layers=1, d=256, n_heads=2, n_kv_heads=2, d_ff=512,

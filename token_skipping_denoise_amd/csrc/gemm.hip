@@ -359,7 +359,8 @@ __global__ __launch_bounds__(256) void k_gemm_f32(const float* __restrict__ A, c
 #endif
 
 #ifndef DLLM_LDS_SWIGLU_ILV_CASES
-#define DLLM_LDS_SWIGLU_ILV_CASES DLLM_LDS_CASE(128, 96, 4, 1, 4, 1) DLLM_LDS_CASE(256, 192, 2, 1, 4, 2)
+#define DLLM_LDS_SWIGLU_ILV_CASES \
+  DLLM_LDS_CASE(128, 96, 4, 1, 4, 1) DLLM_LDS_CASE(256, 192, 2, 1, 4, 2) DLLM_LDS_CASE(128, 256, 2, 1, 2, 4)
 #endif
 
 GemmPlan gemm_plan(int dtype, int M, int N, int K, bool swiglu) {
@@ -377,8 +378,9 @@ GemmPlan gemm_plan(int dtype, int M, int N, int K, bool swiglu) {
   // the shape allows (256 x 192 for the fused SwiGLU product and QKV-like outputs, 256 x 128
   // with a 4- or 2-way K split for the down projection), otherwise 128 x 128 with 2 stages, so
   // that two workgroups share a CU, and split-K up to 4.  With rows padded per sequence, dead
-  // rows fill more of a 256-row tile than of a 128-row one, so the 128-row plans stay where
-  // 256-row tiles measured faster only on fully live rows (Dream-7B's F = 18944 gate/up).
+  // rows fill more of a 256-row tile than of a 128-row one: a SwiGLU width that 96 does not
+  // divide takes interleaved 128 x 256 tiles (faster at every live share measured on
+  // Dream-7B's F = 18944 than 256 x 128 ones, which win only on fully live rows).
   const bool few = M <= 192;
   const bool wide = N > 8192 && N <= 32768;
   p.bm = 128;
@@ -431,6 +433,12 @@ GemmPlan gemm_plan(int dtype, int M, int N, int K, bool swiglu) {
         p.bn = 192;
         p.wm = 4;
         p.wn = 2;
+        p.pd = 12;
+        p.ilv = 1;
+      } else if (N % 128 == 0) {  // 128 outputs over 128-row tiles (Dream-7B's F = 18944)
+        p.bn = 256;
+        p.wm = 2;
+        p.wn = 4;
         p.pd = 12;
         p.ilv = 1;
       } else {
