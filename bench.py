@@ -132,7 +132,7 @@ def kernel_work(dims, rows: int):
         "lm_head": (_ffi.TK_LM_HEAD, R) + gemm(V, d, 4),
         "vocab_conf": (_ffi.TK_VOCAB, R, 4.0 * R * V, 0.0),
         "score": (_ffi.TK_SCORE, 0, 3.0 * B * S * d * e + 8.0 * B * S, 0.0),
-        "select": (_ffi.TK_SELECT, 0, 4.0 * B * S + 4.0 * B * rows, 0.0),
+        "select": (_ffi.TK_SELECT, 0, 4.0 * B * S + 8.0 * B * rows, 0.0),  # scores in; indices + row positions out
     }
 
 
