@@ -463,6 +463,13 @@ GemmPlan gemm_plan(int dtype, int M, int N, int K, bool swiglu) {
       p.pd = 13;
       p.splits = ((long)((M + 255) / 256) * ((N + 127) / 128) >= 768) ? 2 : 4;
       return p;
+    } else if (N % 192 == 0 && N <= 32768) {
+      // QKV-like widths below the wide range (Dream-7B's 4608): 128 x 192 over 4 x 2 waves,
+      // measured no slower than 128 x 128 at any live share and 15% faster on live rows
+      p.bn = 192;
+      p.wm = 4;
+      p.wn = 2;
+      p.pd = 13;
     } else {
       p.pd = 12;
       target = 512;
