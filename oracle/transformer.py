@@ -19,6 +19,8 @@ from __future__ import annotations
 
 import numpy as np
 
+from .numerics import round_bf16
+
 
 def rmsnorm(x: np.ndarray, g: np.ndarray, eps: float) -> np.ndarray:
     """x / sqrt(mean(x^2) + eps) * g over the last axis."""
@@ -54,11 +56,21 @@ def silu(x: np.ndarray) -> np.ndarray:
     return out
 
 
-def attention_rows(q: np.ndarray, k_cache: np.ndarray, v_cache: np.ndarray) -> np.ndarray:
+LOG2E = 1.4426950408889634   # log2(e)
+
+
+def attention_rows(q: np.ndarray, k_cache: np.ndarray, v_cache: np.ndarray, p_store=None) -> np.ndarray:
     """Bidirectional attention of R queries over all S cached keys of one sequence.
 
     q: [R, Hq, D]; k_cache, v_cache: [S, Hkv, D]; query head h reads KV head
     h // (Hq / Hkv).  Every key is visible (no causal mask).  Returns [R, Hq, D].
+
+    ``p_store`` (bf16 storage mode) is the rounding of the softmax weights that multiply V: the
+    GPU holds them in bf16 as the matrix-core operand.  They are taken as w_j = 2^(x_j - M) with
+    x_j = s_j log2(e) and M = ceil(max_j x_j): scaling by a power of two leaves a value's bf16
+    rounding unchanged, so the rounded weights are the same against any integer reference a
+    kernel may use (and however it splits the keys).  The output is sum_j p_store(w_j) V_j over
+    the unrounded sum_j w_j.  Without ``p_store`` the weights stay exact (plain softmax).
     """
     R, Hq, D = q.shape
     S, Hkv, _ = k_cache.shape
@@ -69,10 +81,15 @@ def attention_rows(q: np.ndarray, k_cache: np.ndarray, v_cache: np.ndarray) -> n
         kh = k_cache[:, h // g, :]                       # [S, D]
         vh = v_cache[:, h // g, :]
         s = (q[:, h, :] @ kh.T) * scale                  # [R, S]
-        s = s - np.max(s, axis=1, keepdims=True)
-        p = np.exp(s)
-        p = p / np.sum(p, axis=1, keepdims=True)
-        out[:, h, :] = p @ vh
+        if p_store is None:
+            s = s - np.max(s, axis=1, keepdims=True)
+            p = np.exp(s)
+            p = p / np.sum(p, axis=1, keepdims=True)
+            out[:, h, :] = p @ vh
+        else:
+            x = s * LOG2E
+            w = np.exp2(x - np.ceil(np.max(x, axis=1, keepdims=True)))
+            out[:, h, :] = (p_store(w) @ vh) / np.sum(w, axis=1, keepdims=True)
     return out
 
 
@@ -100,9 +117,10 @@ def layer_rows(lw: dict, x_rows: np.ndarray, pos: np.ndarray, batch: np.ndarray,
     k_cache[batch, pos] = k
     v_cache[batch, pos] = v
     o = np.empty((R, Hq, D), dtype=np.float64)
+    p_store = store if store is round_bf16 else None   # bf16 softmax weights in bf16 storage mode
     for b in np.unique(batch):
         sel = np.nonzero(batch == b)[0]
-        o[sel] = attention_rows(q[sel], k_cache[b], v_cache[b])
+        o[sel] = attention_rows(q[sel], k_cache[b], v_cache[b], p_store)
     o = store(o.reshape(R, Hq * D))
     x = store(x_rows + o @ lw["wo"].T)
     n2 = store(rmsnorm(x, lw["ffn_norm"], eps))
@@ -152,9 +170,14 @@ def dense_forward(weights: dict, tokens: np.ndarray, *, n_heads: int, n_kv_heads
         for b in range(B):
             for h in range(Hq):
                 sc = q[b, :, h, :] @ k[b, :, h // g, :].T / np.sqrt(D)     # [S, S], no mask
-                w = np.exp(sc - sc.max(axis=1, keepdims=True))
-                w /= w.sum(axis=1, keepdims=True)
-                o[b, :, h, :] = w @ v[b, :, h // g, :]
+                if store is round_bf16:   # bf16 weights against a power-of-two reference
+                    xl = sc * LOG2E
+                    w = np.exp2(xl - np.ceil(xl.max(axis=1, keepdims=True)))
+                    o[b, :, h, :] = (store(w) @ v[b, :, h // g, :]) / w.sum(axis=1, keepdims=True)
+                else:
+                    w = np.exp(sc - sc.max(axis=1, keepdims=True))
+                    w /= w.sum(axis=1, keepdims=True)
+                    o[b, :, h, :] = w @ v[b, :, h // g, :]
         o = store(o.reshape(B, S, Hq * D))
         x = store(x + o @ lw["wo"].T)
         n2 = store(rmsnorm(x, lw["ffn_norm"], eps))

@@ -115,3 +115,45 @@ def test_gqa_equals_mha_with_repeated_kv():
     k_rep = np.repeat(k, 2, axis=1)
     v_rep = np.repeat(v, 2, axis=1)
     np.testing.assert_allclose(attention_rows(q, k, v), attention_rows(q, k_rep, v_rep), rtol=1e-14)
+
+
+def test_bf16_softmax_weights_pins():
+    """bf16 storage mode rounds the softmax weights that multiply V (the GPU's matrix-core operand)
+    against a power-of-two reference.  Pins: (1) an exact rounding is the plain softmax; (2) when
+    every weight 2^(x_j - M) is a power of two it is exact in bf16, so the result is the plain
+    softmax; (3) the error is within the rounding bound 2^-9 sum_j p_j |V_j| (RNE to 8 significant
+    bits); (4) shifting all scores of a query by an integer number of log2 units changes nothing,
+    (5) a half-unit shift does change the rounded weights (the reference is an integer, not the
+    row maximum itself)."""
+    from oracle.numerics import round_bf16
+    R, S, H, D = 3, 40, 2, 16
+    q = RNG.standard_normal((R, H, D))
+    k = RNG.standard_normal((S, H, D))
+    v = RNG.standard_normal((S, H, D))
+    exact = attention_rows(q, k, v)
+    np.testing.assert_allclose(attention_rows(q, k, v, p_store=lambda w: w), exact, rtol=1e-12, atol=1e-13)
+    # (2) scores s_j = n_j ln2: weights 2^(n_j - max n) are exact in bf16
+    qd = np.zeros((1, 1, D))
+    qd[0, 0, 0] = np.sqrt(D)            # s_j = k_j[0] with the 1/sqrt(D) scale
+    kd = np.zeros((S, 1, D))
+    kd[:, 0, 0] = RNG.integers(-6, 3, S) * np.log(2.0)
+    vd = RNG.standard_normal((S, 1, D))
+    np.testing.assert_allclose(attention_rows(qd, kd, vd, p_store=round_bf16), attention_rows(qd, kd, vd),
+                               rtol=1e-12, atol=1e-13)
+    # (3) the rounding bound
+    got = attention_rows(q, k, v, p_store=round_bf16)
+    a = attention_rows(q, k, np.abs(v))
+    assert np.all(np.abs(got - exact) <= 2.0 ** -9 * a + 1e-12)
+    assert np.max(np.abs(got - exact)) > 0          # the weights really are rounded
+    # (4), (5): add t u to every key, u = q / |q|^2, so every score of that query rises by t / sqrt(D)
+    for shift, same in ((3.0, True), (0.5, False)):
+        q1 = q[:1, :1]
+        u = q1[0, 0] / float(q1[0, 0] @ q1[0, 0])
+        t = shift * np.log(2.0) * np.sqrt(D)
+        k1 = k[:, :1] + t * u
+        a0 = attention_rows(q1, k[:, :1], v[:, :1], p_store=round_bf16)
+        a1 = attention_rows(q1, k1, v[:, :1], p_store=round_bf16)
+        if same:
+            np.testing.assert_allclose(a1, a0, rtol=1e-12, atol=1e-13)
+        else:
+            assert np.max(np.abs(a1 - a0)) > 1e-6
