@@ -157,6 +157,32 @@ __device__ __forceinline__ float half_swap_sum(float x) {
   return a + b;
 }
 
+// The online softmax keeps its reference maximum as an integer in the exp2 domain (the running
+// max of s * scale * log2 e, rounded up).  Each weight 2^(x - m) is then a power-of-two multiple
+// of its value against any other integer reference, so its bf16 rounding (the matrix-core
+// operand of the V product) and every rescale or merge factor 2^(m_a - m_b) are exact scalings:
+// the output does not depend on how the keys are split over waves, key groups or workgroups.
+__device__ __forceinline__ float pow2_int(float e) { return __builtin_amdgcn_ldexpf(1.f, (int)e); }
+
+// Reference update of one tile: when some query of the wave would see a weight above 2^8, every
+// lane moves its reference to max(m, ceil(tile max)) and rescales its sum and accumulators by
+// the exact power of two; otherwise nothing changes.  mt2: this lane's tile max in the exp2
+// domain (-inf without a finite score).
+template <int NACC>
+__device__ __forceinline__ void softmax_reference(float mt2, float& m_ref, float& l_run, f32x16_t (&oacc)[NACC]) {
+  if (__builtin_amdgcn_ballot_w64(mt2 > m_ref + 8.f) != 0) {
+    const float m_new = fmaxf(m_ref, ceilf(mt2));
+    // an empty state (m = -inf: no finite score yet) has nothing to rescale
+    const float corr = (m_ref == -INFINITY || m_new == -INFINITY) ? 0.f : pow2_int(m_ref - m_new);
+    l_run *= corr;
+    m_ref = m_new;
+#pragma unroll
+    for (int db = 0; db < NACC; ++db)
+#pragma unroll
+      for (int e = 0; e < 16; ++e) oacc[db][e] *= corr;
+  }
+}
+
 // Workgroup coordinates with the query blocks of one (sequence, KV head) kept on one XCD.
 // Workgroups are dealt to the eight XCDs in turn by linear id; when the grid is a multiple of 8,
 // XCD x takes the x-th contiguous eighth of the (query block fastest) work list instead, so the
@@ -279,9 +305,8 @@ __global__ __launch_bounds__(512, 1) void k_attn_bf16(const uint16_t* __restrict
   for (int db = 0; db < kHD / 32; ++db)
 #pragma unroll
     for (int e = 0; e < 16; ++e) oacc[db][e] = 0.f;
-  // running max of the raw scores q.k, and the softmax sum of 2^((s - m) * scale_log2e)
+  // integer reference in the exp2 domain, and the softmax sum of 2^(s * scale_log2e - m)
   float m_run = -INFINITY, l_run = 0.f;
-  const float grow_thr = 8.f / scale_log2e;  // 2^8 in raw score units
 
   // per-lane parts of the fragment addresses
   const int k_row = grp * 32 + l32;
@@ -347,22 +372,12 @@ __global__ __launch_bounds__(512, 1) void k_attn_bf16(const uint16_t* __restrict
 #pragma unroll
     for (int e = 0; e < 16; ++e) mt = fmaxf(mt, sacc[e]);
     mt = half_swap_max(mt);
-    // The reference max m_run only moves when some query of the wave would otherwise see a
-    // weight above 2^8; below that, numerator and sum keep using the old reference, which
-    // changes nothing but rounding and saves rescaling the accumulators on almost every tile.
-    if (__builtin_amdgcn_ballot_w64(mt > m_run + grow_thr) != 0) {
-      const float m_new = fmaxf(m_run, mt);
-      // a lane without a finite score yet keeps the empty state (m = -inf, l = 0)
-      const float corr = (m_new == -INFINITY) ? 1.f : __builtin_amdgcn_exp2f((m_run - m_new) * scale_log2e);
-      l_run *= corr;
-      m_run = m_new;
-#pragma unroll
-      for (int db = 0; db < kHD / 32; ++db)
-#pragma unroll
-        for (int e = 0; e < 16; ++e) oacc[db][e] *= corr;
-    }
+    // The reference only moves when some query of the wave would otherwise see a weight above
+    // 2^8; below that, numerator and sum keep the old reference, which saves rescaling the
+    // accumulators on almost every tile (the weights are exact power-of-two multiples either way).
+    softmax_reference(mt * scale_log2e, m_run, l_run, oacc);
     // m_run = -inf only while every score seen is -inf, so every weight is 0 then
-    const float mc = (m_run == -INFINITY) ? 0.f : m_run * scale_log2e;
+    const float mc = (m_run == -INFINITY) ? 0.f : m_run;
     float rs = 0.f;
 #pragma unroll
     for (int e = 0; e < 16; ++e) {
@@ -415,8 +430,8 @@ __global__ __launch_bounds__(512, 1) void k_attn_bf16(const uint16_t* __restrict
     const float m1 = ml[(gw * 2) * 64 + lane], l1 = ml[(gw * 2 + 1) * 64 + lane];
     const float M = fmaxf(m_run, m1);
     // both -inf only for a group without keys; keep the merged state finite then
-    const float c0 = (m_run == -INFINITY) ? 0.f : __builtin_amdgcn_exp2f((m_run - M) * scale_log2e);
-    const float c1 = (m1 == -INFINITY) ? 0.f : __builtin_amdgcn_exp2f((m1 - M) * scale_log2e);
+    const float c0 = (m_run == -INFINITY) ? 0.f : pow2_int(m_run - M);
+    const float c1 = (m1 == -INFINITY) ? 0.f : pow2_int(m1 - M);
     l_run = l_run * c0 + l1 * c1;
     m_run = M;
 #pragma unroll
@@ -448,7 +463,7 @@ __global__ __launch_bounds__(512, 1) void k_attn_bf16(const uint16_t* __restrict
         *reinterpret_cast<float2*>(pp + d + 2) = make_float2(oacc[db][4 * e4 + 2], oacc[db][4 * e4 + 3]);
       }
     if (hi == 0) {
-      pp[kHD] = m_run * scale_log2e;  // the merge works in the exp2 domain
+      pp[kHD] = m_run;  // the integer reference, exp2 domain
       pp[kHD + 1] = l_run;
     }
     return;
@@ -570,8 +585,7 @@ __global__ __launch_bounds__(256, 1) void k_attn_q32(const uint16_t* __restrict_
   for (int db = 0; db < kHD / 32; ++db)
 #pragma unroll
     for (int e = 0; e < 16; ++e) oacc[db][e] = 0.f;
-  float m_run = -INFINITY, l_run = 0.f;
-  const float grow_thr = 8.f / scale_log2e;  // 2^8 in raw score units
+  float m_run = -INFINITY, l_run = 0.f;  // integer exp2-domain reference, softmax sum
 
   const int k_sw = swz(l32);
   const int v_row = 4 * hi + ((lane & 15) >> 2);              // + 16 hf (+ 8)
@@ -623,17 +637,8 @@ __global__ __launch_bounds__(256, 1) void k_attn_q32(const uint16_t* __restrict_
 #pragma unroll
     for (int e = 0; e < 16; ++e) mt = fmaxf(mt, sacc[e]);
     mt = half_swap_max(mt);
-    if (__builtin_amdgcn_ballot_w64(mt > m_run + grow_thr) != 0) {
-      const float m_new = fmaxf(m_run, mt);
-      const float corr = (m_new == -INFINITY) ? 1.f : __builtin_amdgcn_exp2f((m_run - m_new) * scale_log2e);
-      l_run *= corr;
-      m_run = m_new;
-#pragma unroll
-      for (int db = 0; db < kHD / 32; ++db)
-#pragma unroll
-        for (int e = 0; e < 16; ++e) oacc[db][e] *= corr;
-    }
-    const float mc = (m_run == -INFINITY) ? 0.f : m_run * scale_log2e;
+    softmax_reference(mt * scale_log2e, m_run, l_run, oacc);
+    const float mc = (m_run == -INFINITY) ? 0.f : m_run;
     float rs = 0.f;
 #pragma unroll
     for (int e = 0; e < 16; ++e) {
@@ -682,7 +687,7 @@ __global__ __launch_bounds__(256, 1) void k_attn_q32(const uint16_t* __restrict_
 #pragma unroll
   for (int w = 0; w < kQWaves; ++w) {
     // a wave without keys (or with only masked ones) keeps m = -inf and contributes nothing
-    cw[w] = (mw[w] == -INFINITY) ? 0.f : __builtin_amdgcn_exp2f((mw[w] - M) * scale_log2e);
+    cw[w] = (mw[w] == -INFINITY) ? 0.f : pow2_int(mw[w] - M);
     L += ml[(w * 2 + 1) * 64 + lane] * cw[w];
   }
   if (!qvalid) return;
@@ -709,7 +714,7 @@ __global__ __launch_bounds__(256, 1) void k_attn_q32(const uint16_t* __restrict_
   }
 }
 
-// Combine split-KV partials: O = sum_s O_s 2^(m_s - M) / sum_s l_s 2^(m_s - M).
+// Combine split-KV partials: O = sum_s O_s 2^(m_s - M) / sum_s l_s 2^(m_s - M) (exact powers of two).
 __global__ __launch_bounds__(128) void k_attn_merge(const float* __restrict__ part, int nsplit, long split_stride,
                                                     const int32_t* __restrict__ n_active, int k_max, int Hq,
                                                     uint16_t* __restrict__ o) {
@@ -722,7 +727,7 @@ __global__ __launch_bounds__(128) void k_attn_merge(const float* __restrict__ pa
   float L = 0.f, acc = 0.f;
   for (int sp = 0; sp < nsplit; ++sp) {
     const float* ps = p0 + sp * split_stride;
-    const float w = exp2f(ps[kHD] - M);
+    const float w = (ps[kHD] == -INFINITY) ? 0.f : pow2_int(ps[kHD] - M);  // integer references
     L += ps[kHD + 1] * w;
     acc += ps[d] * w;
   }
