@@ -97,12 +97,12 @@ def llada_generation(dims, k_sparse=128, boundary=4, steps=64, block=32, nested=
     return out
 
 
-def run_generation(model, state, tok0, plan, ws):
+def run_generation(model, state, tok0, plan, ws, timing=None):
     state.tokens.copy_(tok0)
     state.c.have_prev = 0
     state.c.bnd_cur = 0
     for kw in plan:
-        api.skip_step(model, state, api.step_cfg(ws=ws, **kw))
+        api.skip_step(model, state, api.step_cfg(ws=ws, timing=timing, **kw))
 
 
 def ffn_up_bytes(dims, rows: int) -> float:
@@ -147,12 +147,8 @@ def kernel_table(lib, model, state, tok0, plan, ws, dims, rows: int):
         for name, (tk, max_rows, nbytes, flops) in work.items():
             timing = _ffi.Timing(tk, max_rows, ev.n, 0, ctypes.cast(ev.start, ctypes.POINTER(ctypes.c_void_p)),
                                  ctypes.cast(ev.stop, ctypes.POINTER(ctypes.c_void_p)))
-            lib.dllm_set_timing(ctypes.byref(timing))
-            try:
-                run_generation(model, state, tok0, plan, ws)
-                torch.cuda.synchronize()
-            finally:
-                lib.dllm_set_timing(None)
+            run_generation(model, state, tok0, plan, ws, timing)
+            torch.cuda.synchronize()
             if timing.count == 0:
                 continue
             durs = ev.elapsed_ms(timing.count)
@@ -355,7 +351,7 @@ def dcache_schedule(dims, device, k_active=64, refresh_every=16, block=32, unmas
     return steps
 
 
-def run_schedule(model, state, tok0, steps, ws, after_step=None):
+def run_schedule(model, state, tok0, steps, ws, after_step=None, timing=None):
     state.tokens.copy_(tok0)
     state.c.have_prev = 0
     state.c.bnd_cur = 0
@@ -369,7 +365,7 @@ def run_schedule(model, state, tok0, steps, ws, after_step=None):
         else:
             # the schedule's marks; rows the lock rule has already locked stay locked
             torch.maximum(state.force, force, out=state.force)
-        api.skip_step(model, state, api.step_cfg(ws=ws, **kw))
+        api.skip_step(model, state, api.step_cfg(ws=ws, timing=timing, **kw))
         if after_step is not None:
             after_step(kw)
 
@@ -389,12 +385,8 @@ def vocab_pass_stats(lib, model, state, tok0, steps, ws, dims, state_bytes):
 
     timing = _ffi.Timing(_ffi.TK_VOCAB, 0, ev.n, 0, ctypes.cast(ev.start, ctypes.POINTER(ctypes.c_void_p)),
                          ctypes.cast(ev.stop, ctypes.POINTER(ctypes.c_void_p)))
-    lib.dllm_set_timing(ctypes.byref(timing))
-    try:
-        run_schedule(model, state, tok0, steps, ws, after_step=count_rows)
-        torch.cuda.synchronize()
-    finally:
-        lib.dllm_set_timing(None)
+    run_schedule(model, state, tok0, steps, ws, after_step=count_rows, timing=timing)
+    torch.cuda.synchronize()
     n = timing.count
     durs = ev.elapsed_ms(n)
     ev.close()
@@ -490,12 +482,8 @@ def kernel_table_schedule(lib, model, state, tok0, steps, ws, dims, rows):
                 continue
             timing = _ffi.Timing(tk, max_rows, ev.n, 0, ctypes.cast(ev.start, ctypes.POINTER(ctypes.c_void_p)),
                                  ctypes.cast(ev.stop, ctypes.POINTER(ctypes.c_void_p)))
-            lib.dllm_set_timing(ctypes.byref(timing))
-            try:
-                run_schedule(model, state, tok0, steps, ws)
-                torch.cuda.synchronize()
-            finally:
-                lib.dllm_set_timing(None)
+            run_schedule(model, state, tok0, steps, ws, timing=timing)
+            torch.cuda.synchronize()
             if timing.count == 0:
                 continue
             durs = ev.elapsed_ms(timing.count)
@@ -593,8 +581,6 @@ def main():
     else:
         for _ in range(args.warmup):
             run_generation(model, state, tok0, plan, ws)
-        if timing is not None:
-            lib.dllm_set_timing(ctypes.byref(timing))
     torch.cuda.synchronize()
 
     t_start = time.perf_counter()
@@ -602,18 +588,15 @@ def main():
         if graph is not None:
             graph.replay()
         else:
-            run_generation(model, state, tok0, plan, ws)
+            run_generation(model, state, tok0, plan, ws, timing)
     torch.cuda.synchronize()
     elapsed = time.perf_counter() - t_start
-    if timing is not None:
-        if graph is not None:
-            # Event records cannot be replayed from a captured graph: the dominant kernel is
-            # timed over one eager generation issued right after the timed replays (same
-            # kernels, same shapes, same stream).
-            lib.dllm_set_timing(ctypes.byref(timing))
-            run_generation(model, state, tok0, plan, ws)
-            torch.cuda.synchronize()
-        lib.dllm_set_timing(None)
+    if timing is not None and graph is not None:
+        # Event records cannot be replayed from a captured graph: the dominant kernel is
+        # timed over one eager generation issued right after the timed replays (same
+        # kernels, same shapes, same stream).
+        run_generation(model, state, tok0, plan, ws, timing)
+        torch.cuda.synchronize()
 
     gen_tokens = dims.B * (dims.S - dims.prompt)
     value = gen_tokens * args.steps / elapsed

@@ -87,6 +87,15 @@ typedef enum {
                              dilated schedule plans for this round ([DUS] sec. 2) */
 } dllm_unmask_mode;
 
+/* dllm_step_cfg.layer_cache: what each cached layer compares to pick the rows it recomputes
+ * ([DC] section 3: a partial response update decided by feature-vector similarity). */
+typedef enum {
+  DLLM_LCACHE_OFF = 0,
+  DLLM_LCACHE_HIDDEN = 1, /* the hidden state entering the layer, against x_in_cache[l] */
+  DLLM_LCACHE_VALUE = 2   /* the layer's V projection of that input (every unlocked position), against
+                             the V the position holds in the layer's V cache */
+} dllm_layer_cache_mode;
+
 /* Most nested boundaries a step may name (dllm_step_cfg.nested_layer). */
 #define DLLM_MAX_NESTED 3
 
@@ -172,6 +181,29 @@ typedef struct {
   void **x_out_cache;     /* the same for the hidden state leaving layer l */
 } dllm_state;
 
+/* Kernel classes the measurement hook can bracket. */
+typedef enum {
+  DLLM_TK_NONE = 0,
+  DLLM_TK_QKV = 1,      /* QKV product of a layer */
+  DLLM_TK_ATTN = 2,     /* bidirectional attention of a layer */
+  DLLM_TK_O = 3,        /* output projection of a layer */
+  DLLM_TK_FFN_UP = 4,   /* gate/up product with the SwiGLU epilogue */
+  DLLM_TK_FFN_DOWN = 5, /* down projection of a layer */
+  DLLM_TK_LM_HEAD = 6,  /* LM-head product */
+  DLLM_TK_VOCAB = 7,    /* confidence / argmax / KL vocabulary pass */
+  DLLM_TK_SCORE = 8,    /* importance scores */
+  DLLM_TK_SELECT = 9    /* active-row selection */
+} dllm_timed_kernel;
+
+typedef struct {
+  int32_t kernel;     /* dllm_timed_kernel to bracket */
+  int32_t max_rows;   /* only launches whose row capacity is <= max_rows (0: all) */
+  int32_t capacity;   /* number of event pairs in start/stop */
+  int32_t count;      /* out: event pairs recorded so far (the caller resets it) */
+  void **start;       /* host array [capacity] of caller-created hipEvent_t */
+  void **stop;        /* host array [capacity] of caller-created hipEvent_t */
+} dllm_timing;
+
 typedef struct {
   int32_t boundary_layer;   /* b: layers < b run on all rows; 0 <= b <= L */
   int32_t full_step;        /* 1: every layer on every row (first step, refresh) */
@@ -196,14 +228,25 @@ typedef struct {
   int32_t nested_k[DLLM_MAX_NESTED];      /* 0 <= k <= state->k_max */
   /* Per-layer cache ([DC] section 3: partial response update gated by feature similarity; the
    * long-interval prompt cache is force == 2 on prompt positions between full steps).  With
-   * layer_cache = 1, every layer l >= boundary_layer replaces the single selection: each
-   * position's hidden state entering l is scored against x_in_cache[l] with `score` (alpha 0 and
-   * DLLM_VAR_COS give the cosine-similarity test), the top score.k per sequence (forced first,
-   * locked excluded, ties to the lower position) are computed through layer l and written to
-   * both caches, and every other position takes x_out_cache[l] as its output.  The rows computed
-   * at the last layer get the LM head; idx / n_active report them.  A full step fills both caches
-   * of layers >= boundary_layer for every position.  Needs n_nested = 0. */
-  int32_t layer_cache;
+   * layer_cache != DLLM_LCACHE_OFF, every layer l >= boundary_layer replaces the single selection:
+   * each position's feature is scored with `score` (alpha 0 and DLLM_VAR_COS give the
+   * cosine-similarity test) -- DLLM_LCACHE_HIDDEN: its hidden state entering l against
+   * x_in_cache[l]; DLLM_LCACHE_VALUE: the layer's V projection of that input, computed for every
+   * unlocked position, against the V the position holds in v_cache[l] (written when it was last
+   * computed there) -- the top score.k per sequence (forced first, locked excluded, ties to the
+   * lower position) are computed through layer l and written to both caches and the K/V cache,
+   * and every other position takes x_out_cache[l] as its output.  The rows computed at the last
+   * layer get the LM head; idx / n_active report them.  A full step fills both caches of layers
+   * >= boundary_layer for every position.  Needs n_nested = 0; values outside the enum return
+   * DLLM_EINVAL. */
+  int32_t layer_cache;      /* dllm_layer_cache_mode */
+  /* Measurement hook for benchmarks, or NULL: each launch of the chosen kernel class made by
+   * this call is bracketed by hipEventRecord(start[i]) / hipEventRecord(stop[i]) on the call's
+   * stream, for i = count, count + 1, ... until capacity is reached; count is advanced as pairs
+   * are recorded (the caller resets it).  The struct belongs to this call only, so calls on
+   * other threads or streams are unaffected.  Not for use under stream capture.  A malformed
+   * struct returns DLLM_EINVAL before any launch; a failed event record returns DLLM_ELAUNCH. */
+  dllm_timing *timing;
 } dllm_step_cfg;
 
 /* Bytes of device workspace needed by dllm_skip_step / dllm_layer_sparse for
@@ -300,38 +343,6 @@ int dllm_dus_mark(uint8_t *force, int32_t B, int32_t S, int32_t lo, int32_t bloc
  * SureLock lock update and/or confidence unmasking of [block_lo, block_hi).
  * On a full step every row is active, whatever state->k_max is. */
 int dllm_skip_step(const dllm_model *model, dllm_state *state, const dllm_step_cfg *cfg, void *stream);
-
-/* Kernel classes the measurement hook can bracket. */
-typedef enum {
-  DLLM_TK_NONE = 0,
-  DLLM_TK_QKV = 1,      /* QKV product of a layer */
-  DLLM_TK_ATTN = 2,     /* bidirectional attention of a layer */
-  DLLM_TK_O = 3,        /* output projection of a layer */
-  DLLM_TK_FFN_UP = 4,   /* gate/up product with the SwiGLU epilogue */
-  DLLM_TK_FFN_DOWN = 5, /* down projection of a layer */
-  DLLM_TK_LM_HEAD = 6,  /* LM-head product */
-  DLLM_TK_VOCAB = 7,    /* confidence / argmax / KL vocabulary pass */
-  DLLM_TK_SCORE = 8,    /* importance scores */
-  DLLM_TK_SELECT = 9    /* active-row selection */
-} dllm_timed_kernel;
-
-typedef struct {
-  int32_t kernel;     /* dllm_timed_kernel to bracket */
-  int32_t max_rows;   /* only launches whose row capacity is <= max_rows (0: all) */
-  int32_t capacity;   /* number of event pairs in start/stop */
-  int32_t count;      /* out: event pairs recorded so far (the caller resets it) */
-  void **start;       /* host array [capacity] of caller-created hipEvent_t */
-  void **stop;        /* host array [capacity] of caller-created hipEvent_t */
-} dllm_timing;
-
-/* Measurement hook for benchmarks: while installed, each launch of the chosen
- * kernel class made by dllm_skip_step / dllm_layer_sparse is bracketed by
- * hipEventRecord(start[i]) / hipEventRecord(stop[i]) on that call's stream,
- * for i = count, count+1, ... until capacity is reached.  The struct must
- * outlive its installation; NULL removes the hook.  Process-wide, not
- * thread-safe, not for use under stream capture.  Returns DLLM_EINVAL for a
- * malformed struct. */
-int dllm_set_timing(dllm_timing *timing);
 
 /* Human-readable text of a dllm_status. */
 const char *dllm_status_string(int status);

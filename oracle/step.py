@@ -36,7 +36,10 @@ when it was last computed at l (a per-layer output cache).  Both caches keep the
 the computed rows.  A full step computes every row at every layer and fills both caches.  The
 long-interval prompt cache is the caller's force == 2 on prompt positions between full steps.
 After the last layer the rows computed there get the LM head; all others keep their
-statistics (their final hidden state is the cached one).
+statistics (their final hidden state is the cached one).  The compared feature is the row's hidden
+state entering the layer, or (cache_feature "value") the layer's V projection of that input
+against the V the row holds in the layer's K/V cache, i.e. the V computed when the row was last
+computed there: the V projection of every row is the extra cost of this test.
 
 Readings where the pages leave a step open: the mask id is the last vocabulary
 entry and is excluded from softmax and argmax; a locked row (force == 2) skips
@@ -54,7 +57,7 @@ from .importance import VAR_L1N, importance_score
 from .numerics import store_fn
 from .post import surelock_update, unmask_forced, unmask_topn
 from .selection import FORCE_EXCLUDED, select_thresh_cap, select_topk
-from .transformer import layer_rows, lm_logits
+from .transformer import layer_rows, lm_logits, rmsnorm
 from .vocab import conf_kl, kl_state_value
 
 SEL_TOPK, SEL_THRESH_CAP, SEL_UNLOCKED = 0, 1, 2
@@ -99,6 +102,7 @@ class StepCfg:
     unmask_mode: int = UNMASK_CONF
     nested: tuple = ()             # ((layer, k), ...): later layers that narrow the active set
     layer_cache: bool = False      # per-layer partial update from layer b on (dLLM-Cache)
+    cache_feature: str = "hidden"  # what the layer cache compares: "hidden" (the layer input) or "value"
 
 
 @dataclass
@@ -188,6 +192,8 @@ def skip_step(model: OracleModel, st: OracleState, cfg: StepCfg) -> tuple[Oracle
             raise ValueError("nested boundaries and the layer cache do not combine")
         if not full and not st.have_prev:
             raise ValueError("a sparse layer-cache step needs caches filled by an earlier step")
+        if cfg.cache_feature not in ("hidden", "value"):
+            raise ValueError(f"unknown layer-cache feature {cfg.cache_feature!r}")
     elif not full and st.h_bnd_prev is None:
         raise ValueError("a sparse step needs the previous boundary hidden state")
     nested = [(int(nl), int(nk)) for nl, nk in cfg.nested]
@@ -254,7 +260,14 @@ def skip_step(model: OracleModel, st: OracleState, cfg: StepCfg) -> tuple[Oracle
                            n_kv_heads=model.n_kv_heads, rope_base=model.rope_base, eps=model.eps, store=store)
             xo[:] = x
             return
-        s = importance_score(x, xi, st.conf.reshape(-1), st.kl.reshape(-1), alpha=cfg.score.alpha,
+        if cfg.cache_feature == "value":
+            # the layer's V projection of every row's current input against the V cached when the
+            # row was last computed at this layer (its rows of the layer's V cache)
+            v_new = store(store(rmsnorm(x, lw["attn_norm"], model.eps)) @ lw["wv"].T)
+            feat, feat_prev = v_new, st.v_cache[l].reshape(B * S, -1)
+        else:
+            feat, feat_prev = x, xi
+        s = importance_score(feat, feat_prev, st.conf.reshape(-1), st.kl.reshape(-1), alpha=cfg.score.alpha,
                              var=cfg.score.var, conf_inverted=cfg.score.conf_inverted).reshape(B, S)
         sel = np.concatenate([b * S + _select(cfg.score, s[b], st.force[b]) for b in range(B)]).astype(np.int64)
         layer_scores.append(s)

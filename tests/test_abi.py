@@ -35,7 +35,7 @@ def test_every_declared_symbol_is_exported(lib):
 
 
 def test_version_and_status_strings(lib):
-    assert lib.dllm_version() == 100
+    assert lib.dllm_version() == 200
     assert lib.dllm_status_string(0) == b"ok"
     assert lib.dllm_status_string(4) == b"workspace missing or too small"
 
@@ -148,6 +148,28 @@ def test_layer_cache_validation_returns_before_launch(lib):
     # everything valid but no workspace: still no launch
     st.x_out_cache = ctypes.cast(caches, ctypes.POINTER(ctypes.c_void_p))
     assert lib.dllm_skip_step(ctypes.byref(m), ctypes.byref(st), ctypes.byref(cfg), None) == 4
+
+
+def test_timing_hook_is_per_call_and_validated(lib):
+    """The measurement hook travels in the step config of one call (no process-wide state): a
+    malformed hook is refused before any launch, and a well-formed one passes validation."""
+    m, st, cfg, keep = _fake_step_args()
+    cfg.layer_cache = 0
+    cfg.boundary_layer = 1
+    bad = _ffi.Timing(_ffi.TK_QKV, 0, 4, 0, None, None)       # capacity without event arrays
+    cfg.timing = ctypes.pointer(bad)
+    assert lib.dllm_skip_step(ctypes.byref(m), ctypes.byref(st), ctypes.byref(cfg), None) == 1
+    neg = _ffi.Timing(_ffi.TK_QKV, 0, -1, 0, None, None)
+    cfg.timing = ctypes.pointer(neg)
+    assert lib.dllm_skip_step(ctypes.byref(m), ctypes.byref(st), ctypes.byref(cfg), None) == 1
+    ev = (ctypes.c_void_p * 4)()
+    good = _ffi.Timing(_ffi.TK_QKV, 0, 4, 0, ctypes.cast(ev, ctypes.POINTER(ctypes.c_void_p)),
+                       ctypes.cast(ev, ctypes.POINTER(ctypes.c_void_p)))
+    cfg.timing = ctypes.pointer(good)
+    # valid hook, no workspace: refused for the workspace, still before any launch
+    assert lib.dllm_skip_step(ctypes.byref(m), ctypes.byref(st), ctypes.byref(cfg), None) == 4
+    assert good.count == 0
+    assert not hasattr(lib, "dllm_set_timing")
 
 
 def test_struct_layouts_match_header(tmp_path):

@@ -10,7 +10,7 @@ from oracle.dus import dus_rounds
 from oracle.step import (SEL_THRESH_CAP, SEL_TOPK, SEL_UNLOCKED, UNMASK_FORCED, OracleModel, ScoreCfg, StepCfg,
                          new_state, skip_step)
 from synth import workloads
-from tests.gpu_util import DEV, assert_close, np64, selection_gap
+from tests.gpu_util import DEV, assert_close, assert_within, kl_first_order, np64, selection_gap
 from tests.helpers import oracle_weights
 from token_skipping_denoise_amd import api
 
@@ -91,8 +91,12 @@ def test_tiny_fp32_two_iterations():
     np.testing.assert_array_equal(gs.argmax.cpu().numpy(), os_.argmax)
     for l in range(dims.n_layers):
         assert_close(np64(gs.k_cache[l]), os_.k_cache[l], 1e-4, f"K cache {l} after sparse")
+    # fp32 KL: rtol 1e-3 plus 1e-6 absolute.  The kernel combines three O(1) fp32 terms,
+    # KL = t/s - (m - m') - log(s/s'), whose rounding (sums over V terms, hardware exp2 and log)
+    # stays within about 16 ulps of (sum_v p_v |z_v - z'_v| + |m - m'| + 1), i.e. about 1e-6 here,
+    # while the KL values of this step are ~2e-4.
     np.testing.assert_allclose(np64(gs.kl).reshape(-1)[info["rows"]], os_.kl.reshape(-1)[info["rows"]],
-                               rtol=2e-3, atol=2e-6)
+                               rtol=1e-3, atol=1e-6)
 
 
 def _designed_conf(B, S, k, seed):
@@ -175,6 +179,7 @@ def test_bf16_gqa_surelock_iteration(kl_state, vocab):
     gs.tokens.copy_(new_tok)
     os_.tokens = new_tok.numpy().astype(np.int64)
     kc_before = [t.cpu().clone() for t in gs.k_cache]
+    zp_g, zp_o = np64(gs.logits_prev), os_.logits_prev.copy()   # the previous logits the KL compares with
     gsc, osc = _score_cfg_pair(0.0, VAR_L1N, SEL_UNLOCKED, dims.S)
     eps = 5e-3
     api.skip_step(gm, gs, api.step_cfg(0, False, gsc, lock_kl_eps=eps, lock_conf_min=-1.0, ws=ws))
@@ -191,14 +196,20 @@ def test_bf16_gqa_surelock_iteration(kl_state, vocab):
     for l in range(dims.n_layers):
         kc = gs.k_cache[l].cpu().reshape(dims.B * dims.S, -1)
         assert torch.equal(kc[locked], kc_before[l].reshape(dims.B * dims.S, -1)[locked])
-    # KL and the lock rule, away from the threshold
+    # KL: bf16 weights make the GPU's logits differ from the oracle's (within the logits tolerance
+    # checked above); the KL may differ by what those logit differences explain to first order
     gkl = np64(gs.kl).reshape(-1)[rows]
     okl = os_.kl.reshape(-1)[rows]
-    np.testing.assert_allclose(gkl, okl, rtol=5e-2, atol=2e-4)
+    first, rest = kl_first_order(np64(gs.logits_prev)[rows], os_.logits_prev[rows], zp_g[rows], zp_o[rows],
+                                  dims.mask_id)
+    assert_within(gkl, okl + first, rest + 1e-3 * np.abs(okl), "surelock KL beyond its first-order change")
+    # the lock rule: identical decisions wherever the oracle's KL is further from eps than the
+    # GPU's KL can be
     gf = gs.force.cpu().numpy().reshape(-1)
     of = os_.force.reshape(-1)
     assert np.all(gf[locked] == FORCE_EXCLUDED)
-    clear = np.abs(okl - eps) > 5e-4
+    clear = np.abs(okl - eps) > np.abs(first) + rest + 1e-3 * np.abs(okl)
+    assert np.mean(clear) > 0.9
     assert np.array_equal(gf[rows][clear], of[rows][clear])
 
 
@@ -387,16 +398,19 @@ def test_bf16_nested_boundaries():
         assert torch.equal(hn[idle], hn_before[j].reshape(BS, -1)[idle])
 
 
-@pytest.mark.parametrize("case", ["tiers_b1", "changed_b0"])
+@pytest.mark.parametrize("case", ["tiers_b1", "changed_b0", "value_tiers_b1", "value_changed_b0"])
 def test_bf16_layer_cache(case):
     """Per-layer cache steps ([DC] section 3) against the oracle, prompt rows locked between full
     steps.  tiers_b1: layer 0 dense, layers 1-3 cached, alpha 0.8 with two separated confidence
     tiers (8 rows per sequence recomputed at every cached layer).  changed_b0: every layer cached,
-    alpha 0 (cosine change only), k = the 3 positions whose tokens changed."""
+    alpha 0 (cosine change only), k = the 3 positions whose tokens changed.  value_*: the same
+    with the layers' V projections compared against the cached V instead of the hidden states."""
     dims = workloads.shrink(workloads.LLADA, n_layers=4, d=256, n_heads=2, n_kv_heads=2, d_ff=512, vocab=1000,
                             B=2, S=96, prompt=48)
     B, S, L = dims.B, dims.S, dims.n_layers
     BS = B * S
+    feature = "value" if case.startswith("value_") else "hidden"
+    case = case.replace("value_", "")
     b, k, alpha = (1, 8, 0.8) if case == "tiers_b1" else (0, 3, 0.0)
     print(f"layer cache {case}", flush=True)
     gm, om = _models(dims, std=0.05)
@@ -433,8 +447,9 @@ def test_bf16_layer_cache(case):
     xo_before = [t.cpu().clone() for t in gs.x_out]
     hf_before = gs.h_fin.cpu().clone()
     gsc, osc = _score_cfg_pair(alpha, VAR_COS, SEL_TOPK, k)
-    api.skip_step(gm, gs, api.step_cfg(b, False, gsc, ws=ws, layer_cache=True))
-    os_, info = skip_step(om, os_, StepCfg(boundary_layer=b, full_step=False, score=osc, layer_cache=True))
+    api.skip_step(gm, gs, api.step_cfg(b, False, gsc, ws=ws, layer_cache=feature))
+    os_, info = skip_step(om, os_, StepCfg(boundary_layer=b, full_step=False, score=osc, layer_cache=True,
+                                           cache_feature=feature))
     torch.cuda.synchronize()
     assert len(info["layer_rows"]) == L - b
     for s in info["layer_scores"]:        # every layer's selection is well separated

@@ -17,7 +17,7 @@ MAX_NESTED = 3
 EXPORTED = (
     "dllm_workspace_size", "dllm_score_select", "dllm_gather_rows", "dllm_scatter_rows",
     "dllm_layer_sparse", "dllm_confidence_kl", "dllm_skip_step", "dllm_status_string", "dllm_version",
-    "dllm_set_timing", "dllm_dus_mark", "dllm_pack_weight",
+    "dllm_dus_mark", "dllm_pack_weight",
 )
 TK_NONE, TK_QKV, TK_ATTN, TK_O, TK_FFN_UP, TK_FFN_DOWN, TK_LM_HEAD, TK_VOCAB, TK_SCORE, TK_SELECT = range(10)
 
@@ -51,17 +51,17 @@ class StateC(Structure):
                 ("x_in_cache", POINTER(c_void_p)), ("x_out_cache", POINTER(c_void_p))]
 
 
+class Timing(Structure):
+    _fields_ = [("kernel", c_int32), ("max_rows", c_int32), ("capacity", c_int32), ("count", c_int32),
+                ("start", POINTER(c_void_p)), ("stop", POINTER(c_void_p))]
+
+
 class StepCfg(Structure):
     _fields_ = [("boundary_layer", c_int32), ("full_step", c_int32), ("score", ScoreCfg),
                 ("lock_kl_eps", c_float), ("lock_conf_min", c_float), ("unmask_n", c_int32),
                 ("block_lo", c_int32), ("block_hi", c_int32), ("unmask_mode", c_int32), ("ws", c_void_p),
                 ("ws_bytes", c_size_t), ("n_nested", c_int32), ("nested_layer", c_int32 * MAX_NESTED),
-                ("nested_k", c_int32 * MAX_NESTED), ("layer_cache", c_int32)]
-
-
-class Timing(Structure):
-    _fields_ = [("kernel", c_int32), ("max_rows", c_int32), ("capacity", c_int32), ("count", c_int32),
-                ("start", POINTER(c_void_p)), ("stop", POINTER(c_void_p))]
+                ("nested_k", c_int32 * MAX_NESTED), ("layer_cache", c_int32), ("timing", POINTER(Timing))]
 
 
 _LIB = None
@@ -101,8 +101,6 @@ def load(path: str = LIB_PATH) -> ctypes.CDLL:
     lib.dllm_skip_step.argtypes = [POINTER(ModelC), POINTER(StateC), POINTER(StepCfg), c_void_p]
     lib.dllm_status_string.restype = ctypes.c_char_p
     lib.dllm_status_string.argtypes = [c_int32]
-    lib.dllm_set_timing.restype = c_int32
-    lib.dllm_set_timing.argtypes = [POINTER(Timing)]
     lib.dllm_version.restype = c_int32
     lib.dllm_version.argtypes = []
     _LIB = lib

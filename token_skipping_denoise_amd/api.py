@@ -278,9 +278,12 @@ class State:
 
 def step_cfg(boundary_layer: int, full_step: bool, score: _ffi.ScoreCfg | None = None, *, lock_kl_eps=-1.0,
              lock_conf_min=0.9, unmask_n=0, block_lo=0, block_hi=0, unmask_mode=UNMASK_CONF,
-             ws=None, nested=(), layer_cache=False) -> _ffi.StepCfg:
+             ws=None, nested=(), layer_cache=False, timing=None) -> _ffi.StepCfg:
     """nested: ((layer, k), ...) later layers that narrow the active set (at most MAX_NESTED).
-    layer_cache: per-layer partial update from the boundary layer on (needs State(layer_cache=True))."""
+    layer_cache: per-layer partial update from the boundary layer on (needs State(layer_cache=True)),
+    comparing the hidden state entering each layer (True or "hidden") or the layer's V projection of
+    it against the cached V ("value").
+    timing: an _ffi.Timing measurement hook for this call (kept alive by the caller), or None."""
     if len(nested) > _ffi.MAX_NESTED:
         raise DllmError(f"at most {_ffi.MAX_NESTED} nested boundaries")
     c = _ffi.StepCfg()
@@ -300,7 +303,12 @@ def step_cfg(boundary_layer: int, full_step: bool, score: _ffi.ScoreCfg | None =
     for j, (nl, nk) in enumerate(nested):
         c.nested_layer[j] = int(nl)
         c.nested_k[j] = int(nk)
-    c.layer_cache = int(bool(layer_cache))
+    modes = {False: 0, True: 1, "hidden": 1, "value": 2}
+    if layer_cache not in modes:
+        raise DllmError("layer_cache must be False, True / 'hidden' or 'value'")
+    c.layer_cache = modes[layer_cache]
+    if timing is not None:
+        c.timing = ctypes.pointer(timing)
     return c
 
 

@@ -25,40 +25,48 @@ int esize(int dtype) { return dtype == DLLM_F32 ? 4 : 2; }
     if ((expr) != hipSuccess) return DLLM_ELAUNCH; \
   } while (0)
 
-// Measurement hook: brackets launches of one kernel class with caller-created events.
-dllm_timing* g_timing = nullptr;
-
+// Measurement hook of one call (dllm_step_cfg.timing): brackets the launches of one kernel class
+// with caller-created events on the call's stream.  `err` holds the status of the start record;
+// stop() records the end and counts the pair only when both records succeeded.
 struct TimedRegion {
   dllm_timing* t = nullptr;
   hipStream_t s;
   int slot = -1;
-  TimedRegion(int kernel, int rows, hipStream_t st) : s(st) {
-    dllm_timing* g = g_timing;
+  hipError_t err = hipSuccess;
+  TimedRegion(dllm_timing* g, int kernel, int rows, hipStream_t st) : s(st) {
     if (!g || g->kernel != kernel || (g->max_rows > 0 && rows > g->max_rows) || g->count >= g->capacity) return;
     t = g;
     slot = g->count;
-    hipEventRecord((hipEvent_t)g->start[slot], s);
+    err = hipEventRecord((hipEvent_t)g->start[slot], s);
+    if (err != hipSuccess) t = nullptr;
   }
-  ~TimedRegion() {
-    if (!t) return;
-    hipEventRecord((hipEvent_t)t->stop[slot], s);
-    t->count = slot + 1;
+  hipError_t stop() {
+    if (!t) return err;
+    err = hipEventRecord((hipEvent_t)t->stop[slot], s);
+    if (err == hipSuccess) t->count = slot + 1;
+    t = nullptr;
+    return err;
   }
 };
+
+bool timing_ok(const dllm_timing* t) {
+  return !t || (t->capacity >= 0 && t->count >= 0 && (t->capacity == 0 || (t->start && t->stop)));
+}
 
 // Workspace layout for (dims, dtype, k_max).
 struct WsLayout {
   size_t xfull, xact, xn, q, o, h, part, attn, vpart, logits, scores, idx_id, nact_full, rowpos_d, rowpos_s,
-      nforce, row_of, old_row, total;
+      nforce, row_of, old_row, cand_idx, cand_n, cand_rp, total;
 };
 
 long max_part_floats(const dllm_dims& d, int dtype, long M) {
   const int NQKV = (d.n_heads + 2 * d.n_kv_heads) * d.head_dim;
   const int HQD = d.n_heads * d.head_dim;
-  const int Ns[4] = {NQKV, d.d, 2 * d.d_ff, d.d};
-  const int Ks[4] = {d.d, HQD, d.d, d.d_ff};
+  // QKV, O, gate/up, down, and the V projection alone (the per-layer cache's V feature)
+  const int Ns[5] = {NQKV, d.d, 2 * d.d_ff, d.d, d.n_kv_heads * d.head_dim};
+  const int Ks[5] = {d.d, HQD, d.d, d.d_ff, d.d};
   long best = 0;
-  for (int i = 0; i < 4; ++i) {
+  for (int i = 0; i < 5; ++i) {
     const GemmPlan p = gemm_plan(dtype, (int)M, Ns[i], Ks[i]);
     best = std::max(best, (long)p.splits * M * Ns[i]);
   }
@@ -96,6 +104,9 @@ bool plan_ws(const dllm_dims& d, int dtype, int k_max, WsLayout& L) {
   L.nforce = take(Rd);                     // nested boundaries: candidate marks per position
   L.row_of = take(Rd * sizeof(int32_t));   //   active row of each position
   L.old_row = take(Rs * sizeof(int32_t));  //   row before narrowing of each row after it
+  L.cand_idx = take(Rd * sizeof(int32_t)); // per-layer cache, V feature: unlocked positions,
+  L.cand_n = take(d.B * sizeof(int32_t));  //   their count per sequence,
+  L.cand_rp = take(Rd * sizeof(int32_t));  //   and their row positions
   L.total = off;
   return true;
 }
@@ -141,6 +152,7 @@ struct Ctx {
   char* ws;
   WsLayout L;
   hipStream_t s;
+  dllm_timing* timing = nullptr;  // this call's measurement hook, or null
   template <typename T>
   T* at(size_t off) const {
     return reinterpret_cast<T*>(ws + off);
@@ -164,47 +176,59 @@ int run_layer(const Ctx& c, int l, void* x, const int32_t* nact, const int32_t* 
 
   GemmPlan p = gemm_plan(c.dtype, R, NQKV, d.d);
   {
-    TimedRegion t(DLLM_TK_QKV, R, c.s);
+    TimedRegion t(c.timing, DLLM_TK_QKV, R, c.s);
+    DLLM_TRY(t.err);
     DLLM_TRY(launch_gemm(c.dtype, p, xn, w.w_qkv, part, R, NQKV, d.d, nact, kx, c.s));
+    DLLM_TRY(t.stop());
   }
   DLLM_TRY(launch_qkv_epilogue(c.dtype, part, p.splits, (long)R * NQKV, row_pos, R, d.S, d.n_heads, d.n_kv_heads,
                                d.head_dim, c.m->rope_base, q, kc, vc, c.s));
   {
-    TimedRegion t(DLLM_TK_ATTN, R, c.s);
+    TimedRegion t(c.timing, DLLM_TK_ATTN, R, c.s);
+    DLLM_TRY(t.err);
     DLLM_TRY(launch_attention(c.dtype, q, kc, vc, o, nact, d.B, d.S, kx, d.n_heads, d.n_kv_heads, d.head_dim,
                               c.at<float>(c.L.attn), c.s));
+    DLLM_TRY(t.stop());
   }
   p = gemm_plan(c.dtype, R, d.d, HQD);
   {
-    TimedRegion t(DLLM_TK_O, R, c.s);
+    TimedRegion t(c.timing, DLLM_TK_O, R, c.s);
+    DLLM_TRY(t.err);
     DLLM_TRY(launch_gemm(c.dtype, p, o, w.w_o, part, R, d.d, HQD, nact, kx, c.s));
+    DLLM_TRY(t.stop());
   }
   DLLM_TRY(launch_resid_norm(c.dtype, part, p.splits, (long)R * d.d, row_pos, R, d.d, x, w.ffn_norm, eps, xn, c.s));
   if (c.dtype == DLLM_BF16) {
     const PackedPlan pp = w.w_gate_up_packed ? packed_plan(R, 2 * d.d_ff, d.d, true) : PackedPlan{};
     p = gemm_plan(c.dtype, R, d.d_ff, d.d, true);
-    TimedRegion t(DLLM_TK_FFN_UP, R, c.s);
+    TimedRegion t(c.timing, DLLM_TK_FFN_UP, R, c.s);
+    DLLM_TRY(t.err);
     if (pp.ok)
       DLLM_TRY(launch_gemm_packed(pp, xn, w.w_gate_up_packed, nullptr, h, R, 2 * d.d_ff, d.d, d.d_ff, nact, kx, c.s));
     else
       DLLM_TRY(launch_gemm_swiglu(p, xn, w.w_gate_up, h, R, d.d_ff, d.d, nact, kx, c.s));
+    DLLM_TRY(t.stop());
   } else {
     p = gemm_plan(c.dtype, R, 2 * d.d_ff, d.d);
-    TimedRegion t(DLLM_TK_FFN_UP, R, c.s);
+    TimedRegion t(c.timing, DLLM_TK_FFN_UP, R, c.s);
+    DLLM_TRY(t.err);
     DLLM_TRY(launch_gemm(c.dtype, p, xn, w.w_gate_up, part, R, 2 * d.d_ff, d.d, nact, kx, c.s));
     DLLM_TRY(launch_swiglu(c.dtype, part, p.splits, (long)R * 2 * d.d_ff, row_pos, R, d.d_ff, h, c.s));
+    DLLM_TRY(t.stop());
   }
   p = gemm_plan(c.dtype, R, d.d, d.d_ff);
   {
     const PackedPlan pp = (c.dtype == DLLM_BF16 && w.w_down_packed) ? packed_plan(R, d.d, d.d_ff, false)
                                                                      : PackedPlan{};
-    TimedRegion t(DLLM_TK_FFN_DOWN, R, c.s);
+    TimedRegion t(c.timing, DLLM_TK_FFN_DOWN, R, c.s);
+    DLLM_TRY(t.err);
     if (pp.ok) {
       DLLM_TRY(launch_gemm_packed(pp, h, w.w_down_packed, part, nullptr, R, d.d, d.d_ff, 0, nact, kx, c.s));
       p.splits = pp.splits;
     } else {
       DLLM_TRY(launch_gemm(c.dtype, p, h, w.w_down, part, R, d.d, d.d_ff, nact, kx, c.s));
     }
+    DLLM_TRY(t.stop());
   }
   DLLM_TRY(launch_resid_norm(c.dtype, part, p.splits, (long)R * d.d, row_pos, R, d.d, x, next_g, eps, xn, c.s,
                              out_scatter));
@@ -229,13 +253,7 @@ int check_model(const dllm_model* m) {
 
 extern "C" {
 
-int dllm_version(void) { return 100; }
-
-int dllm_set_timing(dllm_timing* t) {
-  if (t && (t->capacity < 0 || (t->capacity > 0 && (!t->start || !t->stop)))) return DLLM_EINVAL;
-  g_timing = t;
-  return DLLM_OK;
-}
+int dllm_version(void) { return 200; }
 
 const char* dllm_status_string(int status) {
   switch (status) {
@@ -433,7 +451,9 @@ int dllm_skip_step(const dllm_model* model, dllm_state* state, const dllm_step_c
     if (cfg->nested_k[j] < 0 || cfg->nested_k[j] > kx) return DLLM_EINVAL;
     if (!state->h_nested[j] || !aligned16(state->h_nested[j])) return DLLM_EINVAL;
   }
+  if (cfg->layer_cache < 0 || cfg->layer_cache > DLLM_LCACHE_VALUE) return DLLM_EINVAL;
   const bool lcache = cfg->layer_cache != 0;
+  const bool vfeat = cfg->layer_cache == DLLM_LCACHE_VALUE;
   if (lcache) {
     if (n_nested != 0 || b_lay >= L || !state->x_in_cache || !state->x_out_cache) return DLLM_EINVAL;
     for (int l = b_lay; l < L; ++l)
@@ -442,7 +462,9 @@ int dllm_skip_step(const dllm_model* model, dllm_state* state, const dllm_step_c
         return DLLM_EINVAL;
   }
 
-  Ctx c{model, &d, model->dtype, (char*)cfg->ws, {}, (hipStream_t)stream};
+  if (!timing_ok(cfg->timing)) return DLLM_EINVAL;
+
+  Ctx c{model, &d, model->dtype, (char*)cfg->ws, {}, (hipStream_t)stream, cfg->timing};
   plan_ws(d, c.dtype, kx, c.L);
   if (!cfg->ws || cfg->ws_bytes < c.L.total) return DLLM_EWORKSPACE;
   const int es = esize(c.dtype);
@@ -472,14 +494,18 @@ int dllm_skip_step(const dllm_model* model, dllm_state* state, const dllm_step_c
     }
     float* scores = c.at<float>(c.L.scores);
     {
-      TimedRegion t(DLLM_TK_SCORE, Rd, c.s);
+      TimedRegion t(c.timing, DLLM_TK_SCORE, Rd, c.s);
+      DLLM_TRY(t.err);
       DLLM_TRY(launch_score(c.dtype, xfull, h_prev, h_next, state->conf, state->kl, state->force, Rd, d.d, sc.alpha,
                             sc.conf_inverted, sc.var, scores, c.s));
+      DLLM_TRY(t.stop());
     }
     {
-      TimedRegion t(DLLM_TK_SELECT, Rd, c.s);
+      TimedRegion t(c.timing, DLLM_TK_SELECT, Rd, c.s);
+      DLLM_TRY(t.err);
       DLLM_TRY(launch_select(scores, state->force, B, S, sc.sel, sc.k, sc.tau, kx, state->idx, state->n_active, c.s,
                              rp_s));
+      DLLM_TRY(t.stop());
     }
     const void* g = (b_lay < L) ? model->layers[b_lay].attn_norm : model->final_norm;
     DLLM_TRY(launch_gather_norm(c.dtype, xfull, rp_s, Rs, d.d, xact, g, eps, xn, c.s));
@@ -521,6 +547,7 @@ int dllm_skip_step(const dllm_model* model, dllm_state* state, const dllm_step_c
   // input rows of the next cached layer: the boundary's input, then each sparse layer's
   // output cache, which holds the current output of every row (no copy back into xfull)
   const void* xin = xfull;
+  bool cand_ready = false;
   auto cached_layer = [&](int l) -> int {
     void* ci = state->x_in_cache[l];
     void* co = state->x_out_cache[l];
@@ -533,10 +560,37 @@ int dllm_skip_step(const dllm_model* model, dllm_state* state, const dllm_step_c
       return DLLM_OK;
     }
     float* scores = c.at<float>(c.L.scores);
-    DLLM_TRY(launch_score(c.dtype, xin, ci, nullptr, state->conf, state->kl, state->force, Rd, d.d, sc.alpha,
-                          sc.conf_inverted, sc.var, scores, c.s));
-    DLLM_TRY(launch_select(scores, state->force, B, S, sc.sel, sc.k, sc.tau, kx, state->idx, state->n_active, c.s,
-                           rp_s));
+    if (vfeat) {
+      // the unlocked positions (the same for every layer of the step), in ascending order
+      int32_t* cand_idx = c.at<int32_t>(c.L.cand_idx);
+      int32_t* cand_n = c.at<int32_t>(c.L.cand_n);
+      int32_t* cand_rp = c.at<int32_t>(c.L.cand_rp);
+      if (!cand_ready) {
+        DLLM_TRY(launch_select(scores, state->force, B, S, DLLM_SEL_UNLOCKED, S, 0.f, S, cand_idx, cand_n, c.s,
+                               cand_rp));
+        cand_ready = true;
+      }
+      // the layer's V projection of every candidate's current input (rows b*S + j, j < cand_n[b]),
+      // stored in the element type, against the V the position holds in the layer's cache
+      const int HKD = d.n_kv_heads * d.head_dim;
+      const char* w_v = (const char*)model->layers[l].w_qkv + (size_t)(d.n_heads + d.n_kv_heads) * d.head_dim * d.d * es;
+      float* part = c.at<float>(c.L.part);
+      void* vnew = c.ws + c.L.q;  // idle until the layer runs
+      DLLM_TRY(launch_gather_norm(c.dtype, xin, cand_rp, Rd, d.d, nullptr, model->layers[l].attn_norm, eps, xn, c.s));
+      const GemmPlan pv = gemm_plan(c.dtype, Rd, HKD, d.d);
+      DLLM_TRY(launch_gemm(c.dtype, pv, xn, w_v, part, Rd, HKD, d.d, cand_n, S, c.s));
+      DLLM_TRY(launch_sum_store(c.dtype, part, pv.splits, (long)Rd * HKD, cand_rp, Rd, HKD, vnew, c.s));
+      uint8_t* nforce = c.at<uint8_t>(c.L.nforce);
+      DLLM_TRY(launch_score_rows(c.dtype, vnew, cand_rp, Rd, state->v_cache[l], state->conf, state->kl, state->force,
+                                 (long)Rd, HKD, sc.alpha, sc.conf_inverted, sc.var, scores, nforce,
+                                 c.at<int32_t>(c.L.row_of), c.s));
+      DLLM_TRY(launch_select(scores, nforce, B, S, sc.sel, sc.k, sc.tau, kx, state->idx, state->n_active, c.s, rp_s));
+    } else {
+      DLLM_TRY(launch_score(c.dtype, xin, ci, nullptr, state->conf, state->kl, state->force, Rd, d.d, sc.alpha,
+                            sc.conf_inverted, sc.var, scores, c.s));
+      DLLM_TRY(launch_select(scores, state->force, B, S, sc.sel, sc.k, sc.tau, kx, state->idx, state->n_active, c.s,
+                             rp_s));
+    }
     // the selected rows, normalised for the layer, and their inputs recorded in the input cache
     DLLM_TRY(launch_gather_norm(c.dtype, xin, rp_s, Rs, d.d, xact, model->layers[l].attn_norm, eps, xn, c.s, ci));
     // the layer's outputs go to the output cache from its last residual kernel
@@ -592,13 +646,17 @@ int dllm_skip_step(const dllm_model* model, dllm_state* state, const dllm_step_c
   GemmPlan p = gemm_plan(c.dtype, R, d.vocab, d.d);
   p.splits = 1;
   {
-    TimedRegion t(DLLM_TK_LM_HEAD, R, c.s);
+    TimedRegion t(c.timing, DLLM_TK_LM_HEAD, R, c.s);
+    DLLM_TRY(t.err);
     DLLM_TRY(launch_gemm(c.dtype, p, xn, model->lm_head, logits, R, d.vocab, d.d, nact, kk, c.s));
+    DLLM_TRY(t.stop());
   }
   {
-    TimedRegion t(DLLM_TK_VOCAB, R, c.s);
+    TimedRegion t(c.timing, DLLM_TK_VOCAB, R, c.s);
+    DLLM_TRY(t.err);
     DLLM_TRY(launch_conf_kl(logits, state->logits_prev, state->logits_prev_dtype, rp, R, d.vocab, model->mask_id,
                             state->have_prev, state->conf, state->argmax, state->kl, c.ws + c.L.vpart, c.s));
+    DLLM_TRY(t.stop());
   }
   if (cfg->lock_kl_eps >= 0.f && state->have_prev)
     DLLM_TRY(launch_lock_update(rp, R, state->conf, state->kl, cfg->lock_kl_eps, cfg->lock_conf_min, state->force,

@@ -36,6 +36,9 @@ hipError_t launch_resid_norm(int dtype, const float* part, int splits, long spli
 // h[r, c] = silu(P[r, c]) * P[r, F + c] with P the summed partials [R, 2F].
 hipError_t launch_swiglu(int dtype, const float* part, int splits, long split_stride, const int32_t* row_pos,
                          int R, int F, void* h, hipStream_t s);
+// dst[r] = sum of the split-K partials of row r, stored in the element type (rows with row_pos >= 0).
+hipError_t launch_sum_store(int dtype, const float* part, int splits, long split_stride, const int32_t* row_pos,
+                            int R, int w, void* dst, hipStream_t s);
 hipError_t launch_copy(const void* src, void* dst, size_t bytes, hipStream_t s);
 
 // ---------------- GEMM (gemm.hip) ----------------

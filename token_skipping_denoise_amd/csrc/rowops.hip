@@ -410,6 +410,47 @@ hipError_t launch_swiglu(int dtype, const float* part, int splits, long split_st
   return hipGetLastError();
 }
 
+// dst[r, :] = the split-K partials of row r summed (in split order) and stored in T, for the rows
+// with row_pos[r] >= 0: a product's rows in the storage precision of the activations.
+template <typename T>
+__global__ __launch_bounds__(256) void k_sum_store(const float* __restrict__ part, int splits, long sstride,
+                                                   const int32_t* __restrict__ row_pos, int R, int w,
+                                                   T* __restrict__ dst) {
+  const long n4 = (long)R * w / 4;
+  for (long e4 = blockIdx.x * (long)blockDim.x + threadIdx.x; e4 < n4; e4 += (long)gridDim.x * blockDim.x) {
+    const long e = e4 * 4;
+    const int r = (int)(e / w);
+    if (row_pos[r] < 0) continue;
+    float4 acc = *reinterpret_cast<const float4*>(part + e);
+    for (int k = 1; k < splits; ++k) {
+      const float4 v = *reinterpret_cast<const float4*>(part + k * sstride + e);
+      acc.x += v.x;
+      acc.y += v.y;
+      acc.z += v.z;
+      acc.w += v.w;
+    }
+    Elem<T>::st(dst, e, acc.x);
+    Elem<T>::st(dst, e + 1, acc.y);
+    Elem<T>::st(dst, e + 2, acc.z);
+    Elem<T>::st(dst, e + 3, acc.w);
+  }
+}
+
+hipError_t launch_sum_store(int dtype, const float* part, int splits, long split_stride, const int32_t* row_pos,
+                            int R, int w, void* dst, hipStream_t s) {
+  if (R <= 0) return hipSuccess;
+  if (w % 4 || split_stride % 4) return hipErrorInvalidValue;
+  const long n4 = (long)R * w / 4;
+  const int grid = (int)((n4 + 255) / 256 < 8192 ? (n4 + 255) / 256 : 8192);
+  if (dtype == 0)
+    hipLaunchKernelGGL(k_sum_store<float>, dim3(grid), dim3(256), 0, s, part, splits, split_stride, row_pos, R, w,
+                       (float*)dst);
+  else
+    hipLaunchKernelGGL(k_sum_store<bf16>, dim3(grid), dim3(256), 0, s, part, splits, split_stride, row_pos, R, w,
+                       (bf16*)dst);
+  return hipGetLastError();
+}
+
 hipError_t launch_copy(const void* src, void* dst, size_t bytes, hipStream_t s) {
   if (bytes == 0) return hipSuccess;
   return hipMemcpyAsync(dst, src, bytes, hipMemcpyDeviceToDevice, s);
