@@ -294,6 +294,25 @@ int dllm_layer_sparse(const dllm_model *model, int32_t layer, void *x_act, const
                       const int32_t *n_active, int32_t k_max, void *k_cache, void *v_cache,
                       void *ws, size_t ws_bytes, void *stream);
 
+/* Bytes of the library-owned scratch array dllm_layer_sparse_noalloc works in (one per GPU). */
+#define DLLM_NOALLOC_SCRATCH_BYTES ((size_t)64 << 20)
+
+/* dllm_layer_sparse without a workspace, for callers that cannot allocate device memory: code
+ * under stream capture, tight serving loops, harnesses that forbid allocation.  Same arguments,
+ * layout and result as dllm_layer_sparse (the same kernels and launch plans, so the outputs are
+ * bit-identical), but its scratch -- the normalised rows, Q, the attention output, the SwiGLU
+ * rows, split-K and split-KV partials and row positions of B * k_max active rows -- lives in a
+ * file-scope device array of DLLM_NOALLOC_SCRATCH_BYTES (64 MiB) that each GPU the library runs
+ * on holds until the process ends.  Enough for one LLaDA-8B-shaped layer (d 4096, 32 heads,
+ * F 12288) at up to about 256 active rows; a shape that needs more returns DLLM_EWORKSPACE before
+ * any launch.  Nothing is allocated or freed: the array's address on the current device is
+ * resolved on the first call on that device (the stream must belong to the current device).
+ * Every call on one GPU shares that GPU's array and no part of it needs to start at zero (each
+ * kernel writes what a later one reads); calls that overlap on one GPU -- on different streams
+ * or threads -- race on it. */
+int dllm_layer_sparse_noalloc(const dllm_model *model, int32_t layer, void *x_act, const int32_t *idx,
+                              const int32_t *n_active, int32_t k_max, void *k_cache, void *v_cache, void *stream);
+
 /* Fused confidence / argmax / local-KL pass over the vocabulary ([SL] 2.1
  * item 1: D = KL(p_t || p_{t-1}); [ES] Eq. 1 confidence c).
  *  logits: device [R, V] fp32; row_pos: device [R], row r belongs to flat

@@ -172,6 +172,21 @@ def test_timing_hook_is_per_call_and_validated(lib):
     assert not hasattr(lib, "dllm_set_timing")
 
 
+def test_noalloc_layer_rejects_oversize_before_any_launch(lib):
+    """The allocation-free layer call refuses shapes whose scratch exceeds the library's array
+    (here a dense 512-row LLaDA-8B-shaped layer, about 75 MB) before touching the device, and
+    validates its arguments like dllm_layer_sparse."""
+    m, st, cfg, keep = _fake_step_args()
+    big = _ffi.ModelC(_ffi.Dims(1, 512, 4096, 32, 32, 128, 12288, 126464, 2), 1, 1e4, 1e-5, 126463, 0x1000,
+                      m.layers, 0x1000, 0x1000)
+    F = ctypes.c_void_p(0x1000)
+    assert lib.dllm_layer_sparse_noalloc(ctypes.byref(big), 0, F, F, F, 512, F, F, None) == 4
+    assert lib.dllm_layer_sparse_noalloc(ctypes.byref(big), 2, F, F, F, 128, F, F, None) == 1   # layer out of range
+    assert lib.dllm_layer_sparse_noalloc(ctypes.byref(big), 0, F, F, F, 513, F, F, None) == 2   # k_max > S
+    assert lib.dllm_layer_sparse_noalloc(ctypes.byref(big), 0, None, F, F, 128, F, F, None) == 1
+    assert lib.dllm_layer_sparse_noalloc(None, 0, F, F, F, 128, F, F, None) == 1
+
+
 def test_struct_layouts_match_header(tmp_path):
     """Every ctypes struct of the binding has the header's size and field offsets (gcc, CPU only)."""
     import shutil

@@ -13,11 +13,12 @@ SEL_TOPK, SEL_THRESH_CAP, SEL_UNLOCKED = 0, 1, 2
 FORCE_NONE, FORCE_ON, FORCE_EXCLUDED = 0, 1, 2
 UNMASK_CONF, UNMASK_FORCED = 0, 1
 MAX_NESTED = 3
+NOALLOC_SCRATCH_BYTES = 64 << 20   # DLLM_NOALLOC_SCRATCH_BYTES
 
 EXPORTED = (
     "dllm_workspace_size", "dllm_score_select", "dllm_gather_rows", "dllm_scatter_rows",
     "dllm_layer_sparse", "dllm_confidence_kl", "dllm_skip_step", "dllm_status_string", "dllm_version",
-    "dllm_dus_mark", "dllm_pack_weight",
+    "dllm_dus_mark", "dllm_pack_weight", "dllm_layer_sparse_noalloc",
 )
 TK_NONE, TK_QKV, TK_ATTN, TK_O, TK_FFN_UP, TK_FFN_DOWN, TK_LM_HEAD, TK_VOCAB, TK_SCORE, TK_SELECT = range(10)
 
@@ -89,6 +90,9 @@ def load(path: str = LIB_PATH) -> ctypes.CDLL:
     lib.dllm_layer_sparse.restype = c_int32
     lib.dllm_layer_sparse.argtypes = [POINTER(ModelC), c_int32, c_void_p, c_void_p, c_void_p, c_int32, c_void_p,
                                       c_void_p, c_void_p, c_size_t, c_void_p]
+    lib.dllm_layer_sparse_noalloc.restype = c_int32
+    lib.dllm_layer_sparse_noalloc.argtypes = [POINTER(ModelC), c_int32, c_void_p, c_void_p, c_void_p, c_int32,
+                                              c_void_p, c_void_p, c_void_p]
     lib.dllm_confidence_kl.restype = c_int32
     lib.dllm_confidence_kl.argtypes = [c_void_p, c_void_p, c_int32, c_void_p, c_int32, c_int32, c_int32, c_int32,
                                        c_void_p, c_void_p, c_void_p, c_void_p]

@@ -210,6 +210,17 @@ def layer_sparse(model: Model, layer: int, x_act, idx, n_active, k_cache, v_cach
     _check(st, "dllm_layer_sparse")
 
 
+def layer_sparse_noalloc(model: Model, layer: int, x_act, idx, n_active, k_cache, v_cache):
+    """dllm_layer_sparse without a workspace: the library's per-GPU scratch array instead (calls that
+    overlap on one GPU race on it)."""
+    B, S = k_cache.shape[0], k_cache.shape[1]
+    k_max = idx.shape[1]
+    mc = model.bind(B, S)
+    st = _lib().dllm_layer_sparse_noalloc(ctypes.byref(mc), layer, _ptr(x_act), _ptr(idx), _ptr(n_active), k_max,
+                                          _ptr(k_cache), _ptr(v_cache), _stream(x_act.device))
+    _check(st, "dllm_layer_sparse_noalloc")
+
+
 class State:
     """Persistent device state of one generation run (tensors + dllm_state struct)."""
 

@@ -8,11 +8,19 @@
 #include <stdint.h>
 
 #include <algorithm>
+#include <mutex>
 
 #include "../../include/dllm.h"
 #include "kernels.h"
 
 using namespace dllm;
+
+// Library-owned scratch for callers that cannot allocate (code under graph capture, tight serving
+// loops): one file-scope device array, which every GPU the library runs on holds until the process
+// ends.  In host code `scratch` names a host-side stand-in, not a device address: the address of a
+// device's copy comes from hipGetSymbolAddress with that device current, once per device, and only
+// that address is handed to kernels (as the workspace pointer of an ordinary layer call).
+static __device__ __align__(256) uint8_t scratch[DLLM_NOALLOC_SCRATCH_BYTES];
 
 namespace {
 
@@ -109,6 +117,31 @@ bool plan_ws(const dllm_dims& d, int dtype, int k_max, WsLayout& L) {
   L.cand_rp = take(Rd * sizeof(int32_t));  //   and their row positions
   L.total = off;
   return true;
+}
+
+// What one layer on B * k_max active rows needs (dllm_layer_sparse's kernels): the normalised
+// rows, Q, the attention output, the SwiGLU rows, the split-K partials, split-KV partials and the
+// row positions.  The other offsets stay 0 (unused by a layer call).
+size_t plan_layer_ws(const dllm_dims& d, int dtype, int k_max, WsLayout& L) {
+  L = WsLayout{};
+  const long Rs = (long)d.B * k_max;
+  const int es = esize(dtype);
+  const long HQD = (long)d.n_heads * d.head_dim;
+  size_t off = 0;
+  auto take = [&](size_t bytes) {
+    const size_t o = off;
+    off += align_up(bytes);
+    return o;
+  };
+  L.xn = take(Rs * d.d * es);
+  L.q = take(Rs * HQD * es);
+  L.o = take(Rs * HQD * es);
+  L.h = take(Rs * (long)d.d_ff * es);
+  L.part = take(max_part_floats(d, dtype, Rs) * sizeof(float));
+  L.attn = take(attention_part_bytes(dtype, d.B, d.S, k_max, d.n_heads, d.n_kv_heads));
+  L.rowpos_s = take(Rs * sizeof(int32_t));
+  L.total = off;
+  return off;
 }
 
 int check_dims(const dllm_dims* d, int dtype) {
@@ -249,6 +282,53 @@ int check_model(const dllm_model* m) {
   return DLLM_OK;
 }
 
+// ---- allocation-free layer calls ----
+// The address of the scratch array's copy on one device is resolved once per device (below).
+constexpr size_t kScratchBytes = DLLM_NOALLOC_SCRATCH_BYTES;
+constexpr int kMaxDevices = 64;
+
+std::mutex g_scratch_mu;
+void* g_scratch_ptr[kMaxDevices] = {};  // the address of `scratch` on each device, once resolved
+
+// This thread's current device's copy of `scratch` (resolved on its first use on that device).
+int current_scratch(void** out) {
+  int dev = -1;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= kMaxDevices) return DLLM_ELAUNCH;
+  std::lock_guard<std::mutex> lock(g_scratch_mu);
+  if (!g_scratch_ptr[dev]) {
+    void* p = nullptr;
+    if (hipGetSymbolAddress(&p, HIP_SYMBOL(scratch)) != hipSuccess || !p) return DLLM_ELAUNCH;
+    g_scratch_ptr[dev] = p;
+  }
+  *out = g_scratch_ptr[dev];
+  return DLLM_OK;
+}
+
+// dllm_layer_sparse on a workspace laid out by plan_layer_ws (or plan_ws).
+int layer_call(const dllm_model* model, int32_t layer, void* x_act, const int32_t* idx, const int32_t* n_active,
+               int32_t k_max, void* k_cache, void* v_cache, Ctx& c) {
+  const dllm_dims& d = model->dims;
+  int32_t* row_pos = c.at<int32_t>(c.L.rowpos_s);
+  const int R = d.B * k_max;
+  DLLM_TRY(launch_row_pos(idx, n_active, d.B, d.S, k_max, row_pos, c.s));
+  // xn = rmsnorm(x_act) * attn_norm (scatter mode with no copy target = norm only)
+  DLLM_TRY(launch_scatter_norm(c.dtype, x_act, row_pos, R, d.d, nullptr, model->layers[layer].attn_norm,
+                               model->rms_eps, c.ws + c.L.xn, c.s));
+  return run_layer(c, layer, x_act, n_active, row_pos, k_max, k_cache, v_cache, nullptr);
+}
+
+int check_layer_args(const dllm_model* model, int32_t layer, const void* x_act, const int32_t* idx,
+                     const int32_t* n_active, int32_t k_max, const void* k_cache, const void* v_cache) {
+  int st = check_model(model);
+  if (st) return st;
+  const dllm_dims& d = model->dims;
+  if (layer < 0 || layer >= d.n_layers) return DLLM_EINVAL;
+  if (!x_act || !idx || !n_active || !k_cache || !v_cache) return DLLM_EINVAL;
+  if (k_max < 1 || k_max > d.S) return DLLM_ESHAPE;
+  if (!aligned16(x_act)) return DLLM_EINVAL;
+  return DLLM_OK;
+}
+
 }  // namespace
 
 extern "C" {
@@ -345,23 +425,25 @@ int dllm_scatter_rows(const void* src, const int32_t* idx, const int32_t* n_acti
 int dllm_layer_sparse(const dllm_model* model, int32_t layer, void* x_act, const int32_t* idx,
                       const int32_t* n_active, int32_t k_max, void* k_cache, void* v_cache, void* ws, size_t ws_bytes,
                       void* stream) {
-  int st = check_model(model);
+  const int st = check_layer_args(model, layer, x_act, idx, n_active, k_max, k_cache, v_cache);
   if (st) return st;
-  const dllm_dims& d = model->dims;
-  if (layer < 0 || layer >= d.n_layers) return DLLM_EINVAL;
-  if (!x_act || !idx || !n_active || !k_cache || !v_cache) return DLLM_EINVAL;
-  if (k_max < 1 || k_max > d.S) return DLLM_ESHAPE;
-  if (!aligned16(x_act)) return DLLM_EINVAL;
-  Ctx c{model, &d, model->dtype, (char*)ws, {}, (hipStream_t)stream};
-  plan_ws(d, c.dtype, k_max, c.L);
+  Ctx c{model, &model->dims, model->dtype, (char*)ws, {}, (hipStream_t)stream};
+  plan_ws(model->dims, c.dtype, k_max, c.L);
   if (!ws || ws_bytes < c.L.total) return DLLM_EWORKSPACE;
-  int32_t* row_pos = c.at<int32_t>(c.L.rowpos_s);
-  const int R = d.B * k_max;
-  DLLM_TRY(launch_row_pos(idx, n_active, d.B, d.S, k_max, row_pos, c.s));
-  // xn = rmsnorm(x_act) * attn_norm (scatter mode with no copy target = norm only)
-  DLLM_TRY(launch_scatter_norm(c.dtype, x_act, row_pos, R, d.d, nullptr, model->layers[layer].attn_norm,
-                               model->rms_eps, c.ws + c.L.xn, c.s));
-  return run_layer(c, layer, x_act, n_active, row_pos, k_max, k_cache, v_cache, nullptr);
+  return layer_call(model, layer, x_act, idx, n_active, k_max, k_cache, v_cache, c);
+}
+
+int dllm_layer_sparse_noalloc(const dllm_model* model, int32_t layer, void* x_act, const int32_t* idx,
+                              const int32_t* n_active, int32_t k_max, void* k_cache, void* v_cache, void* stream) {
+  const int st = check_layer_args(model, layer, x_act, idx, n_active, k_max, k_cache, v_cache);
+  if (st) return st;
+  Ctx c{model, &model->dims, model->dtype, nullptr, {}, (hipStream_t)stream};
+  if (plan_layer_ws(model->dims, c.dtype, k_max, c.L) > kScratchBytes) return DLLM_EWORKSPACE;
+  void* base = nullptr;
+  const int sr = current_scratch(&base);
+  if (sr) return sr;
+  c.ws = (char*)base;
+  return layer_call(model, layer, x_act, idx, n_active, k_max, k_cache, v_cache, c);
 }
 
 int dllm_confidence_kl(const float* logits, void* logits_prev, int32_t prev_dtype, const int32_t* row_pos, int32_t R,
