@@ -363,6 +363,23 @@ int dllm_dus_mark(uint8_t *force, int32_t B, int32_t S, int32_t lo, int32_t bloc
  * On a full step every row is active, whatever state->k_max is. */
 int dllm_skip_step(const dllm_model *model, dllm_state *state, const dllm_step_cfg *cfg, void *stream);
 
+/* Precondition bits recorded by the checking build. */
+enum {
+  DLLM_CHECK_ACTIVE_COUNT = 1, /* n_active[b] outside [0, k_max] */
+  DLLM_CHECK_INDEX_RANGE = 2,  /* a live idx entry outside [0, S) (the row is skipped) */
+  DLLM_CHECK_INDEX_ORDER = 4,  /* live idx entries of a sequence not strictly ascending */
+  DLLM_CHECK_TOKEN_RANGE = 8   /* a token id outside [0, V) (it is clamped) */
+};
+
+/* Debug aid.  libdllm_check.so is the same library built with -DDLLM_CHECK: the kernels that
+ * consume caller-supplied indices (dllm_layer_sparse and its allocation-free variant, the gather /
+ * scatter entry points) and token ids (dllm_skip_step) verify them on the device and OR the
+ * DLLM_CHECK_* bits of any violation into a per-GPU error word, while keeping every access in
+ * bounds.  dllm_check_word synchronises the current device, stores the word in *word and, with
+ * clear != 0, resets it.  In the normal build nothing is checked: it stores 0 and returns
+ * DLLM_EINVAL without touching the device. */
+int dllm_check_word(uint32_t *word, int32_t clear);
+
 /* Human-readable text of a dllm_status. */
 const char *dllm_status_string(int status);
 

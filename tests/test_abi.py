@@ -187,6 +187,18 @@ def test_noalloc_layer_rejects_oversize_before_any_launch(lib):
     assert lib.dllm_layer_sparse_noalloc(None, 0, F, F, F, 128, F, F, None) == 1
 
 
+def test_checking_build_exports_the_same_entry_points(lib):
+    """libdllm_check.so (-DDLLM_CHECK) is the same ABI; the normal build records nothing and says so
+    without touching the device."""
+    chk = _ffi.load_check()
+    for n in declared_functions():
+        assert hasattr(chk, n), n
+    assert chk.dllm_version() == lib.dllm_version()
+    w = ctypes.c_uint32(77)
+    assert lib.dllm_check_word(ctypes.byref(w), 1) == 1 and w.value == 0
+    assert lib.dllm_check_word(None, 0) == 1
+
+
 def test_struct_layouts_match_header(tmp_path):
     """Every ctypes struct of the binding has the header's size and field offsets (gcc, CPU only)."""
     import shutil

@@ -6,6 +6,7 @@ import os
 from ctypes import POINTER, Structure, c_float, c_int32, c_size_t, c_void_p
 
 LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libdllm.so")
+CHECK_LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libdllm_check.so")
 
 DLLM_F32, DLLM_BF16 = 0, 1
 VAR_L1N, VAR_COS, VAR_L2REL, VAR_KL, VAR_NONE = 0, 1, 2, 3, 4
@@ -18,7 +19,7 @@ NOALLOC_SCRATCH_BYTES = 64 << 20   # DLLM_NOALLOC_SCRATCH_BYTES
 EXPORTED = (
     "dllm_workspace_size", "dllm_score_select", "dllm_gather_rows", "dllm_scatter_rows",
     "dllm_layer_sparse", "dllm_confidence_kl", "dllm_skip_step", "dllm_status_string", "dllm_version",
-    "dllm_dus_mark", "dllm_pack_weight", "dllm_layer_sparse_noalloc",
+    "dllm_dus_mark", "dllm_pack_weight", "dllm_layer_sparse_noalloc", "dllm_check_word",
 )
 TK_NONE, TK_QKV, TK_ATTN, TK_O, TK_FFN_UP, TK_FFN_DOWN, TK_LM_HEAD, TK_VOCAB, TK_SCORE, TK_SELECT = range(10)
 
@@ -66,6 +67,7 @@ class StepCfg(Structure):
 
 
 _LIB = None
+_CHECK_LIB = None
 
 
 def load(path: str = LIB_PATH) -> ctypes.CDLL:
@@ -73,6 +75,19 @@ def load(path: str = LIB_PATH) -> ctypes.CDLL:
     global _LIB
     if _LIB is not None:
         return _LIB
+    _LIB = _open(path)
+    return _LIB
+
+
+def load_check() -> ctypes.CDLL:
+    """Load the checking build libdllm_check.so (device-side precondition checks, for debugging)."""
+    global _CHECK_LIB
+    if _CHECK_LIB is None:
+        _CHECK_LIB = _open(CHECK_LIB_PATH)
+    return _CHECK_LIB
+
+
+def _open(path: str) -> ctypes.CDLL:
     if not os.path.exists(path):
         raise RuntimeError(f"{path} is missing: build it with token_skipping_denoise_amd.build.build()")
     lib = ctypes.CDLL(path)
@@ -107,5 +122,6 @@ def load(path: str = LIB_PATH) -> ctypes.CDLL:
     lib.dllm_status_string.argtypes = [c_int32]
     lib.dllm_version.restype = c_int32
     lib.dllm_version.argtypes = []
-    _LIB = lib
+    lib.dllm_check_word.restype = c_int32
+    lib.dllm_check_word.argtypes = [POINTER(ctypes.c_uint32), c_int32]
     return lib

@@ -11,6 +11,7 @@
 #include <mutex>
 
 #include "../../include/dllm.h"
+#include "common.h"
 #include "kernels.h"
 
 using namespace dllm;
@@ -21,6 +22,9 @@ using namespace dllm;
 // device's copy comes from hipGetSymbolAddress with that device current, once per device, and only
 // that address is handed to kernels (as the workspace pointer of an ordinary layer call).
 static __device__ __align__(256) uint8_t scratch[DLLM_NOALLOC_SCRATCH_BYTES];
+
+// Error word of the checking build (-DDLLM_CHECK): the precondition bits kernels set on this GPU.
+static __device__ uint32_t check_word_dev;
 
 namespace {
 
@@ -304,13 +308,35 @@ int current_scratch(void** out) {
   return DLLM_OK;
 }
 
+#ifdef DLLM_CHECK
+void* g_check_ptr[kMaxDevices] = {};  // the address of the error word on each device, once resolved
+#endif
+
+// The current device's error word in the checking build (null in the normal build, where the
+// kernels compile their checks out).
+uint32_t* check_word() {
+#ifdef DLLM_CHECK
+  int dev = -1;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= kMaxDevices) return nullptr;
+  std::lock_guard<std::mutex> lock(g_scratch_mu);
+  if (!g_check_ptr[dev]) {
+    void* p = nullptr;
+    if (hipGetSymbolAddress(&p, HIP_SYMBOL(check_word_dev)) != hipSuccess) return nullptr;
+    g_check_ptr[dev] = p;
+  }
+  return (uint32_t*)g_check_ptr[dev];
+#else
+  return nullptr;
+#endif
+}
+
 // dllm_layer_sparse on a workspace laid out by plan_layer_ws (or plan_ws).
 int layer_call(const dllm_model* model, int32_t layer, void* x_act, const int32_t* idx, const int32_t* n_active,
                int32_t k_max, void* k_cache, void* v_cache, Ctx& c) {
   const dllm_dims& d = model->dims;
   int32_t* row_pos = c.at<int32_t>(c.L.rowpos_s);
   const int R = d.B * k_max;
-  DLLM_TRY(launch_row_pos(idx, n_active, d.B, d.S, k_max, row_pos, c.s));
+  DLLM_TRY(launch_row_pos(idx, n_active, d.B, d.S, k_max, row_pos, c.s, check_word()));
   // xn = rmsnorm(x_act) * attn_norm (scatter mode with no copy target = norm only)
   DLLM_TRY(launch_scatter_norm(c.dtype, x_act, row_pos, R, d.d, nullptr, model->layers[layer].attn_norm,
                                model->rms_eps, c.ws + c.L.xn, c.s));
@@ -334,6 +360,25 @@ int check_layer_args(const dllm_model* model, int32_t layer, const void* x_act, 
 extern "C" {
 
 int dllm_version(void) { return 200; }
+
+int dllm_check_word(uint32_t* word, int32_t clear) {
+  if (!word) return DLLM_EINVAL;
+  *word = 0;
+#ifdef DLLM_CHECK
+  uint32_t* p = check_word();
+  if (!p) return DLLM_ELAUNCH;
+  if (hipDeviceSynchronize() != hipSuccess) return DLLM_ELAUNCH;
+  if (hipMemcpy(word, p, sizeof(uint32_t), hipMemcpyDeviceToHost) != hipSuccess) return DLLM_ELAUNCH;
+  if (clear) {
+    const uint32_t zero = 0;
+    if (hipMemcpy(p, &zero, sizeof(uint32_t), hipMemcpyHostToDevice) != hipSuccess) return DLLM_ELAUNCH;
+  }
+  return DLLM_OK;
+#else
+  (void)clear;
+  return DLLM_EINVAL;  // not a checking build: nothing is recorded
+#endif
+}
 
 const char* dllm_status_string(int status) {
   switch (status) {
@@ -389,12 +434,19 @@ static int gather_scatter(bool gather, const void* src, const int32_t* idx, cons
 // Gather/scatter compute the row positions on the fly from idx/n_active (no workspace).
 namespace {
 __global__ void k_gs_rows(bool gather, const uint4* __restrict__ src, const int32_t* __restrict__ idx,
-                          const int32_t* __restrict__ n_active, int S, int k_max, int nchunk, uint4* __restrict__ dst) {
+                          const int32_t* __restrict__ n_active, int S, int k_max, int nchunk, uint4* __restrict__ dst,
+                          uint32_t* chk) {
   const int r = blockIdx.x;
   const int b = r / k_max, j = r - b * k_max;
-  if (j >= n_active[b]) return;
+  const int na = n_active[b];
+  if (j == 0 && threadIdx.x == 0 && (na < 0 || na > k_max)) check_flag(chk, kChkActiveCount);
+  if (j >= na) return;
   const int i = idx[r];
-  if (i < 0 || i >= S) return;
+  if (i < 0 || i >= S) {
+    if (threadIdx.x == 0) check_flag(chk, kChkIndexRange);
+    return;
+  }
+  if (j > 0 && threadIdx.x == 0 && idx[r - 1] >= i) check_flag(chk, kChkIndexOrder);
   const long pos = (long)b * S + i;
   const uint4* s4 = src + (gather ? pos : (long)r) * nchunk;
   uint4* d4 = dst + (gather ? (long)r : pos) * nchunk;
@@ -408,7 +460,7 @@ int dllm_gather_rows(const void* src, const int32_t* idx, const int32_t* n_activ
   if (st) return st;
   const int nchunk = width * esize(dtype) / 16;
   hipLaunchKernelGGL(k_gs_rows, dim3(B * k_max), dim3(256), 0, (hipStream_t)stream, true, (const uint4*)src, idx,
-                     n_active, S, k_max, nchunk, (uint4*)dst);
+                     n_active, S, k_max, nchunk, (uint4*)dst, check_word());
   return hipGetLastError() == hipSuccess ? DLLM_OK : DLLM_ELAUNCH;
 }
 
@@ -418,7 +470,7 @@ int dllm_scatter_rows(const void* src, const int32_t* idx, const int32_t* n_acti
   if (st) return st;
   const int nchunk = width * esize(dtype) / 16;
   hipLaunchKernelGGL(k_gs_rows, dim3(B * k_max), dim3(256), 0, (hipStream_t)stream, false, (const uint4*)src, idx,
-                     n_active, S, k_max, nchunk, (uint4*)dst);
+                     n_active, S, k_max, nchunk, (uint4*)dst, check_word());
   return hipGetLastError() == hipSuccess ? DLLM_OK : DLLM_ELAUNCH;
 }
 
@@ -567,7 +619,7 @@ int dllm_skip_step(const dllm_model* model, dllm_state* state, const dllm_step_c
   // embedding (+ first layer's norm when layer 0 runs dense)
   const bool l0_dense = full || b_lay > 0;
   DLLM_TRY(launch_embed_norm(c.dtype, model->embed, state->tokens, d.vocab, Rd, d.d,
-                             l0_dense ? model->layers[0].attn_norm : nullptr, eps, xfull, xn, c.s));
+                             l0_dense ? model->layers[0].attn_norm : nullptr, eps, xfull, xn, c.s, check_word()));
 
   auto boundary = [&]() -> int {
     if (full) {

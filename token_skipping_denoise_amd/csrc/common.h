@@ -86,6 +86,19 @@ __device__ __forceinline__ int wave_or(int v) {
   return v;
 }
 
+// Precondition checks of the debug build (compiled with -DDLLM_CHECK): a violated precondition
+// sets its bit in a device error word, while the kernel still keeps every access in bounds (the
+// row is treated as dead, the token id clamped).  The normal build compiles the checks out.
+enum { kChkActiveCount = 1, kChkIndexRange = 2, kChkIndexOrder = 4, kChkTokenRange = 8 };
+__device__ __forceinline__ void check_flag(uint32_t* word, uint32_t bit) {
+#ifdef DLLM_CHECK
+  if (word) atomicOr(word, bit);
+#else
+  (void)word;
+  (void)bit;
+#endif
+}
+
 // Flat position of an active row in the padded layout, or -1 if the row is dead.
 __device__ __forceinline__ int row_position(const int32_t* idx, const int32_t* n_active, int k_max, int S, int r) {
   const int b = r / k_max, j = r - b * k_max;

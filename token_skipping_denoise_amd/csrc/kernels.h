@@ -8,8 +8,9 @@ namespace dllm {
 
 // ---------------- row kernels (rowops.hip) ----------------
 // x[r] = embed[tok[r]] for r < rows; if g: xn[r] = rmsnorm(x[r]) * g.
+// chk (debug build): error word for out-of-range token ids, or null.
 hipError_t launch_embed_norm(int dtype, const void* embed, const int32_t* tokens, int V, int rows, int d,
-                             const void* g, float eps, void* x, void* xn, hipStream_t s);
+                             const void* g, float eps, void* x, void* xn, hipStream_t s, uint32_t* chk = nullptr);
 // dst[r] = src[row_pos[r]] for live rows; if g: dst_norm[r] = rmsnorm(dst[r]) * g; if dst_at_src:
 // dst_at_src[row_pos[r]] = src[row_pos[r]] as well (the same rows copied in place to another buffer).
 hipError_t launch_gather_norm(int dtype, const void* src, const int32_t* row_pos, int R, int w, void* dst,
@@ -18,8 +19,10 @@ hipError_t launch_gather_norm(int dtype, const void* src, const int32_t* row_pos
 hipError_t launch_scatter_norm(int dtype, const void* src, const int32_t* row_pos, int R, int w, void* dst,
                                const void* g, float eps, void* dst_norm, hipStream_t s);
 // row_pos[b*k_max + j] = b*S + idx[b*k_max + j] if j < n_active[b], else -1.
+// chk (debug build): error word for an active count outside [0, k_max], live indices outside
+// [0, S) or not strictly ascending, or null.
 hipError_t launch_row_pos(const int32_t* idx, const int32_t* n_active, int B, int S, int k_max,
-                          int32_t* row_pos, hipStream_t s);
+                          int32_t* row_pos, hipStream_t s, uint32_t* chk = nullptr);
 // idx[b*S + i] = i, n_active[b] = S; if row_pos: row_pos[b*S + i] = b*S + i.
 hipError_t launch_identity_rows(int B, int S, int32_t* idx, int32_t* n_active, hipStream_t s,
                                 int32_t* row_pos = nullptr);

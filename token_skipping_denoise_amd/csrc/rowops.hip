@@ -39,7 +39,7 @@ template <typename T, int MODE, int NT = kRowThreads>
 __global__ __launch_bounds__(NT) void k_rows_norm(const T* __restrict__ src, const int32_t* __restrict__ map,
                                                    int V, int rows, int w, T* __restrict__ dst,
                                                    const T* __restrict__ g, float eps, T* __restrict__ dst_norm,
-                                                   T* __restrict__ dst_at_src) {
+                                                   T* __restrict__ dst_at_src, uint32_t* chk) {
   using E = Elem<T>;
   constexpr int VE = E::kVec;
   constexpr int CH = 1024 / NT;  // 16-byte chunks per thread
@@ -48,6 +48,7 @@ __global__ __launch_bounds__(NT) void k_rows_norm(const T* __restrict__ src, con
   long src_row, dst_row;
   if (MODE == kEmbed) {
     int t = map[r];
+    if ((t < 0 || t >= V) && threadIdx.x == 0) check_flag(chk, kChkTokenRange);
     t = t < 0 ? 0 : (t >= V ? V - 1 : t);
     src_row = t;
     dst_row = r;
@@ -93,22 +94,23 @@ __global__ __launch_bounds__(NT) void k_rows_norm(const T* __restrict__ src, con
 
 template <int MODE>
 static hipError_t rows_norm(int dtype, const void* src, const int32_t* map, int V, int rows, int w, void* dst,
-                            const void* g, float eps, void* dst_norm, hipStream_t s, void* dst_at_src = nullptr) {
+                            const void* g, float eps, void* dst_norm, hipStream_t s, void* dst_at_src = nullptr,
+                            uint32_t* chk = nullptr) {
   if (rows <= 0) return hipSuccess;
   if (w / (dtype == 0 ? 4 : 8) > kRowThreads * kRowChunks) return hipErrorInvalidValue;
   dim3 grid(rows), block(kRowThreads);
   if (dtype == 0)
     hipLaunchKernelGGL((k_rows_norm<float, MODE>), grid, block, 0, s, (const float*)src, map, V, rows, w,
-                       (float*)dst, (const float*)g, eps, (float*)dst_norm, (float*)dst_at_src);
+                       (float*)dst, (const float*)g, eps, (float*)dst_norm, (float*)dst_at_src, chk);
   else
     hipLaunchKernelGGL((k_rows_norm<bf16, MODE>), grid, block, 0, s, (const bf16*)src, map, V, rows, w,
-                       (bf16*)dst, (const bf16*)g, eps, (bf16*)dst_norm, (bf16*)dst_at_src);
+                       (bf16*)dst, (const bf16*)g, eps, (bf16*)dst_norm, (bf16*)dst_at_src, chk);
   return hipGetLastError();
 }
 
 hipError_t launch_embed_norm(int dtype, const void* embed, const int32_t* tokens, int V, int rows, int d,
-                             const void* g, float eps, void* x, void* xn, hipStream_t s) {
-  return rows_norm<kEmbed>(dtype, embed, tokens, V, rows, d, x, g, eps, xn, s);
+                             const void* g, float eps, void* x, void* xn, hipStream_t s, uint32_t* chk) {
+  return rows_norm<kEmbed>(dtype, embed, tokens, V, rows, d, x, g, eps, xn, s, nullptr, chk);
 }
 hipError_t launch_gather_norm(int dtype, const void* src, const int32_t* row_pos, int R, int w, void* dst,
                               const void* g, float eps, void* dst_norm, hipStream_t s, void* dst_at_src) {
@@ -120,23 +122,27 @@ hipError_t launch_scatter_norm(int dtype, const void* src, const int32_t* row_po
 }
 
 __global__ void k_row_pos(const int32_t* __restrict__ idx, const int32_t* __restrict__ n_active, int B, int S,
-                          int k_max, int32_t* __restrict__ row_pos) {
+                          int k_max, int32_t* __restrict__ row_pos, uint32_t* chk) {
   const int r = blockIdx.x * blockDim.x + threadIdx.x;
   if (r >= B * k_max) return;
   const int b = r / k_max, j = r - b * k_max;
+  const int na = n_active[b];
+  if (j == 0 && (na < 0 || na > k_max)) check_flag(chk, kChkActiveCount);
   int p = -1;
-  if (j < n_active[b]) {
+  if (j < na) {
     const int i = idx[r];
     p = (i >= 0 && i < S) ? b * S + i : -1;
+    if (p < 0) check_flag(chk, kChkIndexRange);
+    else if (j > 0 && idx[r - 1] >= i) check_flag(chk, kChkIndexOrder);  // live rows ascend strictly
   }
   row_pos[r] = p;
 }
 
 hipError_t launch_row_pos(const int32_t* idx, const int32_t* n_active, int B, int S, int k_max, int32_t* row_pos,
-                          hipStream_t s) {
+                          hipStream_t s, uint32_t* chk) {
   const int n = B * k_max;
   if (n <= 0) return hipSuccess;
-  hipLaunchKernelGGL(k_row_pos, dim3((n + 255) / 256), dim3(256), 0, s, idx, n_active, B, S, k_max, row_pos);
+  hipLaunchKernelGGL(k_row_pos, dim3((n + 255) / 256), dim3(256), 0, s, idx, n_active, B, S, k_max, row_pos, chk);
   return hipGetLastError();
 }
 
