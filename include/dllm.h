@@ -120,11 +120,14 @@ typedef struct {
   const void *w_gate_up;  /* device [2F, d]: gate rows, then up rows */
   const void *w_down;     /* device [d, F] */
   /* Optional second copies in MFMA fragment order (dllm_pack_weight), or NULL.  When present,
-   * the active-row products they fit (at most 128 rows; the gate/up product over d = 4096 and
-   * the down projection over F = 12288 in 8 K splits) stream them straight into registers
-   * instead of the row-major copies above, which stay in use for every other product. */
+   * the active-row products they fit (at most 128 rows; the gate/up product over d = 4096, the
+   * QKV product over d = 4096 with 12288 outputs in 2 K splits, and the down projection over
+   * F = 12288 in 8 K splits) stream them straight into registers instead of the row-major copies
+   * above, which stay in use for every other product. */
   const void *w_gate_up_packed; /* w_gate_up packed with gate/up interleave F */
   const void *w_down_packed;    /* w_down packed without interleave */
+  const void *w_qkv_packed;     /* w_qkv packed without interleave (QKV over d = 4096 with 12288 outputs,
+                                   in 2 K splits), or NULL */
 } dllm_layer_w;
 
 typedef struct {
@@ -362,6 +365,17 @@ int dllm_dus_mark(uint8_t *force, int32_t B, int32_t S, int32_t lo, int32_t bloc
  * SureLock lock update and/or confidence unmasking of [block_lo, block_hi).
  * On a full step every row is active, whatever state->k_max is. */
 int dllm_skip_step(const dllm_model *model, dllm_state *state, const dllm_step_cfg *cfg, void *stream);
+
+/* Achievable-peak probes for measurement (nothing on the denoising path uses them): the measured
+ * denominators beside the datasheet peaks.
+ *  DLLM_PROBE_COPY: copies the first half of buf into the second half, iters times (a plain HBM
+ *    stream); *work = bytes read + written.
+ *  DLLM_PROBE_MFMA: a loop of iters steps of four independent v_mfma_f32_32x32x16_bf16 chains per
+ *    wave on register operands, 2048 workgroups of 4 waves (8 per CU); buf must hold at least
+ *    2048 * 256 floats (written only in a case the sums cannot reach); *work = flops.
+ *  The work is enqueued on `stream`; the caller times it (e.g. with events). */
+enum { DLLM_PROBE_COPY = 0, DLLM_PROBE_MFMA = 1 };
+int dllm_peak_probe(int32_t kind, void *buf, size_t bytes, int32_t iters, double *work, void *stream);
 
 /* Precondition bits recorded by the checking build. */
 enum {

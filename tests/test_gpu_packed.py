@@ -56,8 +56,8 @@ def test_pack_rejects_bad_shapes(bad):
 
 @pytest.mark.parametrize("k", [64, 128])
 def test_packed_layer_matches_row_major(k):
-    """The LLaDA-8B-shaped layer on k active rows: packed gate/up (fused SwiGLU) and packed down
-    (8 K splits) against the row-major kernels on the same inputs."""
+    """The LLaDA-8B-shaped layer on k active rows: packed QKV (2 K splits), packed gate/up (fused
+    SwiGLU) and packed down (8 K splits) against the row-major kernels on the same inputs."""
     dims = workloads.LLADA_LAYER
     B, S, d = dims.B, dims.S, dims.d
     print(f"packed vs row-major layer k={k}", flush=True)
@@ -66,8 +66,8 @@ def test_packed_layer_matches_row_major(k):
     w = {"embed": emb, "final_norm": torch.ones(d, dtype=torch.bfloat16, device=DEV), "lm_head": emb, "layers": [lw]}
     m_pk = api.Model(w, dims.n_heads, dims.n_kv_heads, 7, pack=True)
     m_rm = api.Model(w, dims.n_heads, dims.n_kv_heads, 7, pack=False)
-    assert m_pk._lw[0].w_gate_up_packed and m_pk._lw[0].w_down_packed
-    assert not m_rm._lw[0].w_gate_up_packed and not m_rm._lw[0].w_down_packed
+    assert m_pk._lw[0].w_gate_up_packed and m_pk._lw[0].w_down_packed and m_pk._lw[0].w_qkv_packed
+    assert not m_rm._lw[0].w_gate_up_packed and not m_rm._lw[0].w_down_packed and not m_rm._lw[0].w_qkv_packed
     kc0 = synth.normal(synth.seed_of(5, 1), (B, S, dims.n_kv_heads, dims.head_dim), 1.0, torch.bfloat16).to(DEV)
     vc0 = synth.normal(synth.seed_of(5, 2), (B, S, dims.n_kv_heads, dims.head_dim), 1.0, torch.bfloat16).to(DEV)
     x0 = synth.normal(synth.seed_of(5, 3), (B * k, d), 1.0, torch.bfloat16).to(DEV)
@@ -81,6 +81,15 @@ def test_packed_layer_matches_row_major(k):
         torch.cuda.synchronize()
         outs.append((x, kc, vc))
     (xp, kp, vp), (xr, kr, vr) = outs
-    assert torch.equal(kp, kr) and torch.equal(vp, vr)   # the QKV path is the same kernel
-    assert_close(np64(xp), np64(xr), 5e-3, "layer output, packed vs row-major")
+    # the two QKV paths sum the reduction in different orders (2 vs 4 K splits), so a stored bf16
+    # K/V element may round one ulp (2^-8 of itself) the other way; untouched rows stay identical
+    written = torch.zeros(S, dtype=torch.bool)
+    written[idx[0].cpu().long()] = True
+    for a, b in ((kp, kr), (vp, vr)):
+        assert_close(np64(a[0][written.to(DEV)]), np64(b[0][written.to(DEV)]), 5e-3, "fresh K/V, packed vs row-major")
+        assert torch.equal(a[0][~written.to(DEV)], b[0][~written.to(DEV)])
+    # two bf16 evaluation orders of the same layer: the flipped Q/K/V roundings move the attention
+    # weights and its output, which carry into the residual stream as they do against the oracle
+    # (about 5e-3 of the largest element for this layer), so the bf16 bar applies
+    assert_close(np64(xp), np64(xr), 2e-2, "layer output, packed vs row-major")
     assert torch.all(torch.isfinite(xp.float()))

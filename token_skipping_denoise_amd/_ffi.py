@@ -19,7 +19,7 @@ NOALLOC_SCRATCH_BYTES = 64 << 20   # DLLM_NOALLOC_SCRATCH_BYTES
 EXPORTED = (
     "dllm_workspace_size", "dllm_score_select", "dllm_gather_rows", "dllm_scatter_rows",
     "dllm_layer_sparse", "dllm_confidence_kl", "dllm_skip_step", "dllm_status_string", "dllm_version",
-    "dllm_dus_mark", "dllm_pack_weight", "dllm_layer_sparse_noalloc", "dllm_check_word",
+    "dllm_dus_mark", "dllm_pack_weight", "dllm_layer_sparse_noalloc", "dllm_check_word", "dllm_peak_probe",
 )
 TK_NONE, TK_QKV, TK_ATTN, TK_O, TK_FFN_UP, TK_FFN_DOWN, TK_LM_HEAD, TK_VOCAB, TK_SCORE, TK_SELECT = range(10)
 
@@ -30,7 +30,7 @@ class Dims(Structure):
 
 class LayerW(Structure):
     _fields_ = [(n, c_void_p) for n in ("attn_norm", "w_qkv", "w_o", "ffn_norm", "w_gate_up", "w_down",
-                                        "w_gate_up_packed", "w_down_packed")]
+                                        "w_gate_up_packed", "w_down_packed", "w_qkv_packed")]
 
 
 class ModelC(Structure):
@@ -122,6 +122,8 @@ def _open(path: str) -> ctypes.CDLL:
     lib.dllm_status_string.argtypes = [c_int32]
     lib.dllm_version.restype = c_int32
     lib.dllm_version.argtypes = []
+    lib.dllm_peak_probe.restype = c_int32
+    lib.dllm_peak_probe.argtypes = [c_int32, c_void_p, c_size_t, c_int32, POINTER(ctypes.c_double), c_void_p]
     lib.dllm_check_word.restype = c_int32
     lib.dllm_check_word.argtypes = [POINTER(ctypes.c_uint32), c_int32]
     return lib

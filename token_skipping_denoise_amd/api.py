@@ -168,8 +168,10 @@ class Model:
             for t in self.layers:
                 t["w_gate_up_packed"] = pack_weight(t["w_gate_up"], interleave_f=F)
                 t["w_down_packed"] = pack_weight(t["w_down"])
+                t["w_qkv_packed"] = pack_weight(t["w_qkv"])
         self._lw = (_ffi.LayerW * L)()
-        names = ("attn_norm", "w_qkv", "w_o", "ffn_norm", "w_gate_up", "w_down", "w_gate_up_packed", "w_down_packed")
+        names = ("attn_norm", "w_qkv", "w_o", "ffn_norm", "w_gate_up", "w_down", "w_gate_up_packed", "w_down_packed",
+                 "w_qkv_packed")
         for i, t in enumerate(self.layers):
             self._lw[i] = _ffi.LayerW(*[_ptr(t.get(k)) for k in names])
         self.dims_tuple = (V, d, n_heads, n_kv_heads, D, F, L)

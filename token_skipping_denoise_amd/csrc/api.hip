@@ -84,6 +84,8 @@ long max_part_floats(const dllm_dims& d, int dtype, long M) {
   }
   const PackedPlan pd = packed_plan((int)M, d.d, d.d_ff, false);  // the packed down projection
   if (dtype == DLLM_BF16 && pd.ok) best = std::max(best, (long)pd.splits * M * d.d);
+  const PackedPlan pq = packed_plan((int)M, NQKV, d.d, false);    // the packed QKV product
+  if (dtype == DLLM_BF16 && pq.ok) best = std::max(best, (long)pq.splits * M * NQKV);
   return best;
 }
 
@@ -213,9 +215,15 @@ int run_layer(const Ctx& c, int l, void* x, const int32_t* nact, const int32_t* 
 
   GemmPlan p = gemm_plan(c.dtype, R, NQKV, d.d);
   {
+    const PackedPlan pp = (c.dtype == DLLM_BF16 && w.w_qkv_packed) ? packed_plan(R, NQKV, d.d, false) : PackedPlan{};
     TimedRegion t(c.timing, DLLM_TK_QKV, R, c.s);
     DLLM_TRY(t.err);
-    DLLM_TRY(launch_gemm(c.dtype, p, xn, w.w_qkv, part, R, NQKV, d.d, nact, kx, c.s));
+    if (pp.ok) {
+      DLLM_TRY(launch_gemm_packed(pp, xn, w.w_qkv_packed, part, nullptr, R, NQKV, d.d, 0, nact, kx, c.s));
+      p.splits = pp.splits;
+    } else {
+      DLLM_TRY(launch_gemm(c.dtype, p, xn, w.w_qkv, part, R, NQKV, d.d, nact, kx, c.s));
+    }
     DLLM_TRY(t.stop());
   }
   DLLM_TRY(launch_qkv_epilogue(c.dtype, part, p.splits, (long)R * NQKV, row_pos, R, d.S, d.n_heads, d.n_kv_heads,
@@ -360,6 +368,20 @@ int check_layer_args(const dllm_model* model, int32_t layer, const void* x_act, 
 extern "C" {
 
 int dllm_version(void) { return 200; }
+
+int dllm_peak_probe(int32_t kind, void* buf, size_t bytes, int32_t iters, double* work, void* stream) {
+  if (!buf || !work || iters < 1) return DLLM_EINVAL;
+  if (!aligned16(buf)) return DLLM_EINVAL;
+  if (kind == DLLM_PROBE_COPY) {
+    if (bytes < 32) return DLLM_ESHAPE;
+  } else if (kind == DLLM_PROBE_MFMA) {
+    if (bytes < (size_t)2048 * 256 * sizeof(float)) return DLLM_ESHAPE;
+  } else {
+    return DLLM_EINVAL;
+  }
+  DLLM_TRY(launch_peak_probe(kind, buf, bytes, iters, work, (hipStream_t)stream));
+  return DLLM_OK;
+}
 
 int dllm_check_word(uint32_t* word, int32_t clear) {
   if (!word) return DLLM_EINVAL;

@@ -214,8 +214,11 @@ __global__ __launch_bounds__(64 * NW, 1) void k_gemm_packed(const uint16_t* __re
 
 }  // namespace
 
-// Stages per split compiled for each epilogue: the fused gate/up product over d = 4096
-// (64 stages), the down projection over F = 12288 in 8 splits (24 stages).
+// Compiled (waves, stages per split, epilogue) cases, chosen so that a launch has one workgroup
+// per CU: the fused gate/up product over d = 4096 (3 waves, 64 stages, 96 packed columns per
+// workgroup); QKV-like products over d = 4096 with N = 384 * 32 columns (3 waves, 2-way K split
+// of 32 stages: 128 column tiles x 2 = 256 workgroups); the down projection over F = 12288
+// (4 waves, 8-way K split of 24 stages).
 PackedPlan packed_plan(int M, int N, int K, bool swiglu) {
   PackedPlan p;
   if (M < 1 || M > kPkRows || K % kPkBK) return p;
@@ -225,6 +228,9 @@ PackedPlan packed_plan(int M, int N, int K, bool swiglu) {
     if (N % 96 || stages != 64) return p;
     p.nw = 3;
     p.splits = 1;
+  } else if (N % 96 == 0 && N / 96 == 128 && stages == 64) {
+    p.nw = 3;
+    p.splits = 2;
   } else {
     if (N % 128) return p;
     const int tiles = N / 128;
@@ -249,6 +255,9 @@ hipError_t launch_gemm_packed(const PackedPlan& p, const void* A, const void* Wp
                        (uint16_t*)H, M, N, K, F, tiles_n, n_active, k_max);
   else if (!H && p.nw == 4 && p.nkc == 24)
     hipLaunchKernelGGL((k_gemm_packed<4, 24, 0>), grid, block, 0, s, (const uint16_t*)A, (const uint16_t*)Wp, C,
+                       (uint16_t*)H, M, N, K, F, tiles_n, n_active, k_max);
+  else if (!H && p.nw == 3 && p.nkc == 32)
+    hipLaunchKernelGGL((k_gemm_packed<3, 32, 0>), grid, block, 0, s, (const uint16_t*)A, (const uint16_t*)Wp, C,
                        (uint16_t*)H, M, N, K, F, tiles_n, n_active, k_max);
   else
     return hipErrorInvalidValue;

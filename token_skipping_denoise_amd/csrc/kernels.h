@@ -112,6 +112,12 @@ hipError_t launch_conf_kl(const float* logits, void* logits_prev, int prev_dtype
                           int V, int exclude_id, int have_prev, float* conf, int32_t* argmax, float* kl, void* partial,
                           hipStream_t s);
 
+// ---------------- achievable-peak probes (peak.hip) ----------------
+// kind 0: copy the first half of buf into the second half, iters times; kind 1: an MFMA loop of
+// iters steps on every CU (buf: at least 2048 * 256 floats, written only in an impossible case).
+// *work: bytes moved (0) or flops (1).
+hipError_t launch_peak_probe(int kind, void* buf, size_t bytes, int iters, double* work, hipStream_t s);
+
 // ---------------- post-step (post.hip) ----------------
 hipError_t launch_lock_update(const int32_t* row_pos, int R, const float* conf, const float* kl, float eps,
                               float conf_min, uint8_t* force, hipStream_t s);
