@@ -350,6 +350,42 @@ def c2_layer_kernels(n_copies=6, k=64, reps=3):
                     "the embedding of 512 rows and a 1024-token LM head")}
 
 
+def profile_layer(which: str, calls: int):
+    """A short program for counter collection: one layer of the given shape called ``calls`` times
+    through dllm_layer_sparse, printing a line after each call.  ``llada128``: the LLaDA-8B layer
+    (S 512) with 128 active rows, the skipped-regime shape of the default workload; ``long205``: the
+    long-context layer (batch 4, S 4096) with 205 active rows per sequence."""
+    import synth
+    dev = "cuda:0"
+    if which == "llada128":
+        dims, n_act = workloads.LLADA_LAYER, [128]
+    else:
+        dims, n_act = workloads.shrink(workloads.LLADA_LONG, n_layers=1), [205] * 4
+    B, S, d = dims.B, dims.S, dims.d
+    k_max = max(n_act)
+    lw = workloads.layer_weights(dims, 0, device=dev)
+    small = torch.zeros((8, d), dtype=torch.bfloat16, device=dev)
+    model = api.Model({"embed": small, "final_norm": torch.ones(d, dtype=torch.bfloat16, device=dev),
+                       "lm_head": small, "layers": [lw]}, dims.n_heads, dims.n_kv_heads, 7)
+    kv = (B, S, dims.n_kv_heads, dims.head_dim)
+    kc = synth.normal(synth.seed_of(dims.cfg_id, 1), kv, 1.0, torch.bfloat16).to(dev)
+    vc = synth.normal(synth.seed_of(dims.cfg_id, 2), kv, 1.0, torch.bfloat16).to(dev)
+    x0 = synth.normal(synth.seed_of(dims.cfg_id, 3), (B * k_max, d), 1.0, torch.bfloat16).to(dev)
+    idx = torch.full((B, k_max), -1, dtype=torch.int32)
+    for b in range(B):
+        rows = synth.permutation(synth.seed_of(dims.cfg_id, 4, b), S)[:n_act[b]]
+        idx[b, :n_act[b]] = torch.sort(rows).values.to(torch.int32)
+    idx, nact = idx.to(dev), torch.tensor(n_act, dtype=torch.int32, device=dev)
+    ws = api.alloc_workspace(model, B, S, k_max)
+    torch.cuda.synchronize()
+    print(f"profile-layer {which}: B {B} S {S} active {n_act}", flush=True)
+    for i in range(calls):
+        x = x0.clone()
+        api.layer_sparse(model, 0, x, idx, nact, kc, vc, ws)
+        torch.cuda.synchronize()
+        print(f"call {i + 1}/{calls} done", flush=True)
+
+
 DOMINANT_KERNEL = "dllm::(anonymous namespace)::k_gemm_packed<3, 64, 2>"
 TRAFFIC_PROFILE = os.path.join(ROOT, "profiles", "gemm_packed_swiglu_llada_128rows_hbm_bytes.md")
 GEMM_SOURCE = os.path.join(ROOT, "token_skipping_denoise_amd", "csrc", "gemm_packed.hip")
@@ -740,6 +776,9 @@ def main():
                     help="only copy a 1 GiB buffer once (reference for the HBM byte counters) and exit")
     ap.add_argument("--cache-feature", choices=("hidden", "value"), default="hidden",
                     help="dcache workload: the feature a cached layer compares (its input, or its V projection)")
+    ap.add_argument("--profile-layer", choices=("llada128", "long205"), default=None,
+                    help="only call one layer of that shape --steps times, a line per call (a short "
+                         "program for counter collection), and exit")
     ap.add_argument("--no-extra", action="store_true",
                     help="llada workload: skip the extra measurements (measured peaks, the one-layer kernel "
                          "latencies, the Dream lock-ramp and long-context runs)")
@@ -752,6 +791,9 @@ def main():
         dst.copy_(src)
         torch.cuda.synchronize()
         print(json.dumps({"copy_bytes_read": n, "copy_bytes_written": n}))
+        return
+    if args.profile_layer:
+        profile_layer(args.profile_layer, args.steps)
         return
     if args.gpus != 1:
         print(f"bench.py runs on one GPU only: --gpus {args.gpus} is not supported "
