@@ -120,14 +120,15 @@ typedef struct {
   const void *w_gate_up;  /* device [2F, d]: gate rows, then up rows */
   const void *w_down;     /* device [d, F] */
   /* Optional second copies in MFMA fragment order (dllm_pack_weight), or NULL.  When present,
-   * the active-row products they fit (at most 128 rows; the gate/up product over d = 4096, the
-   * QKV product over d = 4096 with 12288 outputs in 2 K splits, and the down projection over
-   * F = 12288 in 8 K splits) stream them straight into registers instead of the row-major copies
-   * above, which stay in use for every other product. */
+   * the bf16 QKV, gate/up and down products over at most 128 active rows stream them straight
+   * into registers instead of the row-major copies above (which stay in use for every other
+   * product), whenever the packed planner (dllm_packed_plan) covers the shape: N a multiple of
+   * 64, K a multiple of 64 with at least 6-7 stages of 64 per K split (the LLaDA-8B and Dream-7B
+   * shapes are covered).  The O product keeps its row-major tiles (its 4096 x 4096 weight is too
+   * short a stream per workgroup for the packed form to pay). */
   const void *w_gate_up_packed; /* w_gate_up packed with gate/up interleave F */
   const void *w_down_packed;    /* w_down packed without interleave */
-  const void *w_qkv_packed;     /* w_qkv packed without interleave (QKV over d = 4096 with 12288 outputs,
-                                   in 2 K splits), or NULL */
+  const void *w_qkv_packed;     /* w_qkv packed without interleave */
 } dllm_layer_w;
 
 typedef struct {
@@ -330,6 +331,13 @@ int dllm_confidence_kl(const float *logits, void *logits_prev, int32_t prev_dtyp
                        int32_t V, int32_t exclude_id, int32_t have_prev, float *conf,
                        int32_t *argmax, float *kl, void *stream);
 
+/* The plan of the packed-weight product over M active rows (host only; no device call):
+ * returns 1 and stores the waves per workgroup (*nw, one 32-column block each) and the K splits
+ * (*splits, fp32 partials) when the packed path takes an M x N x K product ([ES] 2.1 item 2:
+ * the active rows' products at batch 1 stream the weights), else returns 0.  swiglu != 0 asks
+ * for the fused gate/up product (N = 2F packed columns, never split).  nw/splits may be NULL. */
+int dllm_packed_plan(int32_t M, int32_t N, int32_t K, int32_t swiglu, int32_t *nw, int32_t *splits);
+
 /* Repacks a bf16 weight W [N, K] (nn.Linear layout) into MFMA B-fragment order for the
  * active-row products ([ES] 2.1 item 2: at batch 1 they stream the weights): fragment
  * (nb, ks) -- 32 output columns x 16 reduction elements -- is 1 KB at element
@@ -369,12 +377,16 @@ int dllm_skip_step(const dllm_model *model, dllm_state *state, const dllm_step_c
 /* Achievable-peak probes for measurement (nothing on the denoising path uses them): the measured
  * denominators beside the datasheet peaks.
  *  DLLM_PROBE_COPY: copies the first half of buf into the second half, iters times (a plain HBM
- *    stream); *work = bytes read + written.
+ *    stream, four 16-byte loads in flight per thread); *work = bytes read + written.
  *  DLLM_PROBE_MFMA: a loop of iters steps of four independent v_mfma_f32_32x32x16_bf16 chains per
  *    wave on register operands, 2048 workgroups of 4 waves (8 per CU); buf must hold at least
  *    2048 * 256 floats (written only in a case the sums cannot reach); *work = flops.
- *  The work is enqueued on `stream`; the caller times it (e.g. with events). */
-enum { DLLM_PROBE_COPY = 0, DLLM_PROBE_MFMA = 1 };
+ *  DLLM_PROBE_READ: a nontemporal read of buf past its first 512 KiB, iters times (the way the
+ *    products stream their weights); the first 512 KiB take one word per thread, written only in a
+ *    case the folded words cannot be known to avoid; bytes must exceed 1 MiB; *work = bytes read.
+ *  The work is enqueued on `stream`; the caller times it (e.g. with events). Errors: DLLM_EINVAL
+ *  (null pointers, unaligned buf, iters < 1, unknown kind), DLLM_ESHAPE (buf too small). */
+enum { DLLM_PROBE_COPY = 0, DLLM_PROBE_MFMA = 1, DLLM_PROBE_READ = 2 };
 int dllm_peak_probe(int32_t kind, void *buf, size_t bytes, int32_t iters, double *work, void *stream);
 
 /* Precondition bits recorded by the checking build. */

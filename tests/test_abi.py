@@ -35,7 +35,7 @@ def test_every_declared_symbol_is_exported(lib):
 
 
 def test_version_and_status_strings(lib):
-    assert lib.dllm_version() == 200
+    assert lib.dllm_version() == 201
     assert lib.dllm_status_string(0) == b"ok"
     assert lib.dllm_status_string(4) == b"workspace missing or too small"
 
@@ -256,3 +256,46 @@ def test_binding_fails_loudly_without_the_library(tmp_path):
             _ffi.load(str(tmp_path / "libdllm.so"))
     finally:
         _ffi._LIB = saved
+
+
+def _plan(lib, M, N, K, swiglu=False):
+    nw, sp = ctypes.c_int32(), ctypes.c_int32()
+    ok = lib.dllm_packed_plan(M, N, K, int(swiglu), ctypes.byref(nw), ctypes.byref(sp))
+    return (nw.value, sp.value) if ok else None
+
+
+def test_packed_plan_choices(lib):
+    """The packed-weight planner (host only): one workgroup per CU, 256 CUs.  At the LLaDA-8B
+    shapes over 128 rows it keeps one full round of 256 workgroups per product; the Dream-7B
+    shapes (d 3584, F 18944, 28 + 2 x 4 heads of 128) are covered too."""
+    # LLaDA-8B: QKV 12288 x 4096, O 4096 x 4096, gate/up 24576 x 4096 (fused), down 4096 x 12288
+    assert _plan(lib, 128, 12288, 4096) == (3, 2)
+    assert _plan(lib, 128, 4096, 4096) == (4, 8)
+    assert _plan(lib, 128, 24576, 4096, swiglu=True) == (3, 1)
+    assert _plan(lib, 128, 4096, 12288) == (4, 8)
+    # Dream-7B: QKV 4608 x 3584 (48 tiles x 4), O 3584 x 3584 and down 3584 x 18944 (28 tiles x 8)
+    assert _plan(lib, 128, 4608, 3584) == (3, 4)
+    assert _plan(lib, 128, 3584, 3584) == (4, 8)
+    assert _plan(lib, 128, 3584, 18944) == (4, 8)
+    assert _plan(lib, 128, 37888, 3584, swiglu=True) is not None
+    # outside the path: more than 128 rows, no rows, K not a multiple of 64, too few stages
+    assert _plan(lib, 129, 4096, 4096) is None
+    assert _plan(lib, 0, 4096, 4096) is None
+    assert _plan(lib, 64, 4096, 4000) is None
+    assert _plan(lib, 64, 4096, 320) is None  # 5 stages of 64: fewer than any wave count keeps in flight
+
+
+def test_packed_plan_invariants(lib):
+    """Every shape with d and F multiples of 64 (and at least 6 stages) gets a plan, and every plan
+    is one the kernel can run: N splits into whole workgroups, every K split holds the stages in
+    flight (7 for 3-4 waves, 6 for 2), split counts are ones the epilogues sum (1, 2, 4, 8), the
+    fused gate/up product is never split."""
+    for N in range(64, 8193, 448):
+        for K in range(384, 20000, 1216):
+            for swiglu in (False, True):
+                p = _plan(lib, 96, N, K, swiglu)
+                assert p is not None, (N, K, swiglu)
+                nw, sp = p
+                assert nw in (2, 3, 4) and N % (32 * nw) == 0 and sp in (1, 2, 4, 8)
+                assert (K // 64) // sp >= (6 if nw == 2 else 7)
+                assert not (swiglu and sp != 1)

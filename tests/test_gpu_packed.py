@@ -1,9 +1,9 @@
 """Weights in MFMA fragment order (dllm_pack_weight) and the products that stream them (GPU).
 
 The packed layout is checked element by element against its definition (an index map built
-here with torch); the layer that uses the packed gate/up and down copies is checked against the
-same layer on the row-major copies, and the full-size LLaDA layer test (test_gpu_fullsize.py)
-checks it against the oracle.
+here with torch); layers whose four products use the packed copies are checked against the same
+layers on the row-major copies (LLaDA-8B and Dream-7B shapes) and against the oracle (a
+Dream-shaped layer here; the full-size LLaDA layer in test_gpu_fullsize.py).
 """
 import numpy as np
 import pytest
@@ -54,25 +54,45 @@ def test_pack_rejects_bad_shapes(bad):
         api.pack_weight(w, interleave_f=bad["f"])
 
 
-@pytest.mark.parametrize("k", [64, 128])
-def test_packed_layer_matches_row_major(k):
-    """The LLaDA-8B-shaped layer on k active rows: packed QKV (2 K splits), packed gate/up (fused
-    SwiGLU) and packed down (8 K splits) against the row-major kernels on the same inputs."""
-    dims = workloads.LLADA_LAYER
+def _packed_products(dims, rows):
+    """The packed plans of the layer's three packed products over `rows` active rows."""
+    nqkv = (dims.n_heads + 2 * dims.n_kv_heads) * dims.head_dim
+    return {"qkv": api.packed_plan(rows, nqkv, dims.d),
+            "gate_up": api.packed_plan(rows, 2 * dims.d_ff, dims.d, swiglu=True),
+            "down": api.packed_plan(rows, dims.d, dims.d_ff)}
+
+
+@pytest.mark.parametrize("shape,k", [("llada", 64), ("llada", 128), ("dream", 64)])
+def test_packed_layer_matches_row_major(shape, k):
+    """A layer on k active rows per sequence, the QKV, gate/up and down products on the packed
+    weights (QKV and down into fp32 K-split partials, gate/up with the fused SwiGLU; O stays on its
+    row-major tiles) against the row-major kernels on the
+    same inputs: the LLaDA-8B layer (1 sequence of 512) and a Dream-7B GQA layer (2 sequences of
+    1024, 128 rows in all, ragged)."""
+    if shape == "llada":
+        dims, n_act = workloads.LLADA_LAYER, [k]
+    else:
+        dims, n_act = workloads.shrink(workloads.DREAM, n_layers=1, B=2), [k, k - 3]
     B, S, d = dims.B, dims.S, dims.d
-    print(f"packed vs row-major layer k={k}", flush=True)
+    plans = _packed_products(dims, B * k)
+    print(f"packed vs row-major layer {shape} k={k} plans={plans}", flush=True)
+    assert all(p is not None for p in plans.values())
     lw = workloads.layer_weights(dims, 0, device=DEV, seed_base=dims.cfg_id)
     emb = torch.zeros((8, d), dtype=torch.bfloat16, device=DEV)
     w = {"embed": emb, "final_norm": torch.ones(d, dtype=torch.bfloat16, device=DEV), "lm_head": emb, "layers": [lw]}
     m_pk = api.Model(w, dims.n_heads, dims.n_kv_heads, 7, pack=True)
     m_rm = api.Model(w, dims.n_heads, dims.n_kv_heads, 7, pack=False)
-    assert m_pk._lw[0].w_gate_up_packed and m_pk._lw[0].w_down_packed and m_pk._lw[0].w_qkv_packed
-    assert not m_rm._lw[0].w_gate_up_packed and not m_rm._lw[0].w_down_packed and not m_rm._lw[0].w_qkv_packed
+    names = ("w_gate_up_packed", "w_down_packed", "w_qkv_packed")
+    assert all(getattr(m_pk._lw[0], n) for n in names)
+    assert not any(getattr(m_rm._lw[0], n) for n in names)
     kc0 = synth.normal(synth.seed_of(5, 1), (B, S, dims.n_kv_heads, dims.head_dim), 1.0, torch.bfloat16).to(DEV)
     vc0 = synth.normal(synth.seed_of(5, 2), (B, S, dims.n_kv_heads, dims.head_dim), 1.0, torch.bfloat16).to(DEV)
     x0 = synth.normal(synth.seed_of(5, 3), (B * k, d), 1.0, torch.bfloat16).to(DEV)
-    idx = torch.sort(synth.permutation(synth.seed_of(5, 4), S)[:k]).values.to(torch.int32).view(1, k).to(DEV)
-    nact = torch.full((B,), k, dtype=torch.int32, device=DEV)
+    idx = torch.full((B, k), -1, dtype=torch.int32)
+    for b in range(B):
+        idx[b, :n_act[b]] = torch.sort(synth.permutation(synth.seed_of(5, 4, b), S)[:n_act[b]]).values.to(torch.int32)
+    idx = idx.to(DEV)
+    nact = torch.tensor(n_act, dtype=torch.int32, device=DEV)
     outs = []
     for m in (m_pk, m_rm):
         x, kc, vc = x0.clone(), kc0.clone(), vc0.clone()
@@ -81,15 +101,30 @@ def test_packed_layer_matches_row_major(k):
         torch.cuda.synchronize()
         outs.append((x, kc, vc))
     (xp, kp, vp), (xr, kr, vr) = outs
-    # the two QKV paths sum the reduction in different orders (2 vs 4 K splits), so a stored bf16
+    # the two QKV paths sum the reduction in different orders (other K splits), so a stored bf16
     # K/V element may round one ulp (2^-8 of itself) the other way; untouched rows stay identical
-    written = torch.zeros(S, dtype=torch.bool)
-    written[idx[0].cpu().long()] = True
-    for a, b in ((kp, kr), (vp, vr)):
-        assert_close(np64(a[0][written.to(DEV)]), np64(b[0][written.to(DEV)]), 5e-3, "fresh K/V, packed vs row-major")
-        assert torch.equal(a[0][~written.to(DEV)], b[0][~written.to(DEV)])
+    for b in range(B):
+        written = torch.zeros(S, dtype=torch.bool, device=DEV)
+        written[idx[b, :n_act[b]].long()] = True
+        for a, c in ((kp, kr), (vp, vr)):
+            assert_close(np64(a[b][written]), np64(c[b][written]), 5e-3, "fresh K/V, packed vs row-major")
+            assert torch.equal(a[b][~written], c[b][~written])
     # two bf16 evaluation orders of the same layer: the flipped Q/K/V roundings move the attention
     # weights and its output, which carry into the residual stream as they do against the oracle
     # (about 5e-3 of the largest element for this layer), so the bf16 bar applies
-    assert_close(np64(xp), np64(xr), 2e-2, "layer output, packed vs row-major")
-    assert torch.all(torch.isfinite(xp.float()))
+    live = torch.cat([torch.arange(b * k, b * k + n_act[b]) for b in range(B)]).to(DEV)
+    assert_close(np64(xp[live]), np64(xr[live]), 2e-2, "layer output, packed vs row-major")
+    assert torch.all(torch.isfinite(xp[live].float()))
+
+
+def test_packed_dream_layer_128_rows_oracle():
+    """A Dream-7B-shaped GQA layer (d 3584, 28 / 4 heads, SwiGLU 18944) over 2 sequences of 1024
+    with 64 and 61 active rows: the three packed products on the packed path (their plans differ from the
+    LLaDA ones: QKV 3 waves x 4 K splits, gate/up 2-wave workgroups), checked against the oracle on the
+    K/V of every active row and the outputs of sampled rows."""
+    from tests.test_gpu_fullsize import _sampled_layer_case
+    dims = workloads.shrink(workloads.DREAM, n_layers=1, B=2)
+    plans = _packed_products(dims, 2 * 64)
+    print(f"dream layer 128 rows packed vs oracle plans={plans}", flush=True)
+    assert all(p is not None for p in plans.values())
+    _sampled_layer_case(dims, [64, 61], n_sample=8, seed=66)

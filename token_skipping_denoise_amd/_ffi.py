@@ -20,6 +20,7 @@ EXPORTED = (
     "dllm_workspace_size", "dllm_score_select", "dllm_gather_rows", "dllm_scatter_rows",
     "dllm_layer_sparse", "dllm_confidence_kl", "dllm_skip_step", "dllm_status_string", "dllm_version",
     "dllm_dus_mark", "dllm_pack_weight", "dllm_layer_sparse_noalloc", "dllm_check_word", "dllm_peak_probe",
+    "dllm_packed_plan",
 )
 TK_NONE, TK_QKV, TK_ATTN, TK_O, TK_FFN_UP, TK_FFN_DOWN, TK_LM_HEAD, TK_VOCAB, TK_SCORE, TK_SELECT = range(10)
 
@@ -122,6 +123,8 @@ def _open(path: str) -> ctypes.CDLL:
     lib.dllm_status_string.argtypes = [c_int32]
     lib.dllm_version.restype = c_int32
     lib.dllm_version.argtypes = []
+    lib.dllm_packed_plan.restype = c_int32
+    lib.dllm_packed_plan.argtypes = [c_int32, c_int32, c_int32, c_int32, POINTER(c_int32), POINTER(c_int32)]
     lib.dllm_peak_probe.restype = c_int32
     lib.dllm_peak_probe.argtypes = [c_int32, c_void_p, c_size_t, c_int32, POINTER(ctypes.c_double), c_void_p]
     lib.dllm_check_word.restype = c_int32

@@ -119,6 +119,14 @@ def dus_mark(force, lo: int, block: int, round: int, *, a: int = 2, rounds: int 
     _check(st, "dllm_dus_mark")
 
 
+def packed_plan(M: int, N: int, K: int, swiglu: bool = False):
+    """(waves per workgroup, K splits) of the packed-weight product over M rows, or None when the
+    packed path does not take that shape (host-side query)."""
+    nw, sp = ctypes.c_int32(), ctypes.c_int32()
+    ok = _lib().dllm_packed_plan(int(M), int(N), int(K), int(bool(swiglu)), ctypes.byref(nw), ctypes.byref(sp))
+    return (nw.value, sp.value) if ok else None
+
+
 def pack_weight(w, interleave_f: int = 0):
     """A [N, K] bf16 weight repacked into MFMA fragment order (new tensor, same device)."""
     if w.dtype != torch.bfloat16 or w.dim() != 2:
@@ -136,9 +144,9 @@ class Model:
     ``weights`` holds per-layer tensors wq/wk/wv/wo/wg/wu/wd and norms (as
     produced by synth.workloads); Q/K/V and gate/up are concatenated once
     here into the fused row layout the library expects.  With ``pack`` (bf16
-    only) the gate/up and down weights are also stored in MFMA fragment order
-    (dllm_pack_weight), which the library streams for the active-row products
-    those copies fit.
+    only) the QKV, gate/up and down weights are also stored in MFMA fragment
+    order (dllm_pack_weight), which the library streams for the active-row
+    products (at most 128 rows) those copies fit.
     """
 
     def __init__(self, weights: dict, n_heads: int, n_kv_heads: int, mask_id: int, rope_base=1e4, rms_eps=1e-5,

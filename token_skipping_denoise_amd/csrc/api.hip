@@ -82,10 +82,13 @@ long max_part_floats(const dllm_dims& d, int dtype, long M) {
     const GemmPlan p = gemm_plan(dtype, (int)M, Ns[i], Ks[i]);
     best = std::max(best, (long)p.splits * M * Ns[i]);
   }
-  const PackedPlan pd = packed_plan((int)M, d.d, d.d_ff, false);  // the packed down projection
-  if (dtype == DLLM_BF16 && pd.ok) best = std::max(best, (long)pd.splits * M * d.d);
-  const PackedPlan pq = packed_plan((int)M, NQKV, d.d, false);    // the packed QKV product
-  if (dtype == DLLM_BF16 && pq.ok) best = std::max(best, (long)pq.splits * M * NQKV);
+  // the packed products (QKV, down) that write split-K partials
+  if (dtype == DLLM_BF16) {
+    for (int i : {0, 3}) {
+      const PackedPlan pp = packed_plan((int)M, Ns[i], Ks[i], false);
+      if (pp.ok) best = std::max(best, (long)pp.splits * M * Ns[i]);
+    }
+  }
   return best;
 }
 
@@ -367,7 +370,7 @@ int check_layer_args(const dllm_model* model, int32_t layer, const void* x_act, 
 
 extern "C" {
 
-int dllm_version(void) { return 200; }
+int dllm_version(void) { return 201; }
 
 int dllm_peak_probe(int32_t kind, void* buf, size_t bytes, int32_t iters, double* work, void* stream) {
   if (!buf || !work || iters < 1) return DLLM_EINVAL;
@@ -376,6 +379,8 @@ int dllm_peak_probe(int32_t kind, void* buf, size_t bytes, int32_t iters, double
     if (bytes < 32) return DLLM_ESHAPE;
   } else if (kind == DLLM_PROBE_MFMA) {
     if (bytes < (size_t)2048 * 256 * sizeof(float)) return DLLM_ESHAPE;
+  } else if (kind == DLLM_PROBE_READ) {
+    if (bytes <= ((size_t)1 << 20)) return DLLM_ESHAPE;
   } else {
     return DLLM_EINVAL;
   }
@@ -529,6 +534,13 @@ int dllm_confidence_kl(const float* logits, void* logits_prev, int32_t prev_dtyp
   DLLM_TRY(launch_conf_kl(logits, logits_prev, prev_dtype, row_pos, R, V, exclude_id, have_prev, conf, argmax, kl,
                           nullptr, (hipStream_t)stream));
   return DLLM_OK;
+}
+
+int dllm_packed_plan(int32_t M, int32_t N, int32_t K, int32_t swiglu, int32_t* nw, int32_t* splits) {
+  const PackedPlan p = packed_plan(M, N, K, swiglu != 0);
+  if (nw) *nw = p.ok ? p.nw : 0;
+  if (splits) *splits = p.ok ? p.splits : 0;
+  return p.ok ? 1 : 0;
 }
 
 int dllm_pack_weight(const void* w, void* w_packed, int32_t N, int32_t K, int32_t interleave_f, void* stream) {

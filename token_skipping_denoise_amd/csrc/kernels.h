@@ -69,9 +69,9 @@ struct PackedPlan {
   bool ok = false;
   int nw = 0;      // waves per workgroup, one 32-column block each
   int splits = 1;  // K splits (fp32 partials)
-  int nkc = 0;     // 64-element stages per split
+  int nkc = 0;     // 64-element stages of the longest split
 };
-// Whether the packed path covers an M x N x K product (M <= 128; compiled stage counts only).
+// Whether (and how) the packed path covers an M x N x K product (M <= 128).
 PackedPlan packed_plan(int M, int N, int K, bool swiglu);
 // swiglu (H non-null): H[m][f] = silu(A Wg^T) * (A Wu^T), N = 2F packed columns; else fp32 partials
 // C[sp][m][n].
