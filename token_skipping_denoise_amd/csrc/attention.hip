@@ -78,6 +78,9 @@ constexpr int kRing = 4;                      // stages shared by the workgroup
 // Fourth word of a raw buffer resource (CDNA): 32-bit data format, no swizzle; out-of-range
 // offsets read as zero.
 constexpr int kBufWord3 = 0x00020000;
+// Cache policy of the K/V stream: nontemporal (the long-context layer measured 93.0 against
+// 95.7 us per launch with default caching).
+constexpr int kNT = 2;
 typedef __attribute__((address_space(3))) void lds_void;
 typedef short short4_t __attribute__((ext_vector_type(4)));
 typedef short short8_t __attribute__((ext_vector_type(8)));
@@ -262,9 +265,9 @@ __global__ __launch_bounds__(512, 1) void k_attn_bf16(const uint16_t* __restrict
 #pragma unroll
     for (int i = 0; i < 2; ++i) {
       const int qi2 = wave * 2 + i;
-      __builtin_amdgcn_raw_ptr_buffer_load_lds(rsk, (lds_void*)(st + qi2 * 1024), 16, voff[i] + so, 0, 0, 0);
+      __builtin_amdgcn_raw_ptr_buffer_load_lds(rsk, (lds_void*)(st + qi2 * 1024), 16, voff[i] + so, 0, 0, kNT);
       __builtin_amdgcn_raw_ptr_buffer_load_lds(rsv, (lds_void*)(st + kTileBytes + qi2 * 1024), 16, voff[i] + so, 0, 0,
-                                               0);
+                                               kNT);
     }
   };
   // the first tiles are requested before the active-row count is known (all addresses are valid
