@@ -357,12 +357,15 @@ def c2_layer_kernels(n_copies=6, k=64, reps=3):
 def profile_layer(which: str, calls: int):
     """A short program for counter collection: one layer of the given shape called ``calls`` times
     through dllm_layer_sparse, printing a line after each call.  ``llada128``: the LLaDA-8B layer
-    (S 512) with 128 active rows, the skipped-regime shape of the default workload; ``long205``: the
-    long-context layer (batch 4, S 4096) with 205 active rows per sequence."""
+    (S 512) with 128 active rows, the skipped-regime shape of the default workload; ``llada512``:
+    the same layer over all 512 rows (the dense layers); ``long205``: the long-context layer
+    (batch 4, S 4096) with 205 active rows per sequence."""
     import synth
     dev = "cuda:0"
     if which == "llada128":
         dims, n_act = workloads.LLADA_LAYER, [128]
+    elif which == "llada512":
+        dims, n_act = workloads.LLADA_LAYER, [512]
     else:
         dims, n_act = workloads.shrink(workloads.LLADA_LONG, n_layers=1), [205] * 4
     B, S, d = dims.B, dims.S, dims.d
@@ -780,7 +783,7 @@ def main():
                     help="only copy a 1 GiB buffer once (reference for the HBM byte counters) and exit")
     ap.add_argument("--cache-feature", choices=("hidden", "value"), default="hidden",
                     help="dcache workload: the feature a cached layer compares (its input, or its V projection)")
-    ap.add_argument("--profile-layer", choices=("llada128", "long205"), default=None,
+    ap.add_argument("--profile-layer", choices=("llada128", "llada512", "long205"), default=None,
                     help="only call one layer of that shape --steps times, a line per call (a short "
                          "program for counter collection), and exit")
     ap.add_argument("--no-extra", action="store_true",
