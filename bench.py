@@ -359,9 +359,30 @@ def profile_layer(which: str, calls: int):
     through dllm_layer_sparse, printing a line after each call.  ``llada128``: the LLaDA-8B layer
     (S 512) with 128 active rows, the skipped-regime shape of the default workload; ``llada512``:
     the same layer over all 512 rows (the dense layers); ``long205``: the long-context layer
-    (batch 4, S 4096) with 205 active rows per sequence."""
+    (batch 4, S 4096) with 205 active rows per sequence; ``step128``: whole sparse iterations of a
+    one-layer model, for the scoring and selection kernels."""
     import synth
     dev = "cuda:0"
+    if which == "step128":
+        # sparse iterations of a one-layer LLaDA-8B-shaped model (1024-token vocabulary) with the
+        # boundary at layer 0 and k = 128: the importance score and the selection at S = 512
+        dims = workloads.shrink(workloads.LLADA, n_layers=1, vocab=1024)
+        w = workloads.model_weights(dims, device=dev, seed_base=200)
+        m = api.Model(w, dims.n_heads, dims.n_kv_heads, dims.mask_id)
+        st = api.State(m, workloads.initial_tokens(dims, device=dev), k_max=128)
+        ws = api.alloc_workspace(m, dims.B, dims.S, 128)
+        api.skip_step(m, st, api.step_cfg(0, True, ws=ws))
+        conf = synth.uniform01(synth.seed_of(2, 104), (dims.B, dims.S)).to(dev)
+        sc = api.score_cfg(alpha=0.5, var=api.VAR_L1N, sel=api.SEL_TOPK, k=128)
+        torch.cuda.synchronize()
+        print(f"profile-layer {which}: B {dims.B} S {dims.S} k 128", flush=True)
+        for i in range(calls):
+            st.conf.copy_(conf)
+            st.tokens[:, 300 + i % 64] = 7 + i   # a changed token, so the boundary state moves
+            api.skip_step(m, st, api.step_cfg(0, False, sc, ws=ws))
+            torch.cuda.synchronize()
+            print(f"call {i + 1}/{calls} done", flush=True)
+        return
     if which == "llada128":
         dims, n_act = workloads.LLADA_LAYER, [128]
     elif which == "llada512":
@@ -783,7 +804,7 @@ def main():
                     help="only copy a 1 GiB buffer once (reference for the HBM byte counters) and exit")
     ap.add_argument("--cache-feature", choices=("hidden", "value"), default="hidden",
                     help="dcache workload: the feature a cached layer compares (its input, or its V projection)")
-    ap.add_argument("--profile-layer", choices=("llada128", "llada512", "long205"), default=None,
+    ap.add_argument("--profile-layer", choices=("llada128", "llada512", "long205", "step128"), default=None,
                     help="only call one layer of that shape --steps times, a line per call (a short "
                          "program for counter collection), and exit")
     ap.add_argument("--no-extra", action="store_true",
