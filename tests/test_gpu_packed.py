@@ -62,13 +62,14 @@ def _packed_products(dims, rows):
             "down": api.packed_plan(rows, dims.d, dims.d_ff)}
 
 
-@pytest.mark.parametrize("shape,k", [("llada", 64), ("llada", 128), ("dream", 64)])
+@pytest.mark.parametrize("shape,k", [("llada", 64), ("llada", 80), ("llada", 128), ("dream", 64), ("dream", 37)])
 def test_packed_layer_matches_row_major(shape, k):
     """A layer on k active rows per sequence, the QKV, gate/up and down products on the packed
     weights (QKV and down into fp32 K-split partials, gate/up with the fused SwiGLU; O stays on its
     row-major tiles) against the row-major kernels on the
-    same inputs: the LLaDA-8B layer (1 sequence of 512) and a Dream-7B GQA layer (2 sequences of
-    1024, 128 rows in all, ragged)."""
+    same inputs: the LLaDA-8B layer (1 sequence of 512; 80 rows leave the last 32-row MFMA block
+    partly clamped) and a Dream-7B GQA layer (2 sequences of 1024, ragged: 64 + 61 and 37 + 34 rows,
+    the second case off every multiple of 16)."""
     if shape == "llada":
         dims, n_act = workloads.LLADA_LAYER, [k]
     else:
