@@ -359,8 +359,10 @@ def profile_layer(which: str, calls: int):
     through dllm_layer_sparse, printing a line after each call.  ``llada128``: the LLaDA-8B layer
     (S 512) with 128 active rows, the skipped-regime shape of the default workload; ``llada512``:
     the same layer over all 512 rows (the dense layers); ``long205``: the long-context layer
-    (batch 4, S 4096) with 205 active rows per sequence; ``step128``: whole sparse iterations of a
-    one-layer model, for the scoring and selection kernels."""
+    (batch 4, S 4096) with 205 active rows per sequence; ``dream1024``: one Dream-7B-shaped layer
+    (batch 8, S 1024, GQA 28/4) over every row, the many-row regime of the lock ramp's first
+    steps; ``step128``: whole sparse iterations of a one-layer model, for the scoring and
+    selection kernels."""
     import synth
     dev = "cuda:0"
     if which == "step128":
@@ -387,6 +389,9 @@ def profile_layer(which: str, calls: int):
         dims, n_act = workloads.LLADA_LAYER, [128]
     elif which == "llada512":
         dims, n_act = workloads.LLADA_LAYER, [512]
+    elif which == "dream1024":
+        dims = workloads.shrink(workloads.DREAM, n_layers=1)
+        n_act = [dims.S] * dims.B
     else:
         dims, n_act = workloads.shrink(workloads.LLADA_LONG, n_layers=1), [205] * 4
     B, S, d = dims.B, dims.S, dims.d
@@ -804,7 +809,7 @@ def main():
                     help="only copy a 1 GiB buffer once (reference for the HBM byte counters) and exit")
     ap.add_argument("--cache-feature", choices=("hidden", "value"), default="hidden",
                     help="dcache workload: the feature a cached layer compares (its input, or its V projection)")
-    ap.add_argument("--profile-layer", choices=("llada128", "llada512", "long205", "step128"), default=None,
+    ap.add_argument("--profile-layer", choices=("llada128", "llada512", "long205", "dream1024", "step128"), default=None,
                     help="only call one layer of that shape --steps times, a line per call (a short "
                          "program for counter collection), and exit")
     ap.add_argument("--no-extra", action="store_true",

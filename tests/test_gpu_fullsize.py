@@ -159,6 +159,17 @@ def test_dream_gqa_layer_full_size_sampled():
     _sampled_layer_case(dims, n_act, n_sample=12, seed=44)
 
 
+def test_dream_gqa_layer_many_rows_sampled():
+    """Dream-7B-shaped layer over (nearly) every row, B 8 x S 1024, ragged (977..1024 live rows):
+    8192 tiled rows take the 16-wave 256 x 256 tiles in the QKV, gate/up + SwiGLU and down
+    products (the first steps of the lock ramp); every fresh K/V row and sampled outputs against
+    the oracle."""
+    dims = workloads.shrink(workloads.DREAM, n_layers=1)
+    n_act = [1024, 1000, 1024, 977, 1024, 1024, 1013, 1024]
+    print("dream layer many rows (sampled)", flush=True)
+    _sampled_layer_case(dims, n_act, n_sample=8, seed=46)
+
+
 def test_long_context_layer_full_size_sampled():
     """Long-context LLaDA layer, B 4 x S 4096, 205 active rows per sequence."""
     dims = workloads.shrink(workloads.LLADA_LONG, n_layers=1)

@@ -350,13 +350,24 @@ __global__ __launch_bounds__(256) void k_gemm_f32(const float* __restrict__ A, c
   DLLM_LDS_CASE(128, 64, 4, 1, 2, 2) DLLM_LDS_CASE(128, 128, 2, 1, 2, 2) DLLM_LDS_CASE(128, 128, 3, 1, 2, 2) \
   DLLM_LDS_CASE(128, 256, 3, 1, 2, 4) DLLM_LDS_CASE(256, 256, 2, 1, 2, 4) DLLM_LDS_CASE(128, 128, 4, 2, 2, 2) \
   DLLM_LDS_CASE(256, 192, 2, 1, 4, 2) DLLM_LDS_CASE(256, 128, 3, 1, 4, 2) DLLM_LDS_CASE(128, 192, 3, 1, 4, 2) \
-  DLLM_LDS_CASE(128, 64, 4, 1, 4, 2) DLLM_LDS_CASE(128, 128, 3, 1, 4, 2)
+  DLLM_LDS_CASE(128, 64, 4, 1, 4, 2) DLLM_LDS_CASE(128, 128, 3, 1, 4, 2) DLLM_LDS_CASE(256, 256, 2, 1, 4, 4)
 #define DLLM_LDS_SWIGLU_CASES                                                                       \
   DLLM_LDS_CASE(128, 128, 3, 1, 2, 2) DLLM_LDS_CASE(128, 128, 3, 2, 2, 2)
 
 #define DLLM_LDS_SWIGLU_ILV_CASES \
-  DLLM_LDS_CASE(128, 96, 4, 1, 4, 1) DLLM_LDS_CASE(256, 192, 2, 1, 4, 2) DLLM_LDS_CASE(128, 256, 2, 1, 2, 4)
+  DLLM_LDS_CASE(128, 96, 4, 1, 4, 1) DLLM_LDS_CASE(256, 192, 2, 1, 4, 2) DLLM_LDS_CASE(128, 256, 2, 1, 2, 4) \
+  DLLM_LDS_CASE(256, 256, 2, 1, 4, 4)
 
+// Thousands of rows (the Dream-7B steps over 8 x 1024 positions, the long-context refreshes over
+// 4 x 4096): 256 x 256 tiles over sixteen wavefronts (4 x 4, four per SIMD, 64 x 64 wave tiles)
+// once the launch holds at least this many workgroups.  At 8192 rows of the Dream-7B layer they
+// took gate/up + SwiGLU 2697 -> 2046 us, down 1319-1370 -> 1168 us and QKV + down together
+// 1678 -> 1478-1485 us against the 8-wave plans below (the lock-ramp run 283 -> 312 tokens/s,
+// the long-context run 417 -> 452);
+// at 512 and 820 rows, with one or two such workgroups per CU, they were slower (gate/up 102.7
+// against 112.4 and 216.7 against 233.5 us), so those keep their tiles.
+constexpr long kWideTileWgsSwiglu = 1024;  // four per CU
+constexpr long kWideTileWgs = 512;         // two per CU
 GemmPlan gemm_plan(int dtype, int M, int N, int K, bool swiglu) {
   GemmPlan p{64, 64, 1, 64, 2};
   if (dtype == 0) {
@@ -368,10 +379,12 @@ GemmPlan gemm_plan(int dtype, int M, int N, int K, bool swiglu) {
   // shapes.  Few rows (HBM bound on the weights): 128-row tiles over eight wavefronts (more
   // waves issuing loads keep more bytes in flight per CU); wide QKV-like outputs take 192
   // columns (256 over 2 x 4 when 192 does not divide them), narrow ones 64 columns with 4
-  // stages, and split-K fills the chip.  Many rows: 256-row tiles over 4 x 2 wavefronts where
-  // the shape allows (256 x 192 for the fused SwiGLU product and QKV-like outputs, 256 x 128
-  // with a 4- or 2-way K split for the down projection), otherwise 128 x 128 with 2 stages, so
-  // that two workgroups share a CU, and split-K up to 4.  With rows padded per sequence, dead
+  // stages, and split-K fills the chip.  Thousands of rows: 256 x 256 tiles over 4 x 4
+  // wavefronts when they fill the CUs two (four for SwiGLU) times over.  Many rows: 256-row
+  // tiles over 4 x 2 wavefronts where the shape allows (256 x 192 for the fused SwiGLU product
+  // and QKV-like outputs, 256 x 128 with a 4- or 2-way K split for the down projection),
+  // otherwise 128 x 128 with 2 stages, so that two workgroups share a CU, and split-K up to 4.
+  // With rows padded per sequence, dead
   // rows fill more of a 256-row tile than of a 128-row one: a SwiGLU width that 96 does not
   // divide takes interleaved 128 x 256 tiles (faster at every live share measured on
   // Dream-7B's F = 18944 than 256 x 128 ones, which win only on fully live rows).
@@ -422,7 +435,15 @@ GemmPlan gemm_plan(int dtype, int M, int N, int K, bool swiglu) {
     // 256-row tiles over 4 x 2 wavefronts: 64 x 96 (or 64 x 64) wave tiles, and eight waves
     // issuing the tile loads (the loads in flight per CU, not the MFMAs, bound these tiles)
     if (swiglu) {
-      if (N % 96 == 0) {  // 96 outputs (192 interleaved gate/up rows) per tile
+      if (N % 128 == 0 && (long)((M + 255) / 256) * (N / 128) >= kWideTileWgsSwiglu) {
+        // 128 outputs (256 interleaved gate/up rows) per tile
+        p.bm = 256;
+        p.bn = 256;
+        p.wm = 4;
+        p.wn = 4;
+        p.pd = 12;
+        p.ilv = 1;
+      } else if (N % 96 == 0) {  // 96 outputs (192 interleaved gate/up rows) per tile
         p.bm = 256;
         p.bn = 192;
         p.wm = 4;
@@ -439,6 +460,16 @@ GemmPlan gemm_plan(int dtype, int M, int N, int K, bool swiglu) {
         p.pd = 13;
         p.kg = 2;
       }
+      return p;
+    }
+    const int big_splits = (K >= 2 * N) ? 2 : 1;  // long reductions (down) in two K halves
+    if (N % 256 == 0 && (long)((M + 255) / 256) * (N / 256) * big_splits >= kWideTileWgs) {
+      p.bm = 256;
+      p.bn = 256;
+      p.wm = 4;
+      p.wn = 4;
+      p.pd = 12;
+      p.splits = big_splits;
       return p;
     }
     if (wide) {
