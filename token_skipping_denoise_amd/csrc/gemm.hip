@@ -38,14 +38,27 @@ __device__ __forceinline__ bool tile_live(int m0, int bm, int M, const int32_t* 
   return false;
 }
 
+// Tile order.  Workgroups are dealt to the eight XCDs in turn by linear id; when the grid is a
+// multiple of 8, XCD x takes the x-th contiguous eighth of the tile list instead.  Within a split
+// the list runs over groups of kGroupM row tiles: the workgroups running together on one XCD
+// cover kGroupM row tiles x several column tiles, so both operands' current k-slabs are shared
+// through that XCD's L2 (row tiles fastest over all rows would share only the weights).  With at
+// most kGroupM row tiles this is the plain row-fastest order.  On one Dream-7B layer over 8192
+// rows, groups of 4 against row-fastest: gate/up 2110 -> 2030 us, QKV + down 773 -> 728 us on
+// average, O 302 -> 240 us (groups of 1: 2097 / 776 / 244; of 8: 2041 / 736 / 258).
+constexpr int kGroupM = 4;
 __device__ __forceinline__ void decode_tile(int nt, int tiles_m, int tiles_n, int& tm, int& tn, int& sp) {
   const int id = blockIdx.x;
   int lin = id;
   if ((nt & 7) == 0) lin = (id & 7) * (nt >> 3) + (id >> 3);
-  tm = lin % tiles_m;
-  const int rest = lin / tiles_m;
-  tn = rest % tiles_n;
-  sp = rest / tiles_n;
+  const int per_split = tiles_m * tiles_n;
+  sp = lin / per_split;
+  lin -= sp * per_split;
+  const int g0 = (lin / (kGroupM * tiles_n)) * kGroupM;
+  const int gm = min(kGroupM, tiles_m - g0);
+  const int r = lin - g0 * tiles_n;
+  tm = g0 + r % gm;
+  tn = r / gm;
 }
 
 // EPI = 0: store fp32 partials C[sp][m][n].
