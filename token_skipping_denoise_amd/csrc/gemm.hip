@@ -119,7 +119,7 @@ __device__ __forceinline__ void issue_tile(const uint16_t* a_base, int a_bytes, 
                                              ob[i] + k0_bytes, 0, 0, 0);
 }
 
-template <int BM, int BN, int NS, int EPI, int OCC, int KG, int WM, int WN>
+template <int BM, int BN, int NS, int EPI, int OCC, int KG, int WM, int WN, int NL>
 __global__ __launch_bounds__(64 * WM * WN * KG, OCC) void k_gemm_lds(const uint16_t* __restrict__ A, const uint16_t* __restrict__ W,
                                                      float* __restrict__ C, uint16_t* __restrict__ H, int M, int N,
                                                      int K, int splits, int tiles_m, int tiles_n,
@@ -127,12 +127,14 @@ __global__ __launch_bounds__(64 * WM * WN * KG, OCC) void k_gemm_lds(const uint1
   constexpr int BK = 64;
   constexpr int TM = BM / (32 * WM), TN = BN / (32 * WN);  // 32x32 blocks per wave
   constexpr int NW = WM * WN * KG;           // wavefronts
-  constexpr int LA = BM / (8 * NW), LB = BN / (8 * NW);  // load instructions per wave per stage (8 rows each)
+  // the first NL waves issue the tile loads (NL = 0: all of them)
+  constexpr int NLW = NL > 0 ? NL : NW;
+  constexpr int LA = BM / (8 * NLW), LB = BN / (8 * NLW);  // load instructions per loading wave per stage (8 rows each)
   constexpr int STAGE = (BM + BN) * BK;      // elements per stage
   constexpr int KS = BK / 16 / KG;           // MFMA k-steps per stage for each k-group
   static_assert(TM * 32 * WM == BM && TN * 32 * WN == BN, "wave tiles are whole 32x32 blocks");
   static_assert(EPI != 1 || TN % 2 == 0, "fused SwiGLU needs an even number of column blocks per wave");
-  static_assert(LA * 8 * NW == BM && LB * 8 * NW == BN, "every wave issues the same number of tile loads");
+  static_assert(LA * 8 * NLW == BM && LB * 8 * NLW == BN && NLW <= NW, "every loading wave issues the same loads");
   static_assert(KG == 1 || NS * STAGE * 2 >= BM * BN * 4, "the k-group reduction reuses the stage ring");
   __shared__ __attribute__((aligned(1024))) uint16_t smem[NS * STAGE];
 
@@ -180,18 +182,21 @@ __global__ __launch_bounds__(64 * WM * WN * KG, OCC) void k_gemm_lds(const uint1
   int oa[LA], ob[LB];  // byte offsets of this lane's chunk in each load, k excluded
 #pragma unroll
   for (int i = 0; i < LA; ++i) {
-    const int row = (wave + NW * i) * 8 + lrow;
+    const int row = (wave + NLW * i) * 8 + lrow;
     const int chunk = (lane & 7) ^ ((row >> 1) & 7);
     oa[i] = ((min(m0 + row, M - 1) - m0) * K + chunk * 8) * 2;
   }
 #pragma unroll
   for (int i = 0; i < LB; ++i) {
-    const int row = (wave + NW * i) * 8 + lrow;
+    const int row = (wave + NLW * i) * 8 + lrow;
     const int chunk = (lane & 7) ^ ((row >> 1) & 7);
     ob[i] = ((min(w_row(row), w_rows - 1) - wr0) * K + chunk * 8) * 2;
   }
+  const bool loads = NL == 0 || wave < NL;
   auto issue = [&](int stage, int kb) {
-    issue_tile<LA, LB, NW, BM, BK>(a_base, a_bytes, oa, w_base, w_bytes, ob, kb * BK * 2, smem + stage * STAGE, wave);
+    if (loads)
+      issue_tile<LA, LB, NLW, BM, BK>(a_base, a_bytes, oa, w_base, w_bytes, ob, kb * BK * 2, smem + stage * STAGE,
+                                       wave);
   };
 
   f32x16_t acc[TM][TN];
@@ -237,7 +242,7 @@ __global__ __launch_bounds__(64 * WM * WN * KG, OCC) void k_gemm_lds(const uint1
   for (int s = 0; s < NS - 1; ++s)
     if (s < nk) issue(s, kb0 + s);
   for (int t = 0; t < nk; ++t) {
-    wait_stages<NS - 2, LA + LB>(nk - 1 - t);  // tiles after t may stay in flight
+    if (loads) wait_stages<NS - 2, LA + LB>(nk - 1 - t);  // tiles after t may stay in flight
     // barrier without a memory fence: a fence would wait for every load in flight
     __builtin_amdgcn_s_barrier();
     if (t + NS - 1 < nk) issue((t + NS - 1) % NS, kb0 + t + NS - 1);
@@ -362,13 +367,13 @@ __global__ __launch_bounds__(256) void k_gemm_f32(const float* __restrict__ A, c
 #define DLLM_LDS_CASES                                                                              \
   DLLM_LDS_CASE(128, 64, 4, 1, 2, 2) DLLM_LDS_CASE(128, 128, 2, 1, 2, 2) DLLM_LDS_CASE(128, 128, 3, 1, 2, 2) \
   DLLM_LDS_CASE(128, 256, 3, 1, 2, 4) DLLM_LDS_CASE(256, 256, 2, 1, 2, 4) DLLM_LDS_CASE(128, 128, 4, 2, 2, 2) \
-  DLLM_LDS_CASE(256, 192, 2, 1, 4, 2) DLLM_LDS_CASE(256, 128, 3, 1, 4, 2) DLLM_LDS_CASE(128, 192, 3, 1, 4, 2) \
+  DLLM_LDS_CASE(256, 128, 3, 1, 4, 2) DLLM_LDS_CASE(128, 192, 3, 1, 4, 2) \
   DLLM_LDS_CASE(128, 64, 4, 1, 4, 2) DLLM_LDS_CASE(128, 128, 3, 1, 4, 2) DLLM_LDS_CASE(256, 256, 2, 1, 4, 4)
 #define DLLM_LDS_SWIGLU_CASES                                                                       \
   DLLM_LDS_CASE(128, 128, 3, 1, 2, 2) DLLM_LDS_CASE(128, 128, 3, 2, 2, 2)
 
 #define DLLM_LDS_SWIGLU_ILV_CASES \
-  DLLM_LDS_CASE(128, 96, 4, 1, 4, 1) DLLM_LDS_CASE(256, 192, 2, 1, 4, 2) DLLM_LDS_CASE(128, 256, 2, 1, 2, 4) \
+  DLLM_LDS_CASE(128, 96, 4, 1, 4, 1) DLLM_LDS_CASE(128, 256, 2, 1, 2, 4) \
   DLLM_LDS_CASE(256, 256, 2, 1, 4, 4)
 
 // Thousands of rows (the Dream-7B steps over 8 x 1024 positions, the long-context refreshes over
@@ -394,11 +399,12 @@ GemmPlan gemm_plan(int dtype, int M, int N, int K, bool swiglu) {
   // columns (256 over 2 x 4 when 192 does not divide them), narrow ones 64 columns with 4
   // stages, and split-K fills the chip.  Thousands of rows: 256 x 256 tiles over 4 x 4
   // wavefronts when they fill the CUs two (four for SwiGLU) times over.  Many rows: 256-row
-  // tiles over 4 x 2 wavefronts where the shape allows (256 x 192 for the fused SwiGLU product
-  // and QKV-like outputs, 256 x 128 with a 4- or 2-way K split for the down projection),
-  // otherwise 128 x 128 with 2 stages, so that two workgroups share a CU, and split-K up to 4.
-  // With rows padded per sequence, dead
-  // rows fill more of a 256-row tile than of a 128-row one: a SwiGLU width that 96 does not
+  // tiles where the shape allows (256 x 192 over 4 x 3 wavefronts, 8 of them loading, for the
+  // fused SwiGLU product and QKV-like outputs: 6-9% faster than over 4 x 2 at 512 and 820
+  // rows; 256 x 128 over 4 x 2 with a 4- or 2-way K split for the down projection), otherwise
+  // 128 x 128 with 2 stages, so that two workgroups share a CU, and split-K up to 4.  With rows
+  // padded per sequence, dead rows fill more of a 256-row tile than of a 128-row one: a SwiGLU
+  // width that 96 does not
   // divide takes interleaved 128 x 256 tiles (faster at every live share measured on
   // Dream-7B's F = 18944 than 256 x 128 ones, which win only on fully live rows).
   const bool few = M <= 192;
@@ -445,8 +451,9 @@ GemmPlan gemm_plan(int dtype, int M, int N, int K, bool swiglu) {
       p.pd = 14;
     }
   } else {
-    // 256-row tiles over 4 x 2 wavefronts: 64 x 96 (or 64 x 64) wave tiles, and eight waves
-    // issuing the tile loads (the loads in flight per CU, not the MFMAs, bound these tiles)
+    // 256-row tiles with 64 x 64 (or 64 x 96 for the down projection's 256 x 128) wave tiles,
+    // eight or more waves issuing the tile loads (the loads in flight per CU, not the MFMAs,
+    // bound these tiles)
     if (swiglu) {
       if (N % 128 == 0 && (long)((M + 255) / 256) * (N / 128) >= kWideTileWgsSwiglu) {
         // 128 outputs (256 interleaved gate/up rows) per tile
@@ -460,7 +467,7 @@ GemmPlan gemm_plan(int dtype, int M, int N, int K, bool swiglu) {
         p.bm = 256;
         p.bn = 192;
         p.wm = 4;
-        p.wn = 2;
+        p.wn = 3;  // 12 waves, 8 of them issuing the tile loads
         p.pd = 12;
         p.ilv = 1;
       } else if (N % 128 == 0) {  // 128 outputs over 128-row tiles (Dream-7B's F = 18944)
@@ -489,7 +496,7 @@ GemmPlan gemm_plan(int dtype, int M, int N, int K, bool swiglu) {
       p.bm = 256;
       p.bn = (N % 192 == 0) ? 192 : 256;
       p.wm = (p.bn == 192) ? 4 : 2;
-      p.wn = (p.bn == 192) ? 2 : 4;
+      p.wn = (p.bn == 192) ? 3 : 4;
       p.pd = 12;
       target = 192;
     } else if (K >= 2 * N && N % 128 == 0 && K / (64 * 4) >= 3) {
@@ -519,7 +526,7 @@ GemmPlan gemm_plan(int dtype, int M, int N, int K, bool swiglu) {
   return p;
 }
 
-template <int BM, int BN, int NS, int EPI, int KG, int WM, int WN>
+template <int BM, int BN, int NS, int EPI, int KG, int WM, int WN, int NL = 0>
 static hipError_t launch_lds(const GemmPlan& p, const void* A, const void* W, float* C, void* H, int M, int N, int K,
                              const int32_t* n_active, int k_max, hipStream_t s) {
   // the kernel's buffer offsets are 32-bit bytes within one tile: BM rows of A, and
@@ -530,7 +537,7 @@ static hipError_t launch_lds(const GemmPlan& p, const void* A, const void* W, fl
   const int tm = (M + BM - 1) / BM, tn = (N + ncols - 1) / ncols;
   constexpr int lds_bytes = NS * (BM + BN) * 64 * 2;
   constexpr int occ = (lds_bytes <= 80 * 1024 && KG * WM * WN == 4) ? 2 : 1;
-  hipLaunchKernelGGL((k_gemm_lds<BM, BN, NS, EPI, occ, KG, WM, WN>), dim3(tm * tn * p.splits), dim3(64 * KG * WM * WN), 0, s,
+  hipLaunchKernelGGL((k_gemm_lds<BM, BN, NS, EPI, occ, KG, WM, WN, NL>), dim3(tm * tn * p.splits), dim3(64 * KG * WM * WN), 0, s,
                      (const uint16_t*)A, (const uint16_t*)W, C, (uint16_t*)H, M, N, K, p.splits, tm, tn, n_active, k_max);
   return hipGetLastError();
 }
@@ -545,6 +552,9 @@ hipError_t launch_gemm(int dtype, const GemmPlan& p, const void* A, const void* 
     return hipGetLastError();
   }
   if (K % 64 != 0) return hipErrorInvalidValue;
+  // 256 x 192 over 4 x 3 wavefronts: the first 8 issue the tile loads (12 would not divide them)
+  if (p.bm == 256 && p.bn == 192 && p.bk == 64 && p.pd == 12 && p.kg == 1 && p.wm == 4 && p.wn == 3)
+    return launch_lds<256, 192, 2, 0, 1, 4, 3, 8>(p, A, W, C, nullptr, M, N, K, n_active, k_max, s);
 #define DLLM_LDS_CASE(BM_, BN_, NS_, KG_, WM_, WN_)                                                \
   if (p.bm == BM_ && p.bn == BN_ && p.bk == 64 && p.pd == 10 + NS_ && p.kg == KG_ && p.wm == WM_ &&  \
       p.wn == WN_) {                                                                                \
@@ -560,6 +570,8 @@ hipError_t launch_gemm_swiglu(const GemmPlan& p, const void* A, const void* W_ga
                               const int32_t* n_active, int k_max, hipStream_t s) {
   if (M <= 0 || F <= 0) return hipSuccess;
   if (K % 64 != 0 || F % (p.bn / 2) != 0 || p.splits != 1) return hipErrorInvalidValue;
+  if (p.ilv && p.bm == 256 && p.bn == 192 && p.bk == 64 && p.pd == 12 && p.kg == 1 && p.wm == 4 && p.wn == 3)
+    return launch_lds<256, 192, 2, 2, 1, 4, 3, 8>(p, A, W_gate_up, nullptr, H, M, F, K, n_active, k_max, s);
 #define DLLM_LDS_CASE(BM_, BN_, NS_, KG_, WM_, WN_)                                                \
   if (p.bm == BM_ && p.bn == BN_ && p.bk == 64 && p.pd == 10 + NS_ && p.kg == KG_ && p.wm == WM_ &&  \
       p.wn == WN_ && !p.ilv) {                                                                      \
