@@ -367,8 +367,9 @@ __global__ __launch_bounds__(256) void k_gemm_f32(const float* __restrict__ A, c
 #define DLLM_LDS_CASES                                                                              \
   DLLM_LDS_CASE(128, 64, 4, 1, 2, 2) DLLM_LDS_CASE(128, 128, 2, 1, 2, 2) DLLM_LDS_CASE(128, 128, 3, 1, 2, 2) \
   DLLM_LDS_CASE(128, 256, 3, 1, 2, 4) DLLM_LDS_CASE(256, 256, 2, 1, 2, 4) DLLM_LDS_CASE(128, 128, 4, 2, 2, 2) \
-  DLLM_LDS_CASE(256, 128, 3, 1, 4, 2) DLLM_LDS_CASE(128, 192, 3, 1, 4, 2) \
-  DLLM_LDS_CASE(128, 64, 4, 1, 4, 2) DLLM_LDS_CASE(128, 128, 3, 1, 4, 2) DLLM_LDS_CASE(256, 256, 2, 1, 4, 4)
+  DLLM_LDS_CASE(128, 192, 3, 1, 4, 2) \
+  DLLM_LDS_CASE(128, 64, 4, 1, 4, 2) DLLM_LDS_CASE(128, 128, 3, 1, 4, 2) DLLM_LDS_CASE(256, 256, 2, 1, 4, 4) \
+  DLLM_LDS_CASE(256, 128, 3, 1, 4, 4)
 #define DLLM_LDS_SWIGLU_CASES                                                                       \
   DLLM_LDS_CASE(128, 128, 3, 1, 2, 2) DLLM_LDS_CASE(128, 128, 3, 2, 2, 2)
 
@@ -401,12 +402,11 @@ GemmPlan gemm_plan(int dtype, int M, int N, int K, bool swiglu) {
   // wavefronts when they fill the CUs two (four for SwiGLU) times over.  Many rows: 256-row
   // tiles where the shape allows (256 x 192 over 4 x 3 wavefronts, 8 of them loading, for the
   // fused SwiGLU product and QKV-like outputs: 6-9% faster than over 4 x 2 at 512 and 820
-  // rows; 256 x 128 over 4 x 2 with a 4- or 2-way K split for the down projection), otherwise
+  // rows; 256 x 128 over 4 x 4 with a 4- or 2-way K split for the down projection), otherwise
   // 128 x 128 with 2 stages, so that two workgroups share a CU, and split-K up to 4.  With rows
   // padded per sequence, dead rows fill more of a 256-row tile than of a 128-row one: a SwiGLU
-  // width that 96 does not
-  // divide takes interleaved 128 x 256 tiles (faster at every live share measured on
-  // Dream-7B's F = 18944 than 256 x 128 ones, which win only on fully live rows).
+  // width that 96 does not divide takes interleaved 128 x 256 tiles (faster at every live share
+  // measured on Dream-7B's F = 18944 than 256 x 128 ones, which win only on fully live rows).
   const bool few = M <= 192;
   const bool wide = N > 8192 && N <= 32768;
   p.bm = 128;
@@ -501,10 +501,11 @@ GemmPlan gemm_plan(int dtype, int M, int N, int K, bool swiglu) {
       target = 192;
     } else if (K >= 2 * N && N % 128 == 0 && K / (64 * 4) >= 3) {
       // long reductions into narrow outputs (the down projection): a 4-way K split, 2-way
-      // once the row tiles alone give three workgroups per CU
+      // once the row tiles alone give three workgroups per CU; 16 waves (64 x 32 wave tiles):
+      // 117.3-117.8 against 123.9-125.1 us over 4 x 2 at 820 rows, no slower at 512
       p.bm = 256;
       p.wm = 4;
-      p.wn = 2;
+      p.wn = 4;
       p.pd = 13;
       p.splits = ((long)((M + 255) / 256) * ((N + 127) / 128) >= 768) ? 2 : 4;
       return p;
