@@ -10,12 +10,14 @@
 // wavefronts (times KG k-groups) per tile, BK = 64, tiles streamed from memory
 // straight into a multi-stage LDS ring with 16-byte buffer loads to LDS (no
 // register staging), XOR-swizzled so MFMA fragment reads are conflict-free.
-// Most plans use eight wavefronts: these kernels are bound by the loads each CU
-// keeps in flight, and more waves issue more of them.  Split-K writes fp32
-// partials that the row epilogues reduce; row tiles with no live row exit at
-// once.
+// Plans use eight to sixteen wavefronts: these kernels are bound by the loads each
+// CU keeps in flight, and more waves issue more of them (LDS reads are not the
+// limit); when a tile's load instructions do not divide over all its waves, only
+// the first NL of them load.  Split-K writes fp32 partials that the row epilogues
+// reduce; row tiles with no live row exit at once.
 // Workgroup ids are remapped so that each XCD works on a contiguous range of
-// tiles, m-tile fastest, so tiles sharing a weight panel share that XCD's L2.
+// tiles, walked in groups of four row tiles, so the workgroups running together
+// on an XCD share both operands' k-slabs through its L2.
 //
 // fp32 path (small fp32 models): LDS-tiled FMA kernel, 64x64 tiles.
 #include "common.h"
