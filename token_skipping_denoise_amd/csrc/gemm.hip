@@ -389,6 +389,11 @@ __global__ __launch_bounds__(256) void k_gemm_f32(const float* __restrict__ A, c
 // against 112.4 and 216.7 against 233.5 us), so those keep their tiles.
 constexpr long kWideTileWgsSwiglu = 1024;  // four per CU
 constexpr long kWideTileWgs = 512;         // two per CU
+// share of the CU slots that a launch of `wgs` one-per-CU workgroups keeps busy over its rounds
+static double round_fill(long wgs) {
+  const long cus = 256;
+  return (double)wgs / (double)(((wgs + cus - 1) / cus) * cus);
+}
 GemmPlan gemm_plan(int dtype, int M, int N, int K, bool swiglu) {
   GemmPlan p{64, 64, 1, 64, 2};
   if (dtype == 0) {
@@ -485,13 +490,25 @@ GemmPlan gemm_plan(int dtype, int M, int N, int K, bool swiglu) {
       return p;
     }
     const int big_splits = (K >= 2 * N) ? 2 : 1;  // long reductions (down) in two K halves
-    if (N % 256 == 0 && (long)((M + 255) / 256) * (N / 256) * big_splits >= kWideTileWgs) {
+    const long row_tiles = (M + 255) / 256;
+    const long big_wgs = row_tiles * (N / 256) * big_splits;
+    if (N % 256 == 0 && big_wgs >= kWideTileWgs) {
       p.bm = 256;
       p.bn = 256;
       p.wm = 4;
       p.wn = 4;
       p.pd = 12;
       p.splits = big_splits;
+      // 192 columns over 4 x 3 waves when their workgroups fill the CUs' last round better:
+      // Dream-7B's QKV at 8192 rows, 768 workgroups (3 full rounds) against 576 (2.25 rounds),
+      // 270.6 against 324.9 us.  Down, the only split product here, took 256 x 128 tiles over
+      // 16 waves at 7 full rounds in 1148 us against 1068 on its 3.5 rounds of 256 x 256, so
+      // the rule does not reach it.
+      const long wgs192 = (big_splits == 1 && N % 192 == 0) ? row_tiles * (N / 192) : 0;
+      if (wgs192 > 0 && round_fill(wgs192) > round_fill(big_wgs)) {
+        p.bn = 192;
+        p.wn = 3;
+      }
       return p;
     }
     if (wide) {
