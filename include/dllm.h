@@ -141,6 +141,12 @@ typedef struct {
   const dllm_layer_w *layers;    /* host array [L] */
   const void *final_norm;        /* device [d] */
   const void *lm_head;           /* device [V, d] */
+  /* Optional second copy of lm_head in MFMA fragment order (dllm_pack_weight, no interleave), or
+   * NULL.  When present, the bf16 LM head over at most 128 computed rows streams it into
+   * registers (one K split: the vocabulary pass reads whole logits) whenever V is a multiple of
+   * 64 and d of 64; every other LM head product keeps the row-major copy.  Same logits up to the
+   * fp32 summation order. */
+  const void *lm_head_packed;
 } dllm_model;
 
 typedef struct {

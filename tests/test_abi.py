@@ -35,7 +35,7 @@ def test_every_declared_symbol_is_exported(lib):
 
 
 def test_version_and_status_strings(lib):
-    assert lib.dllm_version() == 201
+    assert lib.dllm_version() == 300
     assert lib.dllm_status_string(0) == b"ok"
     assert lib.dllm_status_string(4) == b"workspace missing or too small"
 
@@ -185,6 +185,26 @@ def test_noalloc_layer_rejects_oversize_before_any_launch(lib):
     assert lib.dllm_layer_sparse_noalloc(ctypes.byref(big), 0, F, F, F, 513, F, F, None) == 2   # k_max > S
     assert lib.dllm_layer_sparse_noalloc(ctypes.byref(big), 0, None, F, F, 128, F, F, None) == 1
     assert lib.dllm_layer_sparse_noalloc(None, 0, F, F, F, 128, F, F, None) == 1
+
+
+def test_misaligned_packed_weights_rejected(lib):
+    """Packed weight copies are read with 16-byte fragment loads: a model whose packed LM head or
+    packed layer weight is not 16-byte aligned fails validation (EINVAL) before the allocation-free
+    call reaches its scratch-size check (EWORKSPACE for this 512-row shape)."""
+    m, st, cfg, keep = _fake_step_args()
+    F = ctypes.c_void_p(0x1000)
+    big = _ffi.ModelC(_ffi.Dims(1, 512, 4096, 32, 32, 128, 12288, 126464, 2), 1, 1e4, 1e-5, 126463, 0x1000,
+                      m.layers, 0x1000, 0x1000)
+    call = lambda mod: lib.dllm_layer_sparse_noalloc(ctypes.byref(mod), 0, F, F, F, 512, F, F, None)
+    assert call(big) == 4
+    big.lm_head_packed = 0x2000
+    assert call(big) == 4
+    big.lm_head_packed = 0x2008
+    assert call(big) == 1
+    big.lm_head_packed = None
+    lw = (_ffi.LayerW * 2)(*[_ffi.LayerW(*([0x1000] * 6), None, None, 0x3004) for _ in range(2)])
+    big.layers = ctypes.cast(lw, ctypes.POINTER(_ffi.LayerW))
+    assert call(big) == 1
 
 
 def test_checking_build_exports_the_same_entry_points(lib):

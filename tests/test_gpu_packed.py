@@ -3,7 +3,9 @@
 The packed layout is checked element by element against its definition (an index map built
 here with torch); layers whose four products use the packed copies are checked against the same
 layers on the row-major copies (LLaDA-8B and Dream-7B shapes) and against the oracle (a
-Dream-shaped layer here; the full-size LLaDA layer in test_gpu_fullsize.py).
+Dream-shaped layer here; the full-size LLaDA layer in test_gpu_fullsize.py).  The packed LM head
+of a sparse step is checked against the row-major one here and against the oracle by the
+full-size stack tests of test_gpu_fullsize.py.
 """
 import numpy as np
 import pytest
@@ -129,3 +131,44 @@ def test_packed_dream_layer_128_rows_oracle():
     print(f"dream layer 128 rows packed vs oracle plans={plans}", flush=True)
     assert all(p is not None for p in plans.values())
     _sampled_layer_case(dims, [64, 61], n_sample=8, seed=66)
+
+
+@pytest.mark.parametrize("shape", ["llada", "dream"])
+def test_packed_lm_head_matches_row_major(shape):
+    """The LM head over the computed rows of a sparse step (at most 128) streams the packed copy
+    (128-column tiles, one K split); over the 512 or 2048 rows of a full step it keeps the
+    row-major tiles.  Two-layer models at the LLaDA-8B (V 126464, d 4096; 1 sequence, k = 128) and
+    Dream-7B (V 152064, d 3584; 2 sequences, k = 64) shapes, a full step then a sparse step with
+    the boundary after layer 1, with and without the packed LM head: both kernels sum every logit
+    in one fp32 MFMA chain over K in the same order, so confidence, argmax, KL and the unmasked
+    tokens agree bit for bit."""
+    if shape == "llada":
+        dims, k = workloads.shrink(workloads.LLADA, n_layers=2), 128
+    else:
+        dims, k = workloads.shrink(workloads.DREAM, n_layers=2, B=2), 64
+    B, S = dims.B, dims.S
+    plan = api.packed_plan(B * k, dims.vocab, dims.d)
+    print(f"packed lm head {shape} rows={B * k} plan={plan}", flush=True)
+    assert plan is not None
+    w = workloads.model_weights(dims, device=DEV)
+    m_pk = api.Model(w, dims.n_heads, dims.n_kv_heads, dims.mask_id)
+    assert m_pk.lm_head_packed is not None
+    m_rm = api.Model(w, dims.n_heads, dims.n_kv_heads, dims.mask_id)
+    m_rm.lm_head_packed = None
+    m_rm.c.lm_head_packed = None
+    tok = workloads.initial_tokens(dims, device=DEV)
+    lo, hi = dims.prompt, dims.prompt + 32
+    outs = []
+    for m in (m_pk, m_rm):
+        st = api.State(m, tok.clone(), k_max=k, track_kl=True)
+        ws = api.alloc_workspace(m, B, S, k)
+        api.skip_step(m, st, api.step_cfg(1, True, unmask_n=4, block_lo=lo, block_hi=hi, ws=ws))
+        sc = api.score_cfg(alpha=0.5, var=api.VAR_L1N, sel=api.SEL_TOPK, k=k)
+        api.skip_step(m, st, api.step_cfg(1, False, sc, unmask_n=4, block_lo=lo, block_hi=hi, ws=ws))
+        torch.cuda.synchronize()
+        outs.append(st)
+    a, b = outs
+    assert torch.equal(a.n_active, b.n_active) and torch.equal(a.idx, b.idx)
+    assert torch.equal(a.conf, b.conf) and torch.equal(a.argmax, b.argmax)
+    assert torch.equal(a.kl, b.kl)
+    assert torch.equal(a.tokens, b.tokens)

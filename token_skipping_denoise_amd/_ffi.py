@@ -37,7 +37,7 @@ class LayerW(Structure):
 class ModelC(Structure):
     _fields_ = [("dims", Dims), ("dtype", c_int32), ("rope_base", c_float), ("rms_eps", c_float),
                 ("mask_id", c_int32), ("embed", c_void_p), ("layers", POINTER(LayerW)),
-                ("final_norm", c_void_p), ("lm_head", c_void_p)]
+                ("final_norm", c_void_p), ("lm_head", c_void_p), ("lm_head_packed", c_void_p)]
 
 
 class ScoreCfg(Structure):

@@ -146,7 +146,8 @@ class Model:
     here into the fused row layout the library expects.  With ``pack`` (bf16
     only) the QKV, gate/up and down weights are also stored in MFMA fragment
     order (dllm_pack_weight), which the library streams for the active-row
-    products (at most 128 rows) those copies fit.
+    products (at most 128 rows) those copies fit; so is the LM head when the
+    vocabulary is a multiple of 64.
     """
 
     def __init__(self, weights: dict, n_heads: int, n_kv_heads: int, mask_id: int, rope_base=1e4, rms_eps=1e-5,
@@ -177,6 +178,9 @@ class Model:
                 t["w_gate_up_packed"] = pack_weight(t["w_gate_up"], interleave_f=F)
                 t["w_down_packed"] = pack_weight(t["w_down"])
                 t["w_qkv_packed"] = pack_weight(t["w_qkv"])
+        self.lm_head_packed = None
+        if pack and emb.dtype == torch.bfloat16 and V % 64 == 0 and d % 64 == 0:
+            self.lm_head_packed = pack_weight(self.lm_head)
         self._lw = (_ffi.LayerW * L)()
         names = ("attn_norm", "w_qkv", "w_o", "ffn_norm", "w_gate_up", "w_down", "w_gate_up_packed", "w_down_packed",
                  "w_qkv_packed")
@@ -193,6 +197,7 @@ class Model:
         self.c.layers = ctypes.cast(self._lw, ctypes.POINTER(_ffi.LayerW))
         self.c.final_norm = _ptr(self.final_norm)
         self.c.lm_head = _ptr(self.lm_head)
+        self.c.lm_head_packed = _ptr(self.lm_head_packed)
 
     def dims(self, B: int, S: int) -> _ffi.Dims:
         V, d, Hq, Hkv, D, F, L = self.dims_tuple

@@ -288,11 +288,14 @@ int check_model(const dllm_model* m) {
   int st = check_dims(&m->dims, m->dtype);
   if (st) return st;
   if (!m->embed || !m->layers || !m->final_norm || !m->lm_head) return DLLM_EINVAL;
+  if (m->lm_head_packed && !aligned16(m->lm_head_packed)) return DLLM_EINVAL;  // 16-byte fragment loads
   if (m->mask_id < -1 || m->mask_id >= m->dims.vocab) return DLLM_EINVAL;
   if (!(m->rope_base > 0.f) || !(m->rms_eps >= 0.f)) return DLLM_EINVAL;
   for (int l = 0; l < m->dims.n_layers; ++l) {
     const dllm_layer_w& w = m->layers[l];
     if (!w.attn_norm || !w.w_qkv || !w.w_o || !w.ffn_norm || !w.w_gate_up || !w.w_down) return DLLM_EINVAL;
+    for (const void* pk : {w.w_gate_up_packed, w.w_down_packed, w.w_qkv_packed})
+      if (pk && !aligned16(pk)) return DLLM_EINVAL;
   }
   return DLLM_OK;
 }
@@ -370,7 +373,7 @@ int check_layer_args(const dllm_model* model, int32_t layer, const void* x_act, 
 
 extern "C" {
 
-int dllm_version(void) { return 201; }
+int dllm_version(void) { return 300; }
 
 int dllm_peak_probe(int32_t kind, void* buf, size_t bytes, int32_t iters, double* work, void* stream) {
   if (!buf || !work || iters < 1) return DLLM_EINVAL;
@@ -813,10 +816,13 @@ int dllm_skip_step(const dllm_model* model, dllm_state* state, const dllm_step_c
   float* logits = c.at<float>(c.L.logits);
   GemmPlan p = gemm_plan(c.dtype, R, d.vocab, d.d);
   p.splits = 1;
+  const PackedPlan pp =
+      (c.dtype == DLLM_BF16 && model->lm_head_packed) ? packed_plan_whole(R, d.vocab, d.d) : PackedPlan{};
   {
     TimedRegion t(c.timing, DLLM_TK_LM_HEAD, R, c.s);
     DLLM_TRY(t.err);
-    DLLM_TRY(launch_gemm(c.dtype, p, xn, model->lm_head, logits, R, d.vocab, d.d, nact, kk, c.s));
+    if (pp.ok) DLLM_TRY(launch_gemm_packed(pp, xn, model->lm_head_packed, logits, nullptr, R, d.vocab, d.d, 0, nact, kk, c.s));
+    else DLLM_TRY(launch_gemm(c.dtype, p, xn, model->lm_head, logits, R, d.vocab, d.d, nact, kk, c.s));
     DLLM_TRY(t.stop());
   }
   {

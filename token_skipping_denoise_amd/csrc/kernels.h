@@ -73,6 +73,8 @@ struct PackedPlan {
 };
 // Whether (and how) the packed path covers an M x N x K product (M <= 128).
 PackedPlan packed_plan(int M, int N, int K, bool swiglu);
+// The same for a product whose consumer needs whole sums in C (no K split): the LM head.
+PackedPlan packed_plan_whole(int M, int N, int K);
 // swiglu (H non-null): H[m][f] = silu(A Wg^T) * (A Wu^T), N = 2F packed columns; else fp32 partials
 // C[sp][m][n].
 hipError_t launch_gemm_packed(const PackedPlan& p, const void* A, const void* Wp, float* C, void* H, int M, int N,
