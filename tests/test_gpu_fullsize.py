@@ -177,6 +177,16 @@ def test_long_context_layer_full_size_sampled():
     _sampled_layer_case(dims, [205, 205, 205, 205], n_sample=8, seed=55)
 
 
+def test_long_context_refresh_layer_sampled():
+    """Long-context LLaDA layer over (nearly) every row, B 4 x S 4096, the refresh steps' shape:
+    4 x 4095 = 16380 tiled rows (ragged per sequence, the last row tile 252 rows deep) take the
+    register-staged 256 x 256 tiles in the QKV (12288 outputs), gate/up + SwiGLU and split-K down
+    products; every fresh K/V row and sampled outputs against the oracle."""
+    dims = workloads.shrink(workloads.LLADA_LONG, n_layers=1)
+    print("long-context refresh layer (sampled)", flush=True)
+    _sampled_layer_case(dims, [4090, 4001, 4095, 4095], n_sample=8, seed=57)
+
+
 def test_llada_generation_step_properties_full_size():
     """The 32-layer stack at bench shapes: an all-rows-active sparse step reproduces a full step bit
     for bit, and a k = 128 sparse step leaves skipped cache rows untouched and picks valid tokens."""

@@ -20,6 +20,8 @@
 // on an XCD share both operands' k-slabs through its L2.
 //
 // fp32 path (small fp32 models): LDS-tiled FMA kernel, 64x64 tiles.
+#include <type_traits>
+
 #include "common.h"
 #include "kernels.h"
 
@@ -320,6 +322,199 @@ __global__ __launch_bounds__(64 * WM * WN * KG, OCC) void k_gemm_lds(const uint1
   }
 }
 
+// Thousands of rows, register-staged: 256 x 256 tiles over four wavefronts (2 x 2, one per SIMD,
+// 128 x 128 wave tiles whose 256 accumulators per lane sit in the AGPRs).  The direct-to-LDS
+// kernel above keeps one 64-element K stage in flight beside the one being multiplied (two
+// 64 KB stages fill most of the LDS); here the stage loads go to registers first, in two
+// register sets (each wave loads a quarter of a stage: 8 rows of A and 8 of W, 16 B per lane
+// each), so two stages (128 KB per CU) are in flight while one is multiplied from a two-slot LDS
+// ring.  With one wave per SIMD nothing else covers a wave's own waits, so every k-step issues
+// its 16 MFMAs one at a time with the other work between them: the 8 LDS fragment reads of the
+// next k-step, 4 LDS writes of the next stage's register set and 4 loads that refill the written
+// registers with the stage after it.  The LDS layout, fragment reads, k order and epilogues
+// (EPI 0: fp32 partials; EPI 2: SwiGLU over gate/up rows interleaved in 16s) are those of
+// k_gemm_lds, so both kernels give bit-identical results.
+// Measured against the 16-wave kernel on the same inputs, launches alternated, median of 25:
+// Dream-7B at 8192 rows down (2 splits) 992 -> 928 us and O 226 -> 212 us (against its
+// 128 x 128 plan); LLaDA-8B at 16384 rows QKV 1360 -> 1294, O 492 -> 453, down 1372 -> 1318 us
+// and the LM head 13.89 -> 13.21 ms; the fused SwiGLU product the same either way alone (1810
+// against 1817 us at 8192 rows) but faster inside whole runs.  At 512 and 820 rows, with a few
+// hundred workgroups, this kernel is slower.
+template <int EPI>
+__global__ __launch_bounds__(256, 1) void k_gemm_vr(const uint16_t* __restrict__ A, const uint16_t* __restrict__ W,
+                                                    float* __restrict__ C, uint16_t* __restrict__ H, int M, int N, int K,
+                                                    int splits, int tiles_m, int tiles_n,
+                                                    const int32_t* __restrict__ n_active, int k_max) {
+  constexpr int BM = 256, BN = 256, BK = 64, TM = 4, TN = 4;
+  constexpr int STAGE = (BM + BN) * BK;  // elements per ring slot
+  typedef unsigned u32x4_t __attribute__((ext_vector_type(4)));
+  __shared__ __attribute__((aligned(1024))) uint16_t smem[2 * STAGE];  // 128 KB
+
+  int tmi, tni, sp;
+  decode_tile(tiles_m * tiles_n * splits, tiles_m, tiles_n, tmi, tni, sp);
+  const int m0 = tmi * BM;
+  if (!tile_live(m0, BM, M, n_active, k_max)) return;
+  const int nkb = K / BK;
+  const int kb0 = (int)((long)sp * nkb / splits), kb1 = (int)((long)(sp + 1) * nkb / splits);
+  const int nk = kb1 - kb0;
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int wm = wave >> 1, wn = wave & 1;
+
+  const int F = N;  // SwiGLU: N is the number of outputs F; W holds 2F rows
+  const int h0 = tni * (BN / 2);
+  const int w_rows = (EPI == 0) ? N : 2 * F;
+  const int wr0 = (EPI == 0) ? tni * BN : h0;
+  // The last row tile is moved up to end at row M (the launcher ensures M >= 256): it multiplies
+  // rows a0 .. a0 + 255 and stores only those from m0 on, so every load stays inside A.  Weight
+  // rows never pass the end (N a multiple of 256, or F of 128 for SwiGLU).
+  const int a0 = min(m0, M - BM);
+  const uint16_t* a_base = A + (long)a0 * K;
+  const uint16_t* w_base = W + (long)wr0 * K;
+  const __amdgpu_buffer_rsrc_t ra = __builtin_amdgcn_make_buffer_rsrc((void*)a_base, (short)0, BM * K * 2, 0x00020000);
+  const __amdgpu_buffer_rsrc_t rw = __builtin_amdgcn_make_buffer_rsrc(
+      (void*)w_base, (short)0, (int)min((long)(w_rows - wr0) * K * 2, 0x7fffffffL), 0x00020000);
+  // this lane's loads: chunk c of tile rows rb + 32 i (i < 8) of both operands.  The lane's part
+  // of the byte offset is one VGPR per operand; the row step and k go in the scalar offset.
+  const int c = tid & 7, rb = tid >> 3;
+  // weight row of tile row rb + 32 i: wb0 + i * wstep (SwiGLU: 16 gate rows, then the 16 matching
+  // up rows, per 32-row block)
+  const int wb0 = (EPI == 0) ? tni * BN + rb : ((rb & 16) ? F : 0) + h0 + (rb & 15);
+  constexpr int wstep = (EPI == 0) ? 32 : 16;
+  const int va = (rb * K + c * 8) * 2, vw = ((wb0 - wr0) * K + c * 8) * 2;
+  // LDS byte address of this lane's chunk in row rb of a slot; rows rb + 32 i share the swizzle
+  const uint32_t wr_lds = (uint32_t)(rb * BK * 2 + ((c ^ ((rb >> 1) & 7)) << 4));
+
+  u32x4_t R0[16], R1[16];  // register sets: stage s lives in set s & 1 (8 A chunks, then 8 W chunks)
+  // chunk q of a set: A rows rb + 32 q (q < 8), W rows wb0 + wstep (q - 8)
+  auto load_one = [&](u32x4_t* R, int q, int kb) {
+    const int kbytes = kb * BK * 2;
+    if (q < 8) R[q] = __builtin_amdgcn_raw_buffer_load_b128(ra, va, q * 32 * K * 2 + kbytes, 0);
+    else R[q] = __builtin_amdgcn_raw_buffer_load_b128(rw, vw, (q - 8) * wstep * K * 2 + kbytes, 0);
+  };
+  auto write_one = [&](const u32x4_t* R, int q, int slot) {
+    uint8_t* base = reinterpret_cast<uint8_t*>(smem + slot * STAGE) + wr_lds;
+    const int row = (q < 8) ? q * 32 : BM + (q - 8) * 32;
+    *reinterpret_cast<u32x4_t*>(base + row * BK * 2) = R[q];
+  };
+
+  f32x16_t acc[TM][TN];
+#pragma unroll
+  for (int i = 0; i < TM; ++i)
+#pragma unroll
+    for (int j = 0; j < TN; ++j)
+#pragma unroll
+      for (int e = 0; e < 16; ++e) acc[i][j][e] = 0.f;
+
+  const int swz = (lane >> 1) & 7, hi = lane >> 5, r32 = lane & 31;
+  // fragment f < 4: A row block f; f >= 4: W column block f - 4
+  auto frag_addr = [&](const uint16_t* base, int ks, int f) {
+    const int slot = ((ks * 2 + hi) ^ swz) * 8;
+    return (f < 4) ? base + (wm * (BM / 2) + f * 32 + r32) * BK + slot
+                   : base + BM * BK + (wn * (BN / 2) + (f - 4) * 32 + r32) * BK + slot;
+  };
+  bf16x8_t fr[2][8];  // k-step fragments, double-buffered: k-step ks of a stage in fr[ks & 1]
+  // Iteration t multiplies stage t (slot t & 1).  During its first three k-steps it writes stage
+  // t + 1 from set Rn into slot (t + 1) & 1 -- last read before the barrier of iteration t - 1 --
+  // chunk by chunk, refilling each written register with stage t + 3 right after.  Loads complete
+  // in order, and before the write of chunk q exactly 31 of this wave's loads were issued after
+  // the one it needs (Rn's chunks after q, the other set's 16 and the q refills made since), so
+  // every wait is vmcnt(31).  The barrier comes before the last k-step: by then every wave's
+  // writes of stage t + 1 have landed and its reads of slot t & 1 are done (the last k-step's
+  // fragments were read during the one before), so the last k-step's MFMAs cover the reads of
+  // stage t + 1's first fragments.  Past the last stage the refill reads the last stage again and
+  // the writes fill a slot nothing multiplies any more, so every iteration is the same code.
+  auto iteration = [&](int t, u32x4_t* Rn) {
+    const uint16_t* base = smem + (t & 1) * STAGE;
+    const uint16_t* nbase = smem + ((t + 1) & 1) * STAGE;
+    const int kb_refill = kb0 + min(t + 3, nk - 1);
+#pragma unroll
+    for (int ks = 0; ks < BK / 16; ++ks) {
+      if (ks == BK / 16 - 1) {
+        __builtin_amdgcn_s_waitcnt(0xc07f);  // lgkmcnt(0)
+        __builtin_amdgcn_s_barrier();
+        __builtin_amdgcn_sched_barrier(0);
+      }
+      // chunks written in this k-step: 0-5, 6-10, 11-15 over the first three
+      const int q0 = (ks == 0) ? 0 : (ks == 1) ? 6 : 11;
+      const int nq = (ks == 0) ? 6 : (ks == 1 || ks == 2) ? 5 : 0;
+#pragma unroll
+      for (int m = 0; m < 16; ++m) {
+        const int i = m >> 2, j = m & 3;
+        acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(fr[ks & 1][i], fr[ks & 1][4 + j], acc[i][j], 0, 0, 0);
+        if ((m & 1) == 0) {  // the next k-step's fragments (the next stage's first after the last)
+          if (ks + 1 < BK / 16)
+            fr[(ks + 1) & 1][m >> 1] = *reinterpret_cast<const bf16x8_t*>(frag_addr(base, ks + 1, m >> 1));
+          else
+            fr[0][m >> 1] = *reinterpret_cast<const bf16x8_t*>(frag_addr(nbase, 0, m >> 1));
+        } else if ((m >> 1) < nq) {  // one chunk written, then its register refilled
+          const int q = q0 + (m >> 1);
+          wait_vm<31>();
+          write_one(Rn, q, (t + 1) & 1);
+          load_one(Rn, q, kb_refill);
+        }
+        __builtin_amdgcn_sched_barrier(0);
+      }
+    }
+  };
+
+  // prologue (nk >= 3, the launcher's condition): stages 0 and 1 in flight, stage 0 into slot 0,
+  // stage 2 into the freed set, then stage 0's first fragments
+#pragma unroll
+  for (int q = 0; q < 16; ++q) load_one(R0, q, kb0);
+#pragma unroll
+  for (int q = 0; q < 16; ++q) load_one(R1, q, kb0 + 1);
+  wait_vm<16>();
+#pragma unroll
+  for (int q = 0; q < 16; ++q) write_one(R0, q, 0);
+  __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+  for (int q = 0; q < 16; ++q) load_one(R0, q, kb0 + 2);
+  __builtin_amdgcn_s_waitcnt(0xc07f);
+  __builtin_amdgcn_s_barrier();
+#pragma unroll
+  for (int f = 0; f < 8; ++f) fr[0][f] = *reinterpret_cast<const bf16x8_t*>(frag_addr(smem, 0, f));
+  int t = 0;
+  for (; t + 1 < nk; t += 2) {  // stage t + 1 is in set 1, stage t + 2 in set 0
+    iteration(t, R1);
+    iteration(t + 1, R0);
+  }
+  if (t < nk) iteration(t, R1);  // an odd stage count: the last stage
+  wait_vm<0>();                   // no load is left in flight at the end
+  __builtin_amdgcn_s_waitcnt(0xc07f);
+
+  if (EPI == 0) {
+    float* Cs = C + (long)sp * M * N;
+    const int n0 = tni * BN;
+#pragma unroll
+    for (int i = 0; i < TM; ++i)
+#pragma unroll
+      for (int j = 0; j < TN; ++j) {
+        const int col = n0 + wn * (BN / 2) + j * 32 + r32;
+#pragma unroll
+        for (int e = 0; e < 16; ++e) {
+          const int row = a0 + wm * (BM / 2) + i * 32 + 8 * (e >> 2) + 4 * hi + (e & 3);
+          if (row >= m0) Cs[(long)row * N + col] = acc[i][j][e];
+        }
+      }
+  } else {
+    // lane t < 16 of a column block holds gate output t, lane t + 16 the matching up value
+#pragma unroll
+    for (int i = 0; i < TM; ++i)
+#pragma unroll
+      for (int j = 0; j < TN; ++j) {
+        const int col = h0 + ((wn * (BN / 2) + j * 32) >> 1) + (lane & 15);
+#pragma unroll
+        for (int e = 0; e < 16; ++e) {
+          const float v = acc[i][j][e];
+          const float u = __shfl_xor(v, 16, kWave);
+          const int row = a0 + wm * (BM / 2) + i * 32 + 8 * (e >> 2) + 4 * hi + (e & 3);
+          if ((lane & 16) == 0 && row >= m0) H[(long)row * F + col] = f2bf(silu_fast(v) * u);
+        }
+      }
+  }
+}
+
 // fp32: 64x64 tile, BK 16, 256 threads x (4x4) outputs.
 __global__ __launch_bounds__(256) void k_gemm_f32(const float* __restrict__ A, const float* __restrict__ W,
                                                   float* __restrict__ C, int M, int N, int K, int splits, int tiles_m,
@@ -388,6 +583,10 @@ __global__ __launch_bounds__(256) void k_gemm_f32(const float* __restrict__ A, c
 // at 512 and 820 rows, with one or two such workgroups per CU, they were slower (gate/up 102.7
 // against 112.4 and 216.7 against 233.5 us), so those keep their tiles.
 constexpr long kWideTileWgsSwiglu = 1024;  // four per CU
+// The register-staged kernel (k_gemm_vr) from this many rows on: at 512 and 820 rows, with a few
+// hundred such workgroups, it measured slower than the direct-to-LDS plans (QKV 113.4 against
+// 101.4 us at 820 rows, launches alternated).
+constexpr int kVrRows = 2048;
 constexpr long kWideTileWgs = 512;         // two per CU
 // share of the CU slots that a launch of `wgs` one-per-CU workgroups keeps busy over its rounds
 static double round_fill(long wgs) {
@@ -463,13 +662,17 @@ GemmPlan gemm_plan(int dtype, int M, int N, int K, bool swiglu) {
     // bound these tiles)
     if (swiglu) {
       if (N % 128 == 0 && (long)((M + 255) / 256) * (N / 128) >= kWideTileWgsSwiglu) {
-        // 128 outputs (256 interleaved gate/up rows) per tile
+        // 128 outputs (256 interleaved gate/up rows) per tile; from thousands of rows on through
+        // registers over four waves (k_gemm_vr): alone no faster than the 16-wave kernel (1817
+        // against 1810 us at 8192 rows of Dream-7B), but the whole Dream-7B lock-ramp run went
+        // from 332.1-332.5 to 338.9-339.4 tokens/s with it (same box, runs alternated)
         p.bm = 256;
         p.bn = 256;
         p.wm = 4;
         p.wn = 4;
         p.pd = 12;
         p.ilv = 1;
+        p.vr = M >= kVrRows;
       } else if (N % 96 == 0) {  // 96 outputs (192 interleaved gate/up rows) per tile
         p.bm = 256;
         p.bn = 192;
@@ -492,7 +695,10 @@ GemmPlan gemm_plan(int dtype, int M, int N, int K, bool swiglu) {
     const int big_splits = (K >= 2 * N) ? 2 : 1;  // long reductions (down) in two K halves
     const long row_tiles = (M + 255) / 256;
     const long big_wgs = row_tiles * (N / 256) * big_splits;
-    if (N % 256 == 0 && big_wgs >= kWideTileWgs) {
+    // thousands of rows: the register-staged kernel also where its tiles give 1.5 rounds or more
+    // (Dream-7B's O at 8192 rows, 448 workgroups: 212 against 226 us on 128 x 128 tiles)
+    const bool vr_rows = M >= kVrRows;
+    if (N % 256 == 0 && (big_wgs >= kWideTileWgs || (vr_rows && big_wgs >= 384))) {
       p.bm = 256;
       p.bn = 256;
       p.wm = 4;
@@ -505,10 +711,14 @@ GemmPlan gemm_plan(int dtype, int M, int N, int K, bool swiglu) {
       // 16 waves at 7 full rounds in 1148 us against 1068 on its 3.5 rounds of 256 x 256, so
       // the rule does not reach it.
       const long wgs192 = (big_splits == 1 && N % 192 == 0) ? row_tiles * (N / 192) : 0;
-      if (wgs192 > 0 && round_fill(wgs192) > round_fill(big_wgs)) {
+      if (big_wgs >= kWideTileWgs && wgs192 > 0 && round_fill(wgs192) > round_fill(big_wgs)) {
         p.bn = 192;
         p.wn = 3;
+        return p;
       }
+      // from thousands of rows on, through registers over four waves (k_gemm_vr): 4-8% faster
+      // than the 16-wave kernel on every such product measured
+      p.vr = vr_rows ? 1 : 0;
       return p;
     }
     if (wide) {
@@ -562,6 +772,23 @@ static hipError_t launch_lds(const GemmPlan& p, const void* A, const void* W, fl
   return hipGetLastError();
 }
 
+template <int EPI>
+static hipError_t launch_vr(const GemmPlan& p, const void* A, const void* W, float* C, void* H, int M, int N, int K,
+                            const int32_t* n_active, int k_max, hipStream_t s) {
+  // 32-bit buffer offsets within one tile: 256 rows of A, and 256 weight rows (plain) or the
+  // gate..up span F + 128 rows (SwiGLU); every split fills the three-stage prologue; whole row
+  // tiles of loads (the last one moved up), whole weight tiles
+  const long w_span = EPI == 0 ? 256 : (long)N + 128;
+  if (256L * K * 2 > 0x7fffffffL || w_span * K * 2 > 0x7fffffffL || K / 64 / p.splits < 3 || M < 256 ||
+      (EPI == 0 && N % 256) || (EPI != 0 && N % 128))
+    return hipErrorInvalidValue;
+  const int ncols = EPI == 0 ? 256 : 128;
+  const int tm = (M + 255) / 256, tn = N / ncols;
+  hipLaunchKernelGGL((k_gemm_vr<EPI>), dim3(tm * tn * p.splits), dim3(256), 0, s, (const uint16_t*)A,
+                     (const uint16_t*)W, C, (uint16_t*)H, M, N, K, p.splits, tm, tn, n_active, k_max);
+  return hipGetLastError();
+}
+
 hipError_t launch_gemm(int dtype, const GemmPlan& p, const void* A, const void* W, float* C, int M, int N, int K,
                        const int32_t* n_active, int k_max, hipStream_t s) {
   if (M <= 0 || N <= 0) return hipSuccess;
@@ -572,6 +799,10 @@ hipError_t launch_gemm(int dtype, const GemmPlan& p, const void* A, const void* 
     return hipGetLastError();
   }
   if (K % 64 != 0) return hipErrorInvalidValue;
+  if (p.vr) {
+    if (p.bm != 256 || p.bn != 256 || p.bk != 64 || p.ilv) return hipErrorInvalidValue;
+    return launch_vr<0>(p, A, W, C, nullptr, M, N, K, n_active, k_max, s);
+  }
   // 256 x 192 over 4 x 3 wavefronts: the first 8 issue the tile loads (12 would not divide them)
   if (p.bm == 256 && p.bn == 192 && p.bk == 64 && p.pd == 12 && p.kg == 1 && p.wm == 4 && p.wn == 3)
     return launch_lds<256, 192, 2, 0, 1, 4, 3, 8>(p, A, W, C, nullptr, M, N, K, n_active, k_max, s);
@@ -590,6 +821,10 @@ hipError_t launch_gemm_swiglu(const GemmPlan& p, const void* A, const void* W_ga
                               const int32_t* n_active, int k_max, hipStream_t s) {
   if (M <= 0 || F <= 0) return hipSuccess;
   if (K % 64 != 0 || F % (p.bn / 2) != 0 || p.splits != 1) return hipErrorInvalidValue;
+  if (p.vr) {
+    if (p.bm != 256 || p.bn != 256 || p.bk != 64 || !p.ilv) return hipErrorInvalidValue;
+    return launch_vr<2>(p, A, W_gate_up, nullptr, H, M, F, K, n_active, k_max, s);
+  }
   if (p.ilv && p.bm == 256 && p.bn == 192 && p.bk == 64 && p.pd == 12 && p.kg == 1 && p.wm == 4 && p.wn == 3)
     return launch_lds<256, 192, 2, 2, 1, 4, 3, 8>(p, A, W_gate_up, nullptr, H, M, F, K, n_active, k_max, s);
 #define DLLM_LDS_CASE(BM_, BN_, NS_, KG_, WM_, WN_)                                                \

@@ -53,6 +53,7 @@ struct GemmPlan {
   int kg = 1;                  // k-groups of wavefronts per workgroup (bf16)
   int wm = 2, wn = 2;          // wavefronts along the tile's rows and columns (bf16)
   int ilv = 0;                 // SwiGLU: gate/up rows interleaved in 16s inside each 32-row block
+  int vr = 0;                  // 256 x 256 tiles through registers over four waves (k_gemm_vr)
 };
 GemmPlan gemm_plan(int dtype, int M, int N, int K, bool swiglu = false);
 hipError_t launch_gemm(int dtype, const GemmPlan& p, const void* A, const void* W, float* C, int M, int N, int K,
