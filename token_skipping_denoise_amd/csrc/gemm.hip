@@ -331,21 +331,31 @@ __global__ __launch_bounds__(64 * WM * WN * KG, OCC) void k_gemm_lds(const uint1
 // ring.  With one wave per SIMD nothing else covers a wave's own waits, so every k-step issues
 // its 16 MFMAs one at a time with the other work between them: the 8 LDS fragment reads of the
 // next k-step, 4 LDS writes of the next stage's register set and 4 loads that refill the written
-// registers with the stage after it.  The LDS layout, fragment reads, k order and epilogues
+// registers with the stage after it.  Tiles of 256 x 256 serve thousands of rows; 256 x 192 (three
+// column blocks per wave) the plans of that width from 512 rows on.  The LDS layout, fragment
+// reads, k order and epilogues
 // (EPI 0: fp32 partials; EPI 2: SwiGLU over gate/up rows interleaved in 16s) are those of
 // k_gemm_lds, so both kernels give bit-identical results.
 // Measured against the 16-wave kernel on the same inputs, launches alternated, median of 25:
 // Dream-7B at 8192 rows down (2 splits) 992 -> 928 us and O 226 -> 212 us (against its
 // 128 x 128 plan); LLaDA-8B at 16384 rows QKV 1360 -> 1294, O 492 -> 453, down 1372 -> 1318 us
 // and the LM head 13.89 -> 13.21 ms; the fused SwiGLU product the same either way alone (1810
-// against 1817 us at 8192 rows) but faster inside whole runs.  At 512 and 820 rows, with a few
-// hundred workgroups, this kernel is slower.
-template <int EPI>
+// against 1817 us at 8192 rows) but faster inside whole runs.  256 x 192 tiles against the
+// 12-wave direct-to-LDS kernel: QKV 57.2 -> 55.0 us at 512 rows, 105.7 -> 100.9 at 820, 282.5 ->
+// 269.6 at 8192 (Dream-7B); gate/up + SwiGLU 115.5 -> 111.4 at 512, 213.1 -> 210.7 at 820.  At
+// 512 and 820 rows 256 x 256 tiles leave too many CUs idle and are slower.
+// BN = 192 (three column blocks per wave, 14 chunks per register set) serves the 256 x 192 plans.
+template <int EPI, int BN>
 __global__ __launch_bounds__(256, 1) void k_gemm_vr(const uint16_t* __restrict__ A, const uint16_t* __restrict__ W,
                                                     float* __restrict__ C, uint16_t* __restrict__ H, int M, int N, int K,
                                                     int splits, int tiles_m, int tiles_n,
                                                     const int32_t* __restrict__ n_active, int k_max) {
-  constexpr int BM = 256, BN = 256, BK = 64, TM = 4, TN = 4;
+  constexpr int BM = 256, BK = 64, TM = 4, TN = BN / 64;
+  constexpr int NB = BN / 32;  // W chunks per lane and stage
+  constexpr int NQ = 8 + NB;   // chunks per register set
+  constexpr int NF = 4 + TN;   // fragments per k-step
+  constexpr int NM = TM * TN;  // MFMAs per k-step
+  static_assert(BN == 256 || BN == 192, "256- or 192-column tiles");
   constexpr int STAGE = (BM + BN) * BK;  // elements per ring slot
   typedef unsigned u32x4_t __attribute__((ext_vector_type(4)));
   __shared__ __attribute__((aligned(1024))) uint16_t smem[2 * STAGE];  // 128 KB
@@ -385,7 +395,7 @@ __global__ __launch_bounds__(256, 1) void k_gemm_vr(const uint16_t* __restrict__
   // LDS byte address of this lane's chunk in row rb of a slot; rows rb + 32 i share the swizzle
   const uint32_t wr_lds = (uint32_t)(rb * BK * 2 + ((c ^ ((rb >> 1) & 7)) << 4));
 
-  u32x4_t R0[16], R1[16];  // register sets: stage s lives in set s & 1 (8 A chunks, then 8 W chunks)
+  u32x4_t R0[NQ], R1[NQ];  // register sets: stage s lives in set s & 1 (8 A chunks, then NB W chunks)
   // chunk q of a set: A rows rb + 32 q (q < 8), W rows wb0 + wstep (q - 8)
   auto load_one = [&](u32x4_t* R, int q, int kb) {
     const int kbytes = kb * BK * 2;
@@ -413,13 +423,13 @@ __global__ __launch_bounds__(256, 1) void k_gemm_vr(const uint16_t* __restrict__
     return (f < 4) ? base + (wm * (BM / 2) + f * 32 + r32) * BK + slot
                    : base + BM * BK + (wn * (BN / 2) + (f - 4) * 32 + r32) * BK + slot;
   };
-  bf16x8_t fr[2][8];  // k-step fragments, double-buffered: k-step ks of a stage in fr[ks & 1]
+  bf16x8_t fr[2][NF];  // k-step fragments, double-buffered: k-step ks of a stage in fr[ks & 1]
   // Iteration t multiplies stage t (slot t & 1).  During its first three k-steps it writes stage
   // t + 1 from set Rn into slot (t + 1) & 1 -- last read before the barrier of iteration t - 1 --
   // chunk by chunk, refilling each written register with stage t + 3 right after.  Loads complete
-  // in order, and before the write of chunk q exactly 31 of this wave's loads were issued after
-  // the one it needs (Rn's chunks after q, the other set's 16 and the q refills made since), so
-  // every wait is vmcnt(31).  The barrier comes before the last k-step: by then every wave's
+  // in order, and before the write of chunk q exactly 2 NQ - 1 of this wave's loads were issued
+  // after the one it needs (Rn's chunks after q, the other set's NQ and the q refills made
+  // since), so every wait is vmcnt(2 NQ - 1).  The barrier comes before the last k-step: by then every wave's
   // writes of stage t + 1 have landed and its reads of slot t & 1 are done (the last k-step's
   // fragments were read during the one before), so the last k-step's MFMAs cover the reads of
   // stage t + 1's first fragments.  Past the last stage the refill reads the last stage again and
@@ -435,21 +445,28 @@ __global__ __launch_bounds__(256, 1) void k_gemm_vr(const uint16_t* __restrict__
         __builtin_amdgcn_s_barrier();
         __builtin_amdgcn_sched_barrier(0);
       }
-      // chunks written in this k-step: 0-5, 6-10, 11-15 over the first three
-      const int q0 = (ks == 0) ? 0 : (ks == 1) ? 6 : 11;
-      const int nq = (ks == 0) ? 6 : (ks == 1 || ks == 2) ? 5 : 0;
+      // chunks written in this k-step: a third of the set in each of the first three
+      const int q0 = (ks * NQ + 2) / 3, q1 = ((ks + 1) * NQ + 2) / 3;
+      const int nq = (ks < 3) ? q1 - q0 : 0;
 #pragma unroll
-      for (int m = 0; m < 16; ++m) {
-        const int i = m >> 2, j = m & 3;
+      for (int m = 0; m < NM; ++m) {
+        const int i = m / TN, j = m % TN;
         acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(fr[ks & 1][i], fr[ks & 1][4 + j], acc[i][j], 0, 0, 0);
-        if ((m & 1) == 0) {  // the next k-step's fragments (the next stage's first after the last)
-          if (ks + 1 < BK / 16)
-            fr[(ks + 1) & 1][m >> 1] = *reinterpret_cast<const bf16x8_t*>(frag_addr(base, ks + 1, m >> 1));
-          else
-            fr[0][m >> 1] = *reinterpret_cast<const bf16x8_t*>(frag_addr(nbase, 0, m >> 1));
-        } else if ((m >> 1) < nq) {  // one chunk written, then its register refilled
+        // fragment f of the next k-step (the next stage's first after the last) after MFMA 2 f,
+        // or after the last MFMA for the fragments the even slots do not reach
+        const int f = ((m & 1) == 0) ? (m >> 1) : (m == NM - 1 ? NM / 2 : NF);
+        if (f < NF) {
+#pragma unroll
+          for (int g = f; g < ((m == NM - 1) ? NF : f + 1); ++g) {
+            if (ks + 1 < BK / 16)
+              fr[(ks + 1) & 1][g] = *reinterpret_cast<const bf16x8_t*>(frag_addr(base, ks + 1, g));
+            else
+              fr[0][g] = *reinterpret_cast<const bf16x8_t*>(frag_addr(nbase, 0, g));
+          }
+        }
+        if ((m & 1) == 1 && (m >> 1) < nq) {  // one chunk written, then its register refilled
           const int q = q0 + (m >> 1);
-          wait_vm<31>();
+          wait_vm<2 * NQ - 1>();
           write_one(Rn, q, (t + 1) & 1);
           load_one(Rn, q, kb_refill);
         }
@@ -461,19 +478,19 @@ __global__ __launch_bounds__(256, 1) void k_gemm_vr(const uint16_t* __restrict__
   // prologue (nk >= 3, the launcher's condition): stages 0 and 1 in flight, stage 0 into slot 0,
   // stage 2 into the freed set, then stage 0's first fragments
 #pragma unroll
-  for (int q = 0; q < 16; ++q) load_one(R0, q, kb0);
+  for (int q = 0; q < NQ; ++q) load_one(R0, q, kb0);
 #pragma unroll
-  for (int q = 0; q < 16; ++q) load_one(R1, q, kb0 + 1);
-  wait_vm<16>();
+  for (int q = 0; q < NQ; ++q) load_one(R1, q, kb0 + 1);
+  wait_vm<NQ>();
 #pragma unroll
-  for (int q = 0; q < 16; ++q) write_one(R0, q, 0);
+  for (int q = 0; q < NQ; ++q) write_one(R0, q, 0);
   __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
-  for (int q = 0; q < 16; ++q) load_one(R0, q, kb0 + 2);
+  for (int q = 0; q < NQ; ++q) load_one(R0, q, kb0 + 2);
   __builtin_amdgcn_s_waitcnt(0xc07f);
   __builtin_amdgcn_s_barrier();
 #pragma unroll
-  for (int f = 0; f < 8; ++f) fr[0][f] = *reinterpret_cast<const bf16x8_t*>(frag_addr(smem, 0, f));
+  for (int f = 0; f < NF; ++f) fr[0][f] = *reinterpret_cast<const bf16x8_t*>(frag_addr(smem, 0, f));
   int t = 0;
   for (; t + 1 < nk; t += 2) {  // stage t + 1 is in set 1, stage t + 2 in set 0
     iteration(t, R1);
@@ -680,6 +697,7 @@ GemmPlan gemm_plan(int dtype, int M, int N, int K, bool swiglu) {
         p.wn = 3;  // 12 waves, 8 of them issuing the tile loads
         p.pd = 12;
         p.ilv = 1;
+        p.vr = M >= 256;  // through registers: 1-3% faster at 512 and 820 rows
       } else if (N % 128 == 0) {  // 128 outputs over 128-row tiles (Dream-7B's F = 18944)
         p.bn = 256;
         p.wm = 2;
@@ -714,6 +732,7 @@ GemmPlan gemm_plan(int dtype, int M, int N, int K, bool swiglu) {
       if (big_wgs >= kWideTileWgs && wgs192 > 0 && round_fill(wgs192) > round_fill(big_wgs)) {
         p.bn = 192;
         p.wn = 3;
+        p.vr = 1;  // through registers: Dream-7B's QKV at 8192 rows 282.5 -> 269.6 us
         return p;
       }
       // from thousands of rows on, through registers over four waves (k_gemm_vr): 4-8% faster
@@ -727,6 +746,9 @@ GemmPlan gemm_plan(int dtype, int M, int N, int K, bool swiglu) {
       p.wm = (p.bn == 192) ? 4 : 2;
       p.wn = (p.bn == 192) ? 3 : 4;
       p.pd = 12;
+      // 192 columns through registers (k_gemm_vr): QKV 57.2 -> 55.0 us at 512 rows (2 K splits),
+      // 105.7 -> 100.9 us at 820 rows
+      p.vr = (p.bn == 192 && M >= 256) ? 1 : 0;
       target = 192;
     } else if (K >= 2 * N && N % 128 == 0 && K / (64 * 4) >= 3) {
       // long reductions into narrow outputs (the down projection): a 4-way K split, 2-way
@@ -772,19 +794,18 @@ static hipError_t launch_lds(const GemmPlan& p, const void* A, const void* W, fl
   return hipGetLastError();
 }
 
-template <int EPI>
+template <int EPI, int BN>
 static hipError_t launch_vr(const GemmPlan& p, const void* A, const void* W, float* C, void* H, int M, int N, int K,
                             const int32_t* n_active, int k_max, hipStream_t s) {
-  // 32-bit buffer offsets within one tile: 256 rows of A, and 256 weight rows (plain) or the
-  // gate..up span F + 128 rows (SwiGLU); every split fills the three-stage prologue; whole row
+  // 32-bit buffer offsets within one tile: 256 rows of A, and BN weight rows (plain) or the
+  // gate..up span F + BN / 2 rows (SwiGLU); every split fills the three-stage prologue; whole row
   // tiles of loads (the last one moved up), whole weight tiles
-  const long w_span = EPI == 0 ? 256 : (long)N + 128;
-  if (256L * K * 2 > 0x7fffffffL || w_span * K * 2 > 0x7fffffffL || K / 64 / p.splits < 3 || M < 256 ||
-      (EPI == 0 && N % 256) || (EPI != 0 && N % 128))
+  const int ncols = EPI == 0 ? BN : BN / 2;
+  const long w_span = EPI == 0 ? BN : (long)N + BN / 2;
+  if (256L * K * 2 > 0x7fffffffL || w_span * K * 2 > 0x7fffffffL || K / 64 / p.splits < 3 || M < 256 || N % ncols)
     return hipErrorInvalidValue;
-  const int ncols = EPI == 0 ? 256 : 128;
   const int tm = (M + 255) / 256, tn = N / ncols;
-  hipLaunchKernelGGL((k_gemm_vr<EPI>), dim3(tm * tn * p.splits), dim3(256), 0, s, (const uint16_t*)A,
+  hipLaunchKernelGGL((k_gemm_vr<EPI, BN>), dim3(tm * tn * p.splits), dim3(256), 0, s, (const uint16_t*)A,
                      (const uint16_t*)W, C, (uint16_t*)H, M, N, K, p.splits, tm, tn, n_active, k_max);
   return hipGetLastError();
 }
@@ -800,8 +821,10 @@ hipError_t launch_gemm(int dtype, const GemmPlan& p, const void* A, const void* 
   }
   if (K % 64 != 0) return hipErrorInvalidValue;
   if (p.vr) {
-    if (p.bm != 256 || p.bn != 256 || p.bk != 64 || p.ilv) return hipErrorInvalidValue;
-    return launch_vr<0>(p, A, W, C, nullptr, M, N, K, n_active, k_max, s);
+    if (p.bm != 256 || p.bk != 64 || p.ilv) return hipErrorInvalidValue;
+    if (p.bn == 256) return launch_vr<0, 256>(p, A, W, C, nullptr, M, N, K, n_active, k_max, s);
+    if (p.bn == 192) return launch_vr<0, 192>(p, A, W, C, nullptr, M, N, K, n_active, k_max, s);
+    return hipErrorInvalidValue;
   }
   // 256 x 192 over 4 x 3 wavefronts: the first 8 issue the tile loads (12 would not divide them)
   if (p.bm == 256 && p.bn == 192 && p.bk == 64 && p.pd == 12 && p.kg == 1 && p.wm == 4 && p.wn == 3)
@@ -822,8 +845,10 @@ hipError_t launch_gemm_swiglu(const GemmPlan& p, const void* A, const void* W_ga
   if (M <= 0 || F <= 0) return hipSuccess;
   if (K % 64 != 0 || F % (p.bn / 2) != 0 || p.splits != 1) return hipErrorInvalidValue;
   if (p.vr) {
-    if (p.bm != 256 || p.bn != 256 || p.bk != 64 || !p.ilv) return hipErrorInvalidValue;
-    return launch_vr<2>(p, A, W_gate_up, nullptr, H, M, F, K, n_active, k_max, s);
+    if (p.bm != 256 || p.bk != 64 || !p.ilv) return hipErrorInvalidValue;
+    if (p.bn == 256) return launch_vr<2, 256>(p, A, W_gate_up, nullptr, H, M, F, K, n_active, k_max, s);
+    if (p.bn == 192) return launch_vr<2, 192>(p, A, W_gate_up, nullptr, H, M, F, K, n_active, k_max, s);
+    return hipErrorInvalidValue;
   }
   if (p.ilv && p.bm == 256 && p.bn == 192 && p.bk == 64 && p.pd == 12 && p.kg == 1 && p.wm == 4 && p.wn == 3)
     return launch_lds<256, 192, 2, 2, 1, 4, 3, 8>(p, A, W_gate_up, nullptr, H, M, F, K, n_active, k_max, s);
