@@ -19,6 +19,11 @@
 // tiles, walked in groups of four row tiles, so the workgroups running together
 // on an XCD share both operands' k-slabs through its L2.
 //
+// Register-staged variant (k_gemm_vr, the 256 x 192 plans and products of
+// thousands of rows): four wavefronts, one per SIMD, stage the tiles through two
+// register sets two K stages ahead into a two-slot LDS ring, with every other
+// instruction placed between two MFMAs; same layout, k order and results.
+//
 // fp32 path (small fp32 models): LDS-tiled FMA kernel, 64x64 tiles.
 #include <type_traits>
 
