@@ -19,8 +19,8 @@
 // tiles, walked in groups of four row tiles, so the workgroups running together
 // on an XCD share both operands' k-slabs through its L2.
 //
-// Register-staged variant (k_gemm_vr, the 256 x 192 plans and products of
-// thousands of rows): four wavefronts, one per SIMD, stage the tiles through two
+// Register-staged variant (k_gemm_vr, the 256-row plans from 512 rows on, 256 x 256
+// tiles from thousands of rows on): four wavefronts, one per SIMD, stage the tiles through two
 // register sets two K stages ahead into a two-slot LDS ring, with every other
 // instruction placed between two MFMAs; same layout, k order and results.
 //
@@ -349,7 +349,8 @@ __global__ __launch_bounds__(64 * WM * WN * KG, OCC) void k_gemm_lds(const uint1
 // 12-wave direct-to-LDS kernel: QKV 57.2 -> 55.0 us at 512 rows, 105.7 -> 100.9 at 820, 282.5 ->
 // 269.6 at 8192 (Dream-7B); gate/up + SwiGLU 115.5 -> 111.4 at 512, 213.1 -> 210.7 at 820.  At
 // 512 and 820 rows 256 x 256 tiles leave too many CUs idle and are slower.
-// BN = 192 (three column blocks per wave, 14 chunks per register set) serves the 256 x 192 plans.
+// BN = 192 (three column blocks per wave, 14 chunks per register set) serves the 256 x 192 plans,
+// BN = 128 (two, 12 chunks) the 256 x 128 split-K plans of long reductions into narrow outputs.
 template <int EPI, int BN>
 __global__ __launch_bounds__(256, 1) void k_gemm_vr(const uint16_t* __restrict__ A, const uint16_t* __restrict__ W,
                                                     float* __restrict__ C, uint16_t* __restrict__ H, int M, int N, int K,
@@ -360,7 +361,7 @@ __global__ __launch_bounds__(256, 1) void k_gemm_vr(const uint16_t* __restrict__
   constexpr int NQ = 8 + NB;   // chunks per register set
   constexpr int NF = 4 + TN;   // fragments per k-step
   constexpr int NM = TM * TN;  // MFMAs per k-step
-  static_assert(BN == 256 || BN == 192, "256- or 192-column tiles");
+  static_assert(BN == 256 || BN == 192 || BN == 128, "256-, 192- or 128-column tiles");
   constexpr int STAGE = (BM + BN) * BK;  // elements per ring slot
   typedef unsigned u32x4_t __attribute__((ext_vector_type(4)));
   __shared__ __attribute__((aligned(1024))) uint16_t smem[2 * STAGE];  // 128 KB
@@ -764,6 +765,11 @@ GemmPlan gemm_plan(int dtype, int M, int N, int K, bool swiglu) {
       p.wn = 4;
       p.pd = 13;
       p.splits = ((long)((M + 255) / 256) * ((N + 127) / 128) >= 768) ? 2 : 4;
+      // through registers (k_gemm_vr, two 32-column blocks per wave): 60.4 -> 56.7 us at 512 rows,
+      // 122.8 -> 116.6 at 820 (launches alternated, bit-identical); whole runs within their noise
+      // (default generation 750.3-751.4 against 749.7-750.4 tokens/s, long-context run 471.7-473.1
+      // against 473.5-474.2, same box)
+      p.vr = (M >= 256) ? 1 : 0;
       return p;
     } else if (N % 192 == 0 && N <= 32768) {
       // QKV-like widths below the wide range (Dream-7B's 4608): 128 x 192 over 4 x 2 waves,
@@ -829,6 +835,7 @@ hipError_t launch_gemm(int dtype, const GemmPlan& p, const void* A, const void* 
     if (p.bm != 256 || p.bk != 64 || p.ilv) return hipErrorInvalidValue;
     if (p.bn == 256) return launch_vr<0, 256>(p, A, W, C, nullptr, M, N, K, n_active, k_max, s);
     if (p.bn == 192) return launch_vr<0, 192>(p, A, W, C, nullptr, M, N, K, n_active, k_max, s);
+    if (p.bn == 128) return launch_vr<0, 128>(p, A, W, C, nullptr, M, N, K, n_active, k_max, s);
     return hipErrorInvalidValue;
   }
   // 256 x 192 over 4 x 3 wavefronts: the first 8 issue the tile loads (12 would not divide them)
