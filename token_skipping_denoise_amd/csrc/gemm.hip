@@ -327,30 +327,27 @@ __global__ __launch_bounds__(64 * WM * WN * KG, OCC) void k_gemm_lds(const uint1
   }
 }
 
-// Thousands of rows, register-staged: 256 x 256 tiles over four wavefronts (2 x 2, one per SIMD,
-// 128 x 128 wave tiles whose 256 accumulators per lane sit in the AGPRs).  The direct-to-LDS
-// kernel above keeps one 64-element K stage in flight beside the one being multiplied (two
-// 64 KB stages fill most of the LDS); here the stage loads go to registers first, in two
-// register sets (each wave loads a quarter of a stage: 8 rows of A and 8 of W, 16 B per lane
-// each), so two stages (128 KB per CU) are in flight while one is multiplied from a two-slot LDS
-// ring.  With one wave per SIMD nothing else covers a wave's own waits, so every k-step issues
-// its 16 MFMAs one at a time with the other work between them: the 8 LDS fragment reads of the
-// next k-step, 4 LDS writes of the next stage's register set and 4 loads that refill the written
-// registers with the stage after it.  Tiles of 256 x 256 serve thousands of rows; 256 x 192 (three
-// column blocks per wave) the plans of that width from 512 rows on.  The LDS layout, fragment
-// reads, k order and epilogues
-// (EPI 0: fp32 partials; EPI 2: SwiGLU over gate/up rows interleaved in 16s) are those of
-// k_gemm_lds, so both kernels give bit-identical results.
-// Measured against the 16-wave kernel on the same inputs, launches alternated, median of 25:
-// Dream-7B at 8192 rows down (2 splits) 992 -> 928 us and O 226 -> 212 us (against its
-// 128 x 128 plan); LLaDA-8B at 16384 rows QKV 1360 -> 1294, O 492 -> 453, down 1372 -> 1318 us
-// and the LM head 13.89 -> 13.21 ms; the fused SwiGLU product the same either way alone (1810
-// against 1817 us at 8192 rows) but faster inside whole runs.  256 x 192 tiles against the
-// 12-wave direct-to-LDS kernel: QKV 57.2 -> 55.0 us at 512 rows, 105.7 -> 100.9 at 820, 282.5 ->
-// 269.6 at 8192 (Dream-7B); gate/up + SwiGLU 115.5 -> 111.4 at 512, 213.1 -> 210.7 at 820.  At
-// 512 and 820 rows 256 x 256 tiles leave too many CUs idle and are slower.
-// BN = 192 (three column blocks per wave, 14 chunks per register set) serves the 256 x 192 plans,
-// BN = 128 (two, 12 chunks) the 256 x 128 split-K plans of long reductions into narrow outputs.
+// Register-staged: 256 x BN tiles (BN = 256, 192 or 128) over four wavefronts (2 x 2, one per
+// SIMD, 128 x BN/2 wave tiles whose accumulators, up to 256 per lane, sit in the AGPRs).  The
+// direct-to-LDS kernel above keeps one 64-element K stage in flight beside the one being
+// multiplied (two 64 KB stages fill most of the LDS); here the stage loads go to registers first,
+// in two register sets (each wave loads a quarter of a stage: 8 rows of A and BN / 32 of W, 16 B
+// per lane each), so two stages (up to 128 KB per CU) are in flight while one is multiplied from
+// a two-slot LDS ring.  With one wave per SIMD nothing else covers a wave's own waits, so every
+// k-step issues its 4 x BN / 64 MFMAs one at a time with the other work between them: the LDS
+// fragment reads of the next k-step, a third of the LDS writes of the next stage's register set
+// and the loads that refill the written registers with the stage after it.  The LDS layout,
+// fragment reads, k order and epilogues (EPI 0: fp32 partials; EPI 2: SwiGLU over gate/up rows
+// interleaved in 16s) are those of k_gemm_lds, so both kernels give bit-identical results.
+// Measured against the direct-to-LDS kernels on the same inputs, launches alternated, median of
+// 25.  256 x 256 against 16 waves: Dream-7B at 8192 rows down (2 splits) 992 -> 928 us and O
+// 226 -> 212 us (against its 128 x 128 plan); LLaDA-8B at 16384 rows QKV 1360 -> 1294, O
+// 492 -> 453, down 1372 -> 1318 us and the LM head 13.89 -> 13.21 ms; the fused SwiGLU product
+// the same either way alone (1810 against 1817 us at 8192 rows) but faster inside whole runs; at
+// 512 and 820 rows these tiles leave too many CUs idle and are slower.  256 x 192 against 12
+// waves: QKV 57.2 -> 55.0 us at 512 rows, 105.7 -> 100.9 at 820, 282.5 -> 269.6 at 8192
+// (Dream-7B); gate/up + SwiGLU 115.5 -> 111.4 at 512, 213.1 -> 210.7 at 820.  256 x 128 against
+// 16 waves: the split-K down product 60.4 -> 56.7 us at 512 rows, 122.8 -> 116.6 at 820.
 template <int EPI, int BN>
 __global__ __launch_bounds__(256, 1) void k_gemm_vr(const uint16_t* __restrict__ A, const uint16_t* __restrict__ W,
                                                     float* __restrict__ C, uint16_t* __restrict__ H, int M, int N, int K,
@@ -364,7 +361,7 @@ __global__ __launch_bounds__(256, 1) void k_gemm_vr(const uint16_t* __restrict__
   static_assert(BN == 256 || BN == 192 || BN == 128, "256-, 192- or 128-column tiles");
   constexpr int STAGE = (BM + BN) * BK;  // elements per ring slot
   typedef unsigned u32x4_t __attribute__((ext_vector_type(4)));
-  __shared__ __attribute__((aligned(1024))) uint16_t smem[2 * STAGE];  // 128 KB
+  __shared__ __attribute__((aligned(1024))) uint16_t smem[2 * STAGE];  // 96-128 KB
 
   int tmi, tni, sp;
   decode_tile(tiles_m * tiles_n * splits, tiles_m, tiles_n, tmi, tni, sp);
@@ -383,14 +380,14 @@ __global__ __launch_bounds__(256, 1) void k_gemm_vr(const uint16_t* __restrict__
   const int wr0 = (EPI == 0) ? tni * BN : h0;
   // The last row tile is moved up to end at row M (the launcher ensures M >= 256): it multiplies
   // rows a0 .. a0 + 255 and stores only those from m0 on, so every load stays inside A.  Weight
-  // rows never pass the end (N a multiple of 256, or F of 128 for SwiGLU).
+  // rows never pass the end (N a multiple of BN, or F of BN / 2 for SwiGLU).
   const int a0 = min(m0, M - BM);
   const uint16_t* a_base = A + (long)a0 * K;
   const uint16_t* w_base = W + (long)wr0 * K;
   const __amdgpu_buffer_rsrc_t ra = __builtin_amdgcn_make_buffer_rsrc((void*)a_base, (short)0, BM * K * 2, 0x00020000);
   const __amdgpu_buffer_rsrc_t rw = __builtin_amdgcn_make_buffer_rsrc(
       (void*)w_base, (short)0, (int)min((long)(w_rows - wr0) * K * 2, 0x7fffffffL), 0x00020000);
-  // this lane's loads: chunk c of tile rows rb + 32 i (i < 8) of both operands.  The lane's part
+  // this lane's loads: chunk c of A rows rb + 32 i (i < 8) and of NB weight rows.  The lane's part
   // of the byte offset is one VGPR per operand; the row step and k go in the scalar offset.
   const int c = tid & 7, rb = tid >> 3;
   // weight row of tile row rb + 32 i: wb0 + i * wstep (SwiGLU: 16 gate rows, then the 16 matching
